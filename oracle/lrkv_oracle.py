@@ -1,0 +1,536 @@
+"""Plain float64 CPU oracle for Low-Rank Key Value attention (LRKV).
+
+TEST INFRASTRUCTURE ONLY.  This module is the checker, not the product.  It may be
+imported only by ``tests/``, by ``__graft_entry__.smoke()`` and by the CPU-baseline leg
+of ``bench.py``.  The library in ``factored_rank_kv_amd/`` never imports, links or runs
+it, and it shares no code with that library.
+
+What it follows
+---------------
+"LRKV notes" below means the web page *Low-Rank Key Value Attention｜共享缓存与逐头残差*
+(Zhongzhu Zhou's reading notes on O'Neill, Clancy, Matskevichus and Reid, arXiv 2601.11471).
+The method reaches exactly, up to rounding order, the result of plain softmax attention
+over the reconstructed per-head keys and values (LRKV notes §3, the associativity argument
+around eq 6-7 and the worked 2-D example).  So the oracle *is* that plain definition:
+
+1. page walk: read the cached rows of one request out of the paged pool;
+2. reconstruct K_h = S_K + R_K[h] B_K[h]^T and V_h = S_V + R_V[h] B_V[h]^T (eq 2-5);
+3. score each visible key with q_h k_j^T / sqrt(d_h) (§2, the attention definition and the
+   remark that the divisor is the full head width);
+4. one softmax over the visible positions (§2);
+5. o_h = sum_j a_j v_j (§2).
+
+A second, independent coding follows Algorithm 2 of §3 step by step (private query formed
+once, summed branch scores, one softmax, both value branches reduced with the same weights,
+one expansion through B_V[h]^T).  It is used only to check the first one.
+
+The append oracle follows Algorithm 1 of §3: the shared projections X W_S_K and X W_S_V and
+the per-head projections X U_K[h], X U_V[h], computed in float64 and rounded to nearest
+even into the cache dtype, then placed at the rows' token positions.
+
+The cache-size and cost formulas of §4 (eq 9, rank budget, parameter ratio, decode
+arithmetic ratio, tensor-parallel replication) are written with exact rationals.
+
+Readings where the page is silent (each is also listed in the design notes):
+* the visible set of query row i of request b is positions j <= T_b - q_len + i, so a
+  single-row decode sees all T_b cached tokens including the token just appended;
+* masked positions are removed by selection, never multiplied by zero, so whatever bytes sit
+  in unused page slots cannot leak into a result;
+* a request with no visible token returns zeros;
+* Algorithm 2's scaling step names the square root of the head width without saying
+  whether to multiply or divide; the oracle divides by sqrt(d_h), as the attention formula
+  of §2 does, and never uses sqrt(r).
+
+Parity pins: every function here is pinned by tests/test_oracle.py against values the page
+prints (worked example, cache percentages and MiB figures), closed forms, textbook library
+routines (torch scaled-dot-product attention in float64 for the r = 0 and r = d_h cases)
+and brute force on tiny inputs.  Nothing here is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from fractions import Fraction
+
+import numpy as np
+
+F32 = 0
+BF16 = 1
+_ELEM_BYTES = {F32: 4, BF16: 2}
+
+# ---------------------------------------------------------------------------------------
+# Element encodings
+# ---------------------------------------------------------------------------------------
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact bfloat16 -> float64: the 16 stored bits are the high half of a binary32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16, ties to even; return the 16-bit codes.
+
+    Written from the format's definition (8 significant bits, binary32 exponent range),
+    rounding the float64 value once (no detour through binary32, which could round twice).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    flat_x = x.reshape(-1)
+    flat_o = out.reshape(-1)
+    nan = np.isnan(flat_x)
+    flat_o[nan] = 0x7FC0
+    fin = ~nan
+    v = flat_x[fin]
+    sign = np.signbit(v)
+    a = np.abs(v)
+    # exponent e with 2^(e-1) <= a < 2^e (frexp mantissa in [0.5, 1)); zeros give e = 0
+    _, e = np.frexp(a)
+    # spacing of bf16 numbers in [2^(e-1), 2^e) is 2^(e-1-7); subnormals share 2^-133
+    e_eff = np.maximum(e, -125)
+    spacing = np.ldexp(1.0, (e_eff - 8).astype(np.int64))
+    q = np.rint(a / spacing)  # numpy rint rounds half to even
+    r = q * spacing  # exact: q has at most 9 significant bits
+    r = np.where(r >= 2.0**128, np.inf, r)  # past the largest finite bf16 magnitude
+    r = np.where(np.isinf(a), np.inf, r)
+    bits = (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    bits = np.where(sign, bits | np.uint16(0x8000), bits)
+    flat_o[fin] = bits
+    return out
+
+
+def decode_elems(raw: np.ndarray, dtype: int) -> np.ndarray:
+    """Bytes of a cache region -> float64 values (exact widening)."""
+    raw = np.ascontiguousarray(raw, dtype=np.uint8)
+    if dtype == BF16:
+        return bf16_bits_to_f64(raw.view(np.uint16))
+    if dtype == F32:
+        return raw.view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype}")
+
+
+def encode_elems(x: np.ndarray, dtype: int) -> np.ndarray:
+    """float64 values -> bytes in the cache dtype, rounding to nearest even."""
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == BF16:
+        return f64_to_bf16_bits(x).view(np.uint8).reshape(-1)
+    if dtype == F32:
+        return x.astype(np.float32).view(np.uint8).reshape(-1)
+    raise ValueError(f"unknown dtype {dtype}")
+
+
+def round_to_dtype(x: np.ndarray, dtype: int) -> np.ndarray:
+    """float64 -> nearest value of the cache dtype, returned as float64."""
+    return decode_elems(encode_elems(x, dtype), dtype).reshape(np.shape(x))
+
+
+# ---------------------------------------------------------------------------------------
+# Factored paged cache layout (LRKV notes §3: shared and private rows of one token share
+# one page id, so token numbering and page lifetime are identical for both paths)
+# ---------------------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class Layout:
+    num_heads: int  # H
+    head_dim: int  # d_h, width of a shared row S_K[j], S_V[j]
+    rank: int  # r, width of a private row R_K[h, j], R_V[h, j]
+    page_size: int  # P tokens per page
+    dtype: int  # F32 or BF16
+
+    @property
+    def elem_bytes(self) -> int:
+        return _ELEM_BYTES[self.dtype]
+
+    @property
+    def chunk(self) -> int:
+        """Elements per 16-byte chunk."""
+        return 16 // self.elem_bytes
+
+
+def page_elems(L: Layout) -> int:
+    """Elements in one page: P tokens x (2 shared rows of d_h + 2H private rows of r)."""
+    return L.page_size * 2 * (L.head_dim + L.num_heads * L.rank)
+
+
+def page_bytes(L: Layout) -> int:
+    return page_elems(L) * L.elem_bytes
+
+
+def section_base(L: Layout, section: str, head: int = 0) -> int:
+    """Element offset, inside a page, of a section (per head for the private ones).
+
+    Order inside a page: S_K block, S_V block, R_K blocks for heads 0..H-1, R_V blocks for
+    heads 0..H-1.  A shared block holds P x d_h elements, a private block P x r.
+    """
+    P, dh, r, H = L.page_size, L.head_dim, L.rank, L.num_heads
+    if section == "SK":
+        return 0
+    if section == "SV":
+        return P * dh
+    if section == "RK":
+        return 2 * P * dh + head * P * r
+    if section == "RV":
+        return 2 * P * dh + H * P * r + head * P * r
+    raise ValueError(section)
+
+
+def in_block_index(L: Layout, width: int, t: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """Element index of (token slot t, feature k) inside a block of P rows of `width`.
+
+    Chunk-major: the block is a sequence of 16-byte chunk columns; chunk column c holds the
+    P tokens' features [c*C, (c+1)*C) back to back, C = 16 / element bytes.
+    """
+    C = L.chunk
+    if width % C:
+        raise ValueError(f"width {width} is not a multiple of the {C}-element chunk")
+    return ((k // C) * L.page_size + t) * C + (k % C)
+
+
+def _positions_to_pages(L: Layout, table_row: np.ndarray, n: int):
+    j = np.arange(n)
+    return np.asarray(table_row, dtype=np.int64)[j // L.page_size], j % L.page_size
+
+
+def _read_block(pool, L: Layout, pages, t, section, head, width):
+    pe = page_elems(L)
+    b = L.elem_bytes
+    k = np.arange(width)
+    idx = (pages[:, None] * pe + section_base(L, section, head)
+           + in_block_index(L, width, t[:, None], k[None, :]))
+    byte_idx = (idx[..., None] * b + np.arange(b)).reshape(-1)
+    return decode_elems(pool[byte_idx], L.dtype).reshape(len(pages), width)
+
+
+def gather_shared(pool, L: Layout, table_row, n_tokens: int):
+    """Page walk for the shared rows of tokens 0..n_tokens-1: S_K, S_V as [n, d_h] float64.
+
+    Token j lives in page table_row[j // P], slot j % P.
+    """
+    pool = np.asarray(pool, dtype=np.uint8).reshape(-1)
+    pages, t = _positions_to_pages(L, table_row, n_tokens)
+    return (_read_block(pool, L, pages, t, "SK", 0, L.head_dim),
+            _read_block(pool, L, pages, t, "SV", 0, L.head_dim))
+
+
+def gather_private(pool, L: Layout, table_row, n_tokens: int, h: int):
+    """Page walk for head h's private rows: R_K[h], R_V[h] as [n, r] float64."""
+    pool = np.asarray(pool, dtype=np.uint8).reshape(-1)
+    if L.rank == 0:
+        return np.zeros((n_tokens, 0)), np.zeros((n_tokens, 0))
+    pages, t = _positions_to_pages(L, table_row, n_tokens)
+    return (_read_block(pool, L, pages, t, "RK", h, L.rank),
+            _read_block(pool, L, pages, t, "RV", h, L.rank))
+
+
+def gather_request(pool: np.ndarray, L: Layout, table_row: np.ndarray, n_tokens: int) -> dict:
+    """Page walk over every section: S_K, S_V [n, d_h] and R_K, R_V [H, n, r], float64."""
+    SK, SV = gather_shared(pool, L, table_row, n_tokens)
+    priv = [gather_private(pool, L, table_row, n_tokens, h) for h in range(L.num_heads)]
+    return {"SK": SK, "SV": SV,
+            "RK": np.stack([p[0] for p in priv]) if priv else np.zeros((0, n_tokens, L.rank)),
+            "RV": np.stack([p[1] for p in priv]) if priv else np.zeros((0, n_tokens, L.rank))}
+
+
+def storage_dtype(L: Layout):
+    """numpy type holding one cache element's bits."""
+    return np.uint16 if L.dtype == BF16 else np.uint32
+
+
+def pack_pool(L: Layout, page_table, lens, SK, SV, RK, RV, num_pages: int, fill: int = 0):
+    """Bulk placement of whole requests into a fresh pool (the placement rule of
+    `write_rows`, coded separately as a reshape per page so the two check each other).
+
+    SK, SV [sum(lens), d_h] and RK, RV [sum(lens), H, r] hold element *codes* (uint16
+    bfloat16 codes, or uint32 float32 bit patterns), requests back to back in order.
+    Every slot not written (pages no request owns, slots past a request's last token) holds
+    the code `fill`.  Returns the pool as uint8 [num_pages * page_bytes].
+    """
+    st = storage_dtype(L)
+    P, dh, r, H, C = L.page_size, L.head_dim, L.rank, L.num_heads, L.chunk
+    pe = page_elems(L)
+    pool = np.full((num_pages, pe), fill, dtype=st)
+    off = 0
+    for b, T in enumerate(lens):
+        T = int(T)
+        n_pages = -(-T // P)
+        if n_pages == 0:
+            continue
+        ids = np.asarray(page_table[b][:n_pages], dtype=np.int64)
+
+        def blocks(rows, width, heads):
+            # rows [T, heads, width] -> [n_pages, heads * width * P] in chunk-major order
+            padded = np.full((n_pages * P, heads, width), fill, dtype=st)
+            padded[:T] = rows.reshape(T, heads, width)
+            x = padded.reshape(n_pages, P, heads, width // C, C)
+            return x.transpose(0, 2, 3, 1, 4).reshape(n_pages, heads * width * P)
+
+        sk = np.asarray(SK[off:off + T]).view(st) if np.asarray(SK).dtype != st else SK[off:off + T]
+        sv = np.asarray(SV[off:off + T]).view(st) if np.asarray(SV).dtype != st else SV[off:off + T]
+        pool[ids, 0:P * dh] = blocks(sk, dh, 1)
+        pool[ids, P * dh:2 * P * dh] = blocks(sv, dh, 1)
+        if r:
+            rk = np.asarray(RK[off:off + T])
+            rv = np.asarray(RV[off:off + T])
+            rk = rk.view(st) if rk.dtype != st else rk
+            rv = rv.view(st) if rv.dtype != st else rv
+            base = 2 * P * dh
+            pool[ids, base:base + H * P * r] = blocks(rk, r, H)
+            pool[ids, base + H * P * r:base + 2 * H * P * r] = blocks(rv, r, H)
+        off += T
+    return pool.view(np.uint8).reshape(-1)
+
+
+def write_rows(pool: np.ndarray, L: Layout, page_table: np.ndarray, row_req, row_pos,
+               SK, SV, RK, RV) -> np.ndarray:
+    """Place already-rounded rows at their (request, position) in a copy of the pool.
+
+    SK, SV: [n, d_h]; RK, RV: [n, H, r] (float64 values exactly representable in the dtype).
+    Row n goes to page page_table[row_req[n]][row_pos[n] // P], slot row_pos[n] % P, in each
+    section; only those elements change.  Rows must address distinct positions.
+    """
+    out = np.array(pool, dtype=np.uint8, copy=True).reshape(-1)
+    elems = out.view(storage_dtype(L))
+    pe = page_elems(L)
+    H, dh, r = L.num_heads, L.head_dim, L.rank
+    row_req = np.asarray(row_req, np.int64)
+    row_pos = np.asarray(row_pos, np.int64)
+    pages = np.asarray(page_table, np.int64)[row_req, row_pos // L.page_size]
+    t = row_pos % L.page_size
+
+    def put(section, head, width, vals):
+        idx = (pages[:, None] * pe + section_base(L, section, head)
+               + in_block_index(L, width, t[:, None], np.arange(width)[None, :]))
+        elems[idx.reshape(-1)] = encode_elems(vals, L.dtype).view(storage_dtype(L))
+
+    put("SK", 0, dh, np.asarray(SK))
+    put("SV", 0, dh, np.asarray(SV))
+    for h in range(H if r else 0):
+        put("RK", h, r, np.asarray(RK)[:, h])
+        put("RV", h, r, np.asarray(RV)[:, h])
+    return out
+
+
+# ---------------------------------------------------------------------------------------
+# Algorithm 1: build / append the factored cache (LRKV notes §3)
+# ---------------------------------------------------------------------------------------
+
+
+def project_rows(X, W_SK, W_SV, U_K, U_V):
+    """Factored projections of new rows, float64 (eq 2-5; Algorithm 1 steps 02, 04, 05).
+
+    X [n, d]; W_SK, W_SV [d, d_h]; U_K, U_V [d, H, r].
+    Returns S_K, S_V [n, d_h] and R_K, R_V [n, H, r].
+    """
+    X = np.asarray(X, np.float64)
+    SK = X @ np.asarray(W_SK, np.float64)
+    SV = X @ np.asarray(W_SV, np.float64)
+    d, H, r = np.shape(U_K)
+    RK = (X @ np.asarray(U_K, np.float64).reshape(d, H * r)).reshape(-1, H, r)
+    RV = (X @ np.asarray(U_V, np.float64).reshape(d, H * r)).reshape(-1, H, r)
+    return SK, SV, RK, RV
+
+
+def append_reference(pool, L: Layout, X, W_SK, W_SV, U_K, U_V, row_req, row_pos, page_table):
+    """Expected pool after appending rows X (Algorithm 1): project in float64, round each
+    value to nearest even in the cache dtype, write it at the row's (page, slot) in all
+    four sections; every other byte keeps its old value."""
+    SK, SV, RK, RV = project_rows(X, W_SK, W_SV, U_K, U_V)
+    rnd = lambda a: round_to_dtype(a, L.dtype)
+    return write_rows(pool, L, np.asarray(page_table), np.asarray(row_req), np.asarray(row_pos),
+                      rnd(SK), rnd(SV), rnd(RK), rnd(RV))
+
+
+# ---------------------------------------------------------------------------------------
+# Plain attention over reconstructed keys / values (LRKV notes §2 and eq 2-5)
+# ---------------------------------------------------------------------------------------
+
+
+def reconstruct(S: np.ndarray, R: np.ndarray, Bm: np.ndarray) -> np.ndarray:
+    """Full per-head rows from the factored cache: S + R_h B_h^T (eq 2-5).
+
+    S [T, d_h]; R [H, T, r]; Bm [H, d_h, r]  ->  [H, T, d_h].
+    """
+    S = np.asarray(S, np.float64)
+    R = np.asarray(R, np.float64)
+    Bm = np.asarray(Bm, np.float64)
+    return S[None, :, :] + np.matmul(R, np.transpose(Bm, (0, 2, 1)))
+
+
+def softmax_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """Textbook single-query attention: a = softmax(K q * scale), o = a V (§2).
+
+    K, V hold only the visible rows.  With no visible row the result is zero.
+    """
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[1])
+    s = (K @ q) * scale
+    e = np.exp(s - s.max())  # subtracting the max changes nothing in exact arithmetic
+    a = e / e.sum()
+    return a @ V
+
+
+def visible_count(seq_len: int, q_len: int, i: int) -> int:
+    """Query row i of a request holding seq_len tokens sits at position seq_len - q_len + i
+    and sees positions 0..that position (causal mask of §2)."""
+    return max(0, min(seq_len, seq_len - q_len + i + 1))
+
+
+def decode_reference(L: Layout, q, B_K, B_V, pool, page_table, seq_lens, sample=None):
+    """Expected output of the LRKV decode call, by the plain definition.
+
+    q [B, q_len, H, d_h]; B_K, B_V [H, d_h, r]; page_table [B, max_pages]; seq_lens [B].
+    Returns float64 out [B, q_len, H, d_h].  With `sample` (an iterable of (b, i, h)), only
+    those entries are computed; the rest of the returned array is NaN.
+    """
+    q = np.asarray(q, np.float64)
+    Bn, q_len, H, dh = q.shape
+    out = np.full((Bn, q_len, H, dh), np.nan)
+    want = {}
+    if sample is None:
+        for b in range(Bn):
+            want[b] = {(i, h) for i in range(q_len) for h in range(H)}
+    else:
+        for b, i, h in sample:
+            want.setdefault(int(b), set()).add((int(i), int(h)))
+    scale = 1.0 / math.sqrt(dh)
+    BK = np.asarray(B_K, np.float64)
+    BV = np.asarray(B_V, np.float64)
+    for b, items in sorted(want.items()):
+        T = int(seq_lens[b])
+        SK, SV = gather_shared(pool, L, page_table[b], T)
+        for h in sorted({h for _, h in items}):
+            RK, RV = gather_private(pool, L, page_table[b], T, h)
+            K = reconstruct(SK, RK[None], BK[h:h + 1])[0]
+            V = reconstruct(SV, RV[None], BV[h:h + 1])[0]
+            for i, hh in sorted(items):
+                if hh != h:
+                    continue
+                n = visible_count(T, q_len, i)
+                out[b, i, h] = softmax_attention(q[b, i, h], K[:n], V[:n], scale)
+    return out
+
+
+def decode_algorithm2(L: Layout, q, B_K, B_V, pool, page_table, seq_lens):
+    """Second coding, used only to check `decode_reference`: Algorithm 2 of §3, per head.
+
+    p = q B_K[h] once; score_j = (q.S_K[j] + p.R_K[h, j]) / sqrt(d_h); one softmax over the
+    visible rows; a.S_V + (a.R_V[h]) B_V[h]^T.
+    """
+    q = np.asarray(q, np.float64)
+    Bn, q_len, H, dh = q.shape
+    BK = np.asarray(B_K, np.float64)
+    BV = np.asarray(B_V, np.float64)
+    out = np.zeros((Bn, q_len, H, dh))
+    for b in range(Bn):
+        T = int(seq_lens[b])
+        rows = gather_request(pool, L, page_table[b], T)
+        for i in range(q_len):
+            n = visible_count(T, q_len, i)
+            if n == 0:
+                continue
+            for h in range(H):
+                qh = q[b, i, h]
+                p = qh @ BK[h]  # private query, formed once for the whole history
+                shared = rows["SK"][:n] @ qh
+                private = rows["RK"][h, :n] @ p
+                s = (shared + private) / math.sqrt(dh)  # one score per position, then softmax
+                w = np.exp(s - s.max())
+                a = w / w.sum()
+                red_shared = a @ rows["SV"][:n]
+                red_private = a @ rows["RV"][h, :n]  # same weights as the shared branch
+                out[b, i, h] = red_shared + red_private @ BV[h].T  # expand once
+    return out
+
+
+def full_projection_kv(X, W_S, U, Bm):
+    """Per-head rows straight from eq 2: X (W_S + U_h B_h^T), never forming S or R.
+
+    X [n, d]; W_S [d, d_h]; U [d, H, r]; Bm [H, d_h, r]  ->  [H, n, d_h].
+    """
+    X = np.asarray(X, np.float64)
+    W_S = np.asarray(W_S, np.float64)
+    U = np.asarray(U, np.float64)
+    Bm = np.asarray(Bm, np.float64)
+    H = U.shape[1]
+    return np.stack([X @ (W_S + U[:, h, :] @ Bm[h].T) for h in range(H)])
+
+
+# ---------------------------------------------------------------------------------------
+# Blockwise online softmax and the merge of partial results (LRKV notes §3, the fused
+# blockwise paragraph after Algorithm 2: running max, exp-sum and two value accumulators,
+# all rescaled by one factor when the max moves; division by the exp-sum at the end)
+# ---------------------------------------------------------------------------------------
+
+
+def block_state(scores, SV, RV):
+    """State of one block of positions: (m, l, acc_S, acc_R) with m the block max,
+    l = sum exp(s - m), acc_S = sum exp(s - m) S_V[j], acc_R = sum exp(s - m) R_V[j]."""
+    s = np.asarray(scores, np.float64)
+    m = s.max()
+    e = np.exp(s - m)
+    return m, e.sum(), e @ np.asarray(SV, np.float64), e @ np.asarray(RV, np.float64)
+
+
+def merge_states(states):
+    """Combine block states: m* = max m_s, w_s = exp(m_s - m*), l = sum w_s l_s, and the
+    same weights on both accumulators."""
+    m_star = max(st[0] for st in states)
+    w = [math.exp(st[0] - m_star) for st in states]
+    l = sum(wi * st[1] for wi, st in zip(w, states))
+    acc_s = sum(wi * st[2] for wi, st in zip(w, states))
+    acc_r = sum(wi * st[3] for wi, st in zip(w, states))
+    return m_star, l, acc_s, acc_r
+
+
+def finish_state(state, BV_h):
+    """o = (acc_S + acc_R B_V[h]^T) / l (Algorithm 2 steps 08-09 without W_O)."""
+    _, l, acc_s, acc_r = state
+    return (acc_s + acc_r @ np.asarray(BV_h, np.float64).T) / l
+
+
+# ---------------------------------------------------------------------------------------
+# Cache size and cost models (LRKV notes §4), exact rationals
+# ---------------------------------------------------------------------------------------
+
+
+def lrkv_cache_bytes(b: int, N: int, tokens: int, d_h: int, H: int, r: int) -> int:
+    """eq 9: 2 b N (B T) (d_h + H r); `tokens` is B*T, or the sum of actual lengths."""
+    return 2 * b * N * tokens * (d_h + H * r)
+
+
+def mha_cache_bytes(b: int, N: int, tokens: int, d_h: int, H: int) -> int:
+    """Dense multi-head baseline of §4: 2 b N (B T) H d_h."""
+    return 2 * b * N * tokens * H * d_h
+
+
+def cache_ratio(H: int, r: int, d_h: int) -> Fraction:
+    """eq 9 ratio: 1/H + r/d_h."""
+    return Fraction(1, H) + Fraction(r, d_h)
+
+
+def rank_budget(d_h: int, c: Fraction, H: int) -> int:
+    """Largest rank whose cache stays within fraction c of the dense one: floor(d_h (c - 1/H))."""
+    return math.floor(Fraction(d_h) * (Fraction(c) - Fraction(1, H)))
+
+
+def param_ratio(H: int, r: int, d_h: int, d: int) -> Fraction:
+    """K/V projection parameters relative to dense: 1/H + (r/d_h)(1 + d_h/d)."""
+    return Fraction(1, H) + Fraction(r, d_h) * (1 + Fraction(d_h, d))
+
+
+def decode_arith_ratio(T: int, r: int, d_h: int) -> Fraction:
+    """Decode multiply-adds relative to dense: (2 T d_h + 2 T r + 2 r d_h) / (2 T d_h)."""
+    return Fraction(2 * T * d_h + 2 * T * r + 2 * r * d_h, 2 * T * d_h)
+
+
+def tp_replicated_ratio(P: int, H: int, r: int, d_h: int) -> Fraction:
+    """Total payload relative to dense when the shared rows are copied to P devices: P/H + r/d_h."""
+    return Fraction(P, H) + Fraction(r, d_h)
+
+
+def roofline_time(bytes_moved: float, flops: float, beta: float, phi: float) -> float:
+    """Lower bound of §4: time >= max(bytes / bandwidth, flops / compute rate)."""
+    return max(bytes_moved / beta, flops / phi)
