@@ -1,0 +1,142 @@
+"""Python binding of liblrkv.so, the LRKV C-ABI library (include/lrkv.h).
+
+The functions below carry the C entry points' names and argument order and do argument
+marshalling only: a pointer argument may be a torch tensor (its data_ptr() is passed), an
+int address or None; `stream` defaults to torch's current HIP stream.  Every step of the
+computation runs in the library's HIP kernels.  A non-OK status raises LRKVError.
+
+The library is built in-tree by ``python -m factored_rank_kv_amd.build``.  It is loaded on
+the first call; without it every call raises ImportError.  There is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblrkv.so")
+
+LRKV_F32 = 0
+LRKV_BF16 = 1
+
+LRKV_OK = 0
+LRKV_ERR_INVALID_ARG = -1
+LRKV_ERR_UNSUPPORTED = -2
+LRKV_ERR_HIP = -3
+
+
+class lrkv_layout(ctypes.Structure):
+    _fields_ = [
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("rank", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+    def __repr__(self):
+        return (f"lrkv_layout(H={self.num_heads}, d_h={self.head_dim}, r={self.rank}, "
+                f"P={self.page_size}, dtype={'bf16' if self.dtype == LRKV_BF16 else 'f32'})")
+
+
+class LRKVError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lrkv_status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing; build it with "
+                          "`python -m factored_rank_kv_amd.build` (needs hipcc)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    LP = ctypes.POINTER(lrkv_layout)
+    lib.lrkv_page_bytes.argtypes = [LP]
+    lib.lrkv_page_bytes.restype = SZ
+    lib.lrkv_append.argtypes = [LP, P, I32, I32, P, P, P, P, P, P, P, I32, P, I64, P]
+    lib.lrkv_append.restype = ctypes.c_int
+    lib.lrkv_decode_workspace_bytes.argtypes = [LP, I32, I32, I32, I32]
+    lib.lrkv_decode_workspace_bytes.restype = SZ
+    lib.lrkv_decode.argtypes = [LP, P, I32, I32, P, P, P, P, I32, P, I32, I32, P, P, SZ, P]
+    lib.lrkv_decode.restype = ctypes.c_int
+    lib.lrkv_status_string.argtypes = [ctypes.c_int]
+    lib.lrkv_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+EXPORTS = ("lrkv_page_bytes", "lrkv_append", "lrkv_decode_workspace_bytes", "lrkv_decode",
+           "lrkv_status_string")
+
+
+def library():
+    """The loaded ctypes library (loads it on first use)."""
+    return _load()
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+
+    if torch.cuda.is_available() and torch.cuda.is_initialized():
+        return torch.cuda.current_stream().cuda_stream
+    return None
+
+
+def _layout(L):
+    if isinstance(L, lrkv_layout):
+        return ctypes.byref(L)
+    return ctypes.byref(lrkv_layout(*L))
+
+
+def lrkv_status_string(status: int) -> str:
+    return _load().lrkv_status_string(int(status)).decode()
+
+
+def lrkv_page_bytes(layout) -> int:
+    return int(_load().lrkv_page_bytes(_layout(layout)))
+
+
+def lrkv_decode_workspace_bytes(layout, batch, q_len, max_seq_len, chunk_tokens) -> int:
+    return int(_load().lrkv_decode_workspace_bytes(_layout(layout), batch, q_len, max_seq_len,
+                                                    chunk_tokens))
+
+
+def lrkv_append(layout, X, n_rows, d, W_SK, W_SV, U_K, U_V, row_req, row_pos, page_table,
+                max_pages_per_req, pool, num_pages, stream=None, check=True) -> int:
+    st = _load().lrkv_append(_layout(layout), _ptr(X), n_rows, d, _ptr(W_SK), _ptr(W_SV),
+                             _ptr(U_K), _ptr(U_V), _ptr(row_req), _ptr(row_pos),
+                             _ptr(page_table), max_pages_per_req, _ptr(pool), num_pages,
+                             _stream(stream))
+    if check and st != LRKV_OK:
+        raise LRKVError(st, "lrkv_append")
+    return st
+
+
+def lrkv_decode(layout, q, batch, q_len, B_K, B_V, pool, page_table, max_pages_per_req,
+                seq_lens, max_seq_len, chunk_tokens, out, workspace, workspace_bytes,
+                stream=None, check=True) -> int:
+    st = _load().lrkv_decode(_layout(layout), _ptr(q), batch, q_len, _ptr(B_K), _ptr(B_V),
+                             _ptr(pool), _ptr(page_table), max_pages_per_req, _ptr(seq_lens),
+                             max_seq_len, chunk_tokens, _ptr(out), _ptr(workspace),
+                             workspace_bytes, _stream(stream))
+    if check and st != LRKV_OK:
+        raise LRKVError(st, "lrkv_decode")
+    return st

@@ -1,0 +1,195 @@
+// C-ABI entry points of the LRKV library (declared and documented in include/lrkv.h):
+// host-side argument checks, shape dispatch, workspace sizing, launches on the caller's
+// stream.  Nothing here allocates, frees or synchronizes.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/lrkv.h"
+#include "lrkv_launch.h"
+
+namespace {
+
+using namespace lrkv;
+
+enum Variant { V_NONE = -1, V_C0 = 0, V_C1 = 1, V_C3 = 2 };
+
+bool layout_valid(const lrkv_layout* L) {
+  if (!L) return false;
+  if (L->dtype != LRKV_F32 && L->dtype != LRKV_BF16) return false;
+  if (L->num_heads <= 0 || L->head_dim <= 0 || L->rank <= 0) return false;
+  if (L->page_size < 16 || (L->page_size & (L->page_size - 1))) return false;
+  const int chunk = L->dtype == LRKV_BF16 ? 8 : 4;
+  if (L->head_dim % chunk || L->rank % chunk) return false;
+  return true;
+}
+
+Variant find_variant(const lrkv_layout* L) {
+  if (L->page_size != kPage) return V_NONE;
+  const int H = L->num_heads, dh = L->head_dim, r = L->rank;
+  if (L->dtype == LRKV_F32 && H == 4 && dh == 16 && r == 4) return V_C0;
+  if (L->dtype == LRKV_BF16 && H == 16 && dh == 128 && r == 56) return V_C1;
+  if (L->dtype == LRKV_BF16 && H == 32 && dh == 128 && r == 32) return V_C3;
+  return V_NONE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Tokens per chunk of the split: the caller's value, or one that spreads the batch over
+// about two workgroups per compute unit (256 CUs) with at least four pages per chunk.
+int pick_chunk(const lrkv_layout* L, int batch, int q_len, int max_seq_len, int chunk_tokens) {
+  if (chunk_tokens > 0) return chunk_tokens;
+  const int P = L->page_size;
+  const long long work = (long long)batch * q_len * (long long)max_seq_len;
+  const long long target_groups = 512;
+  long long c = (work + target_groups - 1) / target_groups;
+  c = (c + P - 1) / P * P;
+  if (c < 4LL * P) c = 4LL * P;
+  const long long cap = ((long long)max_seq_len + P - 1) / P * P;
+  if (c > cap && cap > 0) c = cap;
+  if (c < P) c = P;
+  return (int)c;
+}
+
+struct DecodeSizes {
+  int chunk;
+  int n_split;
+  size_t p_bytes;
+  size_t part_bytes;
+  size_t total;
+};
+
+DecodeSizes decode_sizes(const lrkv_layout* L, int batch, int q_len, int max_seq_len,
+                         int chunk_tokens) {
+  DecodeSizes z{};
+  z.chunk = pick_chunk(L, batch, q_len, max_seq_len, chunk_tokens);
+  z.n_split = max_seq_len > 0 ? (max_seq_len + z.chunk - 1) / z.chunk : 1;
+  const size_t rows = (size_t)batch * q_len;
+  const size_t H = L->num_heads, r = L->rank, dh = L->head_dim;
+  z.p_bytes = align_up(rows * H * r * sizeof(float), 256);
+  z.part_bytes = align_up(rows * (size_t)z.n_split * H * (2 + dh + r) * sizeof(float), 256);
+  z.total = z.p_bytes + z.part_bytes;
+  return z;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LRKV_OK : LRKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t lrkv_page_bytes(const lrkv_layout* L) {
+  if (!layout_valid(L)) return 0;
+  const size_t b = L->dtype == LRKV_BF16 ? 2 : 4;
+  return (size_t)L->page_size * 2 * ((size_t)L->head_dim + (size_t)L->num_heads * L->rank) * b;
+}
+
+const char* lrkv_status_string(int status) {
+  switch (status) {
+    case LRKV_OK: return "LRKV_OK";
+    case LRKV_ERR_INVALID_ARG: return "LRKV_ERR_INVALID_ARG: invalid argument";
+    case LRKV_ERR_UNSUPPORTED: return "LRKV_ERR_UNSUPPORTED: no kernel variant for this shape";
+    case LRKV_ERR_HIP: return "LRKV_ERR_HIP: HIP runtime error at launch";
+    default: return "LRKV: unknown status";
+  }
+}
+
+size_t lrkv_decode_workspace_bytes(const lrkv_layout* L, int32_t batch, int32_t q_len,
+                                   int32_t max_seq_len, int32_t chunk_tokens) {
+  if (!layout_valid(L) || batch <= 0 || q_len <= 0 || max_seq_len < 0 || chunk_tokens < 0)
+    return 0;
+  if (chunk_tokens % L->page_size) return 0;
+  return decode_sizes(L, batch, q_len, max_seq_len, chunk_tokens).total;
+}
+
+int lrkv_decode(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_len,
+                const void* B_K, const void* B_V, const void* pool, const int32_t* page_table,
+                int32_t max_pages_per_req, const int32_t* seq_lens, int32_t max_seq_len,
+                int32_t chunk_tokens, void* out, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  if (!layout_valid(L)) return LRKV_ERR_INVALID_ARG;
+  if (batch <= 0 || q_len <= 0 || max_pages_per_req <= 0 || max_seq_len < 0)
+    return LRKV_ERR_INVALID_ARG;
+  if (batch > 65535 || q_len > 65535) return LRKV_ERR_INVALID_ARG;
+  if ((long long)max_seq_len > (long long)max_pages_per_req * L->page_size)
+    return LRKV_ERR_INVALID_ARG;
+  if (chunk_tokens < 0 || chunk_tokens % L->page_size) return LRKV_ERR_INVALID_ARG;
+  if (!q || !B_K || !B_V || !pool || !page_table || !seq_lens || !out || !workspace)
+    return LRKV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(B_K) || !aligned16(B_V) || !aligned16(pool) ||
+      !aligned16(page_table) || !aligned16(seq_lens) || !aligned16(out))
+    return LRKV_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return LRKV_ERR_INVALID_ARG;
+  const Variant v = find_variant(L);
+  if (v == V_NONE) return LRKV_ERR_UNSUPPORTED;
+  const DecodeSizes z = decode_sizes(L, batch, q_len, max_seq_len, chunk_tokens);
+  if (workspace_bytes < z.total) return LRKV_ERR_INVALID_ARG;
+  if (z.n_split > 65535) return LRKV_ERR_INVALID_ARG;
+
+  DecodeArgs a{};
+  a.q = q;
+  a.batch = batch;
+  a.q_len = q_len;
+  a.B_K = B_K;
+  a.B_V = B_V;
+  a.pool = pool;
+  a.page_table = page_table;
+  a.max_pages = max_pages_per_req;
+  a.seq_lens = seq_lens;
+  a.n_split = z.n_split;
+  a.chunk = z.chunk;
+  a.out = out;
+  a.p_ws = static_cast<float*>(workspace);
+  a.part_ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + z.p_bytes);
+  a.stream = static_cast<hipStream_t>(stream);
+  switch (v) {
+    case V_C0: return hip_status(launch_decode<ShapeC0>(a));
+    case V_C1: return hip_status(launch_decode<ShapeC1>(a));
+    case V_C3: return hip_status(launch_decode<ShapeC3>(a));
+    default: return LRKV_ERR_UNSUPPORTED;
+  }
+}
+
+int lrkv_append(const lrkv_layout* L, const void* X, int32_t n_rows, int32_t d,
+                const void* W_SK, const void* W_SV, const void* U_K, const void* U_V,
+                const int32_t* row_req, const int32_t* row_pos, const int32_t* page_table,
+                int32_t max_pages_per_req, void* pool, int64_t num_pages, void* stream) {
+  if (!layout_valid(L)) return LRKV_ERR_INVALID_ARG;
+  if (n_rows < 0 || d <= 0 || d % 8 || max_pages_per_req <= 0 || num_pages <= 0)
+    return LRKV_ERR_INVALID_ARG;
+  if (n_rows > 65535 * 8) return LRKV_ERR_INVALID_ARG;
+  if (!X || !W_SK || !W_SV || !U_K || !U_V || !row_req || !row_pos || !page_table || !pool)
+    return LRKV_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(W_SK) || !aligned16(W_SV) || !aligned16(U_K) ||
+      !aligned16(U_V) || !aligned16(row_req) || !aligned16(row_pos) || !aligned16(page_table) ||
+      !aligned16(pool))
+    return LRKV_ERR_INVALID_ARG;
+  const Variant v = find_variant(L);
+  if (v == V_NONE) return LRKV_ERR_UNSUPPORTED;
+  if (n_rows == 0) return LRKV_OK;
+
+  AppendArgs a{};
+  a.X = X;
+  a.n_rows = n_rows;
+  a.d = d;
+  a.W_SK = W_SK;
+  a.W_SV = W_SV;
+  a.U_K = U_K;
+  a.U_V = U_V;
+  a.row_req = row_req;
+  a.row_pos = row_pos;
+  a.page_table = page_table;
+  a.max_pages = max_pages_per_req;
+  a.pool = pool;
+  a.stream = static_cast<hipStream_t>(stream);
+  switch (v) {
+    case V_C0: return hip_status(launch_append<ShapeC0>(a));
+    case V_C1: return hip_status(launch_append<ShapeC1>(a));
+    case V_C3: return hip_status(launch_append<ShapeC3>(a));
+    default: return LRKV_ERR_UNSUPPORTED;
+  }
+}
+
+}  // extern "C"

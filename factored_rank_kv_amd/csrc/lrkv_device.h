@@ -1,0 +1,87 @@
+// Device-side helpers and compile-time shapes shared by the LRKV kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lrkv {
+
+constexpr int kPage = 16;  // tokens per page in this build
+
+// Compile-time description of one kernel variant.  Page layout as in include/lrkv.h:
+// sections S_K, S_V, R_K[0..H-1], R_V[0..H-1], each chunk-major ([chunk][token][16 B]).
+template <int H_, int DH_, int R_, bool BF16_>
+struct Shape {
+  static constexpr int H = H_;
+  static constexpr int DH = DH_;
+  static constexpr int R = R_;
+  static constexpr bool BF = BF16_;
+  static constexpr int EB = BF ? 2 : 4;         // element bytes
+  static constexpr int CE = 16 / EB;            // elements per 16-byte chunk
+  static constexpr int DHC = DH / CE;           // chunks in a shared row
+  static constexpr int RC = R / CE;             // chunks in a private row
+  static constexpr int P = kPage;
+  static constexpr int SEC_S = P * DH * EB;     // bytes of a shared section
+  static constexpr int SEC_R = P * R * EB;      // bytes of one head's private block
+  static constexpr int PAGE = 2 * SEC_S + 2 * H * SEC_R;
+  static constexpr int OFF_SV = SEC_S;
+  static constexpr int OFF_RK = 2 * SEC_S;
+  static constexpr int OFF_RV = 2 * SEC_S + H * SEC_R;
+  static constexpr int PART = 2 + DH + R;       // floats per head in a split partial
+  static_assert(DH % CE == 0 && R % CE == 0, "widths must be whole 16-byte chunks");
+};
+
+// ---- bfloat16 <-> float32 --------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float32 -> bfloat16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+
+// a.x*b.x + a.y*b.y + c on bfloat16 pairs with float32 accumulation (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a),
+                                         __builtin_bit_cast(bf16x2_v, b), c, false);
+}
+
+// ---- lane reductions inside rows of 16 lanes (one head per row) -------------------------
+
+__device__ __forceinline__ float row16_max(float x) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 16));
+  return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 16);
+  return x;
+}
+
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// Query row i of a request holding T tokens sits at position T - q_len + i and sees
+// positions 0..that position.
+__device__ __forceinline__ int visible_tokens(int T, int q_len, int i) {
+  int v = T - q_len + i + 1;
+  v = v < T ? v : T;
+  return v > 0 ? v : 0;
+}
+
+}  // namespace lrkv

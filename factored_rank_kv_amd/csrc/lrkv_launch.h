@@ -1,0 +1,56 @@
+// Host-side launch interface between the C-ABI entry points and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lrkv_device.h"
+
+namespace lrkv {
+
+// The kernel variants of this build: (H, d_h, r, dtype).
+using ShapeC0 = Shape<4, 16, 4, false>;    // float32 single-layer check
+using ShapeC1 = Shape<16, 128, 56, true>;  // bf16, 16 heads, rank 56 (half the dense cache)
+using ShapeC3 = Shape<32, 128, 32, true>;  // bf16, 32 heads, rank 32
+
+struct DecodeArgs {
+  const void* q;
+  int batch;
+  int q_len;
+  const void* B_K;
+  const void* B_V;
+  const void* pool;
+  const int32_t* page_table;
+  int max_pages;
+  const int32_t* seq_lens;
+  int n_split;   // chunks per (request, query row)
+  int chunk;     // tokens per chunk, a multiple of the page size
+  void* out;
+  float* p_ws;   // [batch][q_len][H][r] float32
+  float* part_ws;  // [batch][q_len][n_split][H][2 + d_h + r] float32
+  hipStream_t stream;
+};
+
+struct AppendArgs {
+  const void* X;
+  int n_rows;
+  int d;
+  const void* W_SK;
+  const void* W_SV;
+  const void* U_K;
+  const void* U_V;
+  const int32_t* row_req;
+  const int32_t* row_pos;
+  const int32_t* page_table;
+  int max_pages;
+  void* pool;
+  hipStream_t stream;
+};
+
+template <class S>
+hipError_t launch_decode(const DecodeArgs& a);
+
+template <class S>
+hipError_t launch_append(const AppendArgs& a);
+
+}  // namespace lrkv

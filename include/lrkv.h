@@ -1,0 +1,160 @@
+/*
+ * lrkv.h - C ABI of the LRKV library: Low-Rank Key Value attention decode read straight
+ * from a factored paged KV cache, on AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * Source of the method: the web page "Low-Rank Key Value Attention｜共享缓存与逐头残差"
+ * (Zhongzhu Zhou's reading notes on arXiv 2601.11471), called "LRKV notes" below.
+ *
+ * Each layer has one shared key projection and one shared value projection, and every head
+ * h adds a rank-r residual to each:  W_h = W_S + U_h B_h^T  (LRKV notes §3, eq 2-5).  For a
+ * token x the cache keeps the shared rows S_K = x W_S_K, S_V = x W_S_V (width d_h) once, and
+ * per head the private rows R_K[h] = x U_K[h], R_V[h] = x U_V[h] (width r).  The per-head
+ * bases B_K[h], B_V[h] stay weights.  Full per-head keys and values are never formed.
+ *
+ * ---------------------------------------------------------------------------------------
+ * Factored page layout (one page table for shared and private rows: LRKV notes §3, the
+ * paragraph after Algorithm 1 asking that both kinds of page share token numbering and
+ * lifetime).
+ *
+ *   P   = page_size tokens per page (16 in this build)
+ *   b   = element bytes (4 for LRKV_F32, 2 for LRKV_BF16)
+ *   C   = 16 / b elements per 16-byte chunk; d_h and r must be multiples of C
+ *   page_bytes = P * 2 * (d_h + H*r) * b     (eq 9 of LRKV notes §4, per page)
+ *
+ * A page is four sections, in this order (element offsets from the page start):
+ *   S_K          at 0                         P x d_h elements
+ *   S_V          at P*d_h                     P x d_h
+ *   R_K[h]       at 2*P*d_h + h*P*r           P x r, for h = 0..H-1
+ *   R_V[h]       at 2*P*d_h + H*P*r + h*P*r   P x r, for h = 0..H-1
+ * Inside each section (width w = d_h or r) feature k of token slot t sits at element
+ *   ((k / C) * P + t) * C + (k % C)
+ * i.e. chunk-major: the 16-byte chunk column c holds the P tokens' features [cC, cC+C)
+ * back to back.  One 1 KiB load of a wavefront then hands lane (c, t) one token's chunk.
+ *
+ * Token position j of request b lives in page page_table[b * max_pages_per_req + j / P],
+ * slot j % P, in all four sections.  Page ids index a pool of num_pages * page_bytes bytes.
+ *
+ * ---------------------------------------------------------------------------------------
+ * Conventions for every entry point:
+ *  - Pointers marked "device" are HIP device pointers (hipMalloc / torch CUDA tensors);
+ *    all must be 16-byte aligned.  Pointers to lrkv_layout are host pointers.
+ *  - The caller owns every buffer (pool, page table, lengths, workspace, output).  The
+ *    library never allocates or frees memory and keeps no state between calls; calls are
+ *    re-entrant and thread-safe.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and is
+ *    asynchronous; the library never synchronizes.  Calls that share a workspace or write
+ *    the same pool rows must be ordered by the caller (one stream does that).
+ *  - Every argument check runs on the host before any launch.  Values that live in device
+ *    memory (page ids, lengths, row positions) are not checked: out-of-range values are
+ *    undefined behaviour.
+ *  - Return value: LRKV_OK, or a negative status (lrkv_status_string gives its text).
+ *
+ * Shapes with a kernel variant in this build, (H, d_h, r, dtype):
+ *   (4, 16, 4, LRKV_F32), (16, 128, 56, LRKV_BF16), (32, 128, 32, LRKV_BF16); P = 16.
+ * Any other shape returns LRKV_ERR_UNSUPPORTED.
+ */
+#ifndef LRKV_H
+#define LRKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { LRKV_F32 = 0, LRKV_BF16 = 1 };
+
+enum {
+  LRKV_OK = 0,
+  LRKV_ERR_INVALID_ARG = -1, /* null / misaligned pointer, bad size, workspace too small */
+  LRKV_ERR_UNSUPPORTED = -2, /* (H, d_h, r, dtype, P) without a kernel variant          */
+  LRKV_ERR_HIP = -3          /* the HIP runtime reported an error at launch            */
+};
+
+/* Description of the cache.  Physical rank = logical rank: no padding of r (LRKV notes §4
+ * asks that a padded physical width be recorded apart from the logical rank; this layout
+ * has none). */
+typedef struct lrkv_layout {
+  int32_t num_heads; /* H   */
+  int32_t head_dim;  /* d_h */
+  int32_t rank;      /* r   */
+  int32_t page_size; /* P   */
+  int32_t dtype;     /* LRKV_F32 or LRKV_BF16 */
+} lrkv_layout;
+
+/* Bytes of one page: P * 2 * (d_h + H*r) * b.  With P tokens the dense multi-head cache
+ * would take P * 2 * H * d_h * b, so page_bytes over that is exactly 1/H + r/d_h (LRKV
+ * notes §4, eq 9).  Returns 0 if L is NULL or describes no valid layout. */
+size_t lrkv_page_bytes(const lrkv_layout* L);
+
+/* Algorithm 1 of LRKV notes §3: build or append the factored cache.
+ *
+ * For each new row n (0 <= n < n_rows) computes, with float32 accumulation,
+ *   S_K = X[n] W_SK,  S_V = X[n] W_SV,  R_K[h] = X[n] U_K[:, h, :],  R_V[h] = X[n] U_V[:, h, :]
+ * rounds each value to nearest even in L->dtype and writes it at position row_pos[n] of
+ * request row_req[n], i.e. page page_table[row_req[n] * max_pages_per_req + row_pos[n]/P],
+ * slot row_pos[n] % P, in the four sections.  No other byte of the pool changes.  Prefill
+ * (all rows of a prompt) and single-token append are the same call.
+ *
+ *   X        device, [n_rows][d]     in L->dtype
+ *   W_SK     device, [d][d_h]        in L->dtype
+ *   W_SV     device, [d][d_h]        in L->dtype
+ *   U_K      device, [d][H][r]       in L->dtype (U_K[h] stacked along the columns)
+ *   U_V      device, [d][H][r]       in L->dtype
+ *   row_req  device, [n_rows] int32  request of each row, 0 <= row_req[n] < (table rows)
+ *   row_pos  device, [n_rows] int32  token position of each row; rows must address
+ *                                    distinct (request, position) pairs
+ *   page_table device, [*][max_pages_per_req] int32; the caller assigns the pages
+ *   pool     device, num_pages * lrkv_page_bytes(L) bytes
+ * d must be a positive multiple of 8.  n_rows == 0 is a no-op returning LRKV_OK. */
+int lrkv_append(const lrkv_layout* L, const void* X, int32_t n_rows, int32_t d,
+                const void* W_SK, const void* W_SV, const void* U_K, const void* U_V,
+                const int32_t* row_req, const int32_t* row_pos, const int32_t* page_table,
+                int32_t max_pages_per_req, void* pool, int64_t num_pages, void* stream);
+
+/* Workspace bytes lrkv_decode needs for these sizes (private queries and split partials). */
+size_t lrkv_decode_workspace_bytes(const lrkv_layout* L, int32_t batch, int32_t q_len,
+                                   int32_t max_seq_len, int32_t chunk_tokens);
+
+/* Algorithm 2 of LRKV notes §3 (steps 02-09 without the output projection W_O), read
+ * straight from the factored paged cache.
+ *
+ * For request b, query row i and head h, with T_b = seq_lens[b] cached tokens (the new
+ * token already appended) and the query at position T_b - q_len + i:
+ *   p        = q[b,i,h] B_K[h]                       formed once, float32   (eq 6)
+ *   s_j      = (q[b,i,h] . S_K[j] + p . R_K[h,j]) / sqrt(d_h)   for visible j
+ *   a        = one softmax over the visible positions j <= T_b - q_len + i   (§2)
+ *   out[b,i,h] = a S_V + (a R_V[h]) B_V[h]^T         both branches, same weights (eq 7)
+ * The divisor is sqrt(d_h), the full head width, never sqrt(r) (LRKV notes §2).  Masked
+ * positions are excluded by selection, so unused page slots may hold any bytes (NaN
+ * included).  A row that sees no position gets zeros.  Long histories are split into
+ * chunks whose partial (max, exp-sum, shared acc, private acc) tuples are merged with the
+ * rescaling rule of the fused blockwise paragraph of §3.  q_len = 1 is one decode step;
+ * q_len = T_b is causal prefill over the cache.
+ *
+ *   q          device, [batch][q_len][H][d_h]  in L->dtype
+ *   B_K, B_V   device, [H][d_h][r]             in L->dtype
+ *   pool       device, factored pages (layout above)
+ *   page_table device, [batch][max_pages_per_req] int32
+ *   seq_lens   device, [batch] int32, 0 <= seq_lens[b] <= max_seq_len
+ *   max_seq_len  host value >= every seq_lens[b], and <= max_pages_per_req * P
+ *   chunk_tokens host value: 0 picks the split size; else a positive multiple of P
+ *   out        device, [batch][q_len][H][d_h]  in L->dtype
+ *   workspace  device, >= lrkv_decode_workspace_bytes(L, batch, q_len, max_seq_len,
+ *              chunk_tokens) bytes, 256-byte aligned; contents need not be initialised
+ * Accumulation is float32 throughout. */
+int lrkv_decode(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_len,
+                const void* B_K, const void* B_V, const void* pool, const int32_t* page_table,
+                int32_t max_pages_per_req, const int32_t* seq_lens, int32_t max_seq_len,
+                int32_t chunk_tokens, void* out, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* Text of a status code (static storage). */
+const char* lrkv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LRKV_H */

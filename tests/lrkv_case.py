@@ -1,0 +1,175 @@
+"""Test harness: builds seeded LRKV cases, runs them through the C-ABI library on the GPU and
+through the float64 oracle on the CPU.  Inputs come from `synth` (random draws) and the
+oracle (projection, rounding and page placement); nothing the oracle reads comes from the
+GPU path.
+"""
+
+from __future__ import annotations
+
+import math
+import time
+
+import numpy as np
+import torch
+
+import factored_rank_kv_amd as F
+import oracle as O
+import synth
+
+DEV = "cuda:0"
+
+
+def log(msg):
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+def layout_c(L: O.Layout) -> F.lrkv_layout:
+    return F.lrkv_layout(L.num_heads, L.head_dim, L.rank, L.page_size, L.dtype)
+
+
+def as_codes(x: np.ndarray, dtype: int) -> np.ndarray:
+    """float32 values -> element codes of the cache dtype (uint16 bf16 codes, or uint32 bits)."""
+    if dtype == O.BF16:
+        return synth.to_bf16_bits(x)
+    return np.ascontiguousarray(x, np.float32).view(np.uint32)
+
+
+def codes_f64(codes: np.ndarray, dtype: int) -> np.ndarray:
+    if dtype == O.BF16:
+        return O.bf16_bits_to_f64(codes)
+    return codes.view(np.float32).astype(np.float64)
+
+
+def to_dev(codes: np.ndarray) -> torch.Tensor:
+    """Element codes -> device tensor holding the same bytes."""
+    a = np.ascontiguousarray(codes)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(DEV)
+    if a.dtype == np.uint32:
+        return torch.from_numpy(a.view(np.int32)).to(DEV)
+    if a.dtype == np.uint8:
+        return torch.from_numpy(a).to(DEV)
+    return torch.from_numpy(a).to(DEV)
+
+
+def from_dev(t: torch.Tensor, dtype: int) -> np.ndarray:
+    """Device output tensor (codes) -> float64."""
+    a = t.cpu().numpy()
+    if dtype == O.BF16:
+        return O.bf16_bits_to_f64(a.view(np.uint16))
+    return a.view(np.float32).astype(np.float64)
+
+
+class Case:
+    """A paged cache with queries and bases, held both as host codes and on the device."""
+
+    def __init__(self, L: O.Layout, pool: np.ndarray, table: np.ndarray, lens, q_codes,
+                 BK_codes, BV_codes, num_pages: int):
+        self.L = L
+        self.pool = pool
+        self.table = np.ascontiguousarray(table, np.int32)
+        self.lens = np.asarray(lens, np.int32)
+        self.q_codes = q_codes
+        self.BK_codes = BK_codes
+        self.BV_codes = BV_codes
+        self.num_pages = num_pages
+        self.q64 = codes_f64(q_codes, L.dtype)
+        self.BK64 = codes_f64(BK_codes, L.dtype)
+        self.BV64 = codes_f64(BV_codes, L.dtype)
+        self.B, self.q_len = q_codes.shape[0], q_codes.shape[1]
+        self._dev = None
+
+    @property
+    def dev(self):
+        if self._dev is None:
+            self._dev = dict(
+                pool=None if self.pool is None else to_dev(self.pool), table=to_dev(self.table),
+                lens=to_dev(self.lens), q=to_dev(self.q_codes), BK=to_dev(self.BK_codes),
+                BV=to_dev(self.BV_codes))
+        return self._dev
+
+    def run(self, chunk_tokens: int = 0, max_seq_len: int | None = None, table=None,
+            pool=None) -> torch.Tensor:
+        """lrkv_decode on the device; returns the output codes tensor."""
+        d = self.dev
+        L = self.L
+        msl = int(self.lens.max()) if max_seq_len is None else max_seq_len
+        lay = layout_c(L)
+        ws_bytes = F.lrkv_decode_workspace_bytes(lay, self.B, self.q_len, msl, chunk_tokens)
+        assert ws_bytes > 0
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+        out = torch.empty(self.q_codes.shape, dtype=d["q"].dtype, device=DEV)
+        tab = d["table"] if table is None else table
+        F.lrkv_decode(lay, d["q"], self.B, self.q_len, d["BK"], d["BV"],
+                      d["pool"] if pool is None else pool, tab, self.table.shape[1],
+                      d["lens"], msl, chunk_tokens, out, ws, ws_bytes)
+        torch.cuda.synchronize()
+        return out
+
+    def run_f64(self, **kw) -> np.ndarray:
+        return from_dev(self.run(**kw), self.L.dtype)
+
+    def reference(self, sample=None) -> np.ndarray:
+        return O.decode_reference(self.L, self.q64, self.BK64, self.BV64, self.pool, self.table,
+                                  self.lens, sample=sample)
+
+
+def tolerance(dtype: int) -> float:
+    """Bound on max|gpu - ref| / max|ref|: 1e-2 for a bf16 cache, 1e-5 for float32."""
+    return 1e-2 if dtype == O.BF16 else 1e-5
+
+
+def max_rel_err(got, ref, mask=None) -> float:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if mask is not None:
+        got, ref = got[mask], ref[mask]
+    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+# --------------------------------------------------------------------------------------
+# case builders
+# --------------------------------------------------------------------------------------
+
+
+def bases_and_queries(seed, L: O.Layout, B, q_len, q_scale=1.0):
+    g = np.random.default_rng(seed)
+    H, dh, r = L.num_heads, L.head_dim, L.rank
+    BK = (g.standard_normal((H, dh, r)) / math.sqrt(r)).astype(np.float32)
+    BV = (g.standard_normal((H, dh, r)) / math.sqrt(r)).astype(np.float32)
+    q = synth.queries(seed + 1, B, q_len, H, dh, q_scale)
+    return as_codes(q, L.dtype), as_codes(BK, L.dtype), as_codes(BV, L.dtype)
+
+
+def iid_case(seed, H, dh, r, dtype, lens, q_len=1, permute=True, q_scale=1.0, fill=0):
+    """Cached rows drawn i.i.d. N(0,1), packed by the oracle's bulk placement."""
+    L = O.Layout(H, dh, r, 16, dtype)
+    n = int(sum(lens))
+    SK, SV, RK, RV = synth.factored_rows(seed, n, H, dh, r)
+    table, npg = synth.page_assignment(seed + 7, lens, 16, permute)
+    pool = O.pack_pool(L, table, lens, as_codes(SK, dtype), as_codes(SV, dtype),
+                       as_codes(RK, dtype), as_codes(RV, dtype), npg, fill=fill)
+    qc, bk, bv = bases_and_queries(seed + 13, L, len(lens), q_len, q_scale)
+    return Case(L, pool, table, lens, qc, bk, bv, npg)
+
+
+def projected_case(seed, work: synth.Workload, lens=None, q_len=1, permute=False, q_scale=1.0,
+                   weights=None):
+    """Cached rows = the oracle's Algorithm-1 append of X ~ N(0,1) through the workload's
+    weights (bf16-rounded inputs, float64 projection, nearest-even rounding)."""
+    lens = list(work.lens if lens is None else lens)
+    L = O.Layout(work.H, work.d_h, work.r, work.page_size, work.dtype)
+    w = weights or synth.projection_weights(seed, work.d, work.H, work.d_h, work.r)
+    wc = {k: as_codes(v, L.dtype) for k, v in w.items()}
+    w64 = {k: codes_f64(v, L.dtype) for k, v in wc.items()}
+    n = int(sum(lens))
+    X = synth.activations(seed + 1, n, work.d)
+    X64 = codes_f64(as_codes(X, L.dtype), L.dtype)
+    table, npg = synth.page_assignment(seed + 2, lens, work.page_size, permute)
+    start = np.zeros(npg * O.page_bytes(L), np.uint8)
+    req = np.repeat(np.arange(len(lens)), lens)
+    pos = np.concatenate([np.arange(t) for t in lens]) if n else np.zeros(0, np.int64)
+    pool = O.append_reference(start, L, X64, w64["W_SK"], w64["W_SV"], w64["U_K"], w64["U_V"],
+                              req, pos, table)
+    q = synth.queries(seed + 3, len(lens), q_len, work.H, work.d_h, q_scale)
+    return Case(L, pool, table, lens, as_codes(q, L.dtype), wc["B_K"], wc["B_V"], npg)

@@ -1,0 +1,165 @@
+"""GPU parity of lrkv_decode against the float64 oracle, through the C-ABI library.
+
+Bars (max over compared outputs of |gpu - ref| / max|ref|): 1e-2 for a bf16 cache, 1e-5 for
+float32.  Page-table indexing is checked bit-exactly: a permuted pool must give the same
+output bits as the identity pool.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from lrkv_case import (Case, as_codes, codes_f64, from_dev, iid_case, log, max_rel_err,
+                       projected_case, tolerance, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def check(case: Case, got, ref, mask=None, what=""):
+    err = max_rel_err(got, ref, mask)
+    log(f"{what}: max rel err {err:.3e} (bar {tolerance(case.L.dtype):.0e})")
+    assert err <= tolerance(case.L.dtype), what
+    assert np.all(np.isfinite(got if mask is None else got[mask]))
+
+
+# --------------------------------------------------------------------------------------
+# small shapes: every output compared
+# --------------------------------------------------------------------------------------
+
+
+def test_c0_fp32_decode():
+    log("c0 fp32 decode, 64 cached + 1 new token, contiguous")
+    case = projected_case(0, synth.C0)
+    check(case, case.run_f64(), case.reference(), what="c0")
+
+
+def test_c0_fp32_end_to_end_from_x():
+    """C0 from the raw inputs: GPU append of X, then GPU decode of q = x_new W_q, against the
+    oracle's per-head projection W_h = W_S + U_h B_h^T applied to X directly (eq 2)."""
+    import factored_rank_kv_amd as F
+    from lrkv_case import layout_c
+
+    work = synth.C0
+    w = synth.projection_weights(0, work.d, work.H, work.d_h, work.r, with_wq=True)
+    X = synth.activations(1, 65, work.d)
+    L = O.Layout(work.H, work.d_h, work.r, 16, O.F32)
+    table, npg = synth.page_assignment(2, [65], 16, False)
+    pool = torch.zeros(npg * O.page_bytes(L), dtype=torch.uint8, device="cuda:0")
+    dev = {k: torch.from_numpy(v).to("cuda:0") for k, v in w.items()}
+    Xd = torch.from_numpy(X).to("cuda:0")
+    req = torch.zeros(65, dtype=torch.int32, device="cuda:0")
+    pos = torch.arange(65, dtype=torch.int32, device="cuda:0")
+    tab = torch.from_numpy(table).to("cuda:0")
+    log("c0 append 65 rows")
+    F.lrkv_append(layout_c(L), Xd, 65, work.d, dev["W_SK"], dev["W_SV"], dev["U_K"], dev["U_V"],
+                  req, pos, tab, table.shape[1], pool, npg)
+    q = (X[64].astype(np.float64) @ w["W_q"].astype(np.float64)).astype(np.float32)
+    q = q.reshape(1, 1, work.H, work.d_h)
+    case = Case(L, None, table, [65], q.view(np.uint32), w["B_K"].view(np.uint32),
+                w["B_V"].view(np.uint32), npg)
+    log("c0 decode")
+    got = from_dev(case.run(pool=pool), O.F32)
+    X64 = X.astype(np.float64)
+    K = O.full_projection_kv(X64, w["W_SK"], w["U_K"], w["B_K"])
+    V = O.full_projection_kv(X64, w["W_SV"], w["U_V"], w["B_V"])
+    ref = np.stack([O.softmax_attention(q[0, 0, h].astype(np.float64), K[h], V[h],
+                                        1 / math.sqrt(work.d_h)) for h in range(work.H)])
+    err = max_rel_err(got[0, 0], ref)
+    log(f"c0 end to end: max rel err {err:.3e}")
+    assert err <= 1e-5
+
+
+@pytest.mark.parametrize("chunk", [0, 16, 48])
+def test_c1_shape_ragged_paged_nan_tails(chunk):
+    log(f"c1 shape, ragged lengths, permuted pool, NaN tails, chunk={chunk}")
+    case = iid_case(101, 16, 128, 56, O.BF16, [1, 17, 100, 16, 33, 250], permute=True,
+                    fill=0x7FC0)
+    check(case, case.run_f64(chunk_tokens=chunk), case.reference(), what=f"c1 ragged chunk {chunk}")
+
+
+def test_c3_shape_small():
+    log("c3 shape (32 heads, r=32), ragged, permuted, NaN tails")
+    case = iid_case(102, 32, 128, 32, O.BF16, [5, 64, 129], permute=True, fill=0x7FC0)
+    check(case, case.run_f64(chunk_tokens=32), case.reference(), what="c3 small")
+
+
+def test_c0_shape_ragged():
+    log("c0 shape, ragged, permuted, NaN tails")
+    case = iid_case(103, 4, 16, 4, O.F32, [1, 15, 16, 17, 90], permute=True, fill=0x7FC00000)
+    check(case, case.run_f64(chunk_tokens=16), case.reference(), what="c0 ragged")
+
+
+def test_empty_and_single_token_requests():
+    log("seq_len 0, 1 and 17")
+    case = iid_case(104, 16, 128, 56, O.BF16, [0, 1, 17], permute=True, fill=0x7FC0)
+    got = case.run_f64()
+    ref = case.reference()
+    assert np.all(got[0] == 0.0)
+    check(case, got[1:], ref[1:], what="lens 1, 17")
+
+
+def test_permuted_pool_is_bit_identical_to_identity():
+    """Page-table indexing is exact: the same rows in a permuted pool decode to the same bits."""
+    lens = [70, 33, 129]
+    a = iid_case(105, 16, 128, 56, O.BF16, lens, permute=False)
+    b = iid_case(105, 16, 128, 56, O.BF16, lens, permute=True)
+    assert not np.array_equal(a.table, b.table)
+    for chunk in (16, 64, 0):
+        log(f"identity vs permuted, chunk={chunk}")
+        oa = a.run(chunk_tokens=chunk).cpu()
+        ob = b.run(chunk_tokens=chunk).cpu()
+        assert torch.equal(oa, ob)
+
+
+def test_chunk_sizes_agree():
+    case = iid_case(106, 16, 128, 56, O.BF16, [300, 77], permute=True)
+    ref = case.reference()
+    for chunk in (16, 32, 304):
+        log(f"chunk={chunk}")
+        check(case, case.run_f64(chunk_tokens=chunk), ref, what=f"chunk {chunk}")
+
+
+def test_peaked_softmax_max_in_last_chunk():
+    """q scaled by 8 and the last token's shared key aligned with every head's query: the
+    running max jumps in the last chunk and every earlier chunk must be rescaled to ~0."""
+    lens = [200, 64]
+    case = iid_case(107, 16, 128, 56, O.BF16, lens, permute=True, q_scale=8.0)
+    L = case.L
+    # rebuild S_K of each request's last token as half the sum of that request's queries
+    pool = case.pool.copy()
+    for b, T in enumerate(lens):
+        key = 0.5 * case.q64[b, 0].sum(axis=0)
+        SK_rows = O.gather_request(pool, L, case.table[b], T)
+        new_sk = O.round_to_dtype(key, L.dtype)
+        SK, SV = SK_rows["SK"], SK_rows["SV"]
+        pool = O.write_rows(pool, L, case.table, [b], [T - 1], new_sk[None], SV[T - 1:T],
+                            np.transpose(SK_rows["RK"][:, T - 1:T], (1, 0, 2)),
+                            np.transpose(SK_rows["RV"][:, T - 1:T], (1, 0, 2)))
+    case = Case(L, pool, case.table, lens, case.q_codes, case.BK_codes, case.BV_codes,
+                case.num_pages)
+    ref = case.reference()
+    for chunk in (16, 0):
+        log(f"peaked, chunk={chunk}")
+        check(case, case.run_f64(chunk_tokens=chunk), ref, what=f"peaked chunk {chunk}")
+
+
+def test_repeat_runs_are_bitwise_equal():
+    case = iid_case(108, 16, 128, 56, O.BF16, [513, 1000, 31], permute=True)
+    log("determinism")
+    a = case.run().cpu()
+    b = case.run().cpu()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("shape", [(4, 16, 4, O.F32), (16, 128, 56, O.BF16)])
+def test_multi_row_queries_causal(shape):
+    """q_len > 1: row i sees positions j <= T - q_len + i."""
+    H, dh, r, dt = shape
+    log(f"multi-row queries, shape {shape}")
+    case = iid_case(109, H, dh, r, dt, [40, 7, 16], q_len=5, permute=True,
+                    fill=0x7FC0 if dt == O.BF16 else 0x7FC00000)
+    check(case, case.run_f64(chunk_tokens=16), case.reference(), what=f"multi-row {shape}")

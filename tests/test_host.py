@@ -1,0 +1,150 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every entry point the header
+declares, sizes pages and workspaces by the layout rules, and rejects bad arguments on the
+host before any launch (no call here reaches a kernel)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import factored_rank_kv_amd as F
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lrkv.h")
+
+
+@pytest.fixture(scope="session", autouse=True)
+def built_library():
+    if not os.path.exists(F.LIB_PATH):
+        from factored_rank_kv_amd import build
+
+        build.build()
+    return F.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lrkv_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(built_library):
+    names = declared_functions()
+    assert set(names) == set(F.EXPORTS)
+    for name in names:
+        assert hasattr(built_library, name), name
+        assert callable(getattr(F, name)), name
+
+
+C1 = F.lrkv_layout(16, 128, 56, 16, F.LRKV_BF16)
+C0 = F.lrkv_layout(4, 16, 4, 16, F.LRKV_F32)
+C3 = F.lrkv_layout(32, 128, 32, 16, F.LRKV_BF16)
+
+
+@pytest.mark.parametrize("lay", [C0, C1, C3, F.lrkv_layout(18, 128, 56, 32, F.LRKV_BF16)])
+def test_page_bytes_matches_layout_rule(lay):
+    L = O.Layout(lay.num_heads, lay.head_dim, lay.rank, lay.page_size, lay.dtype)
+    assert F.lrkv_page_bytes(lay) == O.page_bytes(L)
+
+
+def test_page_bytes_rejects_invalid_layouts():
+    assert F.lrkv_page_bytes(F.lrkv_layout(16, 128, 56, 12, F.LRKV_BF16)) == 0  # P not 2^k
+    assert F.lrkv_page_bytes(F.lrkv_layout(16, 128, 50, 16, F.LRKV_BF16)) == 0  # r % 8
+    assert F.lrkv_page_bytes(F.lrkv_layout(16, 130, 56, 16, F.LRKV_BF16)) == 0
+    assert F.lrkv_page_bytes(F.lrkv_layout(16, 128, 56, 16, 7)) == 0
+    assert F.lrkv_page_bytes(F.lrkv_layout(0, 128, 56, 16, F.LRKV_BF16)) == 0
+
+
+def test_workspace_sizes():
+    w = F.lrkv_decode_workspace_bytes(C1, 8, 1, 4096, 0)
+    assert w > 0 and w % 256 == 0
+    # explicit chunks: private queries + one partial tuple per (row, chunk, head)
+    w16 = F.lrkv_decode_workspace_bytes(C1, 8, 1, 4096, 16)
+    rows, H, r, dh = 8, 16, 56, 128
+    p_bytes = -(-rows * H * r * 4 // 256) * 256
+    part = -(-rows * 256 * H * (2 + dh + r) * 4 // 256) * 256
+    assert w16 == p_bytes + part
+    assert F.lrkv_decode_workspace_bytes(C1, 8, 1, 4096, 24) == 0  # not a multiple of P
+    assert F.lrkv_decode_workspace_bytes(C1, 0, 1, 4096, 0) == 0
+
+
+FAKE = 0x10000  # an aligned address that is never dereferenced: every call below is
+                # rejected on the host before any launch
+
+
+def decode_status(lay=C1, **over):
+    args = dict(q=FAKE, batch=2, q_len=1, B_K=FAKE, B_V=FAKE, pool=FAKE, page_table=FAKE,
+                max_pages_per_req=4, seq_lens=FAKE, max_seq_len=64, chunk_tokens=0, out=FAKE,
+                workspace=FAKE, workspace_bytes=1 << 30)
+    args.update(over)
+    return F.lrkv_decode(lay, check=False, stream=0, **args)
+
+
+def test_decode_rejects_bad_arguments_before_launch():
+    bad = F.LRKV_ERR_INVALID_ARG
+    assert decode_status(q=None) == bad
+    assert decode_status(out=None) == bad
+    assert decode_status(workspace=None) == bad
+    assert decode_status(q=FAKE + 8) == bad  # misaligned
+    assert decode_status(workspace=FAKE + 16) == bad  # workspace needs 256-byte alignment
+    assert decode_status(batch=0) == bad
+    assert decode_status(q_len=0) == bad
+    assert decode_status(chunk_tokens=24) == bad
+    assert decode_status(max_seq_len=65) == bad  # more than max_pages * P
+    assert decode_status(workspace_bytes=16) == bad
+    assert decode_status(F.lrkv_layout(16, 128, 56, 12, F.LRKV_BF16)) == bad
+    unsupported = F.LRKV_ERR_UNSUPPORTED
+    assert decode_status(F.lrkv_layout(8, 128, 56, 16, F.LRKV_BF16)) == unsupported
+    assert decode_status(F.lrkv_layout(16, 128, 56, 32, F.LRKV_BF16)) == unsupported
+    assert decode_status(F.lrkv_layout(16, 128, 56, 16, F.LRKV_F32)) == unsupported
+
+
+def append_status(lay=C1, **over):
+    args = dict(X=FAKE, n_rows=4, d=2048, W_SK=FAKE, W_SV=FAKE, U_K=FAKE, U_V=FAKE,
+                row_req=FAKE, row_pos=FAKE, page_table=FAKE, max_pages_per_req=4, pool=FAKE,
+                num_pages=8)
+    args.update(over)
+    return F.lrkv_append(lay, check=False, stream=0, **args)
+
+
+def test_append_rejects_bad_arguments_before_launch():
+    bad = F.LRKV_ERR_INVALID_ARG
+    assert append_status(X=None) == bad
+    assert append_status(d=100) == bad
+    assert append_status(n_rows=-1) == bad
+    assert append_status(pool=FAKE + 4) == bad
+    assert append_status(num_pages=0) == bad
+    assert append_status(F.lrkv_layout(16, 64, 56, 16, F.LRKV_BF16)) == F.LRKV_ERR_UNSUPPORTED
+    assert append_status(n_rows=0) == F.LRKV_OK  # nothing to do, nothing launched
+
+
+def test_status_strings():
+    for st in (F.LRKV_OK, F.LRKV_ERR_INVALID_ARG, F.LRKV_ERR_UNSUPPORTED, F.LRKV_ERR_HIP):
+        assert F.lrkv_status_string(st).startswith("LRKV")
+    with pytest.raises(F.LRKVError) as e:
+        F.lrkv_decode(C1, None, 1, 1, FAKE, FAKE, FAKE, FAKE, 1, FAKE, 16, 0, FAKE, FAKE, 1 << 20,
+                      stream=0)
+    assert e.value.status == F.LRKV_ERR_INVALID_ARG
+
+
+def test_header_is_plain_c():
+    """The header compiles as C with no HIP or torch headers."""
+    import shutil
+    import subprocess
+    import tempfile
+
+    cc = shutil.which("gcc")
+    if not cc:
+        pytest.skip("no gcc")
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "t.c")
+        with open(src, "w") as f:
+            f.write('#include "lrkv.h"\nint main(void){lrkv_layout L={16,128,56,16,LRKV_BF16};'
+                    'return (int)sizeof(L) - 20;}\n')
+        r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+                            "-c", src, "-o", os.path.join(d, "t.o")], capture_output=True,
+                           text=True)
+        assert r.returncode == 0, r.stderr
+    assert ctypes.sizeof(F.lrkv_layout) == 20
