@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""LRKV decode benchmark on one MI355X.
+
+Workload: B = 8 requests of T = 4096 tokens, H = 16 heads, d_h = 128, r = 56, bf16 factored
+paged cache (16-token pages, identity page table), one layer.  The cache is built on the
+GPU by lrkv_append from X ~ N(0,1) and N(0, 1/fan_in) weights (synthetic inputs), then
+replicated so that consecutive steps read different copies (more bytes than the 256 MB
+Infinity Cache holds, so every step reads HBM).
+
+One step = one decode step of the hot path: lrkv_append of the 8 new tokens' rows (at
+position 4095) into the step's pool copy, then lrkv_decode of one query row per request
+over all 4096 positions.  `value` = algorithmic cache bytes per step (eq 9 of the LRKV
+notes: 2 b (sum of T) (d_h + H r)) / measured step time, in GB/s.
+
+Printed: one JSON line on stdout; progress on stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("LRKV decode: achieved HBM GB/s (% peak) + query-heads·tokens/s, B=8 T=4096")
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lrkv_decode_c1_traffic.json")
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    csrc = os.path.join(ROOT, "factored_rank_kv_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record():
+    """HBM bytes per decode call from the committed rocprofv3 counter runs, if they were taken
+    on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != source_digest():
+        return None
+    return rec
+
+
+def bf16_codes(x):
+    import synth
+
+    return synth.to_bf16_bits(x)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=12,
+                    help="pool copies rotated across steps (12 x 128 MiB = 1.5 GiB)")
+    ap.add_argument("--chunk", type=int, default=0, help="chunk_tokens for lrkv_decode (0 = auto)")
+    ap.add_argument("--graph", type=int, default=1, help="replay the step loop from a HIP graph")
+    ap.add_argument("--cpu-baseline", type=int, default=1)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the LRKV decode "
+              "path here is single-GPU, see DESIGN.md for how it would shard", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import factored_rank_kv_amd as F
+    import synth
+
+    dev = torch.device("cuda:0")
+    work = synth.C1
+    B, T, H, dh, r, d = work.B, work.lens[0], work.H, work.d_h, work.r, work.d
+    lay = F.lrkv_layout(H, dh, r, work.page_size, F.LRKV_BF16)
+    page_bytes = F.lrkv_page_bytes(lay)
+    alg_bytes = 2 * 2 * B * T * (dh + H * r)  # eq 9, b = 2, N = 1 layer
+
+    # ---------------- inputs (synthetic, seeded) ----------------
+    t0 = time.time()
+    w = synth.projection_weights(1, d, H, dh, r)
+    wd = {k: torch.from_numpy(bf16_codes(v).view(np.int16)).to(dev) for k, v in w.items()}
+    X = synth.activations(2, B * T, d)  # row b*T + j is request b, position j
+    Xd = torch.from_numpy(bf16_codes(X).view(np.int16)).to(dev)
+    del X
+    q = synth.queries(3, B, 1, H, dh)
+    qd = torch.from_numpy(bf16_codes(q).view(np.int16)).to(dev)
+    table, num_pages = synth.page_assignment(0, [T] * B, work.page_size, permute=False)
+    tab = torch.from_numpy(table).to(dev)
+    lens = torch.full((B,), T, dtype=torch.int32, device=dev)
+    log(f"inputs ready in {time.time() - t0:.1f}s; page {page_bytes} B, {num_pages} pages")
+
+    # cache of the T-1 earlier tokens, built by lrkv_append (prefill of each prompt)
+    pool0 = torch.zeros(num_pages * page_bytes, dtype=torch.uint8, device=dev)
+    req_all = torch.arange(B, dtype=torch.int32, device=dev).repeat_interleave(T - 1)
+    pos_all = torch.arange(T - 1, dtype=torch.int32, device=dev).repeat(B)
+    rows_prev = (torch.arange(B, device=dev)[:, None] * T +
+                 torch.arange(T - 1, device=dev)[None, :]).reshape(-1)
+    X_prev = Xd[rows_prev].contiguous()
+    F.lrkv_append(lay, X_prev, B * (T - 1), d, wd["W_SK"], wd["W_SV"], wd["U_K"], wd["U_V"],
+                  req_all, pos_all, tab, table.shape[1], pool0, num_pages)
+    del X_prev, req_all, pos_all
+    X_new = Xd[torch.arange(B, device=dev) * T + (T - 1)].contiguous()
+    req_new = torch.arange(B, dtype=torch.int32, device=dev)
+    pos_new = torch.full((B,), T - 1, dtype=torch.int32, device=dev)
+    pools = [pool0] + [pool0.clone() for _ in range(args.replicas - 1)]
+    torch.cuda.synchronize()
+    log(f"cache built and replicated x{args.replicas} "
+        f"({args.replicas * pool0.numel() / 2**30:.2f} GiB)")
+
+    ws_bytes = F.lrkv_decode_workspace_bytes(lay, B, 1, T, args.chunk)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, 1, H, dh), dtype=torch.int16, device=dev)
+
+    def append(k):
+        F.lrkv_append(lay, X_new, B, d, wd["W_SK"], wd["W_SV"], wd["U_K"], wd["U_V"], req_new,
+                      pos_new, tab, table.shape[1], pools[k % len(pools)], num_pages)
+
+    def decode(k):
+        F.lrkv_decode(lay, qd, B, 1, wd["B_K"], wd["B_V"], pools[k % len(pools)], tab,
+                      table.shape[1], lens, T, args.chunk, out, ws, ws_bytes)
+
+    def step(k):
+        append(k)
+        decode(k)
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n, use_graph):
+        """Average ms per call of fn over n calls, HIP events on the launch stream."""
+        if use_graph:
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(stream)
+            with torch.cuda.stream(s):
+                fn(0)  # warm the capture stream
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                for k in range(len(pools)):
+                    fn(k)
+            reps = max(1, n // len(pools))
+            n = reps * len(pools)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n, n
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for k in range(n):
+            fn(k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n, n
+
+    # ---------------- warmup + timed steps ----------------
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    use_graph = bool(args.graph)
+    ms_step, n_steps = timed(step, args.steps, use_graph)
+    ms_decode, _ = timed(decode, args.steps, use_graph)
+    ms_append, _ = timed(append, args.steps, use_graph)
+    log(f"step {ms_step * 1e3:.2f} us (decode {ms_decode * 1e3:.2f} us, append "
+        f"{ms_append * 1e3:.2f} us), graph={use_graph}")
+
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        log(f"copy probe: 1 GiB copy {e0.elapsed_time(e1) / 10:.3f} ms = "
+            f"{2 * (1 << 30) / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9:.0f} GB/s (read+write)")
+        del src, dst
+
+    step_s = ms_step * 1e-3
+    dec_s = ms_decode * 1e-3
+    value = alg_bytes / step_s / 1e9
+    achieved = alg_bytes / dec_s / 1e9
+    trec = traffic_record()
+    roofline = {
+        "bound": "hbm",
+        "kernel": "lrkv_decode call (private_query + decode_split + merge_expand kernels)",
+        "achieved": round(achieved, 1),
+        "peak": PEAK_HBM_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / PEAK_HBM_GBS, 4),
+        "traffic": None if trec is None else trec["hbm_bytes_per_call"],
+        "algorithmic_bytes": alg_bytes,
+        "avg_call_us": round(ms_decode * 1e3, 3),
+    }
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": n_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "accumulate": "f32",
+        "data": "synthetic",
+        "config": {"workload": work.name, "B": B, "T": T, "H": H, "d_h": dh, "r": r, "d": d,
+                   "page_size": work.page_size, "layout": "identity page table",
+                   "step": "lrkv_append of B new rows + lrkv_decode (q_len=1)",
+                   "pool_replicas": len(pools), "chunk_tokens": args.chunk,
+                   "hip_graph": use_graph},
+        "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
+        "query_head_tokens_per_s": round(H * B * T / step_s, 1),
+        "query_heads_per_s": round(H * B / step_s, 1),
+        "decode_only_gbps": round(achieved, 1),
+        "append_us": round(ms_append * 1e3, 3),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+
+    if args.cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(work, w, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(work, weights, target_s):
+    """The float64 oracle timed on the host: page walk, reconstruction of K_h and V_h, and
+    textbook attention for a sample of the workload's requests.  Its input pool comes from
+    the oracle's own Algorithm-1 append of the same synthetic rows (untimed)."""
+    import oracle as O
+    import synth
+
+    L = O.Layout(work.H, work.d_h, work.r, work.page_size, O.BF16)
+    n_req = 2
+    T = work.lens[0]
+    t0 = time.time()
+    w64 = {k: O.bf16_bits_to_f64(bf16_codes(v)) for k, v in weights.items()}
+    X = synth.activations(2, n_req * T, work.d)  # same rows as requests 0..n_req-1
+    X64 = O.bf16_bits_to_f64(bf16_codes(X))
+    table, npg = synth.page_assignment(0, [T] * n_req, work.page_size, permute=False)
+    req = np.repeat(np.arange(n_req), T)
+    pos = np.tile(np.arange(T), n_req)
+    pool = O.append_reference(np.zeros(npg * O.page_bytes(L), np.uint8), L, X64, w64["W_SK"],
+                              w64["W_SV"], w64["U_K"], w64["U_V"], req, pos, table)
+    q64 = O.bf16_bits_to_f64(bf16_codes(synth.queries(3, work.B, 1, work.H, work.d_h)))[:n_req]
+    log(f"cpu baseline: sample pool built in {time.time() - t0:.1f}s")
+    passes = 0
+    t_total = 0.0
+    while t_total < target_s and passes < 100:
+        t1 = time.perf_counter()
+        O.decode_reference(L, q64, w64["B_K"], w64["B_V"], pool, table, [T] * n_req)
+        t_total += time.perf_counter() - t1
+        passes += 1
+    per_pass = t_total / passes
+    sample_bytes = 2 * 2 * n_req * T * (work.d_h + work.H * work.r)
+    threads = os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count())
+    log(f"cpu baseline: {passes} passes, {per_pass:.3f} s each")
+    return {
+        "value": round(sample_bytes / per_pass / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{n_req} of the {work.B} requests (T={T}, all {work.H} heads), float64 numpy "
+                   f"oracle, {passes} timed passes ({t_total:.1f} s), same eq-9 bytes metric"),
+        "query_head_tokens_per_s": round(work.H * n_req * T / per_pass, 1),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -31,6 +31,11 @@ HIP_FLAGS = [
 ]
 
 
+# per-source additions: the decode kernels use max reductions that fuse into DPP ops only
+# when NaN operands need not be preserved; masked slots there are removed by integer selects
+EXTRA_FLAGS = {"lrkv_decode.hip": ["-fno-honor-nans"]}
+
+
 def _hipcc() -> str:
     for c in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if c and os.path.exists(c):
@@ -50,7 +55,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(pair):
         src, obj = pair
-        cmd = [hipcc, *HIP_FLAGS, "-c", src, "-o", obj]
+        cmd = [hipcc, *HIP_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

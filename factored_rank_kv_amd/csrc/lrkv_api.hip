@@ -14,6 +14,9 @@ using namespace lrkv;
 
 enum Variant { V_NONE = -1, V_C0 = 0, V_C1 = 1, V_C3 = 2 };
 
+// The split kernel holds one chunk's page ids in LDS (256 pages of 16 tokens).
+constexpr int kMaxChunkTokens = 256 * 16;
+
 bool layout_valid(const lrkv_layout* L) {
   if (!L) return false;
   if (L->dtype != LRKV_F32 && L->dtype != LRKV_BF16) return false;
@@ -47,6 +50,7 @@ int pick_chunk(const lrkv_layout* L, int batch, int q_len, int max_seq_len, int 
   long long c = (work + target_groups - 1) / target_groups;
   c = (c + P - 1) / P * P;
   if (c < 4LL * P) c = 4LL * P;
+  if (c > kMaxChunkTokens) c = kMaxChunkTokens;
   const long long cap = ((long long)max_seq_len + P - 1) / P * P;
   if (c > cap && cap > 0) c = cap;
   if (c < P) c = P;
@@ -68,8 +72,9 @@ DecodeSizes decode_sizes(const lrkv_layout* L, int batch, int q_len, int max_seq
   z.n_split = max_seq_len > 0 ? (max_seq_len + z.chunk - 1) / z.chunk : 1;
   const size_t rows = (size_t)batch * q_len;
   const size_t H = L->num_heads, r = L->rank, dh = L->head_dim;
-  z.p_bytes = align_up(rows * H * r * sizeof(float), 256);
-  z.part_bytes = align_up(rows * (size_t)z.n_split * H * (2 + dh + r) * sizeof(float), 256);
+  z.p_bytes = 0;  // private queries live in the split kernel's LDS
+  const size_t rec = (2 + dh + r + 3) / 4 * 4;  // padded partial record, floats
+  z.part_bytes = align_up(rows * (size_t)z.n_split * H * rec * sizeof(float), 256);
   z.total = z.p_bytes + z.part_bytes;
   return z;
 }
@@ -100,7 +105,7 @@ size_t lrkv_decode_workspace_bytes(const lrkv_layout* L, int32_t batch, int32_t 
                                    int32_t max_seq_len, int32_t chunk_tokens) {
   if (!layout_valid(L) || batch <= 0 || q_len <= 0 || max_seq_len < 0 || chunk_tokens < 0)
     return 0;
-  if (chunk_tokens % L->page_size) return 0;
+  if (chunk_tokens % L->page_size || chunk_tokens > kMaxChunkTokens) return 0;
   return decode_sizes(L, batch, q_len, max_seq_len, chunk_tokens).total;
 }
 
@@ -115,7 +120,8 @@ int lrkv_decode(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_le
   if (batch > 65535 || q_len > 65535) return LRKV_ERR_INVALID_ARG;
   if ((long long)max_seq_len > (long long)max_pages_per_req * L->page_size)
     return LRKV_ERR_INVALID_ARG;
-  if (chunk_tokens < 0 || chunk_tokens % L->page_size) return LRKV_ERR_INVALID_ARG;
+  if (chunk_tokens < 0 || chunk_tokens % L->page_size || chunk_tokens > kMaxChunkTokens)
+    return LRKV_ERR_INVALID_ARG;
   if (!q || !B_K || !B_V || !pool || !page_table || !seq_lens || !out || !workspace)
     return LRKV_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(B_K) || !aligned16(B_V) || !aligned16(pool) ||
@@ -141,7 +147,6 @@ int lrkv_decode(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_le
   a.n_split = z.n_split;
   a.chunk = z.chunk;
   a.out = out;
-  a.p_ws = static_cast<float*>(workspace);
   a.part_ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + z.p_bytes);
   a.stream = static_cast<hipStream_t>(stream);
   switch (v) {

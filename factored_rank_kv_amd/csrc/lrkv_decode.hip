@@ -1,280 +1,488 @@
-// LRKV decode kernels for gfx950: Algorithm 2 of the LRKV notes (§3) read from the
-// factored paged cache, as three launches on the caller's stream:
-//   1. private_query_kernel  p = q B_K[h], once per (request, query row, head)   (eq 6)
-//   2. decode_split_kernel   one workgroup per (request, query row, chunk of pages), all
-//                            heads: shared S_K/S_V tiles staged once in LDS for every head,
-//                            private R_K/R_V rows streamed per head, one online softmax with
-//                            a shared and a private value accumulator (the fused blockwise
-//                            paragraph after Algorithm 2), partial tuples written out
-//   3. merge_expand_kernel   merge the chunks' (max, exp-sum, acc_S, acc_R) tuples with one
-//                            rescale factor per chunk, expand acc_R through B_V[h]^T once,
-//                            divide by the exp-sum (Algorithm 2 steps 08-09 without W_O)
+// LRKV decode kernels for gfx950: Algorithm 2 of the LRKV notes (§3) read straight from the
+// factored paged cache, as two launches on the caller's stream:
+//   1. decode_split_kernel   one workgroup per (chunk of pages, query row, request) covering
+//                            all heads.  Prologue: the chunk's page ids, the request length
+//                            and the query row are fetched together, the first page is put
+//                            in flight, and the private queries p = q B_K[h] of every head
+//                            are formed while it travels (eq 6).  Loop: shared S_K/S_V tiles
+//                            staged once in LDS for every head, private R_K/R_V rows streamed
+//                            per head straight into registers (page k+1 in flight while page
+//                            k is used), one online softmax with a shared and a private value
+//                            accumulator (fused blockwise paragraph after Algorithm 2).
+//                            Writes the chunk's (max, exp-sum, acc_S, acc_R) tuple per head.
+//   2. merge_expand_kernel   merges the chunks' tuples with one rescale factor per chunk,
+//                            expands acc_R through B_V[h]^T once and divides by the exp-sum
+//                            (Algorithm 2 steps 08-09 without W_O).
+//
+// This file is compiled with -fno-honor-nans (max reductions fuse into DPP ops); masked
+// page slots are removed by integer selects, so NaN bytes there never reach arithmetic.
 #include "lrkv_device.h"
 #include "lrkv_launch.h"
 
 namespace lrkv {
 
 // ---------------------------------------------------------------------------------------
-// 1. private query
+// DPP reductions inside a row of 16 lanes (one head per row)
 // ---------------------------------------------------------------------------------------
-template <class S>
-__global__ void __launch_bounds__(1024)
-private_query_kernel(const void* __restrict__ q, const void* __restrict__ BK,
-                     float* __restrict__ p) {
-  const int row = blockIdx.x;
-  const int t = threadIdx.x;
-  if (t >= S::H * S::R) return;
-  const int h = t / S::R;
-  const int k = t - h * S::R;
-  float acc = 0.f;
-  if constexpr (S::BF) {
-    const uint16_t* qh = static_cast<const uint16_t*>(q) + ((size_t)row * S::H + h) * S::DH;
-    const uint16_t* bk = static_cast<const uint16_t*>(BK) + (size_t)h * S::DH * S::R + k;
-#pragma unroll 8
-    for (int d = 0; d < S::DH; ++d) acc = fmaf(bf16_to_f32(qh[d]), bf16_to_f32(bk[d * S::R]), acc);
-  } else {
-    const float* qh = static_cast<const float*>(q) + ((size_t)row * S::H + h) * S::DH;
-    const float* bk = static_cast<const float*>(BK) + (size_t)h * S::DH * S::R + k;
-#pragma unroll 8
-    for (int d = 0; d < S::DH; ++d) acc = fmaf(qh[d], bk[d * S::R], acc);
-  }
-  p[((size_t)row * S::H + h) * S::R + k] = acc;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141; // lane i <-> 7-i inside each half row
+constexpr int kMirror = 0x140;     // lane i <-> 15-i inside the row
+
+__device__ __forceinline__ float r16_max(float x) {
+  x = __builtin_fmaxf(x, dpp_f<kQuadSwap1>(x));
+  x = __builtin_fmaxf(x, dpp_f<kQuadSwap2>(x));
+  x = __builtin_fmaxf(x, dpp_f<kHalfMirror>(x));
+  x = __builtin_fmaxf(x, dpp_f<kMirror>(x));
+  return x;
+}
+__device__ __forceinline__ float r16_sum(float x) {
+  x += dpp_f<kQuadSwap1>(x);
+  x += dpp_f<kQuadSwap2>(x);
+  x += dpp_f<kHalfMirror>(x);
+  x += dpp_f<kMirror>(x);
+  return x;
 }
 
 // ---------------------------------------------------------------------------------------
-// 2. split kernel
+// 1. split kernel
 //
-// Workgroup = (chunk, query row i, request b); H/4 wavefronts; lane = 16*hl + j handles
-// head h = 4*wave + hl and token slot j of the current page for the score, the softmax and
-// the private value accumulator.  For the shared value accumulator the same wavefront
-// switches to lanes over feature pairs (dims 2*lane, 2*lane+1) for its four heads.
+// Workgroup = (chunk, query row qi, request b); H/4 wavefronts.  For the score, the softmax
+// and the private value, lane = 16*hl + j covers head h = 4*wave + hl and token slot j of
+// the page.  For the shared value the wavefront switches to lanes over feature pairs
+// (2*lane, 2*lane+1) of its four heads, with the weights broadcast by readlane.
 //
-// Scores are kept in base-2 units: s = (q.S_K + p.R_K) * log2(e) / sqrt(d_h), so the
-// softmax uses exp2; the merge uses the same units.
+// Scores are in base-2 units, s = (q.S_K + p.R_K) * log2(e)/sqrt(d_h), so exp2 is used here
+// and in the merge.  The running reference max of a head moves only when a page's max
+// exceeds it by more than kRescaleSlack; the exp-sum and both accumulators always share
+// that one reference (and are rescaled together when it moves), so l and acc are the
+// same quantities the blockwise rule defines, expressed against a different common scale.
+// Weights stay <= 2^kRescaleSlack, far from float32 overflow.
 // ---------------------------------------------------------------------------------------
+constexpr int kMaxChunkPages = 256;     // page ids of one chunk held in LDS
+constexpr float kRescaleSlack = 8.0f;   // base-2 units
+
+struct SplitArgs {
+  const void* q;
+  const void* BK;
+  const uint8_t* pool;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  float* part;
+  int max_pages;
+  int q_len;
+  int n_split;
+  int chunk;
+  float score_scale;
+};
+
 template <class S>
-__global__ void __launch_bounds__(S::H * 16)
-decode_split_kernel(const void* __restrict__ q, const float* __restrict__ p,
-                    const uint8_t* __restrict__ pool, const int32_t* __restrict__ page_table,
-                    int max_pages, const int32_t* __restrict__ seq_lens, int q_len, int n_split,
-                    int chunk, float* __restrict__ part, float score_scale) {
-  constexpr int NT = S::H * 16;
-  __shared__ uint4 sk_lds[S::DHC * S::P];  // chunk-major [c][t], as in the page
-  __shared__ uint4 sv_lds[S::P * S::DHC];  // row-major [t][c]: row t is S_V[t][0..DH)
+struct SplitCfg {
+  static constexpr int NT = S::H * 16;
+  static constexpr int S_CHUNKS = 2 * S::DHC * S::P;    // 16-byte chunks of S_K + S_V
+  static constexpr int SPT = (S_CHUNKS + NT - 1) / NT;  // per thread
+  // two resident workgroups per CU (<= 256 registers per lane) up to 8 wavefronts each
+  static constexpr int MIN_BLOCKS = NT >= 512 ? 1 : 2;
+  // LDS rows of q and p per head; odd strides (in 16-byte units) put the four heads of a
+  // wavefront on different banks
+  static constexpr int Q_STRIDE = S::DHC + 1;
+  static constexpr int P_WORDS = S::RC * (S::BF ? 2 : 1);  // bf16: hi chunk, lo chunk
+  static constexpr int P_STRIDE = P_WORDS | 1;
+  // private queries: one job per (head, 16-byte chunk of p), d_h split over PQ_GROUPS
+  static constexpr int PQ_JOBS = S::H * S::RC;
+  static constexpr int PQ_GROUPS = NT / PQ_JOBS > 0 ? NT / PQ_JOBS : 1;
+  static constexpr int PQ_DSPAN = S::DH / PQ_GROUPS;
+  static_assert(S::DH % PQ_GROUPS == 0, "d_h split evenly");
+};
+
+template <class S>
+struct PageRegs {
+  uint4 rk[S::RC];
+  uint4 rv[S::RC];
+  uint4 st[SplitCfg<S>::SPT];
+};
+
+template <class S>
+__device__ __forceinline__ void issue_page(const uint8_t* __restrict__ page, int tid, int h, int j,
+                                           PageRegs<S>& r) {
+  using C = SplitCfg<S>;
+  const uint4* p4 = reinterpret_cast<const uint4*>(page);
+#pragma unroll
+  for (int i = 0; i < C::SPT; ++i) {
+    const int c = tid + i * C::NT;
+    if (C::S_CHUNKS % C::NT == 0 || c < C::S_CHUNKS) r.st[i] = p4[c];
+  }
+  const uint4* rkp = reinterpret_cast<const uint4*>(page + S::OFF_RK + h * S::SEC_R) + j;
+  const uint4* rvp = reinterpret_cast<const uint4*>(page + S::OFF_RV + h * S::SEC_R) + j;
+#pragma unroll
+  for (int c = 0; c < S::RC; ++c) r.rk[c] = rkp[c * S::P];
+#pragma unroll
+  for (int c = 0; c < S::RC; ++c) r.rv[c] = rvp[c * S::P];
+}
+
+// S_V row t (= S_V[t][0..DH)) keeps its 16-byte chunks in XOR-swizzled order inside the
+// row, so the transposing writes below and the row reads of the value loop both avoid
+// bank conflicts.
+template <class S>
+__device__ __forceinline__ int sv_slot(int t, int chunk) {
+  return t * S::DHC + (chunk ^ (t & (S::DHC - 1)));
+}
+
+// S_K keeps the page's chunk-major order; S_V is transposed to rows, and rows of slots
+// past the last visible token are written as zeros so the value loop can run over all P
+// slots (their weights are exactly zero).
+template <class S>
+__device__ __forceinline__ void stage_shared(uint4* __restrict__ sk, uint4* __restrict__ sv,
+                                             int tid, const PageRegs<S>& r, int nvalid) {
+  using C = SplitCfg<S>;
+#pragma unroll
+  for (int i = 0; i < C::SPT; ++i) {
+    const int c = tid + i * C::NT;
+    if (c < S::DHC * S::P) {
+      sk[c] = r.st[i];
+    } else if (C::S_CHUNKS % C::NT == 0 || c < C::S_CHUNKS) {
+      const int cc = c - S::DHC * S::P;
+      const int t = cc % S::P;
+      sv[sv_slot<S>(t, cc / S::P)] = t < nvalid ? r.st[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+}
+
+// p = q B_K[h] for every head of the row, float32 sums over d_h in a fixed order, packed
+// into LDS for the private score.  bf16 cache: per 8-feature chunk, 4 words of bfloat16
+// pairs of hi(p) then 4 words of lo(p) = bf16(p - hi(p)), so p.R_K[h,j] = dot2(hi, r) +
+// dot2(lo, r) keeps about 16 significant bits of p.  float32 cache: p as it is.
+template <class S>
+__device__ __forceinline__ void form_private_queries(const void* __restrict__ BK,
+                                                     const uint4* __restrict__ q_lds,
+                                                     float* __restrict__ pacc,
+                                                     uint4* __restrict__ p_lds, int tid) {
+  using C = SplitCfg<S>;
+  const int job = tid % C::PQ_JOBS;
+  const int g = tid / C::PQ_JOBS;
+  if (g < C::PQ_GROUPS) {
+    const int h = job / S::RC;
+    const int c = job - h * S::RC;
+    float acc[S::CE];
+#pragma unroll
+    for (int e = 0; e < S::CE; ++e) acc[e] = 0.f;
+    const uint8_t* bk = static_cast<const uint8_t*>(BK) +
+                        ((size_t)h * S::DH * S::R + (size_t)c * S::CE) * S::EB;
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q_lds + h * C::Q_STRIDE);
+#pragma unroll 16
+    for (int dd = 0; dd < C::PQ_DSPAN; ++dd) {
+      const int d = g * C::PQ_DSPAN + dd;
+      const uint4 b4 = *reinterpret_cast<const uint4*>(bk + (size_t)d * S::R * S::EB);
+      if constexpr (S::BF) {
+        const float qd = bf16_to_f32(reinterpret_cast<const uint16_t*>(qrow)[d]);
+        acc[0] = fmaf(qd, bf16_lo(b4.x), acc[0]);
+        acc[1] = fmaf(qd, bf16_hi(b4.x), acc[1]);
+        acc[2] = fmaf(qd, bf16_lo(b4.y), acc[2]);
+        acc[3] = fmaf(qd, bf16_hi(b4.y), acc[3]);
+        acc[4] = fmaf(qd, bf16_lo(b4.z), acc[4]);
+        acc[5] = fmaf(qd, bf16_hi(b4.z), acc[5]);
+        acc[6] = fmaf(qd, bf16_lo(b4.w), acc[6]);
+        acc[7] = fmaf(qd, bf16_hi(b4.w), acc[7]);
+      } else {
+        const float qd = reinterpret_cast<const float*>(qrow)[d];
+        acc[0] = fmaf(qd, __uint_as_float(b4.x), acc[0]);
+        acc[1] = fmaf(qd, __uint_as_float(b4.y), acc[1]);
+        acc[2] = fmaf(qd, __uint_as_float(b4.z), acc[2]);
+        acc[3] = fmaf(qd, __uint_as_float(b4.w), acc[3]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < S::CE; ++e) pacc[(g * C::PQ_JOBS + job) * S::CE + e] = acc[e];
+  }
+  __syncthreads();
+  if (tid < C::PQ_JOBS) {
+    const int h = tid / S::RC;
+    const int c = tid - h * S::RC;
+    float p[S::CE];
+#pragma unroll
+    for (int e = 0; e < S::CE; ++e) {
+      float v = 0.f;
+#pragma unroll
+      for (int gg = 0; gg < C::PQ_GROUPS; ++gg) v += pacc[(gg * C::PQ_JOBS + tid) * S::CE + e];
+      p[e] = v;
+    }
+    uint4* dst = p_lds + h * C::P_STRIDE;
+    if constexpr (S::BF) {
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t h0 = f32_to_bf16_rne(p[2 * e]), h1 = f32_to_bf16_rne(p[2 * e + 1]);
+        hi[e] = h0 | (h1 << 16);
+        lo[e] = f32_to_bf16_rne(p[2 * e] - bf16_to_f32((uint16_t)h0)) |
+                (f32_to_bf16_rne(p[2 * e + 1] - bf16_to_f32((uint16_t)h1)) << 16);
+      }
+      dst[2 * c] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      dst[2 * c + 1] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    } else {
+      dst[c] = make_uint4(__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]),
+                          __float_as_uint(p[3]));
+    }
+  }
+}
+
+template <class S>
+struct SplitState {
+  float m_run;       // reference max of the lane's head (equal in its 16 lanes)
+  float l_run;       // this lane's share of the exp-sum
+  float accR[S::R];  // this lane's share of sum_j w_j R_V[h, j]
+  float accS[4][2];  // sum_j w_j S_V[j][2*lane + e] for the wavefront's four heads
+};
+
+template <class S>
+__device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
+                                             const uint4* __restrict__ sv,
+                                             const uint4* __restrict__ q_lds,
+                                             const uint4* __restrict__ p_lds, int h, int j,
+                                             int lane, int nvalid, float score_scale,
+                                             const PageRegs<S>& r, SplitState<S>& st) {
+  using C = SplitCfg<S>;
+  const bool valid = j < nvalid;
+  // ---- score: q . S_K[j] + p . R_K[h, j]   (eq 6)
+  float acc0 = 0.f, acc1 = 0.f;
+  const uint4* qh = q_lds + h * C::Q_STRIDE;
+#pragma unroll
+  for (int c = 0; c < S::DHC; ++c) {
+    const uint4 s4 = sk[c * S::P + j];
+    const uint4 q4 = qh[c];
+    if constexpr (S::BF) {
+      acc0 = dot2_bf16(q4.x, s4.x, acc0);
+      acc1 = dot2_bf16(q4.y, s4.y, acc1);
+      acc0 = dot2_bf16(q4.z, s4.z, acc0);
+      acc1 = dot2_bf16(q4.w, s4.w, acc1);
+    } else {
+      acc0 = fmaf(__uint_as_float(q4.x), __uint_as_float(s4.x), acc0);
+      acc1 = fmaf(__uint_as_float(q4.y), __uint_as_float(s4.y), acc1);
+      acc0 = fmaf(__uint_as_float(q4.z), __uint_as_float(s4.z), acc0);
+      acc1 = fmaf(__uint_as_float(q4.w), __uint_as_float(s4.w), acc1);
+    }
+  }
+  const uint4* ph = p_lds + h * C::P_STRIDE;
+#pragma unroll
+  for (int c = 0; c < S::RC; ++c) {
+    const uint4 k4 = r.rk[c];
+    if constexpr (S::BF) {
+      const uint4 hi = ph[2 * c], lo = ph[2 * c + 1];
+      acc0 = dot2_bf16(hi.x, k4.x, acc0);
+      acc1 = dot2_bf16(hi.y, k4.y, acc1);
+      acc0 = dot2_bf16(hi.z, k4.z, acc0);
+      acc1 = dot2_bf16(hi.w, k4.w, acc1);
+      acc0 = dot2_bf16(lo.x, k4.x, acc0);
+      acc1 = dot2_bf16(lo.y, k4.y, acc1);
+      acc0 = dot2_bf16(lo.z, k4.z, acc0);
+      acc1 = dot2_bf16(lo.w, k4.w, acc1);
+    } else {
+      const uint4 p4 = ph[c];
+      acc0 = fmaf(__uint_as_float(p4.x), __uint_as_float(k4.x), acc0);
+      acc1 = fmaf(__uint_as_float(p4.y), __uint_as_float(k4.y), acc1);
+      acc0 = fmaf(__uint_as_float(p4.z), __uint_as_float(k4.z), acc0);
+      acc1 = fmaf(__uint_as_float(p4.w), __uint_as_float(k4.w), acc1);
+    }
+  }
+  // masked slots leave by selection, never by multiplying with zero
+  const float s = valid ? (acc0 + acc1) * score_scale : -INFINITY;
+
+  // ---- online softmax: the reference moves (and rescales l, acc_S, acc_R by one factor)
+  // only when the page's max clears it by more than the slack
+  const float pm = r16_max(s);
+  const bool bump = pm > st.m_run + kRescaleSlack;
+  if (__any(bump)) {
+    const float m_new = bump ? pm : st.m_run;
+    const float alpha = exp2f(st.m_run - m_new);  // 0 on the first page, 1 if not bumped
+    st.l_run *= alpha;
+#pragma unroll
+    for (int k = 0; k < S::R; ++k) st.accR[k] *= alpha;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const float a = readlane_f(alpha, 16 * x);
+      st.accS[x][0] *= a;
+      st.accS[x][1] *= a;
+    }
+    st.m_run = m_new;
+  }
+  const float w = exp2f(s - st.m_run);  // exactly 0 for masked slots
+  st.l_run += w;
+#pragma unroll
+  for (int c = 0; c < S::RC; ++c) {
+    const uint32_t v4[4] = {valid ? r.rv[c].x : 0u, valid ? r.rv[c].y : 0u,
+                            valid ? r.rv[c].z : 0u, valid ? r.rv[c].w : 0u};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (S::BF) {
+        const int k = 8 * c + 2 * e;
+        st.accR[k] = fmaf(w, bf16_lo(v4[e]), st.accR[k]);
+        st.accR[k + 1] = fmaf(w, bf16_hi(v4[e]), st.accR[k + 1]);
+      } else {
+        const int k = 4 * c + e;
+        st.accR[k] = fmaf(w, __uint_as_float(v4[e]), st.accR[k]);
+      }
+    }
+  }
+
+  // ---- shared value: lanes over feature pairs, weights broadcast by readlane
+  float sA0 = st.accS[0][0], sB0 = st.accS[0][1];
+  float sA1 = st.accS[1][0], sB1 = st.accS[1][1];
+  float sA2 = st.accS[2][0], sB2 = st.accS[2][1];
+  float sA3 = st.accS[3][0], sB3 = st.accS[3][1];
+  const int dl = (2 * lane < S::DH) ? lane : (S::DH / 2 - 1);
+  const int e0 = 2 * dl;  // first feature of the pair
+#pragma unroll
+  for (int t = 0; t < S::P; ++t) {
+    const int slot = sv_slot<S>(t, e0 / S::CE) * S::CE + (e0 % S::CE);  // element index
+    float sv0, sv1;
+    if constexpr (S::BF) {
+      const uint32_t pr = reinterpret_cast<const uint32_t*>(sv)[slot / 2];
+      sv0 = bf16_lo(pr);
+      sv1 = bf16_hi(pr);
+    } else {
+      const float2 pr = reinterpret_cast<const float2*>(sv)[slot / 2];
+      sv0 = pr.x;
+      sv1 = pr.y;
+    }
+    const float w0 = readlane_f(w, t), w1 = readlane_f(w, 16 + t);
+    const float w2 = readlane_f(w, 32 + t), w3 = readlane_f(w, 48 + t);
+    sA0 = fmaf(w0, sv0, sA0);
+    sB0 = fmaf(w0, sv1, sB0);
+    sA1 = fmaf(w1, sv0, sA1);
+    sB1 = fmaf(w1, sv1, sB1);
+    sA2 = fmaf(w2, sv0, sA2);
+    sB2 = fmaf(w2, sv1, sB2);
+    sA3 = fmaf(w3, sv0, sA3);
+    sB3 = fmaf(w3, sv1, sB3);
+  }
+  st.accS[0][0] = sA0; st.accS[0][1] = sB0;
+  st.accS[1][0] = sA1; st.accS[1][1] = sB1;
+  st.accS[2][0] = sA2; st.accS[2][1] = sB2;
+  st.accS[3][0] = sA3; st.accS[3][1] = sB3;
+}
+
+template <class S>
+__global__ void __launch_bounds__(S::H * 16, SplitCfg<S>::MIN_BLOCKS)
+decode_split_kernel(const SplitArgs a) {
+  using C = SplitCfg<S>;
+  __shared__ uint4 sk_lds[2][S::DHC * S::P];  // chunk-major [c][t], double buffered
+  __shared__ uint4 sv_lds[2][S::P * S::DHC];  // rows [t][swizzled c]
+  __shared__ uint4 q_lds[S::H * C::Q_STRIDE];
+  __shared__ uint4 p_lds[S::H * C::P_STRIDE];
+  __shared__ float pacc[C::PQ_GROUPS * C::PQ_JOBS * S::CE];
+  __shared__ int ids_lds[kMaxChunkPages];
 
   const int split = blockIdx.x;
   const int qi = blockIdx.y;
   const int b = blockIdx.z;
-  const int T = seq_lens[b];
-  const int vis = visible_tokens(T, q_len, qi);
-  const int tok0 = split * chunk;
-  const int tok1 = min(vis, tok0 + chunk);
-  if (tok0 >= tok1) return;  // uniform for the whole workgroup
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int hl = lane >> 4;
   const int j = lane & 15;
   const int h = wave * 4 + hl;
-  const size_t row = (size_t)b * q_len + qi;
+  const size_t row = (size_t)b * a.q_len + qi;
 
-  // query of head h: DH elements as 32-bit words (bf16 pairs or floats)
-  constexpr int QW = S::DH * S::EB / 4;
-  uint32_t qv[QW];
+  // requests that do not depend on the request length go out together
+  const int pg0 = split * (a.chunk / S::P);
   {
-    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(q) +
-                                                      (row * S::H + h) * S::DH * S::EB);
-#pragma unroll
-    for (int c = 0; c < S::DHC; ++c) {
-      const uint4 v = src[c];
-      qv[4 * c + 0] = v.x;
-      qv[4 * c + 1] = v.y;
-      qv[4 * c + 2] = v.z;
-      qv[4 * c + 3] = v.w;
-    }
+    const int nid = min(a.chunk / S::P, a.max_pages - pg0);  // table entries of this chunk
+    const int32_t* tab = a.page_table + (size_t)b * a.max_pages + pg0;
+    for (int i = tid; i < nid; i += C::NT) ids_lds[i] = tab[i];
+    const uint4* qsrc = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.q) +
+                                                       row * S::H * S::DH * S::EB);
+    for (int i = tid; i < S::H * S::DHC; i += C::NT)
+      q_lds[(i / S::DHC) * C::Q_STRIDE + i % S::DHC] = qsrc[i];
   }
-  // private query of head h.  bf16 cache: split each float32 p into hi + lo bfloat16 parts
-  // so the private dot product runs on v_dot2_f32_bf16 with ~16 significant bits of p.
-  constexpr int PW = S::BF ? S::R / 2 : S::R;
-  uint32_t phi[PW];
-  uint32_t plo[S::BF ? PW : 1];
-  {
-    const float* ph = p + (row * S::H + h) * S::R;
-    if constexpr (S::BF) {
-#pragma unroll
-      for (int k2 = 0; k2 < PW; ++k2) {
-        const float a = ph[2 * k2], c = ph[2 * k2 + 1];
-        const uint32_t ah = f32_to_bf16_rne(a), ch = f32_to_bf16_rne(c);
-        phi[k2] = ah | (ch << 16);
-        plo[k2] = f32_to_bf16_rne(a - bf16_to_f32((uint16_t)ah)) |
-                  (f32_to_bf16_rne(c - bf16_to_f32((uint16_t)ch)) << 16);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < S::R; ++k) phi[k] = __float_as_uint(ph[k]);
-    }
-  }
+  const int vis = visible_tokens(a.seq_lens[b], a.q_len, qi);
+  const int tok0 = pg0 * S::P;
+  const int tok1 = min(vis, tok0 + a.chunk);
+  if (tok0 >= tok1) return;  // uniform for the whole workgroup
+  __syncthreads();           // page ids and q in LDS
 
-  float m_run = -INFINITY;  // running max (same in the 16 lanes of a head)
-  float l_run = 0.f;        // this lane's share of the exp-sum
-  float accR[S::R];         // this lane's share of sum_j w_j R_V[h, j]
-#pragma unroll
-  for (int k = 0; k < S::R; ++k) accR[k] = 0.f;
-  float accS[4][2];  // sum_j w_j S_V[j][2*lane + e] for the wavefront's four heads
-#pragma unroll
-  for (int x = 0; x < 4; ++x) accS[x][0] = accS[x][1] = 0.f;
-  const int dl = (2 * lane < S::DH) ? lane : (S::DH / 2 - 1);  // feature pair of this lane
-
-  const int32_t* tab = page_table + (size_t)b * max_pages;
-  const int pg0 = tok0 / S::P;
   const int pg1 = (tok1 + S::P - 1) / S::P;
-  for (int pg = pg0; pg < pg1; ++pg) {
-    const uint8_t* page = pool + (size_t)tab[pg] * S::PAGE;
-    const int nvalid = min(S::P, tok1 - pg * S::P);
+  const uint8_t* pool = a.pool;
+  auto page_ptr = [&](int pg) { return pool + (size_t)ids_lds[pg - pg0] * S::PAGE; };
+  auto nvalid = [&](int pg) { return min(S::P, tok1 - pg * S::P); };
 
-    __syncthreads();  // the previous page's LDS tiles are no longer read
-    for (int c = tid; c < 2 * S::DHC * S::P; c += NT) {
-      const uint4 v = reinterpret_cast<const uint4*>(page)[c];
-      if (c < S::DHC * S::P) {
-        sk_lds[c] = v;
-      } else {
-        const int cc = c - S::DHC * S::P;
-        sv_lds[(cc % S::P) * S::DHC + cc / S::P] = v;
-      }
-    }
-    uint4 rk[S::RC], rv[S::RC];
-    {
-      const uint4* rkp = reinterpret_cast<const uint4*>(page + S::OFF_RK + h * S::SEC_R) + j;
-      const uint4* rvp = reinterpret_cast<const uint4*>(page + S::OFF_RV + h * S::SEC_R) + j;
+  PageRegs<S> ra, rb;
+  issue_page<S>(page_ptr(pg0), tid, h, j, ra);  // in flight while p is formed
+  form_private_queries<S>(a.BK, q_lds, pacc, p_lds, tid);
+  stage_shared<S>(sk_lds[0], sv_lds[0], tid, ra, nvalid(pg0));
+  __syncthreads();
+
+  SplitState<S> st;
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
 #pragma unroll
-      for (int c = 0; c < S::RC; ++c) {
-        rk[c] = rkp[c * S::P];
-        rv[c] = rvp[c * S::P];
-      }
-    }
+  for (int k = 0; k < S::R; ++k) st.accR[k] = 0.f;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) st.accS[x][0] = st.accS[x][1] = 0.f;
+
+  for (int pg = pg0; pg < pg1; pg += 2) {
+    // page pg: registers ra, LDS buffer 0; page pg+1 goes in flight into rb
+    const bool has1 = pg + 1 < pg1;
+    if (has1) issue_page<S>(page_ptr(pg + 1), tid, h, j, rb);
+    consume_page<S>(sk_lds[0], sv_lds[0], q_lds, p_lds, h, j, lane, nvalid(pg), a.score_scale,
+                    ra, st);
+    if (has1) stage_shared<S>(sk_lds[1], sv_lds[1], tid, rb, nvalid(pg + 1));
     __syncthreads();
-
-    const bool valid = j < nvalid;
-    // ---- score: q . S_K[j] + p . R_K[h, j]  (eq 6)
-    float acc = 0.f;
-#pragma unroll
-    for (int c = 0; c < S::DHC; ++c) {
-      const uint4 s4 = sk_lds[c * S::P + j];
-      if constexpr (S::BF) {
-        acc = dot2_bf16(qv[4 * c + 0], s4.x, acc);
-        acc = dot2_bf16(qv[4 * c + 1], s4.y, acc);
-        acc = dot2_bf16(qv[4 * c + 2], s4.z, acc);
-        acc = dot2_bf16(qv[4 * c + 3], s4.w, acc);
-      } else {
-        acc = fmaf(__uint_as_float(qv[4 * c + 0]), __uint_as_float(s4.x), acc);
-        acc = fmaf(__uint_as_float(qv[4 * c + 1]), __uint_as_float(s4.y), acc);
-        acc = fmaf(__uint_as_float(qv[4 * c + 2]), __uint_as_float(s4.z), acc);
-        acc = fmaf(__uint_as_float(qv[4 * c + 3]), __uint_as_float(s4.w), acc);
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < S::RC; ++c) {
-      const uint32_t r4[4] = {rk[c].x, rk[c].y, rk[c].z, rk[c].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (S::BF) {
-          acc = dot2_bf16(phi[4 * c + e], r4[e], acc);
-          acc = dot2_bf16(plo[4 * c + e], r4[e], acc);
-        } else {
-          acc = fmaf(__uint_as_float(phi[4 * c + e]), __uint_as_float(r4[e]), acc);
-        }
-      }
-    }
-    // masked slots are removed by selection, never multiplied by zero
-    const float s = valid ? acc * score_scale : -INFINITY;
-
-    // ---- online softmax, one factor rescales exp-sum and both accumulators
-    const float m_new = fmaxf(m_run, row16_max(s));
-    const float alpha = exp2f(m_run - m_new);
-    const float w = exp2f(s - m_new);
-    l_run = l_run * alpha + w;
-    if (!valid) {
-#pragma unroll
-      for (int c = 0; c < S::RC; ++c) rv[c] = make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int c = 0; c < S::RC; ++c) {
-      const uint32_t r4[4] = {rv[c].x, rv[c].y, rv[c].z, rv[c].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (S::BF) {
-          const int k = 8 * c + 2 * e;
-          accR[k] = fmaf(w, bf16_lo(r4[e]), accR[k] * alpha);
-          accR[k + 1] = fmaf(w, bf16_hi(r4[e]), accR[k + 1] * alpha);
-        } else {
-          const int k = 4 * c + e;
-          accR[k] = fmaf(w, __uint_as_float(r4[e]), accR[k] * alpha);
-        }
-      }
-    }
-    m_run = m_new;
-
-    // ---- shared value accumulator: lanes over feature pairs, weights broadcast by readlane
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const float a = readlane_f(alpha, 16 * x);
-      accS[x][0] *= a;
-      accS[x][1] *= a;
-    }
-    for (int t = 0; t < nvalid; ++t) {
-      float sv0, sv1;
-      if constexpr (S::BF) {
-        const uint32_t pr = reinterpret_cast<const uint32_t*>(sv_lds)[t * (S::DH / 2) + dl];
-        sv0 = bf16_lo(pr);
-        sv1 = bf16_hi(pr);
-      } else {
-        const float2 pr = reinterpret_cast<const float2*>(sv_lds)[t * (S::DH / 2) + dl];
-        sv0 = pr.x;
-        sv1 = pr.y;
-      }
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const float wt = readlane_f(w, 16 * x + t);
-        accS[x][0] = fmaf(wt, sv0, accS[x][0]);
-        accS[x][1] = fmaf(wt, sv1, accS[x][1]);
-      }
-    }
+    if (!has1) break;
+    // page pg+1: registers rb, LDS buffer 1; page pg+2 goes in flight into ra
+    const bool has2 = pg + 2 < pg1;
+    if (has2) issue_page<S>(page_ptr(pg + 2), tid, h, j, ra);
+    consume_page<S>(sk_lds[1], sv_lds[1], q_lds, p_lds, h, j, lane, nvalid(pg + 1),
+                    a.score_scale, rb, st);
+    if (has2) stage_shared<S>(sk_lds[0], sv_lds[0], tid, ra, nvalid(pg + 2));
+    __syncthreads();
   }
 
   // ---- partial tuple of this chunk: m, l, acc_S[DH], acc_R[R] per head
-  const float l_tot = row16_sum(l_run);
+  const float l_tot = r16_sum(st.l_run);
 #pragma unroll
-  for (int k = 0; k < S::R; ++k) accR[k] = row16_sum(accR[k]);
-  float* dst = part + ((row * n_split + split) * S::H + h) * S::PART;
+  for (int k = 0; k < S::R; ++k) st.accR[k] = r16_sum(st.accR[k]);
+  float* dst = a.part + ((row * a.n_split + split) * S::H + h) * S::PART_PAD;
   if (j == 0) {
-    dst[0] = m_run;
+    dst[0] = st.m_run;
     dst[1] = l_tot;
   }
 #pragma unroll
   for (int k = 0; k < S::R; ++k)
-    if ((k & 15) == j) dst[2 + S::DH + k] = accR[k];
+    if ((k & 15) == j) dst[2 + S::DH + k] = st.accR[k];
   if (2 * lane < S::DH) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      float* d2 = part + ((row * n_split + split) * S::H + 4 * wave + x) * S::PART + 2 + 2 * lane;
-      d2[0] = accS[x][0];
-      d2[1] = accS[x][1];
+      float2* d2 = reinterpret_cast<float2*>(
+          a.part + ((row * a.n_split + split) * S::H + 4 * wave + x) * S::PART_PAD + 2 + 2 * lane);
+      *d2 = make_float2(st.accS[x][0], st.accS[x][1]);
     }
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// 3. merge + expand
-// Workgroup = (head, query row, request); thread t owns column 1 + t of the partial tuple
-// (l, acc_S[DH], acc_R[R]) and sums it over the chunks with weights exp2(m_s - m*).
+// 2. merge + expand.  Workgroup = (head, query row, request), 256 threads.  Thread t owns
+// one column of the partial record: t < DH -> acc_S[t], t < DH + R -> acc_R[t - DH],
+// t == DH + R -> l.  When every chunk fits in LDS (the usual case) one memory round trip
+// does: the records of all n_split chunks (16-byte loads issued together, before the request
+// length is known; records past the visible chunks are ignored) and the thread's B_V row.
+// Then m* and the weights exp2(m_s - m*) come from the LDS copy, columns are summed over the
+// chunks in chunk order, and o[d] = (A_S[d] + A_R . B_V[h][d]) / L.
 // ---------------------------------------------------------------------------------------
 template <class S>
 __global__ void __launch_bounds__(256)
 merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
                     const int32_t* __restrict__ seq_lens, int q_len, int n_split, int chunk,
                     void* __restrict__ out) {
-  static_assert(1 + S::DH + S::R <= 256, "one thread per column");
+  static_assert(S::DH + S::R + 1 <= 256, "one thread per column");
+  constexpr int PP = S::PART_PAD;
+  constexpr int MS_LDS = (48 * 1024) / (PP * 4);
+  constexpr int MS = MS_LDS < 256 ? MS_LDS : 256;  // chunks per pass held in LDS
+  __shared__ float4 tile[MS * PP / 4];
+  __shared__ float wts[MS];
+  __shared__ float red[4];
   __shared__ float accR_s[S::R];
   __shared__ float l_s;
   const int h = blockIdx.x;
@@ -282,10 +490,30 @@ merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
   const int b = blockIdx.z;
   const int t = threadIdx.x;
   const size_t row = (size_t)b * q_len + qi;
+  const size_t out_off = (row * S::H + h) * S::DH;
+  const int col = t < S::DH + S::R ? 2 + t : (t == S::DH + S::R ? 1 : -1);
+  const float* base = part + (row * n_split * S::H + h) * PP;
+  const size_t stride = (size_t)S::H * PP;  // floats between chunks of the same head
+  const float* tf = reinterpret_cast<const float*>(tile);
+
+  auto load_pass = [&](int s0, int cnt) {
+    for (int i = t; i < cnt * (PP / 4); i += 256) {
+      const int s = i / (PP / 4), c4 = i - s * (PP / 4);
+      tile[i] = reinterpret_cast<const float4*>(base + (size_t)(s0 + s) * stride)[c4];
+    }
+  };
+  // first pass and B_V row go out before the length is known
+  if (n_split <= MS) load_pass(0, n_split);
+  constexpr int BVW = S::R * S::EB / 16;
+  uint4 bvr[BVW];
+  if (t < S::DH) {
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(BV) +
+                                                      ((size_t)h * S::DH + t) * S::R * S::EB);
+#pragma unroll
+    for (int c = 0; c < BVW; ++c) bvr[c] = src[c];
+  }
   const int vis = visible_tokens(seq_lens[b], q_len, qi);
   const int n = (vis + chunk - 1) / chunk;
-  const size_t out_off = (row * S::H + h) * S::DH;
-
   if (n == 0) {  // no visible token: zeros
     if (t < S::DH) {
       if constexpr (S::BF) static_cast<uint16_t*>(out)[out_off + t] = 0;
@@ -293,32 +521,75 @@ merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
     }
     return;
   }
-  const float* base = part + (row * n_split * S::H + h) * S::PART;
-  const size_t stride = (size_t)S::H * S::PART;  // next chunk, same head
-  float m_star = -INFINITY;
-  for (int s = 0; s < n; ++s) m_star = fmaxf(m_star, base[s * stride]);
-  const int col = 1 + t;
-  float v = 0.f;
-  if (col < S::PART) {
-    for (int s = 0; s < n; ++s) v = fmaf(exp2f(base[s * stride] - m_star), base[s * stride + col], v);
-    if (col == 1) l_s = v;
-    else if (col >= 2 + S::DH) accR_s[col - 2 - S::DH] = v;
+  auto block_max = [&](float m) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o));
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    return __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+  };
+
+  float m_star;
+  if (n_split <= MS) {
+    __syncthreads();
+    m_star = block_max(t < n ? tf[t * PP] : -INFINITY);
+  } else {
+    float m = -INFINITY;
+    for (int s = t; s < n; s += 256) m = __builtin_fmaxf(m, base[s * stride]);
+    m_star = block_max(m);
   }
-  __syncthreads();
-  if (col >= 2 && col < 2 + S::DH) {
-    const int d = col - 2;
-    float o = v;  // acc_S[d]
-    if constexpr (S::BF) {
-      const uint16_t* bv = static_cast<const uint16_t*>(BV) + ((size_t)h * S::DH + d) * S::R;
-#pragma unroll 8
-      for (int k = 0; k < S::R; ++k) o = fmaf(accR_s[k], bf16_to_f32(bv[k]), o);
-      static_cast<uint16_t*>(out)[out_off + d] = (uint16_t)f32_to_bf16_rne(o / l_s);
-    } else {
-      const float* bv = static_cast<const float*>(BV) + ((size_t)h * S::DH + d) * S::R;
-#pragma unroll 4
-      for (int k = 0; k < S::R; ++k) o = fmaf(accR_s[k], bv[k], o);
-      static_cast<float*>(out)[out_off + d] = o / l_s;
+
+  float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
+  for (int s0 = 0; s0 < n; s0 += MS) {
+    const int cnt = min(MS, n - s0);
+    if (n_split > MS) {
+      __syncthreads();  // previous pass done with tile
+      load_pass(s0, cnt);
+      __syncthreads();
     }
+    if (t < cnt) wts[t] = exp2f(tf[t * PP] - m_star);
+    __syncthreads();
+    if (col >= 0) {
+      int s = 0;
+      for (; s + 4 <= cnt; s += 4) {
+        v0 = fmaf(wts[s], tf[s * PP + col], v0);
+        v1 = fmaf(wts[s + 1], tf[(s + 1) * PP + col], v1);
+        v2 = fmaf(wts[s + 2], tf[(s + 2) * PP + col], v2);
+        v3 = fmaf(wts[s + 3], tf[(s + 3) * PP + col], v3);
+      }
+      for (; s < cnt; ++s) v0 = fmaf(wts[s], tf[s * PP + col], v0);
+    }
+    __syncthreads();  // wts reused by the next pass
+  }
+  const float v = (v0 + v1) + (v2 + v3);
+  if (col == 1) l_s = v;
+  else if (t >= S::DH && t < S::DH + S::R) accR_s[t - S::DH] = v;
+  __syncthreads();
+
+  if (t < S::DH) {
+    float o = v;  // A_S[t]
+#pragma unroll
+    for (int c = 0; c < BVW; ++c) {
+      if constexpr (S::BF) {
+        o = fmaf(accR_s[8 * c + 0], bf16_lo(bvr[c].x), o);
+        o = fmaf(accR_s[8 * c + 1], bf16_hi(bvr[c].x), o);
+        o = fmaf(accR_s[8 * c + 2], bf16_lo(bvr[c].y), o);
+        o = fmaf(accR_s[8 * c + 3], bf16_hi(bvr[c].y), o);
+        o = fmaf(accR_s[8 * c + 4], bf16_lo(bvr[c].z), o);
+        o = fmaf(accR_s[8 * c + 5], bf16_hi(bvr[c].z), o);
+        o = fmaf(accR_s[8 * c + 6], bf16_lo(bvr[c].w), o);
+        o = fmaf(accR_s[8 * c + 7], bf16_hi(bvr[c].w), o);
+      } else {
+        o = fmaf(accR_s[4 * c + 0], __uint_as_float(bvr[c].x), o);
+        o = fmaf(accR_s[4 * c + 1], __uint_as_float(bvr[c].y), o);
+        o = fmaf(accR_s[4 * c + 2], __uint_as_float(bvr[c].z), o);
+        o = fmaf(accR_s[4 * c + 3], __uint_as_float(bvr[c].w), o);
+      }
+    }
+    if constexpr (S::BF)
+      static_cast<uint16_t*>(out)[out_off + t] = (uint16_t)f32_to_bf16_rne(o / l_s);
+    else
+      static_cast<float*>(out)[out_off + t] = o / l_s;
   }
 }
 
@@ -327,14 +598,20 @@ merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
 // ---------------------------------------------------------------------------------------
 template <class S>
 hipError_t launch_decode(const DecodeArgs& a) {
-  const int rows = a.batch * a.q_len;
-  const int pq_threads = ((S::H * S::R + 63) / 64) * 64;
-  hipLaunchKernelGGL(private_query_kernel<S>, dim3(rows), dim3(pq_threads), 0, a.stream, a.q,
-                     a.B_K, a.p_ws);
-  const float score_scale = 1.4426950408889634f / sqrtf((float)S::DH);
+  SplitArgs s{};
+  s.q = a.q;
+  s.BK = a.B_K;
+  s.pool = static_cast<const uint8_t*>(a.pool);
+  s.page_table = a.page_table;
+  s.seq_lens = a.seq_lens;
+  s.part = a.part_ws;
+  s.max_pages = a.max_pages;
+  s.q_len = a.q_len;
+  s.n_split = a.n_split;
+  s.chunk = a.chunk;
+  s.score_scale = 1.4426950408889634f / sqrtf((float)S::DH);
   hipLaunchKernelGGL(decode_split_kernel<S>, dim3(a.n_split, a.q_len, a.batch), dim3(S::H * 16),
-                     0, a.stream, a.q, a.p_ws, static_cast<const uint8_t*>(a.pool), a.page_table,
-                     a.max_pages, a.seq_lens, a.q_len, a.n_split, a.chunk, a.part_ws, score_scale);
+                     0, a.stream, s);
   hipLaunchKernelGGL(merge_expand_kernel<S>, dim3(S::H, a.q_len, a.batch), dim3(256), 0, a.stream,
                      a.part_ws, a.B_V, a.seq_lens, a.q_len, a.n_split, a.chunk, a.out);
   return hipGetLastError();

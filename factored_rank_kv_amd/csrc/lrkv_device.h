@@ -27,7 +27,8 @@ struct Shape {
   static constexpr int OFF_SV = SEC_S;
   static constexpr int OFF_RK = 2 * SEC_S;
   static constexpr int OFF_RV = 2 * SEC_S + H * SEC_R;
-  static constexpr int PART = 2 + DH + R;       // floats per head in a split partial
+  static constexpr int PART = 2 + DH + R;       // floats of a chunk's partial tuple per head
+  static constexpr int PART_PAD = (PART + 3) / 4 * 4;  // record stride (16-byte rows)
   static_assert(DH % CE == 0 && R % CE == 0, "widths must be whole 16-byte chunks");
 };
 

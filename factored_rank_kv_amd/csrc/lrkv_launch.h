@@ -26,8 +26,7 @@ struct DecodeArgs {
   int n_split;   // chunks per (request, query row)
   int chunk;     // tokens per chunk, a multiple of the page size
   void* out;
-  float* p_ws;   // [batch][q_len][H][r] float32
-  float* part_ws;  // [batch][q_len][n_split][H][2 + d_h + r] float32
+  float* part_ws;  // [batch][q_len][n_split][H][record of 2 + d_h + r floats, padded to 4]
   hipStream_t stream;
 };
 

@@ -60,12 +60,13 @@ def test_page_bytes_rejects_invalid_layouts():
 def test_workspace_sizes():
     w = F.lrkv_decode_workspace_bytes(C1, 8, 1, 4096, 0)
     assert w > 0 and w % 256 == 0
-    # explicit chunks: private queries + one partial tuple per (row, chunk, head)
+    # explicit chunks: one partial tuple per (row, chunk, head)
     w16 = F.lrkv_decode_workspace_bytes(C1, 8, 1, 4096, 16)
     rows, H, r, dh = 8, 16, 56, 128
-    p_bytes = -(-rows * H * r * 4 // 256) * 256
-    part = -(-rows * 256 * H * (2 + dh + r) * 4 // 256) * 256
-    assert w16 == p_bytes + part
+    rec = -(-(2 + dh + r) // 4) * 4  # partial records padded to 16 bytes
+    part = -(-rows * 256 * H * rec * 4 // 256) * 256
+    assert w16 == part
+    assert F.lrkv_decode_workspace_bytes(C1, 8, 1, 4096, 4096 + 16) == 0  # chunk too long
     assert F.lrkv_decode_workspace_bytes(C1, 8, 1, 4096, 24) == 0  # not a multiple of P
     assert F.lrkv_decode_workspace_bytes(C1, 0, 1, 4096, 0) == 0
 
