@@ -51,10 +51,18 @@ __device__ __forceinline__ float r16_sum(float x) {
 // ---------------------------------------------------------------------------------------
 // 1. split kernel
 //
-// Workgroup = (chunk, query row qi, request b); H/4 wavefronts.  For the score, the softmax
-// and the private value, lane = 16*hl + j covers head h = 4*wave + hl and token slot j of
-// the page.  For the shared value the wavefront switches to lanes over feature pairs
-// (2*lane, 2*lane+1) of its four heads, with the weights broadcast by readlane.
+// Workgroup = (chunk, query row qi, request b); NW = H / HPW wavefronts, HPW heads each.
+// For the score, the softmax and the private value, lane = hl*(16*SPLIT) + half*16 + j
+// covers head h = HPW*wave + hl and token slot j of the page; with SPLIT = 2 the two
+// lanes (half = 0, 1) of a (head, token) pair each take half of the features of the dot
+// products and of the private value, and add their partial scores with one swizzle.  For
+// the shared value the wavefront switches to lanes over feature pairs (2*lane, 2*lane+1)
+// of its HPW heads, with the weights broadcast by readlane.
+//
+// Pipeline: pages pg+1 and pg+2 are in flight (three register buffers) while page pg is
+// consumed; the S tiles go through a double-buffered LDS stage.  Page bytes are read with
+// non-temporal loads: the stream is used once and should not evict the small operands that
+// every workgroup re-reads (B_K, queries, page tables).
 //
 // Scores are in base-2 units, s = (q.S_K + p.R_K) * log2(e)/sqrt(d_h), so exp2 is used here
 // and in the merge.  The running reference max of a head moves only when a page's max
@@ -82,46 +90,85 @@ struct SplitArgs {
 
 template <class S>
 struct SplitCfg {
-  static constexpr int NT = S::H * 16;
-  static constexpr int S_CHUNKS = 2 * S::DHC * S::P;    // 16-byte chunks of S_K + S_V
-  static constexpr int SPT = (S_CHUNKS + NT - 1) / NT;  // per thread
-  // two resident workgroups per CU (<= 256 registers per lane) up to 8 wavefronts each
-  static constexpr int MIN_BLOCKS = NT >= 512 ? 1 : 2;
-  // LDS rows of q and p per head; odd strides (in 16-byte units) put the four heads of a
-  // wavefront on different banks
+  static constexpr int HPW = S::H <= 4 ? 4 : (S::H / 8 > 2 ? S::H / 8 : 2);  // heads per wave
+  static constexpr int SPLIT = 4 / HPW;        // lanes per (head, token) pair
+  static constexpr int NW = S::H / HPW;
+  static constexpr int NT = NW * 64;
+  static constexpr int DHC_L = S::DHC / SPLIT;                  // S_K chunks per lane
+  static constexpr int RC_L = (S::RC + SPLIT - 1) / SPLIT;      // private chunks per lane
+  static constexpr int S_CHUNKS = 2 * S::DHC * S::P;            // 16-byte chunks of S_K + S_V
+  static constexpr int SPT = (S_CHUNKS + NT - 1) / NT;          // per thread
+  // LDS rows of q and p per head; odd strides (in 16-byte units) spread a wavefront's
+  // heads over different banks
   static constexpr int Q_STRIDE = S::DHC + 1;
-  static constexpr int P_WORDS = S::RC * (S::BF ? 2 : 1);  // bf16: hi chunk, lo chunk
-  static constexpr int P_STRIDE = P_WORDS | 1;
+  static constexpr int P_PER_CHUNK = S::BF ? 2 : 1;  // uint4 per chunk (bf16: hi, lo)
+  // room for SPLIT*RC_L chunks: the slots past RC hold zeros, so a lane whose half runs
+  // past the last private chunk adds nothing for it
+  static constexpr int P_STRIDE = (SPLIT * RC_L * P_PER_CHUNK) | 1;
   // private queries: one job per (head, 16-byte chunk of p), d_h split over PQ_GROUPS
   static constexpr int PQ_JOBS = S::H * S::RC;
   static constexpr int PQ_GROUPS = NT / PQ_JOBS > 0 ? NT / PQ_JOBS : 1;
   static constexpr int PQ_DSPAN = S::DH / PQ_GROUPS;
+  static_assert(HPW * SPLIT == 4, "64 lanes = HPW heads x SPLIT x 16 tokens");
+  static_assert(S::DHC % SPLIT == 0, "shared chunks split evenly");
   static_assert(S::DH % PQ_GROUPS == 0, "d_h split evenly");
+  static_assert(NT <= 1024, "workgroup size");
 };
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 template <class S>
 struct PageRegs {
-  uint4 rk[S::RC];
-  uint4 rv[S::RC];
+  uint4 rk[SplitCfg<S>::RC_L];
+  uint4 rv[SplitCfg<S>::RC_L];
   uint4 st[SplitCfg<S>::SPT];
 };
 
+// Lane geometry inside the workgroup.
 template <class S>
-__device__ __forceinline__ void issue_page(const uint8_t* __restrict__ page, int tid, int h, int j,
+struct Lane {
+  int tid, lane, wave, hl, half, j, h;
+  __device__ __forceinline__ Lane(int t) {
+    using C = SplitCfg<S>;
+    tid = t;
+    lane = t & 63;
+    wave = t >> 6;
+    hl = lane / (16 * C::SPLIT);
+    half = (lane >> 4) & (C::SPLIT - 1);
+    j = lane & 15;
+    h = wave * C::HPW + hl;
+  }
+};
+
+template <class S>
+__device__ __forceinline__ void issue_page(const uint8_t* __restrict__ page, const Lane<S>& L,
                                            PageRegs<S>& r) {
   using C = SplitCfg<S>;
   const uint4* p4 = reinterpret_cast<const uint4*>(page);
 #pragma unroll
   for (int i = 0; i < C::SPT; ++i) {
-    const int c = tid + i * C::NT;
-    if (C::S_CHUNKS % C::NT == 0 || c < C::S_CHUNKS) r.st[i] = p4[c];
+    const int c = L.tid + i * C::NT;
+    if (C::S_CHUNKS % C::NT == 0 || c < C::S_CHUNKS) r.st[i] = load_stream(p4 + c);
   }
-  const uint4* rkp = reinterpret_cast<const uint4*>(page + S::OFF_RK + h * S::SEC_R) + j;
-  const uint4* rvp = reinterpret_cast<const uint4*>(page + S::OFF_RV + h * S::SEC_R) + j;
+  const uint4* rkp = reinterpret_cast<const uint4*>(page + S::OFF_RK + L.h * S::SEC_R) + L.j;
+  const uint4* rvp = reinterpret_cast<const uint4*>(page + S::OFF_RV + L.h * S::SEC_R) + L.j;
+  // private chunks of this lane; a chunk index past the last one re-reads the last chunk
+  // (its score term has p = 0 and its value term is never written out)
 #pragma unroll
-  for (int c = 0; c < S::RC; ++c) r.rk[c] = rkp[c * S::P];
+  for (int c = 0; c < C::RC_L; ++c) {
+    const int cg = min(L.half * C::RC_L + c, S::RC - 1);
+    r.rk[c] = load_stream(rkp + cg * S::P);
+  }
 #pragma unroll
-  for (int c = 0; c < S::RC; ++c) r.rv[c] = rvp[c * S::P];
+  for (int c = 0; c < C::RC_L; ++c) {
+    const int cg = min(L.half * C::RC_L + c, S::RC - 1);
+    r.rv[c] = load_stream(rvp + cg * S::P);
+  }
 }
 
 // S_V row t (= S_V[t][0..DH)) keeps its 16-byte chunks in XOR-swizzled order inside the
@@ -156,8 +203,37 @@ __device__ __forceinline__ void stage_shared(uint4* __restrict__ sk, uint4* __re
 // into LDS for the private score.  bf16 cache: per 8-feature chunk, 4 words of bfloat16
 // pairs of hi(p) then 4 words of lo(p) = bf16(p - hi(p)), so p.R_K[h,j] = dot2(hi, r) +
 // dot2(lo, r) keeps about 16 significant bits of p.  float32 cache: p as it is.
+// B_K rows of this thread's private-query job: job (head h, 16-byte chunk c of p), rows
+// d in group g's span.  Issued before any page load: vector loads return in issue order,
+// so rows requested after the pages would wait for the pages.
 template <class S>
-__device__ __forceinline__ void form_private_queries(const void* __restrict__ BK,
+struct BKRows {
+  uint4 v[SplitCfg<S>::PQ_DSPAN];
+};
+
+template <class S>
+__device__ __forceinline__ void load_bk_rows(const void* __restrict__ BK, int tid, BKRows<S>& r) {
+  using C = SplitCfg<S>;
+  // threads past the last group load a valid row they never use: no branch, so the loads
+  // stay where they are written
+  const int job = tid % C::PQ_JOBS;
+  const int g = min(tid / C::PQ_JOBS, C::PQ_GROUPS - 1);
+  const int h = job / S::RC;
+  const int c = job - h * S::RC;
+  const uint8_t* bk = static_cast<const uint8_t*>(BK) +
+                      ((size_t)h * S::DH * S::R + (size_t)c * S::CE) * S::EB;
+#pragma unroll
+  for (int dd = 0; dd < C::PQ_DSPAN; ++dd)
+    r.v[dd] = *reinterpret_cast<const uint4*>(bk + (size_t)(g * C::PQ_DSPAN + dd) * S::R * S::EB);
+  asm volatile("" ::: "memory");  // keep them ahead of the page loads that follow
+}
+
+// p = q B_K[h] for every head of the row, float32 sums over d_h in a fixed order, packed
+// into LDS for the private score.  bf16 cache: per 8-feature chunk, 4 words of bfloat16
+// pairs of hi(p) then 4 words of lo(p) = bf16(p - hi(p)), so p.R_K[h,j] = dot2(hi, r) +
+// dot2(lo, r) keeps about 16 significant bits of p.  float32 cache: p as it is.
+template <class S>
+__device__ __forceinline__ void form_private_queries(const BKRows<S>& bkr,
                                                      const uint4* __restrict__ q_lds,
                                                      float* __restrict__ pacc,
                                                      uint4* __restrict__ p_lds, int tid) {
@@ -166,17 +242,14 @@ __device__ __forceinline__ void form_private_queries(const void* __restrict__ BK
   const int g = tid / C::PQ_JOBS;
   if (g < C::PQ_GROUPS) {
     const int h = job / S::RC;
-    const int c = job - h * S::RC;
     float acc[S::CE];
 #pragma unroll
     for (int e = 0; e < S::CE; ++e) acc[e] = 0.f;
-    const uint8_t* bk = static_cast<const uint8_t*>(BK) +
-                        ((size_t)h * S::DH * S::R + (size_t)c * S::CE) * S::EB;
     const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q_lds + h * C::Q_STRIDE);
-#pragma unroll 16
+#pragma unroll
     for (int dd = 0; dd < C::PQ_DSPAN; ++dd) {
       const int d = g * C::PQ_DSPAN + dd;
-      const uint4 b4 = *reinterpret_cast<const uint4*>(bk + (size_t)d * S::R * S::EB);
+      const uint4 b4 = bkr.v[dd];
       if constexpr (S::BF) {
         const float qd = bf16_to_f32(reinterpret_cast<const uint16_t*>(qrow)[d]);
         acc[0] = fmaf(qd, bf16_lo(b4.x), acc[0]);
@@ -197,6 +270,11 @@ __device__ __forceinline__ void form_private_queries(const void* __restrict__ BK
     }
 #pragma unroll
     for (int e = 0; e < S::CE; ++e) pacc[(g * C::PQ_JOBS + job) * S::CE + e] = acc[e];
+  }
+  constexpr int PAD = C::P_STRIDE - S::RC * C::P_PER_CHUNK;  // zero slots per head
+  if constexpr (PAD > 0) {
+    for (int i = tid; i < S::H * PAD; i += C::NT)
+      p_lds[(i / PAD) * C::P_STRIDE + S::RC * C::P_PER_CHUNK + i % PAD] = make_uint4(0u, 0u, 0u, 0u);
   }
   __syncthreads();
   if (tid < C::PQ_JOBS) {
@@ -231,27 +309,36 @@ __device__ __forceinline__ void form_private_queries(const void* __restrict__ BK
 
 template <class S>
 struct SplitState {
-  float m_run;       // reference max of the lane's head (equal in its 16 lanes)
-  float l_run;       // this lane's share of the exp-sum
-  float accR[S::R];  // this lane's share of sum_j w_j R_V[h, j]
-  float accS[4][2];  // sum_j w_j S_V[j][2*lane + e] for the wavefront's four heads
+  float m_run;                                // reference max of the lane's head
+  float l_run;                                // this lane's share of the exp-sum
+  float accR[SplitCfg<S>::RC_L * S::CE];      // its share of sum_j w_j R_V[h, j] (its half)
+  float accS[SplitCfg<S>::HPW][2];            // sum_j w_j S_V[j][2*lane + e] per head
 };
+
+// the partner lane of a (head, token) pair holds the other half of the features
+__device__ __forceinline__ float add_partner(float x) {
+  return x + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
 
 template <class S>
 __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
                                              const uint4* __restrict__ sv,
                                              const uint4* __restrict__ q_lds,
-                                             const uint4* __restrict__ p_lds, int h, int j,
-                                             int lane, int nvalid, float score_scale,
+                                             const uint4* __restrict__ p_lds, const Lane<S>& L,
+                                             int nvalid, float score_scale,
                                              const PageRegs<S>& r, SplitState<S>& st) {
   using C = SplitCfg<S>;
+  const int j = L.j;
   const bool valid = j < nvalid;
-  // ---- score: q . S_K[j] + p . R_K[h, j]   (eq 6)
+  // ---- score: q . S_K[j] + p . R_K[h, j]   (eq 6), this lane's half of the features
   float acc0 = 0.f, acc1 = 0.f;
-  const uint4* qh = q_lds + h * C::Q_STRIDE;
+  const uint4* qh = q_lds + L.h * C::Q_STRIDE + L.half * C::DHC_L;
+  const uint4* skh = sk + L.half * C::DHC_L * S::P;
 #pragma unroll
-  for (int c = 0; c < S::DHC; ++c) {
-    const uint4 s4 = sk[c * S::P + j];
+  for (int c = 0; c < C::DHC_L; ++c) {
+    // at most four chunk pairs of LDS operands in registers at a time
+    if (c % 4 == 0) __builtin_amdgcn_sched_barrier(0);
+    const uint4 s4 = skh[c * S::P + j];
     const uint4 q4 = qh[c];
     if constexpr (S::BF) {
       acc0 = dot2_bf16(q4.x, s4.x, acc0);
@@ -265,12 +352,13 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
       acc1 = fmaf(__uint_as_float(q4.w), __uint_as_float(s4.w), acc1);
     }
   }
-  const uint4* ph = p_lds + h * C::P_STRIDE;
+  const uint4* ph = p_lds + L.h * C::P_STRIDE;
 #pragma unroll
-  for (int c = 0; c < S::RC; ++c) {
+  for (int c = 0; c < C::RC_L; ++c) {
+    const int cg = L.half * C::RC_L + c;  // slots past RC hold p = 0
     const uint4 k4 = r.rk[c];
     if constexpr (S::BF) {
-      const uint4 hi = ph[2 * c], lo = ph[2 * c + 1];
+      const uint4 hi = ph[2 * cg], lo = ph[2 * cg + 1];
       acc0 = dot2_bf16(hi.x, k4.x, acc0);
       acc1 = dot2_bf16(hi.y, k4.y, acc1);
       acc0 = dot2_bf16(hi.z, k4.z, acc0);
@@ -280,15 +368,17 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
       acc0 = dot2_bf16(lo.z, k4.z, acc0);
       acc1 = dot2_bf16(lo.w, k4.w, acc1);
     } else {
-      const uint4 p4 = ph[c];
+      const uint4 p4 = ph[cg];
       acc0 = fmaf(__uint_as_float(p4.x), __uint_as_float(k4.x), acc0);
       acc1 = fmaf(__uint_as_float(p4.y), __uint_as_float(k4.y), acc1);
       acc0 = fmaf(__uint_as_float(p4.z), __uint_as_float(k4.z), acc0);
       acc1 = fmaf(__uint_as_float(p4.w), __uint_as_float(k4.w), acc1);
     }
   }
+  float full = acc0 + acc1;
+  if constexpr (C::SPLIT == 2) full = add_partner(full);
   // masked slots leave by selection, never by multiplying with zero
-  const float s = valid ? (acc0 + acc1) * score_scale : -INFINITY;
+  const float s = valid ? full * score_scale : -INFINITY;
 
   // ---- online softmax: the reference moves (and rescales l, acc_S, acc_R by one factor)
   // only when the page's max clears it by more than the slack
@@ -299,10 +389,10 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
     const float alpha = exp2f(st.m_run - m_new);  // 0 on the first page, 1 if not bumped
     st.l_run *= alpha;
 #pragma unroll
-    for (int k = 0; k < S::R; ++k) st.accR[k] *= alpha;
+    for (int k = 0; k < C::RC_L * S::CE; ++k) st.accR[k] *= alpha;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const float a = readlane_f(alpha, 16 * x);
+    for (int x = 0; x < C::HPW; ++x) {
+      const float a = readlane_f(alpha, x * 16 * C::SPLIT);
       st.accS[x][0] *= a;
       st.accS[x][1] *= a;
     }
@@ -311,7 +401,7 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
   const float w = exp2f(s - st.m_run);  // exactly 0 for masked slots
   st.l_run += w;
 #pragma unroll
-  for (int c = 0; c < S::RC; ++c) {
+  for (int c = 0; c < C::RC_L; ++c) {
     const uint32_t v4[4] = {valid ? r.rv[c].x : 0u, valid ? r.rv[c].y : 0u,
                             valid ? r.rv[c].z : 0u, valid ? r.rv[c].w : 0u};
 #pragma unroll
@@ -328,11 +418,13 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
   }
 
   // ---- shared value: lanes over feature pairs, weights broadcast by readlane
-  float sA0 = st.accS[0][0], sB0 = st.accS[0][1];
-  float sA1 = st.accS[1][0], sB1 = st.accS[1][1];
-  float sA2 = st.accS[2][0], sB2 = st.accS[2][1];
-  float sA3 = st.accS[3][0], sB3 = st.accS[3][1];
-  const int dl = (2 * lane < S::DH) ? lane : (S::DH / 2 - 1);
+  float sA[C::HPW], sB[C::HPW];
+#pragma unroll
+  for (int x = 0; x < C::HPW; ++x) {
+    sA[x] = st.accS[x][0];
+    sB[x] = st.accS[x][1];
+  }
+  const int dl = (2 * L.lane < S::DH) ? L.lane : (S::DH / 2 - 1);
   const int e0 = 2 * dl;  // first feature of the pair
 #pragma unroll
   for (int t = 0; t < S::P; ++t) {
@@ -347,25 +439,22 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
       sv0 = pr.x;
       sv1 = pr.y;
     }
-    const float w0 = readlane_f(w, t), w1 = readlane_f(w, 16 + t);
-    const float w2 = readlane_f(w, 32 + t), w3 = readlane_f(w, 48 + t);
-    sA0 = fmaf(w0, sv0, sA0);
-    sB0 = fmaf(w0, sv1, sB0);
-    sA1 = fmaf(w1, sv0, sA1);
-    sB1 = fmaf(w1, sv1, sB1);
-    sA2 = fmaf(w2, sv0, sA2);
-    sB2 = fmaf(w2, sv1, sB2);
-    sA3 = fmaf(w3, sv0, sA3);
-    sB3 = fmaf(w3, sv1, sB3);
+#pragma unroll
+    for (int x = 0; x < C::HPW; ++x) {
+      const float wt = readlane_f(w, x * 16 * C::SPLIT + t);
+      sA[x] = fmaf(wt, sv0, sA[x]);
+      sB[x] = fmaf(wt, sv1, sB[x]);
+    }
   }
-  st.accS[0][0] = sA0; st.accS[0][1] = sB0;
-  st.accS[1][0] = sA1; st.accS[1][1] = sB1;
-  st.accS[2][0] = sA2; st.accS[2][1] = sB2;
-  st.accS[3][0] = sA3; st.accS[3][1] = sB3;
+#pragma unroll
+  for (int x = 0; x < C::HPW; ++x) {
+    st.accS[x][0] = sA[x];
+    st.accS[x][1] = sB[x];
+  }
 }
 
 template <class S>
-__global__ void __launch_bounds__(S::H * 16, SplitCfg<S>::MIN_BLOCKS)
+__global__ void __launch_bounds__(SplitCfg<S>::NT, 1)
 decode_split_kernel(const SplitArgs a) {
   using C = SplitCfg<S>;
   __shared__ uint4 sk_lds[2][S::DHC * S::P];  // chunk-major [c][t], double buffered
@@ -378,85 +467,107 @@ decode_split_kernel(const SplitArgs a) {
   const int split = blockIdx.x;
   const int qi = blockIdx.y;
   const int b = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int hl = lane >> 4;
-  const int j = lane & 15;
-  const int h = wave * 4 + hl;
+  const Lane<S> L(threadIdx.x);
+  const int tid = L.tid;
   const size_t row = (size_t)b * a.q_len + qi;
 
-  // requests that do not depend on the request length go out together
+  // the request length (scalar load) and this chunk's page ids and query row (vector
+  // loads) travel together
   const int pg0 = split * (a.chunk / S::P);
-  {
-    const int nid = min(a.chunk / S::P, a.max_pages - pg0);  // table entries of this chunk
-    const int32_t* tab = a.page_table + (size_t)b * a.max_pages + pg0;
-    for (int i = tid; i < nid; i += C::NT) ids_lds[i] = tab[i];
-    const uint4* qsrc = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.q) +
-                                                       row * S::H * S::DH * S::EB);
-    for (int i = tid; i < S::H * S::DHC; i += C::NT)
-      q_lds[(i / S::DHC) * C::Q_STRIDE + i % S::DHC] = qsrc[i];
+  const int nid = min(a.chunk / S::P, a.max_pages - pg0);  // table entries of this chunk
+  const int32_t* tab = a.page_table + (size_t)b * a.max_pages + pg0;
+  int id_r[(kMaxChunkPages + C::NT - 1) / C::NT];
+#pragma unroll
+  for (int k = 0; k < (kMaxChunkPages + C::NT - 1) / C::NT; ++k) {
+    const int i = tid + k * C::NT;
+    if (i < nid) id_r[k] = tab[i];
+  }
+  constexpr int QCH = (S::H * S::DHC + C::NT - 1) / C::NT;
+  uint4 q_r[QCH];
+  const uint4* qsrc = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.q) +
+                                                     row * S::H * S::DH * S::EB);
+#pragma unroll
+  for (int k = 0; k < QCH; ++k) {
+    const int i = tid + k * C::NT;
+    if (i < S::H * S::DHC) q_r[k] = qsrc[i];
   }
   const int vis = visible_tokens(a.seq_lens[b], a.q_len, qi);
   const int tok0 = pg0 * S::P;
   const int tok1 = min(vis, tok0 + a.chunk);
   if (tok0 >= tok1) return;  // uniform for the whole workgroup
-  __syncthreads();           // page ids and q in LDS
+
+  BKRows<S> bkr;
+  load_bk_rows<S>(a.BK, tid, bkr);  // ahead of every page load
+#pragma unroll
+  for (int k = 0; k < (kMaxChunkPages + C::NT - 1) / C::NT; ++k) {
+    const int i = tid + k * C::NT;
+    if (i < nid) ids_lds[i] = id_r[k];
+  }
+#pragma unroll
+  for (int k = 0; k < QCH; ++k) {
+    const int i = tid + k * C::NT;
+    if (i < S::H * S::DHC) q_lds[(i / S::DHC) * C::Q_STRIDE + i % S::DHC] = q_r[k];
+  }
+  __syncthreads();  // page ids and q in LDS
 
   const int pg1 = (tok1 + S::P - 1) / S::P;
   const uint8_t* pool = a.pool;
   auto page_ptr = [&](int pg) { return pool + (size_t)ids_lds[pg - pg0] * S::PAGE; };
   auto nvalid = [&](int pg) { return min(S::P, tok1 - pg * S::P); };
 
-  PageRegs<S> ra, rb;
-  issue_page<S>(page_ptr(pg0), tid, h, j, ra);  // in flight while p is formed
-  form_private_queries<S>(a.BK, q_lds, pacc, p_lds, tid);
-  stage_shared<S>(sk_lds[0], sv_lds[0], tid, ra, nvalid(pg0));
+  PageRegs<S> r0, r1, r2;
+  // pages pg0, pg0+1 go in flight while the private queries are formed
+  issue_page<S>(page_ptr(pg0), L, r0);
+  if (pg0 + 1 < pg1) issue_page<S>(page_ptr(pg0 + 1), L, r1);
+  form_private_queries<S>(bkr, q_lds, pacc, p_lds, tid);
+  stage_shared<S>(sk_lds[0], sv_lds[0], tid, r0, nvalid(pg0));
   __syncthreads();
 
   SplitState<S> st;
   st.m_run = -INFINITY;
   st.l_run = 0.f;
 #pragma unroll
-  for (int k = 0; k < S::R; ++k) st.accR[k] = 0.f;
+  for (int k = 0; k < C::RC_L * S::CE; ++k) st.accR[k] = 0.f;
 #pragma unroll
-  for (int x = 0; x < 4; ++x) st.accS[x][0] = st.accS[x][1] = 0.f;
+  for (int x = 0; x < C::HPW; ++x) st.accS[x][0] = st.accS[x][1] = 0.f;
 
-  for (int pg = pg0; pg < pg1; pg += 2) {
-    // page pg: registers ra, LDS buffer 0; page pg+1 goes in flight into rb
-    const bool has1 = pg + 1 < pg1;
-    if (has1) issue_page<S>(page_ptr(pg + 1), tid, h, j, rb);
-    consume_page<S>(sk_lds[0], sv_lds[0], q_lds, p_lds, h, j, lane, nvalid(pg), a.score_scale,
-                    ra, st);
-    if (has1) stage_shared<S>(sk_lds[1], sv_lds[1], tid, rb, nvalid(pg + 1));
+  // one pipeline step: page pg is in `cur` and LDS buffer `buf`, page pg+1 in `nxt`; page
+  // pg+2 goes in flight into `fre`.  Returns false when pg was the last page.
+  auto step = [&](int pg, int buf, PageRegs<S>& cur, PageRegs<S>& nxt, PageRegs<S>& fre) {
+    if (pg + 2 < pg1) issue_page<S>(page_ptr(pg + 2), L, fre);
+    consume_page<S>(sk_lds[buf], sv_lds[buf], q_lds, p_lds, L, nvalid(pg), a.score_scale, cur, st);
+    const bool more = pg + 1 < pg1;
+    if (more) stage_shared<S>(sk_lds[buf ^ 1], sv_lds[buf ^ 1], tid, nxt, nvalid(pg + 1));
     __syncthreads();
-    if (!has1) break;
-    // page pg+1: registers rb, LDS buffer 1; page pg+2 goes in flight into ra
-    const bool has2 = pg + 2 < pg1;
-    if (has2) issue_page<S>(page_ptr(pg + 2), tid, h, j, ra);
-    consume_page<S>(sk_lds[1], sv_lds[1], q_lds, p_lds, h, j, lane, nvalid(pg + 1),
-                    a.score_scale, rb, st);
-    if (has2) stage_shared<S>(sk_lds[0], sv_lds[0], tid, ra, nvalid(pg + 2));
-    __syncthreads();
+    return more;
+  };
+  for (int pg = pg0;; pg += 3) {
+    const int buf = (pg - pg0) & 1;
+    if (!step(pg, buf, r0, r1, r2)) break;
+    if (!step(pg + 1, buf ^ 1, r1, r2, r0)) break;
+    if (!step(pg + 2, buf, r2, r0, r1)) break;
   }
 
   // ---- partial tuple of this chunk: m, l, acc_S[DH], acc_R[R] per head
   const float l_tot = r16_sum(st.l_run);
 #pragma unroll
-  for (int k = 0; k < S::R; ++k) st.accR[k] = r16_sum(st.accR[k]);
-  float* dst = a.part + ((row * a.n_split + split) * S::H + h) * S::PART_PAD;
-  if (j == 0) {
+  for (int k = 0; k < C::RC_L * S::CE; ++k) st.accR[k] = r16_sum(st.accR[k]);
+  float* dst = a.part + ((row * a.n_split + split) * S::H + L.h) * S::PART_PAD;
+  if (L.j == 0 && L.half == 0) {
     dst[0] = st.m_run;
     dst[1] = l_tot;
   }
 #pragma unroll
-  for (int k = 0; k < S::R; ++k)
-    if ((k & 15) == j) dst[2 + S::DH + k] = st.accR[k];
-  if (2 * lane < S::DH) {
+  for (int k = 0; k < C::RC_L * S::CE; ++k) {
+    const int kg = L.half * C::RC_L * S::CE + k;  // feature of R_V
+    if ((k & 15) == L.j && kg < S::R) dst[2 + S::DH + kg] = st.accR[k];
+  }
+  if (2 * L.lane < S::DH) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < C::HPW; ++x) {
       float2* d2 = reinterpret_cast<float2*>(
-          a.part + ((row * a.n_split + split) * S::H + 4 * wave + x) * S::PART_PAD + 2 + 2 * lane);
+          a.part + ((row * a.n_split + split) * S::H + C::HPW * L.wave + x) * S::PART_PAD + 2 +
+          2 * L.lane);
       *d2 = make_float2(st.accS[x][0], st.accS[x][1]);
     }
   }
@@ -610,8 +721,8 @@ hipError_t launch_decode(const DecodeArgs& a) {
   s.n_split = a.n_split;
   s.chunk = a.chunk;
   s.score_scale = 1.4426950408889634f / sqrtf((float)S::DH);
-  hipLaunchKernelGGL(decode_split_kernel<S>, dim3(a.n_split, a.q_len, a.batch), dim3(S::H * 16),
-                     0, a.stream, s);
+  hipLaunchKernelGGL(decode_split_kernel<S>, dim3(a.n_split, a.q_len, a.batch),
+                     dim3(SplitCfg<S>::NT), 0, a.stream, s);
   hipLaunchKernelGGL(merge_expand_kernel<S>, dim3(S::H, a.q_len, a.batch), dim3(256), 0, a.stream,
                      a.part_ws, a.B_V, a.seq_lens, a.q_len, a.n_split, a.chunk, a.out);
   return hipGetLastError();
