@@ -217,7 +217,7 @@ def main():
     trec = traffic_record()
     roofline = {
         "bound": "hbm",
-        "kernel": "lrkv_decode call (private_query + decode_split + merge_expand kernels)",
+        "kernel": "lrkv_decode call (decode_split_kernel + merge_expand_kernel)",
         "achieved": round(achieved, 1),
         "peak": PEAK_HBM_GBS,
         "unit": "GB/s",

@@ -40,14 +40,22 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Tokens per chunk of the split: the caller's value, or one that spreads the batch over
-// about two workgroups per compute unit (256 CUs) with at least four pages per chunk.
+// Tokens per chunk of the split: the caller's value, or, for 0, a size from the batch's
+// padded work (batch x q_len x max_seq_len tokens).  A split workgroup fills one compute unit
+// (512 threads at up to 256 VGPRs), so one dispatch wave is 256 groups: spread the work over
+// that many chunks while they come out at most 1024 tokens long; beyond that, use chunks of
+// at least 1024 tokens over about four waves, which keeps the per-chunk set-up (page ids,
+// private queries) small next to the stream and lets the dispatcher even out ragged lengths.
 int pick_chunk(const lrkv_layout* L, int batch, int q_len, int max_seq_len, int chunk_tokens) {
   if (chunk_tokens > 0) return chunk_tokens;
   const int P = L->page_size;
   const long long work = (long long)batch * q_len * (long long)max_seq_len;
-  const long long target_groups = 512;
-  long long c = (work + target_groups - 1) / target_groups;
+  const long long one_wave = 256, long_chunk = 1024;
+  long long c = (work + one_wave - 1) / one_wave;
+  if (c > long_chunk) {
+    const long long four_waves = (work + 4 * one_wave - 1) / (4 * one_wave);
+    c = four_waves > long_chunk ? four_waves : long_chunk;
+  }
   c = (c + P - 1) / P * P;
   if (c < 4LL * P) c = 4LL * P;
   if (c > kMaxChunkTokens) c = kMaxChunkTokens;

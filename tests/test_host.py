@@ -66,6 +66,12 @@ def test_workspace_sizes():
     rec = -(-(2 + dh + r) // 4) * 4  # partial records padded to 16 bytes
     part = -(-rows * 256 * H * rec * 4 // 256) * 256
     assert w16 == part
+    # automatic chunks: B=8, T=4096 spreads over one wave of 256 groups (128-token chunks)
+    assert F.lrkv_decode_workspace_bytes(C1, 8, 1, 4096, 0) == \
+        F.lrkv_decode_workspace_bytes(C1, 8, 1, 4096, 128)
+    # B=4, T=131072 goes in 1024-token chunks
+    assert F.lrkv_decode_workspace_bytes(C3, 4, 1, 131072, 0) == \
+        F.lrkv_decode_workspace_bytes(C3, 4, 1, 131072, 1024)
     assert F.lrkv_decode_workspace_bytes(C1, 8, 1, 4096, 4096 + 16) == 0  # chunk too long
     assert F.lrkv_decode_workspace_bytes(C1, 8, 1, 4096, 24) == 0  # not a multiple of P
     assert F.lrkv_decode_workspace_bytes(C1, 0, 1, 4096, 0) == 0
