@@ -59,7 +59,7 @@ __device__ __forceinline__ float r16_sum(float x) {
 // the shared value the wavefront switches to lanes over feature pairs (2*lane, 2*lane+1)
 // of its HPW heads, with the weights broadcast by readlane.
 //
-// Pipeline: pages pg+1 and pg+2 are in flight (three register buffers) while page pg is
+// Pipeline: four register buffers; pages pg+1..pg+3 are in flight while page pg is
 // consumed; the S tiles go through a double-buffered LDS stage.  Page bytes are read with
 // non-temporal loads: the stream is used once and should not evict the small operands that
 // every workgroup re-reads (B_K, queries, page tables).
@@ -109,6 +109,12 @@ struct SplitCfg {
   static constexpr int PQ_JOBS = S::H * S::RC;
   static constexpr int PQ_GROUPS = NT / PQ_JOBS > 0 ? NT / PQ_JOBS : 1;
   static constexpr int PQ_DSPAN = S::DH / PQ_GROUPS;
+  // bf16 cache: the shared value sum_j w[h][j] S_V[j] runs on MFMA, wave w owning the
+  // 16-feature tile [16w, 16w+16) for every head (HT tiles of 16 heads)
+  static constexpr bool MFMA_SV = S::BF;
+  static constexpr int HT = S::H / 16 > 0 ? S::H / 16 : 1;
+  static_assert(!MFMA_SV || (S::H % 16 == 0 && NW * 16 == S::DH && S::P == 16),
+                "MFMA shared value: 16-head tiles, one 16-feature tile per wave, 16-token pages");
   static_assert(HPW * SPLIT == 4, "64 lanes = HPW heads x SPLIT x 16 tokens");
   static_assert(S::DHC % SPLIT == 0, "shared chunks split evenly");
   static_assert(S::DH % PQ_GROUPS == 0, "d_h split evenly");
@@ -179,12 +185,15 @@ __device__ __forceinline__ int sv_slot(int t, int chunk) {
   return t * S::DHC + (chunk ^ (t & (S::DHC - 1)));
 }
 
-// S_K keeps the page's chunk-major order; S_V is transposed to rows, and rows of slots
-// past the last visible token are written as zeros so the value loop can run over all P
-// slots (their weights are exactly zero).
+// S_K keeps the page's chunk-major order.  float32 cache: S_V is transposed to rows for the
+// value loop.  bf16 cache: S_V is transposed to feature rows svt[d][t] (16 tokens of one
+// feature contiguous), the B operand layout of the MFMA value product.  Slots past the last
+// visible token are written as zeros (their weights are exactly zero, and 0 x NaN would
+// not be).
 template <class S>
 __device__ __forceinline__ void stage_shared(uint4* __restrict__ sk, uint4* __restrict__ sv,
-                                             int tid, const PageRegs<S>& r, int nvalid) {
+                                             uint16_t* __restrict__ svt, int tid,
+                                             const PageRegs<S>& r, int nvalid) {
   using C = SplitCfg<S>;
 #pragma unroll
   for (int i = 0; i < C::SPT; ++i) {
@@ -194,8 +203,50 @@ __device__ __forceinline__ void stage_shared(uint4* __restrict__ sk, uint4* __re
     } else if (C::S_CHUNKS % C::NT == 0 || c < C::S_CHUNKS) {
       const int cc = c - S::DHC * S::P;
       const int t = cc % S::P;
-      sv[sv_slot<S>(t, cc / S::P)] = t < nvalid ? r.st[i] : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 v = t < nvalid ? r.st[i] : make_uint4(0u, 0u, 0u, 0u);
+      if constexpr (C::MFMA_SV) {
+        uint16_t* col = svt + (cc / S::P) * S::CE * S::P + t;  // feature 8*(cc/P), token t
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          col[(2 * e) * S::P] = (uint16_t)(w4[e] & 0xffffu);
+          col[(2 * e + 1) * S::P] = (uint16_t)(w4[e] >> 16);
+        }
+      } else {
+        sv[sv_slot<S>(t, cc / S::P)] = v;
+      }
     }
+  }
+}
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Shared value of one page on MFMA (bf16 cache): for every head tile,
+//   acc[h][d] = acc[h][d] * alpha[h] + sum_t W[h][t] S_V[t][d],   d in this wave's tile,
+// with W held as bfloat16 hi + lo parts (two products, ~16 significant bits of each
+// weight).  v_mfma_f32_16x16x16_bf16 lane layout: A[i][k] at lane 16*(k/4) + i, element
+// k%4; B[k][j] at lane 16*(k/4) + j; D[i][j] at lane 16*(i/4) + j, element i%4.
+template <class S>
+__device__ __forceinline__ void shared_value_mfma(f32x4* acc, const uint16_t* __restrict__ wl,
+                                                  const float* __restrict__ al,
+                                                  const uint16_t* __restrict__ svt, int wave,
+                                                  int lane) {
+  using C = SplitCfg<S>;
+  const int i = lane & 15, g = lane >> 4;
+  const short4v b = *reinterpret_cast<const short4v*>(svt + (16 * wave + i) * S::P + 4 * g);
+#pragma unroll
+  for (int ht = 0; ht < C::HT; ++ht) {
+    const float4 a4 = *reinterpret_cast<const float4*>(al + 16 * ht + 4 * g);
+    acc[ht][0] *= a4.x;
+    acc[ht][1] *= a4.y;
+    acc[ht][2] *= a4.z;
+    acc[ht][3] *= a4.w;
+    const short4v whi = *reinterpret_cast<const short4v*>(wl + (16 * ht + i) * S::P + 4 * g);
+    const short4v wlo =
+        *reinterpret_cast<const short4v*>(wl + (S::H + 16 * ht + i) * S::P + 4 * g);
+    acc[ht] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(whi, b, acc[ht], 0, 0, 0);
+    acc[ht] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wlo, b, acc[ht], 0, 0, 0);
   }
 }
 
@@ -312,7 +363,8 @@ struct SplitState {
   float m_run;                                // reference max of the lane's head
   float l_run;                                // this lane's share of the exp-sum
   float accR[SplitCfg<S>::RC_L * S::CE];      // its share of sum_j w_j R_V[h, j] (its half)
-  float accS[SplitCfg<S>::HPW][2];            // sum_j w_j S_V[j][2*lane + e] per head
+  float accS[SplitCfg<S>::HPW][2];            // float32 cache: sum_j w_j S_V[j][2*lane + e]
+  f32x4 accT[SplitCfg<S>::HT];                // bf16 cache: MFMA tiles of acc_S (see above)
 };
 
 // the partner lane of a (head, token) pair holds the other half of the features
@@ -324,9 +376,10 @@ template <class S>
 __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
                                              const uint4* __restrict__ sv,
                                              const uint4* __restrict__ q_lds,
-                                             const uint4* __restrict__ p_lds, const Lane<S>& L,
-                                             int nvalid, float score_scale,
-                                             const PageRegs<S>& r, SplitState<S>& st) {
+                                             const uint4* __restrict__ p_lds,
+                                             uint16_t* __restrict__ wl, float* __restrict__ al,
+                                             const Lane<S>& L, int nvalid, float score_scale,
+                                             PageRegs<S>& r, SplitState<S>& st) {
   using C = SplitCfg<S>;
   const int j = L.j;
   const bool valid = j < nvalid;
@@ -384,26 +437,48 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
   // only when the page's max clears it by more than the slack
   const float pm = r16_max(s);
   const bool bump = pm > st.m_run + kRescaleSlack;
-  if (__any(bump)) {
+  float alpha = 1.f;
+  if (__builtin_expect(__any(bump), 0)) {  // rare after the first page: a real branch
+    asm volatile("" ::: "memory");
     const float m_new = bump ? pm : st.m_run;
-    const float alpha = exp2f(st.m_run - m_new);  // 0 on the first page, 1 if not bumped
+    alpha = exp2f(st.m_run - m_new);  // 0 on the first page, 1 if not bumped
     st.l_run *= alpha;
 #pragma unroll
     for (int k = 0; k < C::RC_L * S::CE; ++k) st.accR[k] *= alpha;
+    if constexpr (!C::MFMA_SV) {
 #pragma unroll
-    for (int x = 0; x < C::HPW; ++x) {
-      const float a = readlane_f(alpha, x * 16 * C::SPLIT);
-      st.accS[x][0] *= a;
-      st.accS[x][1] *= a;
+      for (int x = 0; x < C::HPW; ++x) {
+        const float a = readlane_f(alpha, x * 16 * C::SPLIT);
+        st.accS[x][0] *= a;
+        st.accS[x][1] *= a;
+      }
     }
     st.m_run = m_new;
   }
   const float w = exp2f(s - st.m_run);  // exactly 0 for masked slots
   st.l_run += w;
+  if constexpr (C::MFMA_SV) {
+    // weights as bfloat16 hi + lo for the MFMA shared value of this page (run by every
+    // wave after the next barrier), and the head's rescale factor for its accumulator
+    if (L.half == 0) {
+      const uint32_t hi = f32_to_bf16_rne(w);
+      const uint32_t lo = f32_to_bf16_rne(w - bf16_to_f32((uint16_t)hi));
+      wl[L.h * S::P + L.j] = (uint16_t)hi;
+      wl[(S::H + L.h) * S::P + L.j] = (uint16_t)lo;
+      if (L.j == 0) al[L.h] = alpha;
+    }
+  }
+  // only the last page of a request has empty slots: their R_V bytes are replaced by
+  // zeros there (selection), full pages skip the selects
+  if (__builtin_expect(nvalid < S::P, 0)) {
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int c = 0; c < C::RC_L; ++c)
+      if (!valid) r.rv[c] = make_uint4(0u, 0u, 0u, 0u);
+  }
 #pragma unroll
   for (int c = 0; c < C::RC_L; ++c) {
-    const uint32_t v4[4] = {valid ? r.rv[c].x : 0u, valid ? r.rv[c].y : 0u,
-                            valid ? r.rv[c].z : 0u, valid ? r.rv[c].w : 0u};
+    const uint32_t v4[4] = {r.rv[c].x, r.rv[c].y, r.rv[c].z, r.rv[c].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if constexpr (S::BF) {
@@ -417,39 +492,34 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
     }
   }
 
-  // ---- shared value: lanes over feature pairs, weights broadcast by readlane
-  float sA[C::HPW], sB[C::HPW];
+  // ---- shared value (float32 cache): lanes over feature pairs, weights broadcast by
+  // readlane.  The bf16 cache does this on MFMA (shared_value_mfma).
+  if constexpr (!C::MFMA_SV) {
+    float sA[C::HPW], sB[C::HPW];
 #pragma unroll
-  for (int x = 0; x < C::HPW; ++x) {
-    sA[x] = st.accS[x][0];
-    sB[x] = st.accS[x][1];
-  }
-  const int dl = (2 * L.lane < S::DH) ? L.lane : (S::DH / 2 - 1);
-  const int e0 = 2 * dl;  // first feature of the pair
+    for (int x = 0; x < C::HPW; ++x) {
+      sA[x] = st.accS[x][0];
+      sB[x] = st.accS[x][1];
+    }
+    const int dl = (2 * L.lane < S::DH) ? L.lane : (S::DH / 2 - 1);
+    const int e0 = 2 * dl;  // first feature of the pair
 #pragma unroll
-  for (int t = 0; t < S::P; ++t) {
-    const int slot = sv_slot<S>(t, e0 / S::CE) * S::CE + (e0 % S::CE);  // element index
-    float sv0, sv1;
-    if constexpr (S::BF) {
-      const uint32_t pr = reinterpret_cast<const uint32_t*>(sv)[slot / 2];
-      sv0 = bf16_lo(pr);
-      sv1 = bf16_hi(pr);
-    } else {
+    for (int t = 0; t < S::P; ++t) {
+      const int slot = sv_slot<S>(t, e0 / S::CE) * S::CE + (e0 % S::CE);  // element index
       const float2 pr = reinterpret_cast<const float2*>(sv)[slot / 2];
-      sv0 = pr.x;
-      sv1 = pr.y;
+      const float sv0 = pr.x, sv1 = pr.y;
+#pragma unroll
+      for (int x = 0; x < C::HPW; ++x) {
+        const float wt = readlane_f(w, x * 16 * C::SPLIT + t);
+        sA[x] = fmaf(wt, sv0, sA[x]);
+        sB[x] = fmaf(wt, sv1, sB[x]);
+      }
     }
 #pragma unroll
     for (int x = 0; x < C::HPW; ++x) {
-      const float wt = readlane_f(w, x * 16 * C::SPLIT + t);
-      sA[x] = fmaf(wt, sv0, sA[x]);
-      sB[x] = fmaf(wt, sv1, sB[x]);
+      st.accS[x][0] = sA[x];
+      st.accS[x][1] = sB[x];
     }
-  }
-#pragma unroll
-  for (int x = 0; x < C::HPW; ++x) {
-    st.accS[x][0] = sA[x];
-    st.accS[x][1] = sB[x];
   }
 }
 
@@ -457,8 +527,18 @@ template <class S>
 __global__ void __launch_bounds__(SplitCfg<S>::NT, 1)
 decode_split_kernel(const SplitArgs a) {
   using C = SplitCfg<S>;
+  constexpr int SV_ROWS = C::MFMA_SV ? 1 : S::P * S::DHC;
+  constexpr int SVT_BUFS = C::MFMA_SV ? 3 : 1;
+  constexpr int SVT_ELEMS = C::MFMA_SV ? S::DH * S::P : 8;
+  constexpr int W_ELEMS = C::MFMA_SV ? 2 * S::H * S::P : 8;
   __shared__ uint4 sk_lds[2][S::DHC * S::P];  // chunk-major [c][t], double buffered
-  __shared__ uint4 sv_lds[2][S::P * S::DHC];  // rows [t][swizzled c]
+  __shared__ uint4 sv_lds[2][SV_ROWS];        // float32 cache: rows [t][swizzled c]
+  // bf16 cache: S_V feature rows [d][t] (three buffers: page k is read by the MFMA during
+  // step k+1 while page k+2 is staged), weights hi/lo [2][H][t] and rescale factors [H]
+  // of the last consumed page (two buffers)
+  __shared__ __align__(16) uint16_t svt_lds[SVT_BUFS][SVT_ELEMS];
+  __shared__ __align__(16) uint16_t w_lds[2][W_ELEMS];
+  __shared__ __align__(16) float al_lds[2][S::H];
   __shared__ uint4 q_lds[S::H * C::Q_STRIDE];
   __shared__ uint4 p_lds[S::H * C::P_STRIDE];
   __shared__ float pacc[C::PQ_GROUPS * C::PQ_JOBS * S::CE];
@@ -515,12 +595,14 @@ decode_split_kernel(const SplitArgs a) {
   auto page_ptr = [&](int pg) { return pool + (size_t)ids_lds[pg - pg0] * S::PAGE; };
   auto nvalid = [&](int pg) { return min(S::P, tok1 - pg * S::P); };
 
-  PageRegs<S> r0, r1, r2;
-  // pages pg0, pg0+1 go in flight while the private queries are formed
+  PageRegs<S> r0, r1, r2, r3;
+  // pages pg0, pg0+1 go in flight while the private queries are formed (the B_K rows
+  // hold the registers of a third buffer until then); page pg0+2 follows right after
   issue_page<S>(page_ptr(pg0), L, r0);
   if (pg0 + 1 < pg1) issue_page<S>(page_ptr(pg0 + 1), L, r1);
   form_private_queries<S>(bkr, q_lds, pacc, p_lds, tid);
-  stage_shared<S>(sk_lds[0], sv_lds[0], tid, r0, nvalid(pg0));
+  if (pg0 + 2 < pg1) issue_page<S>(page_ptr(pg0 + 2), L, r2);
+  stage_shared<S>(sk_lds[0], sv_lds[0], svt_lds[0], tid, r0, nvalid(pg0));
   __syncthreads();
 
   SplitState<S> st;
@@ -530,22 +612,39 @@ decode_split_kernel(const SplitArgs a) {
   for (int k = 0; k < C::RC_L * S::CE; ++k) st.accR[k] = 0.f;
 #pragma unroll
   for (int x = 0; x < C::HPW; ++x) st.accS[x][0] = st.accS[x][1] = 0.f;
+#pragma unroll
+  for (int x = 0; x < C::HT; ++x) st.accT[x] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // one pipeline step: page pg is in `cur` and LDS buffer `buf`, page pg+1 in `nxt`; page
-  // pg+2 goes in flight into `fre`.  Returns false when pg was the last page.
+  // one pipeline step: page pg is in `cur` and LDS buffer `buf`, page pg+1 in `nxt`, page
+  // pg+2 in flight; page pg+3 goes in flight into `fre`.  bf16 cache: the shared value of
+  // page pg-1 (weights written last step) goes through MFMA first.  Returns false when pg
+  // was the last page.
   auto step = [&](int pg, int buf, PageRegs<S>& cur, PageRegs<S>& nxt, PageRegs<S>& fre) {
-    if (pg + 2 < pg1) issue_page<S>(page_ptr(pg + 2), L, fre);
-    consume_page<S>(sk_lds[buf], sv_lds[buf], q_lds, p_lds, L, nvalid(pg), a.score_scale, cur, st);
+    if (pg + 3 < pg1) issue_page<S>(page_ptr(pg + 3), L, fre);
+    const int k = pg - pg0;
+    if constexpr (C::MFMA_SV) {
+      if (k > 0)
+        shared_value_mfma<S>(st.accT, w_lds[buf ^ 1], al_lds[buf ^ 1], svt_lds[(k + 2) % 3],
+                             L.wave, L.lane);
+    }
+    consume_page<S>(sk_lds[buf], sv_lds[buf], q_lds, p_lds, w_lds[buf], al_lds[buf], L,
+                    nvalid(pg), a.score_scale, cur, st);
     const bool more = pg + 1 < pg1;
-    if (more) stage_shared<S>(sk_lds[buf ^ 1], sv_lds[buf ^ 1], tid, nxt, nvalid(pg + 1));
+    if (more)
+      stage_shared<S>(sk_lds[buf ^ 1], sv_lds[buf ^ 1], svt_lds[C::MFMA_SV ? (k + 1) % 3 : 0],
+                      tid, nxt, nvalid(pg + 1));
     __syncthreads();
     return more;
   };
-  for (int pg = pg0;; pg += 3) {
-    const int buf = (pg - pg0) & 1;
-    if (!step(pg, buf, r0, r1, r2)) break;
-    if (!step(pg + 1, buf ^ 1, r1, r2, r0)) break;
-    if (!step(pg + 2, buf, r2, r0, r1)) break;
+  for (int pg = pg0;; pg += 4) {
+    if (!step(pg, 0, r0, r1, r3)) break;
+    if (!step(pg + 1, 1, r1, r2, r0)) break;
+    if (!step(pg + 2, 0, r2, r3, r1)) break;
+    if (!step(pg + 3, 1, r3, r0, r2)) break;
+  }
+  if constexpr (C::MFMA_SV) {  // shared value of the last page
+    const int kl = pg1 - 1 - pg0;
+    shared_value_mfma<S>(st.accT, w_lds[kl & 1], al_lds[kl & 1], svt_lds[kl % 3], L.wave, L.lane);
   }
 
   // ---- partial tuple of this chunk: m, l, acc_S[DH], acc_R[R] per head
@@ -562,7 +661,16 @@ decode_split_kernel(const SplitArgs a) {
     const int kg = L.half * C::RC_L * S::CE + k;  // feature of R_V
     if ((k & 15) == L.j && kg < S::R) dst[2 + S::DH + kg] = st.accR[k];
   }
-  if (2 * L.lane < S::DH) {
+  if constexpr (C::MFMA_SV) {
+    // MFMA tile: lane holds heads 16*ht + 4*(lane/16) + e, feature 16*wave + lane%16
+    float* rec = a.part + (row * a.n_split + split) * S::H * S::PART_PAD;
+#pragma unroll
+    for (int ht = 0; ht < C::HT; ++ht)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        rec[(16 * ht + 4 * (L.lane >> 4) + e) * S::PART_PAD + 2 + 16 * L.wave + (L.lane & 15)] =
+            st.accT[ht][e];
+  } else if (2 * L.lane < S::DH) {
 #pragma unroll
     for (int x = 0; x < C::HPW; ++x) {
       float2* d2 = reinterpret_cast<float2*>(
