@@ -76,6 +76,14 @@ struct DecodeSizes {
 DecodeSizes decode_sizes(const lrkv_layout* L, int batch, int q_len, int max_seq_len,
                          int chunk_tokens) {
   DecodeSizes z{};
+  if (L->dtype == LRKV_BF16 && q_len >= kPrefillMinRows) {
+    // multi-query kernel: no split, no workspace (one 256-byte block keeps the pointer
+    // contract uniform)
+    z.chunk = chunk_tokens > 0 ? chunk_tokens : L->page_size;
+    z.n_split = 1;
+    z.total = 256;
+    return z;
+  }
   z.chunk = pick_chunk(L, batch, q_len, max_seq_len, chunk_tokens);
   z.n_split = max_seq_len > 0 ? (max_seq_len + z.chunk - 1) / z.chunk : 1;
   const size_t rows = (size_t)batch * q_len;

@@ -817,6 +817,9 @@ merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
 // ---------------------------------------------------------------------------------------
 template <class S>
 hipError_t launch_decode(const DecodeArgs& a) {
+  if constexpr (S::BF) {
+    if (a.q_len >= kPrefillMinRows) return launch_prefill<S>(a);
+  }
   SplitArgs s{};
   s.q = a.q;
   s.BK = a.B_K;

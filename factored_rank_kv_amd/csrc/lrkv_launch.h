@@ -52,4 +52,11 @@ hipError_t launch_decode(const DecodeArgs& a);
 template <class S>
 hipError_t launch_append(const AppendArgs& a);
 
+// Query rows per request at or above which a bf16 lrkv_decode call takes the multi-query
+// (prefill) kernel; it needs no workspace.
+constexpr int kPrefillMinRows = 64;
+
+template <class S>
+hipError_t launch_prefill(const DecodeArgs& a);
+
 }  // namespace lrkv

@@ -1,0 +1,384 @@
+// LRKV multi-query (prefill) attention over the factored paged cache, bf16, on MFMA.
+//
+// Per head h and query row i at position pos_i (LRKV notes §3, eq 6-7, with the causal
+// mask of §2):
+//   s_ij = (q_i . S_K[j] + p_i . R_K[h, j]) / sqrt(d_h),  p_i = q_i B_K[h],  j <= pos_i
+//   o_i  = (sum_j a_ij S_V[j] + (sum_j a_ij R_V[h, j]) B_V[h]^T) / sum_j a_ij
+// with a_ij = exp(s_ij - m_i) and one running max m_i per row (blockwise, as in the fused
+// paragraph after Algorithm 2).  Full per-head keys and values are never formed.
+//
+// Workgroup = (head h, tile of 128 query rows, request b); 8 wavefronts of 16 rows.  The
+// key loop walks tiles of 64 positions (four pages): S_K, S_V, R_K[h] and R_V[h] of the
+// tile are staged in LDS (token-major rows) and shared by the eight wavefronts.  Every
+// product is computed transposed, tokens (or features) by query rows:
+//   S^T  = S_K Q^T + R_K[h] P^T          (P^T = B_K[h]^T Q^T, formed once per tile of rows)
+//   O_S^T += S_V^T A^T,  O_R^T += R_V[h]^T A^T,   O^T = O_S^T + B_V[h] O_R^T at the end,
+// so that the score tile's MFMA output layout (lane = query row, four consecutive tokens)
+// is exactly the B-operand layout of the value products, and each lane owns one query row
+// for the softmax rescale.  S_V^T and R_V^T operands come from ds_read_b64_tr_b16 on the
+// token-major rows.  P, A and the final O_R are held as bf16; P and O_R as hi + lo pairs.
+//
+// MFMA lane layouts used (v_mfma_f32_16x16x32_bf16 / 16x16x16_bf16): A[i][k] at lane
+// 16*(k/KL) + i, element k%KL; B[k][j] at lane 16*(k/KL) + j; D[i][j] at lane 16*(i/4) + j,
+// element i%4 (KL = 8 for K = 32, 4 for K = 16).
+#include "lrkv_device.h"
+#include "lrkv_launch.h"
+
+namespace lrkv {
+
+namespace {
+
+typedef __bf16 bf16x8_p __attribute__((ext_vector_type(8)));
+typedef short short4_p __attribute__((ext_vector_type(4)));
+typedef short short8_p __attribute__((ext_vector_type(8)));
+typedef float f32x4_p __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_p lds_s4;
+
+__device__ __forceinline__ f32x4_p mfma32(const bf16x8_p& a, const bf16x8_p& b, f32x4_p c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_p mfma16(const short4_p& a, const short4_p& b, f32x4_p c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+// 16-lane transposing read: lane j of each 16-lane group reads 4 elements at its address;
+// lane i receives element i%4 of lanes 4e + i/4, e = 0..3.
+__device__ __forceinline__ short4_p read_tr(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p));
+}
+__device__ __forceinline__ short4_p pack4(float a, float b, float c, float d) {
+  const uint32_t lo = f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
+  const uint32_t hi = f32_to_bf16_rne(c) | (f32_to_bf16_rne(d) << 16);
+  return __builtin_bit_cast(short4_p, make_uint2(lo, hi));
+}
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi), four at a time
+__device__ __forceinline__ void split4(const f32x4_p& x, short4_p& hi, short4_p& lo) {
+  float h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = bf16_to_f32((uint16_t)f32_to_bf16_rne(x[e]));
+    l[e] = x[e] - h[e];
+  }
+  hi = pack4(h[0], h[1], h[2], h[3]);
+  lo = pack4(l[0], l[1], l[2], l[3]);
+}
+
+__device__ __forceinline__ float xor_max(float x) {
+  x = __builtin_fmaxf(x, __shfl_xor(x, 16));
+  return __builtin_fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float xor_sum(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+}  // namespace
+
+template <class S>
+struct PrefillCfg {
+  static constexpr int NW = 8, NT = 512;
+  static constexpr int BQ = 16 * NW;           // query rows per workgroup
+  static constexpr int BT = 64;                // tokens per key tile (four pages)
+  static constexpr int PPT = BT / S::P;        // pages per key tile
+  static constexpr int RP = 64;                // private width padded to 4 blocks of 16
+  static constexpr int SK_STRIDE = S::DH * 2 + 16;   // bytes per token row of S_K
+  static constexpr int SV_STRIDE = S::DH * 2 + 32;   // ... of S_V (transposing reads)
+  static constexpr int R_STRIDE = RP * 2 + 16;       // ... of R_K[h], R_V[h], B_K, B_V rows
+  static constexpr int SK_OFF = 0;
+  static constexpr int SV_OFF = SK_OFF + BT * SK_STRIDE;
+  static constexpr int RK_OFF = SV_OFF + BT * SV_STRIDE;
+  static constexpr int RV_OFF = RK_OFF + BT * R_STRIDE;
+  static constexpr int LDS = RV_OFF + BT * R_STRIDE;
+  static constexpr int KB = S::DH / 32;        // K blocks of the shared score
+  static constexpr int FB = S::DH / 16;        // feature blocks of O_S
+  static constexpr int RB = RP / 16;           // blocks of the private width
+  // 16-byte chunks staged per key tile, and per thread
+  static constexpr int S_CH = PPT * S::DHC * S::P;   // of S_K (same for S_V)
+  static constexpr int R_CH = PPT * S::RC * S::P;    // of R_K[h] (same for R_V[h])
+  static constexpr int S_PT = (S_CH + NT - 1) / NT;
+  static constexpr int R_PT = (R_CH + NT - 1) / NT;
+  static_assert(S::BF && S::P == 16 && S::R <= RP && S::DH % 32 == 0, "prefill shape");
+  static_assert(S::DH * S::R * 2 <= LDS, "B_K / B_V staging fits");
+  static_assert(S::DH * R_STRIDE <= LDS, "padded B_K / B_V rows fit");
+};
+
+struct PrefillArgs {
+  const void* q;
+  const void* BK;
+  const void* BV;
+  const uint8_t* pool;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  void* out;
+  int max_pages;
+  int q_len;
+  int q_tiles;
+  int n_groups;       // batch * q_tiles
+  float score_scale;  // log2(e) / sqrt(d_h)
+};
+
+// Stage a [rows x R] bf16 matrix (B_K[h] or B_V[h]) as rows of RP columns (zeros past R).
+template <class S>
+__device__ __forceinline__ void stage_basis(uint8_t* lds, const void* src, int h, int t) {
+  using C = PrefillCfg<S>;
+  const uint4* g = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(src) +
+                                                  (size_t)h * S::DH * S::R * 2);
+  for (int i = t; i < S::DH * (C::RP / 8); i += C::NT) {
+    const int row = i / (C::RP / 8), c = i % (C::RP / 8);
+    const uint4 v = c < S::RC ? g[row * S::RC + c] : make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4*>(lds + row * C::R_STRIDE + 16 * c) = v;
+  }
+}
+
+template <class S>
+__global__ void __launch_bounds__(512, 1)
+prefill_kernel(const PrefillArgs a) {
+  using C = PrefillCfg<S>;
+  __shared__ __align__(16) uint8_t lds[C::LDS];
+  __shared__ int ids[C::PPT];
+
+  // heaviest query tiles (most key tiles under the causal mask) first; the 16 heads of one
+  // (request, query tile) run back to back on one XCD, where they share the S tiles in L2
+  const int Lb = blockIdx.x;
+  const int xcd = Lb & 7, jx = Lb >> 3;
+  const int h = jx % S::H;
+  const int group = xcd + 8 * (jx / S::H);  // (request, query tile) index
+  if (group >= a.n_groups) return;
+  const int nb = a.n_groups / a.q_tiles;   // requests
+  const int b = group % nb;
+  const int qt = a.q_tiles - 1 - group / nb;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int T = a.seq_lens[b];
+  const int row = qt * C::BQ + 16 * wave + li;  // this lane's query row
+  const bool row_ok = row < a.q_len;
+  const int pos = T - a.q_len + row;            // its position; sees tokens 0..pos
+  // last position any row of the workgroup sees
+  const int last_row = min(a.q_len - 1, qt * C::BQ + C::BQ - 1);
+  const int pos_max = min(T - a.q_len + last_row, T - 1);
+  const int n_tiles = pos_max >= 0 ? pos_max / C::BT + 1 : 0;
+
+  // ---- q rows of this wavefront as MFMA operands: lane (lg, li) holds row li's features
+  // 32 kb + 8 lg .. +7 (A layout of Q = B layout of Q^T)
+  bf16x8_p qv[C::KB];
+  {
+    const uint4* qrow = reinterpret_cast<const uint4*>(
+        static_cast<const uint8_t*>(a.q) +
+        (((size_t)b * a.q_len + (row_ok ? row : 0)) * S::H + h) * S::DH * 2);
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+      const uint4 v = row_ok ? qrow[4 * kb + lg] : make_uint4(0u, 0u, 0u, 0u);
+      qv[kb] = __builtin_bit_cast(bf16x8_p, v);
+    }
+  }
+
+  // ---- P^T = B_K[h]^T Q^T (private queries of the 16 rows), hi/lo bf16 B operands of the
+  // private score: block rb holds P^T[16 rb + 4 lg + e][row li]
+  short4_p pth[C::RB], ptl[C::RB];
+  stage_basis<S>(lds, a.BK, h, t);
+  __syncthreads();
+#pragma unroll
+  for (int rb = 0; rb < C::RB; ++rb) {
+    f32x4_p acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+      // A = B_K^T: lane (lg, li) needs B_K[32 kb + 8 lg + e][16 rb + li]
+      const uint8_t* base = lds + (32 * kb + 8 * lg + li / 4) * C::R_STRIDE + (16 * rb + 4 * (li & 3)) * 2;
+      const short4_p lo = read_tr(base);
+      const short4_p hi = read_tr(base + 4 * C::R_STRIDE);
+      const bf16x8_p av = __builtin_bit_cast(bf16x8_p, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc = mfma32(av, qv[kb], acc);
+    }
+    split4(acc, pth[rb], ptl[rb]);
+  }
+  __syncthreads();  // B_K staging area is reused by the key tiles
+
+  // zero pad columns of the R_K / R_V rows (never overwritten by staging)
+  for (int i = t; i < 2 * C::BT * (C::RP / 8 - S::RC); i += C::NT) {
+    const int which = i / (C::BT * (C::RP / 8 - S::RC));
+    const int rem = i % (C::BT * (C::RP / 8 - S::RC));
+    const int tok = rem / (C::RP / 8 - S::RC), c = S::RC + rem % (C::RP / 8 - S::RC);
+    *reinterpret_cast<uint4*>(lds + (which ? C::RV_OFF : C::RK_OFF) + tok * C::R_STRIDE + 16 * c) =
+        make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  f32x4_p os[C::FB], orr[C::RB];
+#pragma unroll
+  for (int i = 0; i < C::FB; ++i) os[i] = f32x4_p{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < C::RB; ++i) orr[i] = f32x4_p{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;  // l_part: this lane's 4-token share of the sum
+
+  const int32_t* tab = a.page_table + (size_t)b * a.max_pages;
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    // ---- stage the tile: page ids, then S_K, S_V, R_K[h], R_V[h] as token-major rows;
+    // slots at or past T hold zeros (their weights are zero, 0 x NaN would not be)
+    if (t < C::PPT) ids[t] = tab[kt * C::PPT + t < a.max_pages ? kt * C::PPT + t : 0];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < C::S_PT; ++k) {
+      const int i = t + k * C::NT;
+      if (i < C::S_CH) {
+        const int pg = i / (S::DHC * S::P), rem = i % (S::DHC * S::P);
+        const int c = rem / S::P, slot = rem % S::P;
+        const int tok = pg * S::P + slot;
+        const bool live = kt * C::BT + tok < T;
+        const uint8_t* page = a.pool + (size_t)ids[pg] * S::PAGE;
+        const uint4 vk = live ? *reinterpret_cast<const uint4*>(page + 16 * rem) : make_uint4(0u, 0u, 0u, 0u);
+        const uint4 vv = live ? *reinterpret_cast<const uint4*>(page + S::OFF_SV + 16 * rem) : make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(lds + C::SK_OFF + tok * C::SK_STRIDE + 16 * c) = vk;
+        *reinterpret_cast<uint4*>(lds + C::SV_OFF + tok * C::SV_STRIDE + 16 * c) = vv;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < C::R_PT; ++k) {
+      const int i = t + k * C::NT;
+      if (i < C::R_CH) {
+        const int pg = i / (S::RC * S::P), rem = i % (S::RC * S::P);
+        const int c = rem / S::P, slot = rem % S::P;
+        const int tok = pg * S::P + slot;
+        const bool live = kt * C::BT + tok < T;
+        const uint8_t* page = a.pool + (size_t)ids[pg] * S::PAGE;
+        const uint4 vk = live ? *reinterpret_cast<const uint4*>(page + S::OFF_RK + h * S::SEC_R + 16 * rem) : make_uint4(0u, 0u, 0u, 0u);
+        const uint4 vv = live ? *reinterpret_cast<const uint4*>(page + S::OFF_RV + h * S::SEC_R + 16 * rem) : make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(lds + C::RK_OFF + tok * C::R_STRIDE + 16 * c) = vk;
+        *reinterpret_cast<uint4*>(lds + C::RV_OFF + tok * C::R_STRIDE + 16 * c) = vv;
+      }
+    }
+    __syncthreads();
+
+    // ---- scores S^T for the 4 token blocks: lane (lg, li) gets tokens 16 tb + 4 lg + e of
+    // row li
+    f32x4_p sc[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      f32x4_p acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+        const bf16x8_p kv = *reinterpret_cast<const bf16x8_p*>(
+            lds + C::SK_OFF + (16 * tb + li) * C::SK_STRIDE + 64 * kb + 16 * lg);
+        acc = mfma32(kv, qv[kb], acc);
+      }
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb) {
+        const short4_p rk = *reinterpret_cast<const short4_p*>(
+            lds + C::RK_OFF + (16 * tb + li) * C::R_STRIDE + 32 * rb + 8 * lg);
+        acc = mfma16(rk, pth[rb], acc);
+        acc = mfma16(rk, ptl[rb], acc);
+      }
+      sc[tb] = acc;
+    }
+
+    // ---- online softmax per row: scores are tokens j = kt*BT + 16 tb + 4 lg + e of row li
+    float mt = -INFINITY;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = kt * C::BT + 16 * tb + 4 * lg + e;
+        const bool ok = row_ok && j <= pos;  // j < T follows from pos < T
+        const float s = ok ? sc[tb][e] * a.score_scale : -INFINITY;
+        sc[tb][e] = s;
+        mt = __builtin_fmaxf(mt, s);
+      }
+    mt = xor_max(mt);
+    const bool bump = mt > m_run + 8.0f;
+    if (__builtin_expect(__any(bump), 0)) {
+      asm volatile("" ::: "memory");
+      const float m_new = bump ? mt : m_run;
+      const float alpha = m_run == m_new ? 1.f : exp2f(m_run - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int i = 0; i < C::FB; ++i) os[i] *= alpha;
+#pragma unroll
+      for (int i = 0; i < C::RB; ++i) orr[i] *= alpha;
+      m_run = m_new;
+    }
+    short4_p pa[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[e] = sc[tb][e] == -INFINITY ? 0.f : exp2f(sc[tb][e] - m_run);
+        l_part += p[e];
+      }
+      pa[tb] = pack4(p[0], p[1], p[2], p[3]);
+    }
+
+    // ---- values: O_S^T[16 fb + ..][row] += S_V^T A^T, O_R^T likewise; the A operand of
+    // block (fb, tb) is S_V[16 tb + 4 lg' + e][16 fb + li'] by a transposing read
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+      for (int fb = 0; fb < C::FB; ++fb) {
+        const short4_p v = read_tr(lds + C::SV_OFF + (16 * tb + 4 * lg + li / 4) * C::SV_STRIDE +
+                                   (16 * fb + 4 * (li & 3)) * 2);
+        os[fb] = mfma16(v, pa[tb], os[fb]);
+      }
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb) {
+        const short4_p v = read_tr(lds + C::RV_OFF + (16 * tb + 4 * lg + li / 4) * C::R_STRIDE +
+                                   (16 * rb + 4 * (li & 3)) * 2);
+        orr[rb] = mfma16(v, pa[tb], orr[rb]);
+      }
+    }
+    __syncthreads();  // the tile is overwritten next
+  }
+
+  // ---- expansion through B_V[h] and normalisation:
+  // O^T[16 fb + 4 lg + e][row li] = O_S^T + sum_rb B_V[16 fb + .][16 rb + .] O_R^T[16 rb + .][row]
+  stage_basis<S>(lds, a.BV, h, t);
+  __syncthreads();
+  short4_p orh[C::RB], orl[C::RB];
+#pragma unroll
+  for (int rb = 0; rb < C::RB; ++rb) split4(orr[rb], orh[rb], orl[rb]);
+  const float l_row = xor_sum(l_part);
+  const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+  const size_t orow = (((size_t)b * a.q_len + row) * S::H + h) * S::DH;
+#pragma unroll
+  for (int fb = 0; fb < C::FB; ++fb) {
+    f32x4_p acc = os[fb];
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb) {
+      // A = B_V[h]: lane (lg, li) holds B_V[16 fb + li][16 rb + 4 lg .. +3]
+      const short4_p bv = *reinterpret_cast<const short4_p*>(
+          lds + (16 * fb + li) * C::R_STRIDE + (16 * rb + 4 * lg) * 2);
+      acc = mfma16(bv, orh[rb], acc);
+      acc = mfma16(bv, orl[rb], acc);
+    }
+    if (row_ok) {
+      const uint32_t w0 = f32_to_bf16_rne(acc[0] * inv) | (f32_to_bf16_rne(acc[1] * inv) << 16);
+      const uint32_t w1 = f32_to_bf16_rne(acc[2] * inv) | (f32_to_bf16_rne(acc[3] * inv) << 16);
+      *reinterpret_cast<uint2*>(out + orow + 16 * fb + 4 * lg) = make_uint2(w0, w1);
+    }
+  }
+}
+
+template <class S>
+hipError_t launch_prefill(const DecodeArgs& a) {
+  using C = PrefillCfg<S>;
+  PrefillArgs p{};
+  p.q = a.q;
+  p.BK = a.B_K;
+  p.BV = a.B_V;
+  p.pool = static_cast<const uint8_t*>(a.pool);
+  p.page_table = a.page_table;
+  p.seq_lens = a.seq_lens;
+  p.out = a.out;
+  p.max_pages = a.max_pages;
+  p.q_len = a.q_len;
+  p.q_tiles = (a.q_len + C::BQ - 1) / C::BQ;
+  p.score_scale = 1.4426950408889634f / sqrtf((float)S::DH);
+  p.n_groups = a.batch * p.q_tiles;
+  const int blocks = ((p.n_groups + 7) / 8) * 8 * S::H;
+  hipLaunchKernelGGL(prefill_kernel<S>, dim3(blocks), dim3(C::NT), 0, a.stream, p);
+  return hipGetLastError();
+}
+
+template hipError_t launch_prefill<ShapeC1>(const DecodeArgs&);
+template hipError_t launch_prefill<ShapeC3>(const DecodeArgs&);
+
+}  // namespace lrkv
