@@ -79,6 +79,8 @@ def main():
     ap.add_argument("--graph", type=int, default=1, help="replay the step loop from a HIP graph")
     ap.add_argument("--cpu-baseline", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--prefill", type=int, default=1,
+                    help="also time the B=4 x 8192 prefill (append + multi-query attention)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration runs)")
     args = ap.parse_args()
@@ -255,10 +257,85 @@ def main():
         "cpu_baseline": None,
     }
 
+    if args.prefill:
+        result["prefill"] = prefill_bench(torch, F, synth, dev)
+
     if args.cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(work, w, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def prefill_bench(torch, F, synth, dev):
+    """B=4 prompts of T=8192, d=2048, H=16, d_h=128, r=56: lrkv_append of all 32768 rows
+    (the X [W_SK | W_SV | U_K | U_V] product on MFMA) into a permuted 2048-page pool, then
+    lrkv_decode with q_len = 8192 (causal multi-query attention on MFMA).  Synthetic X,
+    weights and Q (seeded draws, bf16)."""
+    work = synth.C4
+    B, T, H, dh, r, d = work.B, work.lens[0], work.H, work.d_h, work.r, work.d
+    lay = F.lrkv_layout(H, dh, r, work.page_size, F.LRKV_BF16)
+    n = B * T
+    w = synth.projection_weights(41, d, H, dh, r)
+    wd = {k: torch.from_numpy(bf16_codes(v).view(np.int16)).to(dev) for k, v in w.items()}
+    g = torch.Generator(device=dev)
+    g.manual_seed(42)
+    X = torch.randn(n, d, device=dev, generator=g).to(torch.bfloat16).view(torch.int16)
+    q = torch.randn(B, T, H, dh, device=dev, generator=g).to(torch.bfloat16).view(torch.int16)
+    table, npg = synth.page_assignment(43, [T] * B, work.page_size, permute=True)
+    tab = torch.from_numpy(table).to(dev)
+    pool = torch.zeros(npg * F.lrkv_page_bytes(lay), dtype=torch.uint8, device=dev)
+    req = torch.arange(B, dtype=torch.int32, device=dev).repeat_interleave(T)
+    pos = torch.arange(T, dtype=torch.int32, device=dev).repeat(B)
+    lens = torch.full((B,), T, dtype=torch.int32, device=dev)
+    out = torch.empty(B, T, H, dh, dtype=torch.int16, device=dev)
+    ws_bytes = F.lrkv_decode_workspace_bytes(lay, B, T, T, 0)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def append():
+        F.lrkv_append(lay, X, n, d, wd["W_SK"], wd["W_SV"], wd["U_K"], wd["U_V"], req, pos, tab,
+                      table.shape[1], pool, npg)
+
+    def attend():
+        F.lrkv_decode(lay, q, B, T, wd["B_K"], wd["B_V"], pool, tab, table.shape[1], lens, T, 0,
+                      out, ws, ws_bytes)
+
+    def ms_of(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_app = ms_of(append, 10)
+    ms_att = ms_of(attend, 10)
+    fl_app = 2.0 * n * d * (2 * dh + 2 * H * r)
+    pairs = B * T * (T + 1) / 2
+    fl_att = pairs * H * 4 * (dh + r) + B * T * H * 4 * dh * r  # scores + values, p + expansion
+    tf_app = fl_app / (ms_app * 1e-3) / 1e12
+    tf_att = fl_att / (ms_att * 1e-3) / 1e12
+    log(f"prefill: append {ms_app:.3f} ms ({tf_app:.0f} TFLOP/s), attention {ms_att:.3f} ms "
+        f"({tf_att:.0f} TFLOP/s)")
+    return {
+        "workload": work.name, "B": B, "T": T, "d": d,
+        "append_ms": round(ms_app, 4), "append_tflops": round(tf_app, 1),
+        "attention_ms": round(ms_att, 4), "attention_tflops": round(tf_att, 1),
+        "roofline_append": {"bound": "mfma", "achieved": round(tf_app, 1),
+                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(tf_app / PEAK_BF16_TFLOPS, 4),
+                            "flop": fl_app},
+        "roofline_attention": {"bound": "mfma", "achieved": round(tf_att, 1),
+                               "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(tf_att / PEAK_BF16_TFLOPS, 4),
+                               "flop": fl_att},
+    }
 
 
 def cpu_baseline(work, weights, target_s):
