@@ -571,13 +571,15 @@ decode_split_kernel(const SplitArgs a) {
     const int i = tid + k * C::NT;
     if (i < S::H * S::DHC) q_r[k] = qsrc[i];
   }
-  const int vis = visible_tokens(a.seq_lens[b], a.q_len, qi);
+  // the request length is read first (a scalar load); B_K rows, which depend on nothing,
+  // follow at once, ahead of every page load
+  const int len_b = a.seq_lens[b];
+  BKRows<S> bkr;
+  load_bk_rows<S>(a.BK, tid, bkr);
+  const int vis = visible_tokens(len_b, a.q_len, qi);
   const int tok0 = pg0 * S::P;
   const int tok1 = min(vis, tok0 + a.chunk);
   if (tok0 >= tok1) return;  // uniform for the whole workgroup
-
-  BKRows<S> bkr;
-  load_bk_rows<S>(a.BK, tid, bkr);  // ahead of every page load
 #pragma unroll
   for (int k = 0; k < (kMaxChunkPages + C::NT - 1) / C::NT; ++k) {
     const int i = tid + k * C::NT;
