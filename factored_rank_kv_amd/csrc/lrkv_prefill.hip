@@ -88,6 +88,8 @@ struct PrefillCfg {
   static constexpr int RK_OFF = SV_OFF + BT * SV_STRIDE;
   static constexpr int RV_OFF = RK_OFF + BT * R_STRIDE;
   static constexpr int LDS = RV_OFF + BT * R_STRIDE;
+  static constexpr int IDB = 256;              // page ids held in LDS at a time
+  static constexpr int TPB = IDB / PPT;        // key tiles they cover
   static constexpr int KB = S::DH / 32;        // K blocks of the shared score
   static constexpr int FB = S::DH / 16;        // feature blocks of O_S
   static constexpr int RB = RP / 16;           // blocks of the private width
@@ -134,7 +136,7 @@ __global__ void __launch_bounds__(512, 1)
 prefill_kernel(const PrefillArgs a) {
   using C = PrefillCfg<S>;
   __shared__ __align__(16) uint8_t lds[C::LDS];
-  __shared__ int ids[C::PPT];
+  __shared__ int ids_blk[C::IDB];  // page ids of key tiles [64 k, 64 k + 64)
 
   // heaviest query tiles (most key tiles under the causal mask) first; the 16 heads of one
   // (request, query tile) run back to back on one XCD, where they share the S tiles in L2
@@ -211,24 +213,43 @@ prefill_kernel(const PrefillArgs a) {
   float m_run = -INFINITY, l_part = 0.f;  // l_part: this lane's 4-token share of the sum
 
   const int32_t* tab = a.page_table + (size_t)b * a.max_pages;
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    // ---- stage the tile: page ids, then S_K, S_V, R_K[h], R_V[h] as token-major rows;
-    // slots at or past T hold zeros (their weights are zero, 0 x NaN would not be)
-    if (t < C::PPT) ids[t] = tab[kt * C::PPT + t < a.max_pages ? kt * C::PPT + t : 0];
-    __syncthreads();
+  auto fill_ids = [&](int kt0) {  // page ids of key tiles kt0 .. kt0 + TPB - 1 (0 past the table)
+    for (int i = t; i < C::IDB; i += C::NT) {
+      const int pg = kt0 * C::PPT + i;
+      ids_blk[i] = pg < a.max_pages ? tab[pg] : 0;
+    }
+  };
+  uint4 sk_r[C::S_PT], sv_r[C::S_PT], rk_r[C::R_PT], rv_r[C::R_PT];
+  auto load_tile = [&](int kt) {
+    const int* tid_s = ids_blk + (kt % C::TPB) * C::PPT;
+#pragma unroll
+    for (int k = 0; k < C::S_PT; ++k) {
+      const int i = t + k * C::NT;
+      const int pg = i / (S::DHC * S::P), rem = i % (S::DHC * S::P);
+      const bool live = i < C::S_CH && kt * C::BT + pg * S::P + rem % S::P < T;
+      const uint8_t* page = a.pool + (size_t)tid_s[live ? pg : 0] * S::PAGE;
+      sk_r[k] = live ? *reinterpret_cast<const uint4*>(page + 16 * rem) : make_uint4(0u, 0u, 0u, 0u);
+      sv_r[k] = live ? *reinterpret_cast<const uint4*>(page + S::OFF_SV + 16 * rem) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < C::R_PT; ++k) {
+      const int i = t + k * C::NT;
+      const int pg = i / (S::RC * S::P), rem = i % (S::RC * S::P);
+      const bool live = i < C::R_CH && kt * C::BT + pg * S::P + rem % S::P < T;
+      const uint8_t* page = a.pool + (size_t)tid_s[live ? pg : 0] * S::PAGE + h * S::SEC_R;
+      rk_r[k] = live ? *reinterpret_cast<const uint4*>(page + S::OFF_RK + 16 * rem) : make_uint4(0u, 0u, 0u, 0u);
+      rv_r[k] = live ? *reinterpret_cast<const uint4*>(page + S::OFF_RV + 16 * rem) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto store_tile = [&]() {
 #pragma unroll
     for (int k = 0; k < C::S_PT; ++k) {
       const int i = t + k * C::NT;
       if (i < C::S_CH) {
         const int pg = i / (S::DHC * S::P), rem = i % (S::DHC * S::P);
-        const int c = rem / S::P, slot = rem % S::P;
-        const int tok = pg * S::P + slot;
-        const bool live = kt * C::BT + tok < T;
-        const uint8_t* page = a.pool + (size_t)ids[pg] * S::PAGE;
-        const uint4 vk = live ? *reinterpret_cast<const uint4*>(page + 16 * rem) : make_uint4(0u, 0u, 0u, 0u);
-        const uint4 vv = live ? *reinterpret_cast<const uint4*>(page + S::OFF_SV + 16 * rem) : make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4*>(lds + C::SK_OFF + tok * C::SK_STRIDE + 16 * c) = vk;
-        *reinterpret_cast<uint4*>(lds + C::SV_OFF + tok * C::SV_STRIDE + 16 * c) = vv;
+        const int tok = pg * S::P + rem % S::P, c = rem / S::P;
+        *reinterpret_cast<uint4*>(lds + C::SK_OFF + tok * C::SK_STRIDE + 16 * c) = sk_r[k];
+        *reinterpret_cast<uint4*>(lds + C::SV_OFF + tok * C::SV_STRIDE + 16 * c) = sv_r[k];
       }
     }
 #pragma unroll
@@ -236,16 +257,18 @@ prefill_kernel(const PrefillArgs a) {
       const int i = t + k * C::NT;
       if (i < C::R_CH) {
         const int pg = i / (S::RC * S::P), rem = i % (S::RC * S::P);
-        const int c = rem / S::P, slot = rem % S::P;
-        const int tok = pg * S::P + slot;
-        const bool live = kt * C::BT + tok < T;
-        const uint8_t* page = a.pool + (size_t)ids[pg] * S::PAGE;
-        const uint4 vk = live ? *reinterpret_cast<const uint4*>(page + S::OFF_RK + h * S::SEC_R + 16 * rem) : make_uint4(0u, 0u, 0u, 0u);
-        const uint4 vv = live ? *reinterpret_cast<const uint4*>(page + S::OFF_RV + h * S::SEC_R + 16 * rem) : make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4*>(lds + C::RK_OFF + tok * C::R_STRIDE + 16 * c) = vk;
-        *reinterpret_cast<uint4*>(lds + C::RV_OFF + tok * C::R_STRIDE + 16 * c) = vv;
+        const int tok = pg * S::P + rem % S::P, c = rem / S::P;
+        *reinterpret_cast<uint4*>(lds + C::RK_OFF + tok * C::R_STRIDE + 16 * c) = rk_r[k];
+        *reinterpret_cast<uint4*>(lds + C::RV_OFF + tok * C::R_STRIDE + 16 * c) = rv_r[k];
       }
     }
+  };
+  fill_ids(0);
+  __syncthreads();
+  if (n_tiles > 0) load_tile(0);
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    store_tile();
     __syncthreads();
 
     // ---- scores S^T for the 4 token blocks: lane (lg, li) gets tokens 16 tb + 4 lg + e of
@@ -323,6 +346,14 @@ prefill_kernel(const PrefillArgs a) {
                                    (16 * rb + 4 * (li & 3)) * 2);
         orr[rb] = mfma16(v, pa[tb], orr[rb]);
       }
+    }
+    if (kt + 1 < n_tiles) {
+      if ((kt + 1) % C::TPB == 0) {  // next block of page ids (uniform over the workgroup)
+        __syncthreads();
+        fill_ids(kt + 1);
+        __syncthreads();
+      }
+      load_tile(kt + 1);
     }
     __syncthreads();  // the tile is overwritten next
   }
