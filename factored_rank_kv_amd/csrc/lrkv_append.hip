@@ -62,18 +62,28 @@ __device__ __forceinline__ void store_elem(void* pool, size_t e, float v) {
 
 // ---------------------------------------------------------------------------------------
 // Few rows (a decode step appends one row per request).  Workgroup = one 16-byte chunk of
-// product columns (8 bf16 / 4 f32) x up to 8 rows; 256 threads = 8 rows x 32 k-lanes.
-// Reading the weights once dominates, so the grid has one workgroup per chunk; chunks that
-// share a 128-byte line are given to blocks on the same XCD (blocks go to XCDs round robin).
-// bf16: pairs of k go through v_dot2_f32_bf16 (products exact, float32 sums); v_perm_b32
-// packs (W[k][c], W[k+1][c]) from two weight rows.
+// product columns (8 bf16 / 4 f32) x up to 8 rows, 256 threads.  Reading the weights once
+// dominates and each workgroup reads only its d x 16-byte column strip, so thread t takes
+// the 8 consecutive k of slice t (slices 256 apart for d > 2048) and issues all its weight
+// and X loads at once: one memory round trip per pass.  Each thread then holds 8 x CE
+// partial sums (row, column), which a halving exchange across the wavefront reduces
+// (each round a lane keeps half of the sums and adds its partner's copy of that half), so
+// lane i ends with sum i over the wavefront; four wavefronts add in a fixed order.
+// Chunks that share a 128-byte line of a weight row go to blocks on the same XCD (blocks
+// go to the XCDs round robin).  bf16: v_perm_b32 packs (W[k][c], W[k+1][c]) from two weight
+// rows and v_dot2_f32_bf16 multiplies them with (X[n][k], X[n][k+1]) (products exact,
+// float32 sums).
 // ---------------------------------------------------------------------------------------
 template <class S>
 __global__ void __launch_bounds__(256)
 append_few_rows_kernel(AppendArgs a, int n_chunks) {
   constexpr int CE = S::CE;
-  constexpr int KS = S::BF ? 2 : 1;  // k values per step
-  __shared__ float red[4][8][CE];
+  constexpr int KT = 8;                 // k per thread per pass
+  constexpr int NV = 8 * CE;            // sums per thread: 8 rows x CE columns
+  constexpr int XW = KT * S::EB / 16;   // 16-byte X loads per row and pass
+  constexpr int LOG_NV = NV == 64 ? 6 : 5;
+  static_assert(NV == 64 || NV == 32, "8 rows x one 16-byte chunk of columns");
+  __shared__ float red[4][NV];
   const int bx = blockIdx.x;
   const int chunk = (n_chunks % 8 == 0) ? (bx % 8) * (n_chunks / 8) + bx / 8 : bx;
   const int col0 = chunk * CE;
@@ -82,70 +92,96 @@ append_few_rows_kernel(AppendArgs a, int n_chunks) {
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
-  const int n = t & 7;
-  const int kl = t >> 3;  // 0..31
-  const int row = blockIdx.y * 8 + n;
-  const bool active = row < a.n_rows;
+  const int row0 = blockIdx.y * 8;
+  const int nr = min(8, a.n_rows - row0);
+  const size_t wrow = (size_t)ldw * S::EB;  // bytes per weight row
+  const uint8_t* wcol = W + (size_t)wc * S::EB;
+  const uint8_t* X = static_cast<const uint8_t*>(a.X);
 
-  float acc[CE];
+  float v[NV];
 #pragma unroll
-  for (int e = 0; e < CE; ++e) acc[e] = 0.f;
-  if (active) {
-    const size_t wrow = (size_t)ldw * S::EB;  // bytes per weight row
-    const uint8_t* wcol = W + (size_t)wc * S::EB;
+  for (int i = 0; i < NV; ++i) v[i] = 0.f;
+  for (int k0 = KT * t; k0 < a.d; k0 += KT * 256) {
+    uint4 w[KT];
+#pragma unroll
+    for (int i = 0; i < KT; ++i) w[i] = *reinterpret_cast<const uint4*>(wcol + (size_t)(k0 + i) * wrow);
+    uint4 x[8][XW];
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+      for (int q = 0; q < XW; ++q)
+        x[n][q] = n < nr ? *reinterpret_cast<const uint4*>(
+                               X + ((size_t)(row0 + n) * a.d + k0) * S::EB + 16 * q)
+                         : make_uint4(0u, 0u, 0u, 0u);
     if constexpr (S::BF) {
-      const uint32_t* xr = reinterpret_cast<const uint32_t*>(
-          static_cast<const uint16_t*>(a.X) + (size_t)row * a.d);
-#pragma unroll 4
-      for (int k = kl * KS; k < a.d; k += 32 * KS) {
-        const uint4 w0 = *reinterpret_cast<const uint4*>(wcol + (size_t)k * wrow);
-        const uint4 w1 = *reinterpret_cast<const uint4*>(wcol + (size_t)(k + 1) * wrow);
-        const uint32_t x = xr[k >> 1];
-        const uint32_t a0[4] = {w0.x, w0.y, w0.z, w0.w};
-        const uint32_t a1[4] = {w1.x, w1.y, w1.z, w1.w};
+      // pk[kp][c] = (W[k0 + 2kp][c], W[k0 + 2kp + 1][c])
+      uint32_t pk[KT / 2][CE];
+#pragma unroll
+      for (int kp = 0; kp < KT / 2; ++kp) {
+        const uint32_t a0[4] = {w[2 * kp].x, w[2 * kp].y, w[2 * kp].z, w[2 * kp].w};
+        const uint32_t a1[4] = {w[2 * kp + 1].x, w[2 * kp + 1].y, w[2 * kp + 1].z,
+                                w[2 * kp + 1].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = __builtin_amdgcn_perm(a1[e], a0[e], 0x05040100u);  // col 2e
-          const uint32_t hi = __builtin_amdgcn_perm(a1[e], a0[e], 0x07060302u);  // col 2e+1
-          acc[2 * e] = dot2_bf16(x, lo, acc[2 * e]);
-          acc[2 * e + 1] = dot2_bf16(x, hi, acc[2 * e + 1]);
+          pk[kp][2 * e] = __builtin_amdgcn_perm(a1[e], a0[e], 0x05040100u);
+          pk[kp][2 * e + 1] = __builtin_amdgcn_perm(a1[e], a0[e], 0x07060302u);
         }
       }
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const uint32_t xs[4] = {x[n][0].x, x[n][0].y, x[n][0].z, x[n][0].w};
+#pragma unroll
+        for (int kp = 0; kp < KT / 2; ++kp)
+#pragma unroll
+          for (int c = 0; c < CE; ++c) v[n * CE + c] = dot2_bf16(xs[kp], pk[kp][c], v[n * CE + c]);
+      }
     } else {
-      const float* xr = static_cast<const float*>(a.X) + (size_t)row * a.d;
-#pragma unroll 4
-      for (int k = kl; k < a.d; k += 32) {
-        const float4 w = *reinterpret_cast<const float4*>(wcol + (size_t)k * wrow);
-        const float x = xr[k];
-        acc[0] = fmaf(x, w.x, acc[0]);
-        acc[1] = fmaf(x, w.y, acc[1]);
-        acc[2] = fmaf(x, w.z, acc[2]);
-        acc[3] = fmaf(x, w.w, acc[3]);
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const float xs[8] = {__uint_as_float(x[n][0].x), __uint_as_float(x[n][0].y),
+                             __uint_as_float(x[n][0].z), __uint_as_float(x[n][0].w),
+                             __uint_as_float(x[n][XW - 1].x), __uint_as_float(x[n][XW - 1].y),
+                             __uint_as_float(x[n][XW - 1].z), __uint_as_float(x[n][XW - 1].w)};
+#pragma unroll
+        for (int i = 0; i < KT; ++i) {
+          const float wk[4] = {__uint_as_float(w[i].x), __uint_as_float(w[i].y),
+                               __uint_as_float(w[i].z), __uint_as_float(w[i].w)};
+#pragma unroll
+          for (int c = 0; c < CE; ++c) v[n * CE + c] = fmaf(xs[i], wk[c], v[n * CE + c]);
+        }
       }
     }
   }
-  // sum over the 32 k-lanes: 8 per wavefront (lane bits 3..5), then 4 wavefronts
+  // halving exchange: after the round with mask m the sum index's bit log2(m) equals the
+  // lane's; once one sum is left, the remaining rounds add the partner's copy
 #pragma unroll
-  for (int e = 0; e < CE; ++e) {
-    acc[e] += __shfl_xor(acc[e], 8);
-    acc[e] += __shfl_xor(acc[e], 16);
-    acc[e] += __shfl_xor(acc[e], 32);
-  }
-  if (lane < 8) {
+  for (int s = 0; s < 6; ++s) {
+    const int m = 32 >> s;
+    const int half = NV >> (s + 1);
+    if (half >= 1) {
+      const bool up = (lane & m) != 0;
 #pragma unroll
-    for (int e = 0; e < CE; ++e) red[wave][n][e] = acc[e];
+      for (int i = 0; i < half; ++i) {
+        const float mine = up ? v[i + half] : v[i];
+        const float give = up ? v[i] : v[i + half];
+        v[i] = mine + __shfl_xor(give, m);
+      }
+    } else {
+      v[0] += __shfl_xor(v[0], m);
+    }
   }
+  if ((lane & ((64 >> LOG_NV) - 1)) == 0) red[wave][lane >> (6 - LOG_NV)] = v[0];
   __syncthreads();
-  if (t < 8 * CE) {
-    const int rn = t / CE, e = t % CE;
-    const int r = blockIdx.y * 8 + rn;
-    if (r < a.n_rows) {
-      const float v = (red[0][rn][e] + red[1][rn][e]) + (red[2][rn][e] + red[3][rn][e]);
+  if (t < NV) {
+    const int n = t / CE, c = t % CE;
+    if (n < nr) {
+      const float sum = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
+      const int r = row0 + n;
       const int req = a.row_req[r];
       const int pos = a.row_pos[r];
       const int page = a.page_table[(size_t)req * a.max_pages + pos / S::P];
-      store_elem<S>(a.pool, (size_t)page * (S::PAGE / S::EB) + append_dest<S>(col0 + e, pos % S::P),
-                    v);
+      store_elem<S>(a.pool, (size_t)page * (S::PAGE / S::EB) + append_dest<S>(col0 + c, pos % S::P),
+                    sum);
     }
   }
 }
