@@ -62,6 +62,19 @@ def traffic_record():
     return rec
 
 
+def device_weights(w, dev):
+    """bf16 codes on the device; the append weights (held [d][...]) in the output-major order
+    lrkv_append reads ([...][d])."""
+    import torch
+
+    out = {}
+    for k, v in w.items():
+        if k in ("W_SK", "W_SV", "U_K", "U_V"):
+            v = np.ascontiguousarray(v.reshape(v.shape[0], -1).T)
+        out[k] = torch.from_numpy(bf16_codes(v).view(np.int16)).to(dev)
+    return out
+
+
 def bf16_codes(x):
     import synth
 
@@ -105,7 +118,7 @@ def main():
     # ---------------- inputs (synthetic, seeded) ----------------
     t0 = time.time()
     w = synth.projection_weights(1, d, H, dh, r)
-    wd = {k: torch.from_numpy(bf16_codes(v).view(np.int16)).to(dev) for k, v in w.items()}
+    wd = device_weights(w, dev)
     X = synth.activations(2, B * T, d)  # row b*T + j is request b, position j
     Xd = torch.from_numpy(bf16_codes(X).view(np.int16)).to(dev)
     del X
@@ -279,7 +292,7 @@ def prefill_bench(torch, F, synth, dev):
     lay = F.lrkv_layout(H, dh, r, work.page_size, F.LRKV_BF16)
     n = B * T
     w = synth.projection_weights(41, d, H, dh, r)
-    wd = {k: torch.from_numpy(bf16_codes(v).view(np.int16)).to(dev) for k, v in w.items()}
+    wd = device_weights(w, dev)
     g = torch.Generator(device=dev)
     g.manual_seed(42)
     X = torch.randn(n, d, device=dev, generator=g).to(torch.bfloat16).view(torch.int16)

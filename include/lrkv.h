@@ -97,11 +97,13 @@ size_t lrkv_page_bytes(const lrkv_layout* L);
  * slot row_pos[n] % P, in the four sections.  No other byte of the pool changes.  Prefill
  * (all rows of a prompt) and single-token append are the same call.
  *
+ * The weights are held output-major (the [out][in] order of a linear layer's weight): the
+ * d weights that produce one output coordinate are contiguous.
  *   X        device, [n_rows][d]     in L->dtype
- *   W_SK     device, [d][d_h]        in L->dtype
- *   W_SV     device, [d][d_h]        in L->dtype
- *   U_K      device, [d][H][r]       in L->dtype (U_K[h] stacked along the columns)
- *   U_V      device, [d][H][r]       in L->dtype
+ *   W_SK     device, [d_h][d]        in L->dtype, element [c][k] = W_SK[k][c]
+ *   W_SV     device, [d_h][d]        in L->dtype, element [c][k] = W_SV[k][c]
+ *   U_K      device, [H][r][d]       in L->dtype, element [h][j][k] = U_K[h][k][j]
+ *   U_V      device, [H][r][d]       in L->dtype, element [h][j][k] = U_V[h][k][j]
  *   row_req  device, [n_rows] int32  request of each row, 0 <= row_req[n] < (table rows)
  *   row_pos  device, [n_rows] int32  token position of each row; rows must address
  *                                    distinct (request, position) pairs

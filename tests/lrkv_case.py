@@ -40,6 +40,12 @@ def codes_f64(codes: np.ndarray, dtype: int) -> np.ndarray:
     return codes.view(np.float32).astype(np.float64)
 
 
+def output_major(w: np.ndarray) -> np.ndarray:
+    """An append weight held [d][...] (W_SK [d][d_h], U_K [d][H][r]) -> the output-major
+    order lrkv_append reads ([d_h][d], [H][r][d]; contiguous)."""
+    return np.ascontiguousarray(np.asarray(w).reshape(w.shape[0], -1).T)
+
+
 def to_dev(codes: np.ndarray) -> torch.Tensor:
     """Element codes -> device tensor holding the same bytes."""
     a = np.ascontiguousarray(codes)

@@ -14,7 +14,7 @@ import torch
 import factored_rank_kv_amd as F
 import oracle as O
 import synth
-from lrkv_case import as_codes, codes_f64, layout_c, log, to_dev
+from lrkv_case import as_codes, codes_f64, layout_c, log, output_major, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -24,7 +24,7 @@ SENTINEL_BF16 = 0x7FBF  # a NaN code: no finite projection can produce it
 def run_append(L, Xc, wc, req, pos, table, npg, start_pool):
     d = Xc.shape[1]
     pool = to_dev(start_pool)
-    dev = {k: to_dev(v) for k, v in wc.items()}
+    dev = {k: to_dev(output_major(v)) for k, v in wc.items()}
     F.lrkv_append(layout_c(L), to_dev(Xc), Xc.shape[0], d, dev["W_SK"], dev["W_SV"], dev["U_K"],
                   dev["U_V"], to_dev(np.asarray(req, np.int32)), to_dev(np.asarray(pos, np.int32)),
                   to_dev(np.ascontiguousarray(table, np.int32)), table.shape[1], pool, npg)

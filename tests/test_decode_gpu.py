@@ -41,7 +41,7 @@ def test_c0_fp32_end_to_end_from_x():
     """C0 from the raw inputs: GPU append of X, then GPU decode of q = x_new W_q, against the
     oracle's per-head projection W_h = W_S + U_h B_h^T applied to X directly (eq 2)."""
     import factored_rank_kv_amd as F
-    from lrkv_case import layout_c
+    from lrkv_case import layout_c, output_major
 
     work = synth.C0
     w = synth.projection_weights(0, work.d, work.H, work.d_h, work.r, with_wq=True)
@@ -49,7 +49,8 @@ def test_c0_fp32_end_to_end_from_x():
     L = O.Layout(work.H, work.d_h, work.r, 16, O.F32)
     table, npg = synth.page_assignment(2, [65], 16, False)
     pool = torch.zeros(npg * O.page_bytes(L), dtype=torch.uint8, device="cuda:0")
-    dev = {k: torch.from_numpy(v).to("cuda:0") for k, v in w.items()}
+    dev = {k: torch.from_numpy(output_major(w[k])).to("cuda:0")
+           for k in ("W_SK", "W_SV", "U_K", "U_V")}
     Xd = torch.from_numpy(X).to("cuda:0")
     req = torch.zeros(65, dtype=torch.int32, device="cuda:0")
     pos = torch.arange(65, dtype=torch.int32, device="cuda:0")
