@@ -90,18 +90,10 @@ struct SplitArgs {
 
 template <class S>
 struct SplitCfg {
-  // heads per workgroup: with 16 or more heads a chunk's heads go to two workgroups (two
-  // per compute unit), each reading the chunk's S tiles (the second read hits L2) and
-  // forming the private queries of its own heads only
-  static constexpr int HG = S::H >= 16 ? S::H / 2 : S::H;
-  static constexpr int NHG = S::H / HG;       // workgroups per (chunk, query row, request)
-  static constexpr int HPW = HG <= 4 ? 4 : (HG / 4 > 2 ? HG / 4 : 2);  // heads per wave
+  static constexpr int HPW = S::H <= 4 ? 4 : (S::H / 8 > 2 ? S::H / 8 : 2);  // heads per wave
   static constexpr int SPLIT = 4 / HPW;        // lanes per (head, token) pair
-  static constexpr int NW = HG / HPW;
+  static constexpr int NW = S::H / HPW;
   static constexpr int NT = NW * 64;
-  // pages held in registers: two workgroups share a compute unit when the heads are split
-  // (each keeps three pages in flight), one workgroup keeps four
-  static constexpr int DEPTH = NHG > 1 ? 3 : 4;
   static constexpr int DHC_L = S::DHC / SPLIT;                  // S_K chunks per lane
   static constexpr int RC_L = (S::RC + SPLIT - 1) / SPLIT;      // private chunks per lane
   static constexpr int S_CHUNKS = 2 * S::DHC * S::P;            // 16-byte chunks of S_K + S_V
@@ -114,20 +106,15 @@ struct SplitCfg {
   // past the last private chunk adds nothing for it
   static constexpr int P_STRIDE = (SPLIT * RC_L * P_PER_CHUNK) | 1;
   // private queries: one job per (head, 16-byte chunk of p), d_h split over PQ_GROUPS
-  static constexpr int PQ_JOBS = HG * S::RC;
+  static constexpr int PQ_JOBS = S::H * S::RC;
   static constexpr int PQ_GROUPS = NT / PQ_JOBS > 0 ? NT / PQ_JOBS : 1;
   static constexpr int PQ_DSPAN = S::DH / PQ_GROUPS;
-  // bf16 cache: the shared value sum_j w[h][j] S_V[j] runs on MFMA, wave w owning the FT
-  // 16-feature tiles [16 (FT w + f), +16) for every head of the workgroup (HT tiles of 16
-  // head rows; rows past HG, when HG < 16, are computed from unset LDS and never stored:
-  // an MFMA output row depends on its own A row only)
+  // bf16 cache: the shared value sum_j w[h][j] S_V[j] runs on MFMA, wave w owning the
+  // 16-feature tile [16w, 16w+16) for every head (HT tiles of 16 heads)
   static constexpr bool MFMA_SV = S::BF;
-  static constexpr int HT = (HG + 15) / 16;
-  static constexpr int HROWS = 16 * HT;
-  static constexpr int FT = S::DH / (16 * NW) > 0 ? S::DH / (16 * NW) : 1;
-  static_assert(!MFMA_SV || (FT * 16 * NW == S::DH && S::P == 16),
-                "MFMA shared value: whole 16-feature tiles per wave, 16-token pages");
-  static_assert(S::H % HG == 0, "head groups split the heads evenly");
+  static constexpr int HT = S::H / 16 > 0 ? S::H / 16 : 1;
+  static_assert(!MFMA_SV || (S::H % 16 == 0 && NW * 16 == S::DH && S::P == 16),
+                "MFMA shared value: 16-head tiles, one 16-feature tile per wave, 16-token pages");
   static_assert(HPW * SPLIT == 4, "64 lanes = HPW heads x SPLIT x 16 tokens");
   static_assert(S::DHC % SPLIT == 0, "shared chunks split evenly");
   static_assert(S::DH % PQ_GROUPS == 0, "d_h split evenly");
@@ -151,8 +138,8 @@ struct PageRegs {
 // Lane geometry inside the workgroup.
 template <class S>
 struct Lane {
-  int tid, lane, wave, hl, half, j, hloc, h;  // hloc: head within the workgroup, h: global
-  __device__ __forceinline__ Lane(int t, int hg) {
+  int tid, lane, wave, hl, half, j, h;
+  __device__ __forceinline__ Lane(int t) {
     using C = SplitCfg<S>;
     tid = t;
     lane = t & 63;
@@ -160,8 +147,7 @@ struct Lane {
     hl = lane / (16 * C::SPLIT);
     half = (lane >> 4) & (C::SPLIT - 1);
     j = lane & 15;
-    hloc = wave * C::HPW + hl;
-    h = hg * C::HG + hloc;
+    h = wave * C::HPW + hl;
   }
 };
 
@@ -242,30 +228,25 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // weight).  v_mfma_f32_16x16x16_bf16 lane layout: A[i][k] at lane 16*(k/4) + i, element
 // k%4; B[k][j] at lane 16*(k/4) + j; D[i][j] at lane 16*(i/4) + j, element i%4.
 template <class S>
-__device__ __forceinline__ void shared_value_mfma(f32x4 (*acc)[SplitCfg<S>::FT],
-                                                  const uint16_t* __restrict__ wl,
+__device__ __forceinline__ void shared_value_mfma(f32x4* acc, const uint16_t* __restrict__ wl,
                                                   const float* __restrict__ al,
                                                   const uint16_t* __restrict__ svt, int wave,
                                                   int lane) {
   using C = SplitCfg<S>;
   const int i = lane & 15, g = lane >> 4;
+  const short4v b = *reinterpret_cast<const short4v*>(svt + (16 * wave + i) * S::P + 4 * g);
 #pragma unroll
   for (int ht = 0; ht < C::HT; ++ht) {
     const float4 a4 = *reinterpret_cast<const float4*>(al + 16 * ht + 4 * g);
+    acc[ht][0] *= a4.x;
+    acc[ht][1] *= a4.y;
+    acc[ht][2] *= a4.z;
+    acc[ht][3] *= a4.w;
     const short4v whi = *reinterpret_cast<const short4v*>(wl + (16 * ht + i) * S::P + 4 * g);
     const short4v wlo =
-        *reinterpret_cast<const short4v*>(wl + (C::HROWS + 16 * ht + i) * S::P + 4 * g);
-#pragma unroll
-    for (int f = 0; f < C::FT; ++f) {
-      const short4v b = *reinterpret_cast<const short4v*>(
-          svt + (16 * (C::FT * wave + f) + i) * S::P + 4 * g);
-      acc[ht][f][0] *= a4.x;
-      acc[ht][f][1] *= a4.y;
-      acc[ht][f][2] *= a4.z;
-      acc[ht][f][3] *= a4.w;
-      acc[ht][f] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(whi, b, acc[ht][f], 0, 0, 0);
-      acc[ht][f] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wlo, b, acc[ht][f], 0, 0, 0);
-    }
+        *reinterpret_cast<const short4v*>(wl + (S::H + 16 * ht + i) * S::P + 4 * g);
+    acc[ht] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(whi, b, acc[ht], 0, 0, 0);
+    acc[ht] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wlo, b, acc[ht], 0, 0, 0);
   }
 }
 
@@ -282,16 +263,14 @@ struct BKRows {
 };
 
 template <class S>
-__device__ __forceinline__ void load_bk_rows(const void* __restrict__ BK, int tid, int hg,
-                                             BKRows<S>& r) {
+__device__ __forceinline__ void load_bk_rows(const void* __restrict__ BK, int tid, BKRows<S>& r) {
   using C = SplitCfg<S>;
   // threads past the last group load a valid row they never use: no branch, so the loads
   // stay where they are written
   const int job = tid % C::PQ_JOBS;
   const int g = min(tid / C::PQ_JOBS, C::PQ_GROUPS - 1);
-  const int hj = job / S::RC;  // head of the job within the group
-  const int c = job - hj * S::RC;
-  const int h = hg * C::HG + hj;
+  const int h = job / S::RC;
+  const int c = job - h * S::RC;
   const uint8_t* bk = static_cast<const uint8_t*>(BK) +
                       ((size_t)h * S::DH * S::R + (size_t)c * S::CE) * S::EB;
 #pragma unroll
@@ -345,7 +324,7 @@ __device__ __forceinline__ void form_private_queries(const BKRows<S>& bkr,
   }
   constexpr int PAD = C::P_STRIDE - S::RC * C::P_PER_CHUNK;  // zero slots per head
   if constexpr (PAD > 0) {
-    for (int i = tid; i < C::HG * PAD; i += C::NT)
+    for (int i = tid; i < S::H * PAD; i += C::NT)
       p_lds[(i / PAD) * C::P_STRIDE + S::RC * C::P_PER_CHUNK + i % PAD] = make_uint4(0u, 0u, 0u, 0u);
   }
   __syncthreads();
@@ -385,7 +364,7 @@ struct SplitState {
   float l_run;                                // this lane's share of the exp-sum
   float accR[SplitCfg<S>::RC_L * S::CE];      // its share of sum_j w_j R_V[h, j] (its half)
   float accS[SplitCfg<S>::HPW][2];            // float32 cache: sum_j w_j S_V[j][2*lane + e]
-  f32x4 accT[SplitCfg<S>::HT][SplitCfg<S>::FT];  // bf16 cache: MFMA tiles of acc_S
+  f32x4 accT[SplitCfg<S>::HT];                // bf16 cache: MFMA tiles of acc_S (see above)
 };
 
 // the partner lane of a (head, token) pair holds the other half of the features
@@ -406,7 +385,7 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
   const bool valid = j < nvalid;
   // ---- score: q . S_K[j] + p . R_K[h, j]   (eq 6), this lane's half of the features
   float acc0 = 0.f, acc1 = 0.f;
-  const uint4* qh = q_lds + L.hloc * C::Q_STRIDE + L.half * C::DHC_L;
+  const uint4* qh = q_lds + L.h * C::Q_STRIDE + L.half * C::DHC_L;
   const uint4* skh = sk + L.half * C::DHC_L * S::P;
 #pragma unroll
   for (int c = 0; c < C::DHC_L; ++c) {
@@ -426,7 +405,7 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
       acc1 = fmaf(__uint_as_float(q4.w), __uint_as_float(s4.w), acc1);
     }
   }
-  const uint4* ph = p_lds + L.hloc * C::P_STRIDE;
+  const uint4* ph = p_lds + L.h * C::P_STRIDE;
 #pragma unroll
   for (int c = 0; c < C::RC_L; ++c) {
     const int cg = L.half * C::RC_L + c;  // slots past RC hold p = 0
@@ -484,9 +463,9 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
     if (L.half == 0) {
       const uint32_t hi = f32_to_bf16_rne(w);
       const uint32_t lo = f32_to_bf16_rne(w - bf16_to_f32((uint16_t)hi));
-      wl[L.hloc * S::P + L.j] = (uint16_t)hi;
-      wl[(C::HROWS + L.hloc) * S::P + L.j] = (uint16_t)lo;
-      if (L.j == 0) al[L.hloc] = alpha;
+      wl[L.h * S::P + L.j] = (uint16_t)hi;
+      wl[(S::H + L.h) * S::P + L.j] = (uint16_t)lo;
+      if (L.j == 0) al[L.h] = alpha;
     }
   }
   // only the last page of a request has empty slots: their R_V bytes are replaced by
@@ -551,7 +530,7 @@ decode_split_kernel(const SplitArgs a) {
   constexpr int SV_ROWS = C::MFMA_SV ? 1 : S::P * S::DHC;
   constexpr int SVT_BUFS = C::MFMA_SV ? 3 : 1;
   constexpr int SVT_ELEMS = C::MFMA_SV ? S::DH * S::P : 8;
-  constexpr int W_ELEMS = C::MFMA_SV ? 2 * C::HROWS * S::P : 8;
+  constexpr int W_ELEMS = C::MFMA_SV ? 2 * S::H * S::P : 8;
   __shared__ uint4 sk_lds[2][S::DHC * S::P];  // chunk-major [c][t], double buffered
   __shared__ uint4 sv_lds[2][SV_ROWS];        // float32 cache: rows [t][swizzled c]
   // bf16 cache: S_V feature rows [d][t] (three buffers: page k is read by the MFMA during
@@ -559,22 +538,16 @@ decode_split_kernel(const SplitArgs a) {
   // of the last consumed page (two buffers)
   __shared__ __align__(16) uint16_t svt_lds[SVT_BUFS][SVT_ELEMS];
   __shared__ __align__(16) uint16_t w_lds[2][W_ELEMS];
-  __shared__ __align__(16) float al_lds[2][C::HROWS];
-  __shared__ uint4 q_lds[C::HG * C::Q_STRIDE];
-  __shared__ uint4 p_lds[C::HG * C::P_STRIDE];
+  __shared__ __align__(16) float al_lds[2][S::H];
+  __shared__ uint4 q_lds[S::H * C::Q_STRIDE];
+  __shared__ uint4 p_lds[S::H * C::P_STRIDE];
   __shared__ float pacc[C::PQ_GROUPS * C::PQ_JOBS * S::CE];
   __shared__ int ids_lds[kMaxChunkPages];
 
-  // blockIdx.x -> (chunk, head group): the head groups of one chunk go to the same XCD
-  // (blocks go to the 8 XCDs round robin), one after the other, so the S tiles they both
-  // read are still in that XCD's L2 for the second
-  const int xcd = blockIdx.x & 7, jj = blockIdx.x >> 3;
-  const int hg = jj % C::NHG;
-  const int split = (jj / C::NHG) * 8 + xcd;
-  if (split >= a.n_split) return;
+  const int split = blockIdx.x;
   const int qi = blockIdx.y;
   const int b = blockIdx.z;
-  const Lane<S> L(threadIdx.x, hg);
+  const Lane<S> L(threadIdx.x);
   const int tid = L.tid;
   const size_t row = (size_t)b * a.q_len + qi;
 
@@ -589,20 +562,20 @@ decode_split_kernel(const SplitArgs a) {
     const int i = tid + k * C::NT;
     if (i < nid) id_r[k] = tab[i];
   }
-  constexpr int QCH = (C::HG * S::DHC + C::NT - 1) / C::NT;
+  constexpr int QCH = (S::H * S::DHC + C::NT - 1) / C::NT;
   uint4 q_r[QCH];
-  const uint4* qsrc = reinterpret_cast<const uint4*>(
-      static_cast<const uint8_t*>(a.q) + (row * S::H + hg * C::HG) * S::DH * S::EB);
+  const uint4* qsrc = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.q) +
+                                                     row * S::H * S::DH * S::EB);
 #pragma unroll
   for (int k = 0; k < QCH; ++k) {
     const int i = tid + k * C::NT;
-    if (i < C::HG * S::DHC) q_r[k] = qsrc[i];
+    if (i < S::H * S::DHC) q_r[k] = qsrc[i];
   }
   // the request length is read first (a scalar load); B_K rows, which depend on nothing,
   // follow at once, ahead of every page load
   const int len_b = a.seq_lens[b];
   BKRows<S> bkr;
-  load_bk_rows<S>(a.BK, tid, hg, bkr);
+  load_bk_rows<S>(a.BK, tid, bkr);
   const int vis = visible_tokens(len_b, a.q_len, qi);
   const int tok0 = pg0 * S::P;
   const int tok1 = min(vis, tok0 + a.chunk);
@@ -615,7 +588,7 @@ decode_split_kernel(const SplitArgs a) {
 #pragma unroll
   for (int k = 0; k < QCH; ++k) {
     const int i = tid + k * C::NT;
-    if (i < C::HG * S::DHC) q_lds[(i / S::DHC) * C::Q_STRIDE + i % S::DHC] = q_r[k];
+    if (i < S::H * S::DHC) q_lds[(i / S::DHC) * C::Q_STRIDE + i % S::DHC] = q_r[k];
   }
   __syncthreads();  // page ids and q in LDS
 
@@ -626,12 +599,11 @@ decode_split_kernel(const SplitArgs a) {
 
   PageRegs<S> r0, r1, r2, r3;
   // pages pg0, pg0+1 go in flight while the private queries are formed (the B_K rows
-  // hold the registers of a further buffer until then); with four buffers page pg0+2
-  // follows right after, with three the first step issues it
+  // hold the registers of a third buffer until then); page pg0+2 follows right after
   issue_page<S>(page_ptr(pg0), L, r0);
   if (pg0 + 1 < pg1) issue_page<S>(page_ptr(pg0 + 1), L, r1);
   form_private_queries<S>(bkr, q_lds, pacc, p_lds, tid);
-  if (C::DEPTH == 4 && pg0 + 2 < pg1) issue_page<S>(page_ptr(pg0 + 2), L, r2);
+  if (pg0 + 2 < pg1) issue_page<S>(page_ptr(pg0 + 2), L, r2);
   stage_shared<S>(sk_lds[0], sv_lds[0], svt_lds[0], tid, r0, nvalid(pg0));
   __syncthreads();
 
@@ -643,16 +615,14 @@ decode_split_kernel(const SplitArgs a) {
 #pragma unroll
   for (int x = 0; x < C::HPW; ++x) st.accS[x][0] = st.accS[x][1] = 0.f;
 #pragma unroll
-  for (int x = 0; x < C::HT; ++x)
-#pragma unroll
-    for (int f = 0; f < C::FT; ++f) st.accT[x][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int x = 0; x < C::HT; ++x) st.accT[x] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // one pipeline step: page pg is in `cur` and LDS buffer `buf`, page pg+1 in `nxt`; with
-  // four buffers page pg+2 is in flight and page pg+3 goes in flight into `fre`, with
-  // three page pg+2 goes into `fre`.  bf16 cache: the shared value of page pg-1 (weights
-  // written last step) goes through MFMA first.  Returns false when pg was the last page.
+  // one pipeline step: page pg is in `cur` and LDS buffer `buf`, page pg+1 in `nxt`, page
+  // pg+2 in flight; page pg+3 goes in flight into `fre`.  bf16 cache: the shared value of
+  // page pg-1 (weights written last step) goes through MFMA first.  Returns false when pg
+  // was the last page.
   auto step = [&](int pg, int buf, PageRegs<S>& cur, PageRegs<S>& nxt, PageRegs<S>& fre) {
-    if (pg + C::DEPTH - 1 < pg1) issue_page<S>(page_ptr(pg + C::DEPTH - 1), L, fre);
+    if (pg + 3 < pg1) issue_page<S>(page_ptr(pg + 3), L, fre);
     const int k = pg - pg0;
     if constexpr (C::MFMA_SV) {
       if (k > 0)
@@ -668,22 +638,11 @@ decode_split_kernel(const SplitArgs a) {
     __syncthreads();
     return more;
   };
-  if constexpr (C::DEPTH == 4) {
-    for (int pg = pg0;; pg += 4) {
-      if (!step(pg, 0, r0, r1, r3)) break;
-      if (!step(pg + 1, 1, r1, r2, r0)) break;
-      if (!step(pg + 2, 0, r2, r3, r1)) break;
-      if (!step(pg + 3, 1, r3, r0, r2)) break;
-    }
-  } else {
-    for (int pg = pg0;; pg += 6) {
-      if (!step(pg, 0, r0, r1, r2)) break;
-      if (!step(pg + 1, 1, r1, r2, r0)) break;
-      if (!step(pg + 2, 0, r2, r0, r1)) break;
-      if (!step(pg + 3, 1, r0, r1, r2)) break;
-      if (!step(pg + 4, 0, r1, r2, r0)) break;
-      if (!step(pg + 5, 1, r2, r0, r1)) break;
-    }
+  for (int pg = pg0;; pg += 4) {
+    if (!step(pg, 0, r0, r1, r3)) break;
+    if (!step(pg + 1, 1, r1, r2, r0)) break;
+    if (!step(pg + 2, 0, r2, r3, r1)) break;
+    if (!step(pg + 3, 1, r3, r0, r2)) break;
   }
   if constexpr (C::MFMA_SV) {  // shared value of the last page
     const int kl = pg1 - 1 - pg0;
@@ -705,26 +664,19 @@ decode_split_kernel(const SplitArgs a) {
     if ((k & 15) == L.j && kg < S::R) dst[2 + S::DH + kg] = st.accR[k];
   }
   if constexpr (C::MFMA_SV) {
-    // MFMA tiles: lane holds local heads 16*ht + 4*(lane/16) + e, feature
-    // 16*(FT*wave + f) + lane%16
-    float* rec = a.part + ((row * a.n_split + split) * S::H + hg * C::HG) * S::PART_PAD;
+    // MFMA tile: lane holds heads 16*ht + 4*(lane/16) + e, feature 16*wave + lane%16
+    float* rec = a.part + (row * a.n_split + split) * S::H * S::PART_PAD;
 #pragma unroll
     for (int ht = 0; ht < C::HT; ++ht)
 #pragma unroll
-      for (int f = 0; f < C::FT; ++f)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int hl = 16 * ht + 4 * (L.lane >> 4) + e;
-          if (C::HG % 16 == 0 || hl < C::HG)
-            rec[hl * S::PART_PAD + 2 + 16 * (C::FT * L.wave + f) + (L.lane & 15)] =
-                st.accT[ht][f][e];
-        }
+      for (int e = 0; e < 4; ++e)
+        rec[(16 * ht + 4 * (L.lane >> 4) + e) * S::PART_PAD + 2 + 16 * L.wave + (L.lane & 15)] =
+            st.accT[ht][e];
   } else if (2 * L.lane < S::DH) {
 #pragma unroll
     for (int x = 0; x < C::HPW; ++x) {
       float2* d2 = reinterpret_cast<float2*>(
-          a.part + ((row * a.n_split + split) * S::H + hg * C::HG + C::HPW * L.wave + x) *
-                       S::PART_PAD + 2 +
+          a.part + ((row * a.n_split + split) * S::H + C::HPW * L.wave + x) * S::PART_PAD + 2 +
           2 * L.lane);
       *d2 = make_float2(st.accS[x][0], st.accS[x][1]);
     }
@@ -882,8 +834,7 @@ hipError_t launch_decode(const DecodeArgs& a) {
   s.n_split = a.n_split;
   s.chunk = a.chunk;
   s.score_scale = 1.4426950408889634f / sqrtf((float)S::DH);
-  const int nx = (a.n_split + 7) / 8 * 8 * SplitCfg<S>::NHG;
-  hipLaunchKernelGGL(decode_split_kernel<S>, dim3(nx, a.q_len, a.batch),
+  hipLaunchKernelGGL(decode_split_kernel<S>, dim3(a.n_split, a.q_len, a.batch),
                      dim3(SplitCfg<S>::NT), 0, a.stream, s);
   hipLaunchKernelGGL(merge_expand_kernel<S>, dim3(S::H, a.q_len, a.batch), dim3(256), 0, a.stream,
                      a.part_ws, a.B_V, a.seq_lens, a.q_len, a.n_split, a.chunk, a.out);
