@@ -441,7 +441,7 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
   if (__builtin_expect(__any(bump), 0)) {  // rare after the first page: a real branch
     asm volatile("" ::: "memory");
     const float m_new = bump ? pm : st.m_run;
-    alpha = exp2f(st.m_run - m_new);  // 0 on the first page, 1 if not bumped
+    alpha = exp2_fast(st.m_run - m_new);  // 0 on the first page, 1 if not bumped
     st.l_run *= alpha;
 #pragma unroll
     for (int k = 0; k < C::RC_L * S::CE; ++k) st.accR[k] *= alpha;
@@ -455,7 +455,7 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
     }
     st.m_run = m_new;
   }
-  const float w = exp2f(s - st.m_run);  // exactly 0 for masked slots
+  const float w = exp2_fast(s - st.m_run);  // exactly 0 for masked slots
   st.l_run += w;
   if constexpr (C::MFMA_SV) {
     // weights as bfloat16 hi + lo for the MFMA shared value of this page (run by every
@@ -768,7 +768,7 @@ merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
       load_pass(s0, cnt);
       __syncthreads();
     }
-    if (t < cnt) wts[t] = exp2f(tf[t * PP] - m_star);
+    if (t < cnt) wts[t] = exp2_fast(tf[t * PP] - m_star);
     __syncthreads();
     if (col >= 0) {
       int s = 0;

@@ -40,19 +40,22 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// float32 -> bfloat16, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
-}
-
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+
+// float32 -> bfloat16, round to nearest even (v_cvt_pk_bf16_f32); NaN stays a NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// two values in one conversion: lo in bits 0..15, hi in bits 16..31
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{lo, hi}, bf16x2_v));
+}
+
+// 2^x by v_exp_f32 (results below the float32 normal range may flush to zero: they only
+// ever weigh softmax terms next to a weight of at least 1)
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // a.x*b.x + a.y*b.y + c on bfloat16 pairs with float32 accumulation (v_dot2_f32_bf16).
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {

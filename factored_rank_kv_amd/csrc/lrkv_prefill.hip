@@ -7,9 +7,10 @@
 // with a_ij = exp(s_ij - m_i) and one running max m_i per row (blockwise, as in the fused
 // paragraph after Algorithm 2).  Full per-head keys and values are never formed.
 //
-// Workgroup = (head h, tile of 128 query rows, request b); 8 wavefronts of 16 rows.  The
-// key loop walks tiles of 64 positions (four pages): S_K, S_V, R_K[h] and R_V[h] of the
-// tile are staged in LDS (token-major rows) and shared by the eight wavefronts.  Every
+// Workgroup = (head h, tile of 128 query rows, request b); 8 wavefronts of RW blocks of 16
+// rows (RW = 1; with RW > 1 the blocks of a wavefront share every operand read from LDS).
+// The key loop walks tiles of 64 positions (four pages): S_K, S_V, R_K[h] and R_V[h] of
+// the tile are staged in LDS (token-major rows) and shared by the wavefronts.  Every
 // product is computed transposed, tokens (or features) by query rows:
 //   S^T  = S_K Q^T + R_K[h] P^T          (P^T = B_K[h]^T Q^T, formed once per tile of rows)
 //   O_S^T += S_V^T A^T,  O_R^T += R_V[h]^T A^T,   O^T = O_S^T + B_V[h] O_R^T at the end,
@@ -45,10 +46,13 @@ __device__ __forceinline__ f32x4_p mfma16(const short4_p& a, const short4_p& b, 
 __device__ __forceinline__ short4_p read_tr(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p));
 }
+// two 4-element halves as one 8-element operand (the K = 32 product pairs two K = 16 blocks:
+// any order of k works as long as both operands use the same one)
+__device__ __forceinline__ bf16x8_p cat8(const short4_p& lo, const short4_p& hi) {
+  return __builtin_bit_cast(bf16x8_p, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 __device__ __forceinline__ short4_p pack4(float a, float b, float c, float d) {
-  const uint32_t lo = f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
-  const uint32_t hi = f32_to_bf16_rne(c) | (f32_to_bf16_rne(d) << 16);
-  return __builtin_bit_cast(short4_p, make_uint2(lo, hi));
+  return __builtin_bit_cast(short4_p, make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d)));
 }
 // x = hi + lo with hi = bf16(x), lo = bf16(x - hi), four at a time
 __device__ __forceinline__ void split4(const f32x4_p& x, short4_p& hi, short4_p& lo) {
@@ -75,8 +79,9 @@ __device__ __forceinline__ float xor_sum(float x) {
 
 template <class S>
 struct PrefillCfg {
-  static constexpr int NW = 8, NT = 512;
-  static constexpr int BQ = 16 * NW;           // query rows per workgroup
+  static constexpr int NW = 8, NT = 64 * NW;
+  static constexpr int RW = 1;                 // 16-row blocks per wavefront
+  static constexpr int BQ = 16 * RW * NW;      // query rows per workgroup
   static constexpr int BT = 64;                // tokens per key tile (four pages)
   static constexpr int PPT = BT / S::P;        // pages per key tile
   static constexpr int RP = 64;                // private width padded to 4 blocks of 16
@@ -132,9 +137,10 @@ __device__ __forceinline__ void stage_basis(uint8_t* lds, const void* src, int h
 }
 
 template <class S>
-__global__ void __launch_bounds__(512, 1)
+__global__ void __launch_bounds__(PrefillCfg<S>::NT, 1)
 prefill_kernel(const PrefillArgs a) {
   using C = PrefillCfg<S>;
+  constexpr int RW = C::RW;
   __shared__ __align__(16) uint8_t lds[C::LDS];
   __shared__ int ids_blk[C::IDB];  // page ids of key tiles [64 k, 64 k + 64)
 
@@ -153,48 +159,67 @@ prefill_kernel(const PrefillArgs a) {
   const int lane = t & 63, wave = t >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int T = a.seq_lens[b];
-  const int row = qt * C::BQ + 16 * wave + li;  // this lane's query row
-  const bool row_ok = row < a.q_len;
-  const int pos = T - a.q_len + row;            // its position; sees tokens 0..pos
+  // this lane's query rows (one per row block) and their positions (row sees 0..pos)
+  int row[RW], pos[RW];
+  bool row_ok[RW];
+#pragma unroll
+  for (int w = 0; w < RW; ++w) {
+    row[w] = qt * C::BQ + 16 * (RW * wave + w) + li;
+    row_ok[w] = row[w] < a.q_len;
+    pos[w] = T - a.q_len + row[w];
+  }
   // last position any row of the workgroup sees
   const int last_row = min(a.q_len - 1, qt * C::BQ + C::BQ - 1);
   const int pos_max = min(T - a.q_len + last_row, T - 1);
   const int n_tiles = pos_max >= 0 ? pos_max / C::BT + 1 : 0;
 
-  // ---- q rows of this wavefront as MFMA operands: lane (lg, li) holds row li's features
-  // 32 kb + 8 lg .. +7 (A layout of Q = B layout of Q^T)
-  bf16x8_p qv[C::KB];
-  {
+  // ---- q rows as MFMA operands: lane (lg, li) holds row li's features 32 kb + 8 lg .. +7
+  // (A layout of Q = B layout of Q^T)
+  bf16x8_p qv[RW][C::KB];
+#pragma unroll
+  for (int w = 0; w < RW; ++w) {
     const uint4* qrow = reinterpret_cast<const uint4*>(
         static_cast<const uint8_t*>(a.q) +
-        (((size_t)b * a.q_len + (row_ok ? row : 0)) * S::H + h) * S::DH * 2);
+        (((size_t)b * a.q_len + (row_ok[w] ? row[w] : 0)) * S::H + h) * S::DH * 2);
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
-      const uint4 v = row_ok ? qrow[4 * kb + lg] : make_uint4(0u, 0u, 0u, 0u);
-      qv[kb] = __builtin_bit_cast(bf16x8_p, v);
+      const uint4 v = row_ok[w] ? qrow[4 * kb + lg] : make_uint4(0u, 0u, 0u, 0u);
+      qv[w][kb] = __builtin_bit_cast(bf16x8_p, v);
     }
   }
 
-  // ---- P^T = B_K[h]^T Q^T (private queries of the 16 rows), hi/lo bf16 B operands of the
-  // private score: block rb holds P^T[16 rb + 4 lg + e][row li]
-  short4_p pth[C::RB], ptl[C::RB];
+  // ---- P^T = B_K[h]^T Q^T (private queries of the rows), hi/lo bf16 B operands of the
+  // private score: block rb holds P^T[16 rb + 4 lg + e][row li]; pairs of blocks make the
+  // K = 32 operands (element e < 4: rank 32 kp + 4 lg + e, element 4 + e: rank
+  // 32 kp + 16 + 4 lg + e)
+  short4_p pth[RW][C::RB], ptl[RW][C::RB];
   stage_basis<S>(lds, a.BK, h, t);
   __syncthreads();
 #pragma unroll
   for (int rb = 0; rb < C::RB; ++rb) {
-    f32x4_p acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4_p acc[RW];
+#pragma unroll
+    for (int w = 0; w < RW; ++w) acc[w] = f32x4_p{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
       // A = B_K^T: lane (lg, li) needs B_K[32 kb + 8 lg + e][16 rb + li]
       const uint8_t* base = lds + (32 * kb + 8 * lg + li / 4) * C::R_STRIDE + (16 * rb + 4 * (li & 3)) * 2;
-      const short4_p lo = read_tr(base);
-      const short4_p hi = read_tr(base + 4 * C::R_STRIDE);
-      const bf16x8_p av = __builtin_bit_cast(bf16x8_p, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc = mfma32(av, qv[kb], acc);
+      const bf16x8_p av = cat8(read_tr(base), read_tr(base + 4 * C::R_STRIDE));
+#pragma unroll
+      for (int w = 0; w < RW; ++w) acc[w] = mfma32(av, qv[w][kb], acc[w]);
     }
-    split4(acc, pth[rb], ptl[rb]);
+#pragma unroll
+    for (int w = 0; w < RW; ++w) split4(acc[w], pth[w][rb], ptl[w][rb]);
   }
   __syncthreads();  // B_K staging area is reused by the key tiles
+  bf16x8_p pkh[RW][C::RB / 2], pkl[RW][C::RB / 2];
+#pragma unroll
+  for (int w = 0; w < RW; ++w)
+#pragma unroll
+    for (int kp = 0; kp < C::RB / 2; ++kp) {
+      pkh[w][kp] = cat8(pth[w][2 * kp], pth[w][2 * kp + 1]);
+      pkl[w][kp] = cat8(ptl[w][2 * kp], ptl[w][2 * kp + 1]);
+    }
 
   // zero pad columns of the R_K / R_V rows (never overwritten by staging)
   for (int i = t; i < 2 * C::BT * (C::RP / 8 - S::RC); i += C::NT) {
@@ -205,12 +230,21 @@ prefill_kernel(const PrefillArgs a) {
         make_uint4(0u, 0u, 0u, 0u);
   }
 
-  f32x4_p os[C::FB], orr[C::RB];
+  f32x4_p os[RW][C::FB], orr[RW][C::RB];
 #pragma unroll
-  for (int i = 0; i < C::FB; ++i) os[i] = f32x4_p{0.f, 0.f, 0.f, 0.f};
+  for (int w = 0; w < RW; ++w) {
 #pragma unroll
-  for (int i = 0; i < C::RB; ++i) orr[i] = f32x4_p{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_part = 0.f;  // l_part: this lane's 4-token share of the sum
+    for (int i = 0; i < C::FB; ++i) os[w][i] = f32x4_p{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < C::RB; ++i) orr[w][i] = f32x4_p{0.f, 0.f, 0.f, 0.f};
+  }
+  // m_run: running max of the row; l_part: this lane's 4-token share of its exp-sum
+  float m_run[RW], l_part[RW];
+#pragma unroll
+  for (int w = 0; w < RW; ++w) {
+    m_run[w] = -INFINITY;
+    l_part[w] = 0.f;
+  }
 
   const int32_t* tab = a.page_table + (size_t)b * a.max_pages;
   auto fill_ids = [&](int kt0) {  // page ids of key tiles kt0 .. kt0 + TPB - 1 (0 past the table)
@@ -272,79 +306,102 @@ prefill_kernel(const PrefillArgs a) {
     __syncthreads();
 
     // ---- scores S^T for the 4 token blocks: lane (lg, li) gets tokens 16 tb + 4 lg + e of
-    // row li
-    f32x4_p sc[4];
+    // row li of each row block; every operand read from LDS serves both row blocks
+    f32x4_p sc[RW][4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-      f32x4_p acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4_p acc[RW];
+#pragma unroll
+      for (int w = 0; w < RW; ++w) acc[w] = f32x4_p{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
         const bf16x8_p kv = *reinterpret_cast<const bf16x8_p*>(
             lds + C::SK_OFF + (16 * tb + li) * C::SK_STRIDE + 64 * kb + 16 * lg);
-        acc = mfma32(kv, qv[kb], acc);
+#pragma unroll
+        for (int w = 0; w < RW; ++w) acc[w] = mfma32(kv, qv[w][kb], acc[w]);
+      }
+      // private part, K = 32 per product, ranks ordered as in pkh / pkl
+#pragma unroll
+      for (int kp = 0; kp < C::RB / 2; ++kp) {
+        const uint8_t* rkrow = lds + C::RK_OFF + (16 * tb + li) * C::R_STRIDE + 64 * kp + 8 * lg;
+        const bf16x8_p rk = cat8(*reinterpret_cast<const short4_p*>(rkrow),
+                                 *reinterpret_cast<const short4_p*>(rkrow + 32));
+#pragma unroll
+        for (int w = 0; w < RW; ++w) {
+          acc[w] = mfma32(rk, pkh[w][kp], acc[w]);
+          acc[w] = mfma32(rk, pkl[w][kp], acc[w]);
+        }
       }
 #pragma unroll
-      for (int rb = 0; rb < C::RB; ++rb) {
-        const short4_p rk = *reinterpret_cast<const short4_p*>(
-            lds + C::RK_OFF + (16 * tb + li) * C::R_STRIDE + 32 * rb + 8 * lg);
-        acc = mfma16(rk, pth[rb], acc);
-        acc = mfma16(rk, ptl[rb], acc);
-      }
-      sc[tb] = acc;
+      for (int w = 0; w < RW; ++w) sc[w][tb] = acc[w];
     }
 
     // ---- online softmax per row: scores are tokens j = kt*BT + 16 tb + 4 lg + e of row li
-    float mt = -INFINITY;
+    // probabilities as the B operands of the value products: pp[w][tp] element e < 4 is
+    // token 32 tp + 4 lg + e, element 4 + e is token 32 tp + 16 + 4 lg + e
+    bf16x8_p pp[RW][2];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+    for (int w = 0; w < RW; ++w) {
+      float mt = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = kt * C::BT + 16 * tb + 4 * lg + e;
-        const bool ok = row_ok && j <= pos;  // j < T follows from pos < T
-        const float s = ok ? sc[tb][e] * a.score_scale : -INFINITY;
-        sc[tb][e] = s;
-        mt = __builtin_fmaxf(mt, s);
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = kt * C::BT + 16 * tb + 4 * lg + e;
+          const bool ok = row_ok[w] && j <= pos[w];  // j < T follows from pos < T
+          const float s = ok ? sc[w][tb][e] * a.score_scale : -INFINITY;
+          sc[w][tb][e] = s;
+          mt = __builtin_fmaxf(mt, s);
+        }
+      mt = xor_max(mt);
+      const bool bump = mt > m_run[w] + 8.0f;
+      if (__builtin_expect(__any(bump), 0)) {
+        asm volatile("" ::: "memory");
+        const float m_new = bump ? mt : m_run[w];
+        const float alpha = m_run[w] == m_new ? 1.f : exp2_fast(m_run[w] - m_new);
+        l_part[w] *= alpha;
+#pragma unroll
+        for (int i = 0; i < C::FB; ++i) os[w][i] *= alpha;
+#pragma unroll
+        for (int i = 0; i < C::RB; ++i) orr[w][i] *= alpha;
+        m_run[w] = m_new;
       }
-    mt = xor_max(mt);
-    const bool bump = mt > m_run + 8.0f;
-    if (__builtin_expect(__any(bump), 0)) {
-      asm volatile("" ::: "memory");
-      const float m_new = bump ? mt : m_run;
-      const float alpha = m_run == m_new ? 1.f : exp2f(m_run - m_new);
-      l_part *= alpha;
 #pragma unroll
-      for (int i = 0; i < C::FB; ++i) os[i] *= alpha;
+      for (int tp = 0; tp < 2; ++tp) {
+        float p[8];
 #pragma unroll
-      for (int i = 0; i < C::RB; ++i) orr[i] *= alpha;
-      m_run = m_new;
-    }
-    short4_p pa[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      float p[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[e] = sc[tb][e] == -INFINITY ? 0.f : exp2f(sc[tb][e] - m_run);
-        l_part += p[e];
+        for (int e = 0; e < 8; ++e) {
+          const float s = sc[w][2 * tp + e / 4][e % 4];
+          p[e] = s == -INFINITY ? 0.f : exp2_fast(s - m_run[w]);
+          l_part[w] += p[e];
+        }
+        pp[w][tp] = __builtin_bit_cast(
+            bf16x8_p, make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                 pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
       }
-      pa[tb] = pack4(p[0], p[1], p[2], p[3]);
     }
 
-    // ---- values: O_S^T[16 fb + ..][row] += S_V^T A^T, O_R^T likewise; the A operand of
-    // block (fb, tb) is S_V[16 tb + 4 lg' + e][16 fb + li'] by a transposing read
+    // ---- values: O_S^T[16 fb + ..][row] += S_V^T A^T, O_R^T likewise, token blocks 2 tp
+    // and 2 tp + 1 in one K = 32 product (element e < 4: token 32 tp + 4 lg + e, element
+    // 4 + e: token 32 tp + 16 + 4 lg + e, in both operands); the A operand of block
+    // (fb, tb) is S_V[16 tb + 4 lg' + e][16 fb + li'] by a transposing read
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+    for (int tp = 0; tp < 2; ++tp) {
+      const uint8_t* svr = lds + C::SV_OFF + (32 * tp + 4 * lg + li / 4) * C::SV_STRIDE;
+      const uint8_t* rvr = lds + C::RV_OFF + (32 * tp + 4 * lg + li / 4) * C::R_STRIDE;
 #pragma unroll
       for (int fb = 0; fb < C::FB; ++fb) {
-        const short4_p v = read_tr(lds + C::SV_OFF + (16 * tb + 4 * lg + li / 4) * C::SV_STRIDE +
-                                   (16 * fb + 4 * (li & 3)) * 2);
-        os[fb] = mfma16(v, pa[tb], os[fb]);
+        const uint8_t* v0 = svr + (16 * fb + 4 * (li & 3)) * 2;
+        const bf16x8_p v = cat8(read_tr(v0), read_tr(v0 + 16 * C::SV_STRIDE));
+#pragma unroll
+        for (int w = 0; w < RW; ++w) os[w][fb] = mfma32(v, pp[w][tp], os[w][fb]);
       }
 #pragma unroll
       for (int rb = 0; rb < C::RB; ++rb) {
-        const short4_p v = read_tr(lds + C::RV_OFF + (16 * tb + 4 * lg + li / 4) * C::R_STRIDE +
-                                   (16 * rb + 4 * (li & 3)) * 2);
-        orr[rb] = mfma16(v, pa[tb], orr[rb]);
+        const uint8_t* v0 = rvr + (16 * rb + 4 * (li & 3)) * 2;
+        const bf16x8_p v = cat8(read_tr(v0), read_tr(v0 + 16 * C::R_STRIDE));
+#pragma unroll
+        for (int w = 0; w < RW; ++w) orr[w][rb] = mfma32(v, pp[w][tp], orr[w][rb]);
       }
     }
     if (kt + 1 < n_tiles) {
@@ -362,28 +419,31 @@ prefill_kernel(const PrefillArgs a) {
   // O^T[16 fb + 4 lg + e][row li] = O_S^T + sum_rb B_V[16 fb + .][16 rb + .] O_R^T[16 rb + .][row]
   stage_basis<S>(lds, a.BV, h, t);
   __syncthreads();
-  short4_p orh[C::RB], orl[C::RB];
-#pragma unroll
-  for (int rb = 0; rb < C::RB; ++rb) split4(orr[rb], orh[rb], orl[rb]);
-  const float l_row = xor_sum(l_part);
-  const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
   uint16_t* out = static_cast<uint16_t*>(a.out);
-  const size_t orow = (((size_t)b * a.q_len + row) * S::H + h) * S::DH;
 #pragma unroll
-  for (int fb = 0; fb < C::FB; ++fb) {
-    f32x4_p acc = os[fb];
+  for (int w = 0; w < RW; ++w) {
+    short4_p orh[C::RB], orl[C::RB];
 #pragma unroll
-    for (int rb = 0; rb < C::RB; ++rb) {
-      // A = B_V[h]: lane (lg, li) holds B_V[16 fb + li][16 rb + 4 lg .. +3]
-      const short4_p bv = *reinterpret_cast<const short4_p*>(
-          lds + (16 * fb + li) * C::R_STRIDE + (16 * rb + 4 * lg) * 2);
-      acc = mfma16(bv, orh[rb], acc);
-      acc = mfma16(bv, orl[rb], acc);
-    }
-    if (row_ok) {
-      const uint32_t w0 = f32_to_bf16_rne(acc[0] * inv) | (f32_to_bf16_rne(acc[1] * inv) << 16);
-      const uint32_t w1 = f32_to_bf16_rne(acc[2] * inv) | (f32_to_bf16_rne(acc[3] * inv) << 16);
-      *reinterpret_cast<uint2*>(out + orow + 16 * fb + 4 * lg) = make_uint2(w0, w1);
+    for (int rb = 0; rb < C::RB; ++rb) split4(orr[w][rb], orh[rb], orl[rb]);
+    const float l_row = xor_sum(l_part[w]);
+    const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+    const size_t orow = (((size_t)b * a.q_len + row[w]) * S::H + h) * S::DH;
+#pragma unroll
+    for (int fb = 0; fb < C::FB; ++fb) {
+      f32x4_p acc = os[w][fb];
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb) {
+        // A = B_V[h]: lane (lg, li) holds B_V[16 fb + li][16 rb + 4 lg .. +3]
+        const short4_p bv = *reinterpret_cast<const short4_p*>(
+            lds + (16 * fb + li) * C::R_STRIDE + (16 * rb + 4 * lg) * 2);
+        acc = mfma16(bv, orh[rb], acc);
+        acc = mfma16(bv, orl[rb], acc);
+      }
+      if (row_ok[w]) {
+        const uint32_t w0 = f32_to_bf16_rne(acc[0] * inv) | (f32_to_bf16_rne(acc[1] * inv) << 16);
+        const uint32_t w1 = f32_to_bf16_rne(acc[2] * inv) | (f32_to_bf16_rne(acc[3] * inv) << 16);
+        *reinterpret_cast<uint2*>(out + orow + 16 * fb + 4 * lg) = make_uint2(w0, w1);
+      }
     }
   }
 }
