@@ -179,34 +179,45 @@ append_few_rows_f32_kernel(AppendArgs a) {
 
 
 // ---------------------------------------------------------------------------------------
-// Many rows (prefill, cache build), bf16: the product on MFMA.  Workgroup = 128 rows x 128
-// product columns (one 128-column slice of one weight matrix), 256 threads = 2 x 2 waves of
-// 64 x 64, K in steps of 32 through double-buffered LDS; v_mfma_f32_16x16x32_bf16 with
-// float32 accumulation.  X tiles ([row][k]) and weight tiles ([column][k], the weights
-// being output-major) are stored alike, and each lane reads the 8 consecutive k of one row
-// (A operand) or of one column (B operand) as one 16-byte LDS read.  The 128 x 128 result is rounded to bf16 into LDS, then written to the pages as
-// 16-byte chunks (16 consecutive rows of one page fill 256 contiguous bytes of a section).
-// Blocks are numbered so that the 128-column slices of one row block run on one XCD
-// (blocks go to the 8 XCDs round robin), where they share that row block's X in L2.
+// Many rows (prefill, cache build), bf16: the product on MFMA.  Workgroup = BM rows x 128
+// product columns (one 128-column slice of one weight matrix), 256 threads = 2 x 2
+// wavefronts of BM/2 x 64, K in steps of 32 through double-buffered LDS;
+// v_mfma_f32_16x16x32_bf16 with float32 accumulation.  X tiles ([row][k]) and weight tiles
+// ([column][k], the weights being output-major) are stored alike, and each lane reads the
+// 8 consecutive k of one row (A operand) or of one column (B operand) as one 16-byte LDS
+// read; a wavefront's A and B reads serve (BM/32) x 4 products, so taller wavefront tiles
+// read less LDS per product.  The BM x 128 result is rounded to bf16 into LDS, then written
+// to the pages as 16-byte chunks (16 consecutive rows of one page fill 256 contiguous bytes
+// of a section).  Blocks are numbered so that the 128-column slices of one row block run
+// on one XCD (blocks go to the 8 XCDs round robin), where they share that row block's X in
+// L2.
 // ---------------------------------------------------------------------------------------
 template <class S>
 struct GemmCfg {
-  static constexpr int BM = 128, BN = 128, BK = 32, NT = 256;
-  static constexpr int XS = BK * 2;              // bytes per X row / weight column in LDS
-  static constexpr int X_BYTES = BM * XS;        // 8 KiB
-  static constexpr int W_BYTES = BN * XS;        // 8 KiB
+  static constexpr int BM = 256, BN = 128, BK = 32, NT = 256;
+  static constexpr int WM = BM / 2;              // rows per wavefront
+  static constexpr int IT = WM / 16, JT = 4;     // 16 x 16 product tiles per wavefront
+  // bytes per X row / weight column in LDS: 64 bytes of k and 32 of padding (measured:
+  // fewer bank conflicts on the operand reads than 64 or 80)
+  static constexpr int XS = BK * 2 + 32;
+  static constexpr int X_BYTES = BM * XS;
+  static constexpr int W_BYTES = BN * XS;
   static constexpr int STAGE = X_BYTES + W_BYTES;
+  static constexpr int KCH = BK * 2 / 16;        // 16-byte k-chunks per row and stage
+  static constexpr int XC = BM * KCH / NT;       // 16-byte X chunks staged per thread
+  static constexpr int WC = BN * KCH / NT;       // ... weight chunks
   static constexpr int OS = BN * 2 + 16;         // bytes per output row in LDS (padded)
   static constexpr int NS_TILES = S::DH / BN;    // slices of W_SK (and of W_SV)
   static constexpr int NU_TILES = S::H * S::R / BN;  // slices of U_K (and of U_V)
   static constexpr int COL_TILES = 2 * NS_TILES + 2 * NU_TILES;
   static_assert(S::BF && S::DH % BN == 0 && (S::H * S::R) % BN == 0, "128-column slices");
+  static_assert(KCH == 4 && XC * NT == BM * KCH && WC * NT == BN * KCH, "whole chunks per thread");
   // the output tile reuses the stage buffers
   static constexpr int SMEM = 2 * STAGE > BM * OS ? 2 * STAGE : BM * OS;
 };
 
 template <class S>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)
 append_gemm_kernel(AppendArgs a, int row_tiles) {
   using G = GemmCfg<S>;
   __shared__ __align__(16) uint8_t smem[G::SMEM];
@@ -232,90 +243,103 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
   const int wm = wave >> 1, wn = wave & 1;
   const int li = lane & 15, lg = lane >> 4;
 
-  if (t < G::BM) {
-    const int r = row0 + t;
+  for (int i = t; i < G::BM; i += G::NT) {
+    const int r = row0 + i;
     int page = 0, slot = 0;
     if (r < a.n_rows) {
       const int req = a.row_req[r], pos = a.row_pos[r];
       page = a.page_table[(size_t)req * a.max_pages + pos / S::P];
       slot = pos % S::P;
     }
-    row_page[t] = page;
-    row_slot[t] = slot;
+    row_page[i] = page;
+    row_slot[i] = slot;
   }
 
-  // global -> register staging, X and weights alike: 2 chunks of 16 B per thread (row or
-  // column t/4 (+64), k-chunk t%4)
+  // global -> register staging, X and weights alike: chunk c of a thread is row (or
+  // column) t/4 + 64 c, k-chunk t%4; rows past the end read a valid row whose result is
+  // dropped
   const uint8_t* X = static_cast<const uint8_t*>(a.X);
   const size_t xrow = (size_t)a.d * 2;  // bytes per X row and per weight row
-  const int xr0 = min(row0 + t / 4, a.n_rows - 1);  // rows past the end read a valid
-  const int xr1 = min(row0 + t / 4 + 64, a.n_rows - 1);  // row whose result is dropped
-  const uint8_t* xp0 = X + xr0 * xrow + 16 * (t & 3);
-  const uint8_t* xp1 = X + xr1 * xrow + 16 * (t & 3);
-  const uint8_t* wp0 = W + (size_t)(t / 4) * xrow + 16 * (t & 3);
-  const uint8_t* wp1 = wp0 + 64 * xrow;
-  const int xo0 = (t / 4) * G::XS + 16 * (t & 3), xo1 = xo0 + 64 * G::XS;
-  const int wo0 = G::X_BYTES + xo0, wo1 = G::X_BYTES + xo1;
-  uint4 x0, x1, w0, w1;
-#define LRKV_LOAD_STAGE(k0)                                                   \
-  x0 = *reinterpret_cast<const uint4*>(xp0 + (size_t)(k0) * 2);               \
-  x1 = *reinterpret_cast<const uint4*>(xp1 + (size_t)(k0) * 2);               \
-  w0 = *reinterpret_cast<const uint4*>(wp0 + (size_t)(k0) * 2);               \
-  w1 = *reinterpret_cast<const uint4*>(wp1 + (size_t)(k0) * 2);
-#define LRKV_STORE_STAGE(buf)                                                 \
-  *reinterpret_cast<uint4*>(smem + (buf) * G::STAGE + xo0) = x0;              \
-  *reinterpret_cast<uint4*>(smem + (buf) * G::STAGE + xo1) = x1;              \
-  *reinterpret_cast<uint4*>(smem + (buf) * G::STAGE + wo0) = w0;              \
-  *reinterpret_cast<uint4*>(smem + (buf) * G::STAGE + wo1) = w1;
-
-  f32x4_v acc[4][4];
+  const uint8_t* xp = X + 16 * (t & 3);
+  const uint8_t* wp = W + (size_t)(t / 4) * xrow + 16 * (t & 3);
+  const int xlast = a.n_rows - 1 - row0 - t / 4;  // chunks with 64 c > xlast read row n-1
+  const int so = (t / 4) * G::XS + 16 * (t & 3);  // LDS offset of chunk 0
+  typedef unsigned int stage_v __attribute__((ext_vector_type(4)));
+  stage_v xr[G::XC], wr[G::WC];
+  f32x4_v acc[G::IT][G::JT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < G::IT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < G::JT; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
 
   const int nk = a.d / G::BK;
-  LRKV_LOAD_STAGE(0)
-  LRKV_STORE_STAGE(0)
+  {
+#pragma unroll
+    for (int c = 0; c < G::XC; ++c)
+      xr[c] = *reinterpret_cast<const stage_v*>(
+          xp + (size_t)(row0 + t / 4 + min(64 * c, xlast)) * xrow + 0);
+#pragma unroll
+    for (int c = 0; c < G::WC; ++c)
+      wr[c] = *reinterpret_cast<const stage_v*>(wp + (size_t)(64 * c) * xrow + 0);
+#pragma unroll
+    for (int c = 0; c < G::XC; ++c)
+      *reinterpret_cast<stage_v*>(smem + so + 64 * c * G::XS) = xr[c];
+#pragma unroll
+    for (int c = 0; c < G::WC; ++c)
+      *reinterpret_cast<stage_v*>(smem + G::X_BYTES + so + 64 * c * G::XS) = wr[c];
+  }
   __syncthreads();
   for (int ks = 0; ks < nk; ++ks) {
     const int buf = ks & 1;
-    if (ks + 1 < nk) { LRKV_LOAD_STAGE((ks + 1) * G::BK) }
+    if (ks + 1 < nk) {
+#pragma unroll
+      for (int c = 0; c < G::XC; ++c)
+        xr[c] = *reinterpret_cast<const stage_v*>(
+            xp + (size_t)(row0 + t / 4 + min(64 * c, xlast)) * xrow + (size_t)((ks + 1) * G::BK) * 2);
+#pragma unroll
+      for (int c = 0; c < G::WC; ++c)
+        wr[c] = *reinterpret_cast<const stage_v*>(wp + (size_t)(64 * c) * xrow + (size_t)((ks + 1) * G::BK) * 2);
+    }
     const uint8_t* st = smem + buf * G::STAGE;
-    bf16x8_v av[4], bv[4];
+    bf16x8_v bv[G::JT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      av[i] = *reinterpret_cast<const bf16x8_v*>(st + (64 * wm + 16 * i + li) * G::XS + 16 * lg);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < G::JT; ++j)
       bv[j] = *reinterpret_cast<const bf16x8_v*>(st + G::X_BYTES +
                                                  (64 * wn + 16 * j + li) * G::XS + 16 * lg);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < G::IT; ++i) {
+      const bf16x8_v av =
+          *reinterpret_cast<const bf16x8_v*>(st + (G::WM * wm + 16 * i + li) * G::XS + 16 * lg);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
-    if (ks + 1 < nk) { LRKV_STORE_STAGE(buf ^ 1) }
+      for (int j = 0; j < G::JT; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[j], acc[i][j], 0, 0, 0);
+    }
+    if (ks + 1 < nk) {
+#pragma unroll
+      for (int c = 0; c < G::XC; ++c)
+        *reinterpret_cast<stage_v*>(smem + (buf ^ 1) * G::STAGE + so + 64 * c * G::XS) = xr[c];
+#pragma unroll
+      for (int c = 0; c < G::WC; ++c)
+        *reinterpret_cast<stage_v*>(smem + (buf ^ 1) * G::STAGE + G::X_BYTES + so + 64 * c * G::XS) =
+            wr[c];
+    }
     __syncthreads();
   }
-
-#undef LRKV_LOAD_STAGE
-#undef LRKV_STORE_STAGE
 
   // result tile -> bf16 [row][column] in LDS (D[i][j] at lane 16*(i/4) + j, element i%4)
   uint8_t* ot = smem;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < G::IT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < G::JT; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 64 * wm + 16 * i + 4 * lg + e;
+        const int r = G::WM * wm + 16 * i + 4 * lg + e;
         const int c = 64 * wn + 16 * j + li;
         *reinterpret_cast<uint16_t*>(ot + r * G::OS + 2 * c) = (uint16_t)f32_to_bf16_rne(acc[i][j][e]);
       }
   __syncthreads();
-  // 16-byte chunks to the pages: thread -> (row t%128 ... ), column chunks
+  // 16-byte chunks to the pages: chunk idx -> row idx % BM, column chunk idx / BM
   uint16_t* pool = static_cast<uint16_t*>(a.pool);
 #pragma unroll
   for (int k = 0; k < (G::BM * G::BN / 8) / G::NT; ++k) {

@@ -85,8 +85,9 @@ struct PrefillCfg {
   static constexpr int BT = 64;                // tokens per key tile (four pages)
   static constexpr int PPT = BT / S::P;        // pages per key tile
   static constexpr int RP = 64;                // private width padded to 4 blocks of 16
-  static constexpr int SK_STRIDE = S::DH * 2 + 16;   // bytes per token row of S_K
-  static constexpr int SV_STRIDE = S::DH * 2 + 32;   // ... of S_V (transposing reads)
+  // bytes per token row of S_K and of S_V (padding picked by measured LDS bank conflicts)
+  static constexpr int SK_STRIDE = S::DH * 2 + 32;
+  static constexpr int SV_STRIDE = S::DH * 2 + 32;
   static constexpr int R_STRIDE = RP * 2 + 16;       // ... of R_K[h], R_V[h], B_K, B_V rows
   static constexpr int SK_OFF = 0;
   static constexpr int SV_OFF = SK_OFF + BT * SK_STRIDE;
