@@ -67,8 +67,30 @@ def test_exact_inputs_bit_exact_with_sentinels(shape, n_rows):
         n_rows * (2 * dh + 2 * H * r)
 
 
+@pytest.mark.parametrize("n_rows,d", [(3, 8), (21, 40), (50, 96)])
+def test_exact_inputs_small_widths(n_rows, d):
+    """Few-row appends with d below one 32-wide block per wavefront (d = 8: only the first
+    wavefront has k; d = 40: a partial block) and with several 16-row blocks."""
+    H, dh, r = 16, 128, 56
+    L = O.Layout(H, dh, r, 16, O.BF16)
+    g = np.random.default_rng(270 + d)
+    X = ternary(g, (n_rows, d))
+    w = {"W_SK": ternary(g, (d, dh)), "W_SV": ternary(g, (d, dh)),
+         "U_K": ternary(g, (d, H, r)), "U_V": ternary(g, (d, H, r))}
+    wc = {k: as_codes(v, O.BF16) for k, v in w.items()}
+    lens = [40, 33]
+    table, npg = synth.page_assignment(271, lens, 16, True)
+    pairs = g.permutation([(b, p) for b, t in enumerate(lens) for p in range(t)])[:n_rows]
+    req, pos = pairs[:, 0], pairs[:, 1]
+    start = np.full(npg * O.page_elems(L), SENTINEL_BF16, np.uint16).view(np.uint8)
+    log(f"append exact, {n_rows} rows, d={d}")
+    got = run_append(L, as_codes(X, O.BF16), wc, req, pos, table, npg, start)
+    exp = expected(L, as_codes(X, O.BF16), wc, req, pos, table, start)
+    assert np.array_equal(got, exp)
+
+
 @pytest.mark.parametrize("shape", [(16, 128, 56), (32, 128, 32)])
-@pytest.mark.parametrize("n_rows,d", [(64, 256), (300, 256), (300, 264)])
+@pytest.mark.parametrize("n_rows,d", [(64, 256), (300, 256), (300, 264), (470, 256)])
 def test_exact_inputs_bit_exact_many_rows(shape, n_rows, d):
     """Prefill-sized appends (the MFMA product; d = 264 is not a multiple of its 32-wide K
     step and takes the row kernel): exact arithmetic, bit-exact pool with sentinels, a
