@@ -69,9 +69,12 @@ def test_workspace_sizes():
     # automatic chunks: B=8, T=4096 spreads over one wave of 256 groups (128-token chunks)
     assert F.lrkv_decode_workspace_bytes(C1, 8, 1, 4096, 0) == \
         F.lrkv_decode_workspace_bytes(C1, 8, 1, 4096, 128)
-    # B=4, T=131072 goes in 1024-token chunks
+    # B=4, T=131072 also fills one wave: 2048-token chunks (the automatic maximum)
     assert F.lrkv_decode_workspace_bytes(C3, 4, 1, 131072, 0) == \
-        F.lrkv_decode_workspace_bytes(C3, 4, 1, 131072, 1024)
+        F.lrkv_decode_workspace_bytes(C3, 4, 1, 131072, 2048)
+    # B=32 padded to 32768 tokens would want 4096: capped at 2048
+    assert F.lrkv_decode_workspace_bytes(C1, 32, 1, 32768, 0) == \
+        F.lrkv_decode_workspace_bytes(C1, 32, 1, 32768, 2048)
     assert F.lrkv_decode_workspace_bytes(C1, 8, 1, 4096, 4096 + 16) == 0  # chunk too long
     assert F.lrkv_decode_workspace_bytes(C1, 8, 1, 4096, 24) == 0  # not a multiple of P
     assert F.lrkv_decode_workspace_bytes(C1, 0, 1, 4096, 0) == 0
