@@ -91,6 +91,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=0, help="chunk_tokens for lrkv_decode (0 = auto)")
     ap.add_argument("--graph", type=int, default=1, help="replay the step loop from a HIP graph")
     ap.add_argument("--cpu-baseline", type=int, default=1)
+    ap.add_argument("--other-decodes", type=int, default=1,
+                    help="also time decode on the ragged B=32 and the B=4 x 131072 workloads")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--prefill", type=int, default=1,
                     help="also time the B=4 x 8192 prefill (append + multi-query attention)")
@@ -272,6 +274,8 @@ def main():
 
     if args.prefill:
         result["prefill"] = prefill_bench(torch, F, synth, dev)
+    if args.other_decodes:
+        result["other_decodes"] = other_decodes(torch, F, synth, dev)
 
     if args.cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(work, w, args.cpu_seconds)
@@ -349,6 +353,60 @@ def prefill_bench(torch, F, synth, dev):
                                "frac": round(tf_att / PEAK_BF16_TFLOPS, 4),
                                "flop": fl_att},
     }
+
+
+def other_decodes(torch, F, synth, dev):
+    """Single-query decode on the two large workloads, for context next to the headline B=8
+    line: B=32 requests of ragged lengths (uniform in 512..32768, permuted pages) and B=4
+    requests of 131072 tokens (H=32, r=32).  The cache holds N(0, 1) bf16 draws (the kernels
+    do the same work whatever the values); each pool (about 2.2 and 2.4 GiB) is larger than
+    the 256 MB Infinity Cache.  Reported at the automatic split size and, for the ragged
+    batch, at 768-token chunks."""
+    out = {}
+    for work, chunks in ((synth.C2, (0, 768)), (synth.C3, (0,))):
+        H, dh, r, B = work.H, work.d_h, work.r, work.B
+        lay = F.lrkv_layout(H, dh, r, work.page_size, F.LRKV_BF16)
+        lens = list(work.lens)
+        table, npg = synth.page_assignment(5, lens, work.page_size, permute=True)
+        g = torch.Generator(device=dev)
+        g.manual_seed(7)
+        pool = torch.randn(npg * F.lrkv_page_bytes(lay) // 2, device=dev, generator=g,
+                           dtype=torch.bfloat16).view(torch.uint8)
+        q = torch.randn(B, 1, H, dh, device=dev, generator=g).to(torch.bfloat16).view(torch.int16)
+        BK = (torch.randn(H, dh, r, device=dev, generator=g) / r ** 0.5).to(torch.bfloat16)
+        BV = (torch.randn(H, dh, r, device=dev, generator=g) / r ** 0.5).to(torch.bfloat16)
+        tab = torch.from_numpy(table).to(dev)
+        lt = torch.tensor(lens, dtype=torch.int32, device=dev)
+        msl = max(lens)
+        alg = 2 * 2 * sum(lens) * (dh + H * r)
+        o = torch.empty(B, 1, H, dh, dtype=torch.int16, device=dev)
+        for ch in chunks:
+            n = F.lrkv_decode_workspace_bytes(lay, B, 1, msl, ch)
+            ws = torch.empty(n, dtype=torch.uint8, device=dev)
+
+            def call():
+                F.lrkv_decode(lay, q, B, 1, BK.view(torch.int16), BV.view(torch.int16), pool, tab,
+                              table.shape[1], lt, msl, ch, o, ws, n)
+
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / 20 * 1e3
+            gbs = alg / us / 1e3
+            key = work.name + ("" if ch == 0 else f"_chunk{ch}")
+            out[key] = {"call_us": round(us, 2), "algorithmic_bytes": alg,
+                        "achieved_gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+                        "chunk_tokens": ch}
+            log(f"{key}: {us:.1f} us per call, {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f} %)")
+        del pool
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(work, weights, target_s):
