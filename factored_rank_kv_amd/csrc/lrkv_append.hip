@@ -68,8 +68,8 @@ typedef float f32x4_v __attribute__((ext_vector_type(4)));
 // results dropped (an output row of the product depends on its own A row only).  The
 // destination (request, position, then page) of each stored element is requested before
 // and during the operand loads.  The four partial tiles add in a fixed order through LDS.
-// Workgroups whose columns share 128-byte lines are not needed: each column's weights are
-// one contiguous run of d values.
+// Each column's weights are one contiguous run of d values, so the workgroups need no
+// placement on XCDs to share cache lines.
 // ---------------------------------------------------------------------------------------
 template <class S>
 __global__ void __launch_bounds__(256)

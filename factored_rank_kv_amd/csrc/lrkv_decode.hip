@@ -2,13 +2,14 @@
 // factored paged cache, as two launches on the caller's stream:
 //   1. decode_split_kernel   one workgroup per (chunk of pages, query row, request) covering
 //                            all heads.  Prologue: the chunk's page ids, the request length
-//                            and the query row are fetched together, the first page is put
-//                            in flight, and the private queries p = q B_K[h] of every head
-//                            are formed while it travels (eq 6).  Loop: shared S_K/S_V tiles
-//                            staged once in LDS for every head, private R_K/R_V rows streamed
-//                            per head straight into registers (page k+1 in flight while page
-//                            k is used), one online softmax with a shared and a private value
-//                            accumulator (fused blockwise paragraph after Algorithm 2).
+//                            and the query row are fetched together with the B_K rows, the
+//                            first two pages are put in flight, and the private queries
+//                            p = q B_K[h] of every head are formed while they travel (eq 6).
+//                            Loop: shared S_K/S_V tiles staged once in LDS for every head,
+//                            private R_K/R_V rows streamed per head straight into registers
+//                            (pages k+1..k+3 in flight while page k is used), one online
+//                            softmax with a shared and a private value accumulator (fused
+//                            blockwise paragraph after Algorithm 2).
 //                            Writes the chunk's (max, exp-sum, acc_S, acc_R) tuple per head.
 //   2. merge_expand_kernel   merges the chunks' tuples with one rescale factor per chunk,
 //                            expands acc_R through B_V[h]^T once and divides by the exp-sum
@@ -55,9 +56,10 @@ __device__ __forceinline__ float r16_sum(float x) {
 // For the score, the softmax and the private value, lane = hl*(16*SPLIT) + half*16 + j
 // covers head h = HPW*wave + hl and token slot j of the page; with SPLIT = 2 the two
 // lanes (half = 0, 1) of a (head, token) pair each take half of the features of the dot
-// products and of the private value, and add their partial scores with one swizzle.  For
-// the shared value the wavefront switches to lanes over feature pairs (2*lane, 2*lane+1)
-// of its HPW heads, with the weights broadcast by readlane.
+// products and of the private value, and add their partial scores with one swizzle.  The
+// shared value runs on MFMA for a bf16 cache (shared_value_mfma, one page behind the
+// scores); for a float32 cache the wavefront switches to lanes over feature pairs
+// (2*lane, 2*lane+1) of its HPW heads, with the weights broadcast by readlane.
 //
 // Pipeline: four register buffers; pages pg+1..pg+3 are in flight while page pg is
 // consumed; the S tiles go through a double-buffered LDS stage.  Page bytes are read with
