@@ -85,9 +85,10 @@ struct PrefillCfg {
   static constexpr int BT = 64;                // tokens per key tile (four pages)
   static constexpr int PPT = BT / S::P;        // pages per key tile
   static constexpr int RP = 64;                // private width padded to 4 blocks of 16
-  // bytes per token row of S_K and of S_V (padding picked by measured LDS bank conflicts)
-  static constexpr int SK_STRIDE = S::DH * 2 + 32;
-  static constexpr int SV_STRIDE = S::DH * 2 + 32;
+  // S_K and S_V token rows of 256 bytes, 16-byte chunk c of row t at chunk position
+  // c ^ (t & 15) (see s_slot)
+  static constexpr int SK_STRIDE = S::DH * 2;
+  static constexpr int SV_STRIDE = S::DH * 2;
   static constexpr int R_STRIDE = RP * 2 + 16;       // ... of R_K[h], R_V[h], B_K, B_V rows
   static constexpr int SK_OFF = 0;
   static constexpr int SV_OFF = SK_OFF + BT * SK_STRIDE;
@@ -105,9 +106,18 @@ struct PrefillCfg {
   static constexpr int S_PT = (S_CH + NT - 1) / NT;
   static constexpr int R_PT = (R_CH + NT - 1) / NT;
   static_assert(S::BF && S::P == 16 && S::R <= RP && S::DH % 32 == 0, "prefill shape");
+  static_assert(S::DHC == 16, "16 chunks per S row (the swizzle flips 4 bits)");
   static_assert(S::DH * S::R * 2 <= LDS, "B_K / B_V staging fits");
   static_assert(S::DH * R_STRIDE <= LDS, "padded B_K / B_V rows fit");
 };
+
+// Byte offset of 16-byte chunk c of token row t in an S_K / S_V tile: chunk position
+// c ^ (t & 15).  Measured with the LDS bank-conflict counter on this part: the staging
+// writes and the score reads (16 consecutive rows, one chunk per 16 lanes) run without
+// conflicts, where padded rows left the writes (288-byte rows) or the reads (272-byte rows)
+// at twice the cycles; the transposing value reads (4 rows x 2 neighbouring chunks per 16
+// lanes) keep a small excess.
+__device__ __forceinline__ int s_slot(int t, int c) { return t * 256 + 16 * (c ^ (t & 15)); }
 
 struct PrefillArgs {
   const void* q;
@@ -283,8 +293,8 @@ prefill_kernel(const PrefillArgs a) {
       if (i < C::S_CH) {
         const int pg = i / (S::DHC * S::P), rem = i % (S::DHC * S::P);
         const int tok = pg * S::P + rem % S::P, c = rem / S::P;
-        *reinterpret_cast<uint4*>(lds + C::SK_OFF + tok * C::SK_STRIDE + 16 * c) = sk_r[k];
-        *reinterpret_cast<uint4*>(lds + C::SV_OFF + tok * C::SV_STRIDE + 16 * c) = sv_r[k];
+        *reinterpret_cast<uint4*>(lds + C::SK_OFF + s_slot(tok, c)) = sk_r[k];
+        *reinterpret_cast<uint4*>(lds + C::SV_OFF + s_slot(tok, c)) = sv_r[k];
       }
     }
 #pragma unroll
@@ -317,7 +327,7 @@ prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
         const bf16x8_p kv = *reinterpret_cast<const bf16x8_p*>(
-            lds + C::SK_OFF + (16 * tb + li) * C::SK_STRIDE + 64 * kb + 16 * lg);
+            lds + C::SK_OFF + s_slot(16 * tb + li, 4 * kb + lg));
 #pragma unroll
         for (int w = 0; w < RW; ++w) acc[w] = mfma32(kv, qv[w][kb], acc[w]);
       }
@@ -388,11 +398,13 @@ prefill_kernel(const PrefillArgs a) {
     // (fb, tb) is S_V[16 tb + 4 lg' + e][16 fb + li'] by a transposing read
 #pragma unroll
     for (int tp = 0; tp < 2; ++tp) {
-      const uint8_t* svr = lds + C::SV_OFF + (32 * tp + 4 * lg + li / 4) * C::SV_STRIDE;
+      const int svrow = 32 * tp + 4 * lg + li / 4;  // second read: row + 16, same position
       const uint8_t* rvr = lds + C::RV_OFF + (32 * tp + 4 * lg + li / 4) * C::R_STRIDE;
 #pragma unroll
       for (int fb = 0; fb < C::FB; ++fb) {
-        const uint8_t* v0 = svr + (16 * fb + 4 * (li & 3)) * 2;
+        // features 16 fb + 4 (li & 3) .. +3: chunk 2 fb + (li & 3) / 2, half li & 1
+        const uint8_t* v0 =
+            lds + C::SV_OFF + s_slot(svrow, 2 * fb + ((li & 3) >> 1)) + 8 * (li & 1);
         const bf16x8_p v = cat8(read_tr(v0), read_tr(v0 + 16 * C::SV_STRIDE));
 #pragma unroll
         for (int w = 0; w < RW; ++w) os[w][fb] = mfma32(v, pp[w][tp], os[w][fb]);
