@@ -85,8 +85,7 @@ struct PrefillCfg {
   static constexpr int BT = 64;                // tokens per key tile (four pages)
   static constexpr int PPT = BT / S::P;        // pages per key tile
   static constexpr int RP = 64;                // private width padded to 4 blocks of 16
-  // S_K and S_V token rows of 256 bytes, 16-byte chunk c of row t at chunk position
-  // c ^ (t & 15) (see s_slot)
+  // S_K and S_V token rows of 256 bytes with swizzled chunk positions (sk_slot, sv_slot)
   static constexpr int SK_STRIDE = S::DH * 2;
   static constexpr int SV_STRIDE = S::DH * 2;
   static constexpr int R_STRIDE = RP * 2 + 16;       // ... of R_K[h], R_V[h], B_K, B_V rows
@@ -111,13 +110,15 @@ struct PrefillCfg {
   static_assert(S::DH * R_STRIDE <= LDS, "padded B_K / B_V rows fit");
 };
 
-// Byte offset of 16-byte chunk c of token row t in an S_K / S_V tile: chunk position
-// c ^ (t & 15).  Measured with the LDS bank-conflict counter on this part: the staging
-// writes and the score reads (16 consecutive rows, one chunk per 16 lanes) run without
-// conflicts, where padded rows left the writes (288-byte rows) or the reads (272-byte rows)
-// at twice the cycles; the transposing value reads (4 rows x 2 neighbouring chunks per 16
-// lanes) keep a small excess.
-__device__ __forceinline__ int s_slot(int t, int c) { return t * 256 + 16 * (c ^ (t & 15)); }
+// Byte offsets of 16-byte chunk c of token row t in the S_K and S_V tiles (256-byte rows):
+// chunk position c ^ (t & 15) for S_K and c ^ (9 t & 15) for S_V.  Measured with the LDS
+// bank-conflict counter on this part, each tile's two access patterns then run without
+// conflicts: for S_K the staging writes and the score reads (16 consecutive rows, one
+// chunk per 16 lanes), for S_V the staging writes and the transposing value reads (4 rows
+// x 2 neighbouring chunks per 16 lanes).  No one of the swizzles tried (nor padded rows)
+// serves all three patterns.
+__device__ __forceinline__ int sk_slot(int t, int c) { return t * 256 + 16 * (c ^ (t & 15)); }
+__device__ __forceinline__ int sv_slot(int t, int c) { return t * 256 + 16 * (c ^ ((9 * t) & 15)); }
 
 struct PrefillArgs {
   const void* q;
@@ -293,8 +294,8 @@ prefill_kernel(const PrefillArgs a) {
       if (i < C::S_CH) {
         const int pg = i / (S::DHC * S::P), rem = i % (S::DHC * S::P);
         const int tok = pg * S::P + rem % S::P, c = rem / S::P;
-        *reinterpret_cast<uint4*>(lds + C::SK_OFF + s_slot(tok, c)) = sk_r[k];
-        *reinterpret_cast<uint4*>(lds + C::SV_OFF + s_slot(tok, c)) = sv_r[k];
+        *reinterpret_cast<uint4*>(lds + C::SK_OFF + sk_slot(tok, c)) = sk_r[k];
+        *reinterpret_cast<uint4*>(lds + C::SV_OFF + sv_slot(tok, c)) = sv_r[k];
       }
     }
 #pragma unroll
@@ -327,7 +328,7 @@ prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
         const bf16x8_p kv = *reinterpret_cast<const bf16x8_p*>(
-            lds + C::SK_OFF + s_slot(16 * tb + li, 4 * kb + lg));
+            lds + C::SK_OFF + sk_slot(16 * tb + li, 4 * kb + lg));
 #pragma unroll
         for (int w = 0; w < RW; ++w) acc[w] = mfma32(kv, qv[w][kb], acc[w]);
       }
@@ -404,7 +405,7 @@ prefill_kernel(const PrefillArgs a) {
       for (int fb = 0; fb < C::FB; ++fb) {
         // features 16 fb + 4 (li & 3) .. +3: chunk 2 fb + (li & 3) / 2, half li & 1
         const uint8_t* v0 =
-            lds + C::SV_OFF + s_slot(svrow, 2 * fb + ((li & 3) >> 1)) + 8 * (li & 1);
+            lds + C::SV_OFF + sv_slot(svrow, 2 * fb + ((li & 3) >> 1)) + 8 * (li & 1);
         const bf16x8_p v = cat8(read_tr(v0), read_tr(v0 + 16 * C::SV_STRIDE));
 #pragma unroll
         for (int w = 0; w < RW; ++w) os[w][fb] = mfma32(v, pp[w][tp], os[w][fb]);
