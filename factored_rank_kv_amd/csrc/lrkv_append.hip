@@ -197,9 +197,12 @@ struct GemmCfg {
   static constexpr int BM = 256, BN = 128, BK = 32, NT = 256;
   static constexpr int WM = BM / 2;              // rows per wavefront
   static constexpr int IT = WM / 16, JT = 4;     // 16 x 16 product tiles per wavefront
-  // bytes per X row / weight column in LDS: 64 bytes of k and 32 of padding (measured:
-  // fewer bank conflicts on the operand reads than 64 or 80)
-  static constexpr int XS = BK * 2 + 32;
+  // bytes per X row / weight column in LDS: the 64 bytes of k, the four 16-byte chunks of
+  // row r at positions c ^ ((r ^ r >> 1) & 3).  Measured with the LDS bank-conflict counter
+  // on this part: both the operand reads (16 consecutive rows, one chunk per 16 lanes) and
+  // the staging writes (4 rows x 4 chunks per 16 lanes) run without conflicts, where rows
+  // padded to 96 bytes left the writes at twice the cycles.
+  static constexpr int XS = BK * 2;
   static constexpr int X_BYTES = BM * XS;
   static constexpr int W_BYTES = BN * XS;
   static constexpr int STAGE = X_BYTES + W_BYTES;
@@ -263,7 +266,10 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
   const uint8_t* xp = X + 16 * (t & 3);
   const uint8_t* wp = W + (size_t)(t / 4) * xrow + 16 * (t & 3);
   const int xlast = a.n_rows - 1 - row0 - t / 4;  // chunks with 64 c > xlast read row n-1
-  const int so = (t / 4) * G::XS + 16 * (t & 3);  // LDS offset of chunk 0
+  // LDS offset of this thread's chunk 0 (row t/4; the other chunks are 64 c rows below,
+  // with the same swizzle)
+  const int so = (t / 4) * G::XS + 16 * ((t & 3) ^ (((t / 4) ^ (t / 8)) & 3));
+  const int lsw = 16 * (lg ^ ((li ^ (li >> 1)) & 3));  // operand reads: rows 16 x + li
   typedef unsigned int stage_v __attribute__((ext_vector_type(4)));
   stage_v xr[G::XC], wr[G::WC];
   f32x4_v acc[G::IT][G::JT];
@@ -305,11 +311,11 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
 #pragma unroll
     for (int j = 0; j < G::JT; ++j)
       bv[j] = *reinterpret_cast<const bf16x8_v*>(st + G::X_BYTES +
-                                                 (64 * wn + 16 * j + li) * G::XS + 16 * lg);
+                                                 (64 * wn + 16 * j + li) * G::XS + lsw);
 #pragma unroll
     for (int i = 0; i < G::IT; ++i) {
       const bf16x8_v av =
-          *reinterpret_cast<const bf16x8_v*>(st + (G::WM * wm + 16 * i + li) * G::XS + 16 * lg);
+          *reinterpret_cast<const bf16x8_v*>(st + (G::WM * wm + 16 * i + li) * G::XS + lsw);
 #pragma unroll
       for (int j = 0; j < G::JT; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[j], acc[i][j], 0, 0, 0);
