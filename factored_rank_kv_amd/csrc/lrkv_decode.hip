@@ -87,8 +87,60 @@ struct SplitArgs {
   int q_len;
   int n_split;
   int chunk;
+  int batch;
+  int groups;  // balanced mode: split workgroups (0: one workgroup per chunk)
   float score_scale;
 };
+
+// Balanced split (single query row per request): the batch's pages, request after request,
+// are cut into `groups` equal ranges, one per split workgroup, whatever the lengths; a range
+// crossing requests is processed as one segment per request.  The segment of request b in
+// workgroup w writes its partial tuples at record slot w + b: slots are unique (ranges
+// are ordered, so w' > w implies b' >= b) and a request's slots are consecutive, in page
+// order.  Both kernels derive the ranges from the lengths on the device.
+constexpr int kBalancedMaxBatch = 1024;
+
+// pref[b] = pages of requests 0..b-1 (pref[B] = all pages), one page per P tokens started,
+// at most max_pages per request; every thread of the block takes part, the result is in
+// LDS after the call.
+template <int NT, int P>
+__device__ __forceinline__ int page_prefix(const int32_t* __restrict__ seq_lens, int B,
+                                           int max_pages, int* pref, int* wsum, int tid) {
+  constexpr int PER = (kBalancedMaxBatch + NT - 1) / NT;
+  int cnt[PER];
+  int s = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = tid * PER + k;
+    cnt[k] = i < B ? min((max(seq_lens[i], 0) + P - 1) / P, max_pages) : 0;
+    s += cnt[k];
+  }
+  const int lane = tid & 63, wave = tid >> 6;
+  int x = s;  // inclusive scan over the wavefront
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int acc = x - s;
+  for (int w = 0; w < wave; ++w) acc += wsum[w];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = tid * PER + k;
+    if (i < B) pref[i] = acc;
+    acc += cnt[k];
+  }
+  if (tid == NT - 1) pref[B] = acc;  // the last thread holds the last requests
+  __syncthreads();
+  return pref[B];
+}
+
+// The workgroup whose range holds page p: the largest w with floor(w N / G) <= p.
+__device__ __forceinline__ int group_of_page(int p, int N, int G) {
+  return (int)(((long long)(p + 1) * G - 1) / N);
+}
 
 template <class S>
 struct SplitCfg {
@@ -525,7 +577,7 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
   }
 }
 
-template <class S>
+template <class S, bool BAL>
 __global__ void __launch_bounds__(SplitCfg<S>::NT, 1)
 decode_split_kernel(const SplitArgs a) {
   using C = SplitCfg<S>;
@@ -545,18 +597,49 @@ decode_split_kernel(const SplitArgs a) {
   __shared__ uint4 p_lds[S::H * C::P_STRIDE];
   __shared__ float pacc[C::PQ_GROUPS * C::PQ_JOBS * S::CE];
   __shared__ int ids_lds[kMaxChunkPages];
+  __shared__ int pref_lds[BAL ? kBalancedMaxBatch + 1 : 1];
+  __shared__ int wsum_lds[BAL ? C::NW : 1];
 
-  const int split = blockIdx.x;
-  const int qi = blockIdx.y;
-  const int b = blockIdx.z;
-  const Lane<S> L(threadIdx.x);
+  // segment: request b, query row qi, pages [pg0, pg_end) of the request, record slot
+  int b, qi, pg0, pg_end;
+  size_t slot;
+  int g_hi = 0;  // balanced: end of this workgroup's range (page index over the batch)
+  if constexpr (BAL) {
+    const int N = page_prefix<C::NT, S::P>(a.seq_lens, a.batch, a.max_pages, pref_lds, wsum_lds,
+                                           (int)threadIdx.x);
+    const int g_lo = (int)((long long)blockIdx.x * N / a.groups);
+    g_hi = (int)((long long)(blockIdx.x + 1) * N / a.groups);
+    if (g_lo >= g_hi) return;  // uniform for the whole workgroup
+    int lo = 0, hi = a.batch - 1;  // the request holding page g_lo
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (pref_lds[mid + 1] > g_lo) hi = mid;
+      else lo = mid + 1;
+    }
+    b = lo;
+    qi = 0;
+    pg0 = g_lo - pref_lds[b];
+    pg_end = min(g_hi, pref_lds[b + 1]) - pref_lds[b];
+    slot = (size_t)blockIdx.x + b;
+  } else {
+    qi = blockIdx.y;
+    b = blockIdx.z;
+    pg0 = blockIdx.x * (a.chunk / S::P);
+    pg_end = pg0 + a.chunk / S::P;
+    slot = ((size_t)b * a.q_len + qi) * a.n_split + blockIdx.x;
+  }
+  for (;;) {
+  // the lane's geometry is derived anew for each segment: values computed from it are then
+  // not kept live across the segment loop (which made the balanced kernel spill)
+  int t_in = (int)threadIdx.x;
+  if constexpr (BAL) asm volatile("" : "+v"(t_in));
+  const Lane<S> L(t_in);
   const int tid = L.tid;
   const size_t row = (size_t)b * a.q_len + qi;
 
-  // the request length (scalar load) and this chunk's page ids and query row (vector
+  // the request length (scalar load) and this segment's page ids and query row (vector
   // loads) travel together
-  const int pg0 = split * (a.chunk / S::P);
-  const int nid = min(a.chunk / S::P, a.max_pages - pg0);  // table entries of this chunk
+  const int nid = min(pg_end - pg0, a.max_pages - pg0);  // table entries of this segment
   const int32_t* tab = a.page_table + (size_t)b * a.max_pages + pg0;
   int id_r[(kMaxChunkPages + C::NT - 1) / C::NT];
 #pragma unroll
@@ -580,8 +663,9 @@ decode_split_kernel(const SplitArgs a) {
   load_bk_rows<S>(a.BK, tid, bkr);
   const int vis = visible_tokens(len_b, a.q_len, qi);
   const int tok0 = pg0 * S::P;
-  const int tok1 = min(vis, tok0 + a.chunk);
-  if (tok0 >= tok1) return;  // uniform for the whole workgroup
+  // pages past the table row are never read, whatever the lengths say
+  const int tok1 = min(vis, min(pg_end, a.max_pages) * S::P);
+  if (tok0 < tok1) {  // uniform for the whole workgroup
 #pragma unroll
   for (int k = 0; k < (kMaxChunkPages + C::NT - 1) / C::NT; ++k) {
     const int i = tid + k * C::NT;
@@ -599,13 +683,19 @@ decode_split_kernel(const SplitArgs a) {
   auto page_ptr = [&](int pg) { return pool + (size_t)ids_lds[pg - pg0] * S::PAGE; };
   auto nvalid = [&](int pg) { return min(S::P, tok1 - pg * S::P); };
 
+  // register buffers of pages: four (pages k+1..k+3 in flight while k is consumed), or two
+  // in the balanced split, whose loop over segments leaves less room (page k+2 then goes in
+  // flight once page k is consumed)
+  constexpr int DEPTH = BAL ? 2 : 4;
   PageRegs<S> r0, r1, r2, r3;
   // pages pg0, pg0+1 go in flight while the private queries are formed (the B_K rows
-  // hold the registers of a third buffer until then); page pg0+2 follows right after
+  // hold the registers of a further buffer until then); with four buffers page pg0+2
+  // follows right after, with three the first step issues it
   issue_page<S>(page_ptr(pg0), L, r0);
   if (pg0 + 1 < pg1) issue_page<S>(page_ptr(pg0 + 1), L, r1);
   form_private_queries<S>(bkr, q_lds, pacc, p_lds, tid);
-  if (pg0 + 2 < pg1) issue_page<S>(page_ptr(pg0 + 2), L, r2);
+  if (DEPTH == 4 && pg0 + 2 < pg1) issue_page<S>(page_ptr(pg0 + 2), L, r2);
+  (void)r3;
   stage_shared<S>(sk_lds[0], sv_lds[0], svt_lds[0], tid, r0, nvalid(pg0));
   __syncthreads();
 
@@ -619,12 +709,12 @@ decode_split_kernel(const SplitArgs a) {
 #pragma unroll
   for (int x = 0; x < C::HT; ++x) st.accT[x] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // one pipeline step: page pg is in `cur` and LDS buffer `buf`, page pg+1 in `nxt`, page
-  // pg+2 in flight; page pg+3 goes in flight into `fre`.  bf16 cache: the shared value of
-  // page pg-1 (weights written last step) goes through MFMA first.  Returns false when pg
-  // was the last page.
+  // one pipeline step: page pg is in `cur` and LDS buffer `buf`, page pg+1 in `nxt`; with
+  // four buffers page pg+2 is in flight and page pg+3 goes in flight into `fre`, with three
+  // page pg+2 goes into `fre`.  bf16 cache: the shared value of page pg-1 (weights written
+  // last step) goes through MFMA first.  Returns false when pg was the last page.
   auto step = [&](int pg, int buf, PageRegs<S>& cur, PageRegs<S>& nxt, PageRegs<S>& fre) {
-    if (pg + 3 < pg1) issue_page<S>(page_ptr(pg + 3), L, fre);
+    if (DEPTH > 2 && pg + DEPTH - 1 < pg1) issue_page<S>(page_ptr(pg + DEPTH - 1), L, fre);
     const int k = pg - pg0;
     if constexpr (C::MFMA_SV) {
       if (k > 0)
@@ -637,14 +727,22 @@ decode_split_kernel(const SplitArgs a) {
     if (more)
       stage_shared<S>(sk_lds[buf ^ 1], sv_lds[buf ^ 1], svt_lds[C::MFMA_SV ? (k + 1) % 3 : 0],
                       tid, nxt, nvalid(pg + 1));
+    if (DEPTH == 2 && pg + 2 < pg1) issue_page<S>(page_ptr(pg + 2), L, fre);  // fre is cur
     __syncthreads();
     return more;
   };
-  for (int pg = pg0;; pg += 4) {
-    if (!step(pg, 0, r0, r1, r3)) break;
-    if (!step(pg + 1, 1, r1, r2, r0)) break;
-    if (!step(pg + 2, 0, r2, r3, r1)) break;
-    if (!step(pg + 3, 1, r3, r0, r2)) break;
+  if constexpr (DEPTH == 4) {
+    for (int pg = pg0;; pg += 4) {
+      if (!step(pg, 0, r0, r1, r3)) break;
+      if (!step(pg + 1, 1, r1, r2, r0)) break;
+      if (!step(pg + 2, 0, r2, r3, r1)) break;
+      if (!step(pg + 3, 1, r3, r0, r2)) break;
+    }
+  } else {
+    for (int pg = pg0;; pg += 2) {
+      if (!step(pg, 0, r0, r1, r0)) break;
+      if (!step(pg + 1, 1, r1, r0, r1)) break;
+    }
   }
   if constexpr (C::MFMA_SV) {  // shared value of the last page
     const int kl = pg1 - 1 - pg0;
@@ -655,7 +753,7 @@ decode_split_kernel(const SplitArgs a) {
   const float l_tot = r16_sum(st.l_run);
 #pragma unroll
   for (int k = 0; k < C::RC_L * S::CE; ++k) st.accR[k] = r16_sum(st.accR[k]);
-  float* dst = a.part + ((row * a.n_split + split) * S::H + L.h) * S::PART_PAD;
+  float* dst = a.part + (slot * S::H + L.h) * S::PART_PAD;
   if (L.j == 0 && L.half == 0) {
     dst[0] = st.m_run;
     dst[1] = l_tot;
@@ -667,7 +765,7 @@ decode_split_kernel(const SplitArgs a) {
   }
   if constexpr (C::MFMA_SV) {
     // MFMA tile: lane holds heads 16*ht + 4*(lane/16) + e, feature 16*wave + lane%16
-    float* rec = a.part + (row * a.n_split + split) * S::H * S::PART_PAD;
+    float* rec = a.part + slot * S::H * S::PART_PAD;
 #pragma unroll
     for (int ht = 0; ht < C::HT; ++ht)
 #pragma unroll
@@ -678,11 +776,21 @@ decode_split_kernel(const SplitArgs a) {
 #pragma unroll
     for (int x = 0; x < C::HPW; ++x) {
       float2* d2 = reinterpret_cast<float2*>(
-          a.part + ((row * a.n_split + split) * S::H + C::HPW * L.wave + x) * S::PART_PAD + 2 +
-          2 * L.lane);
+          a.part + (slot * S::H + C::HPW * L.wave + x) * S::PART_PAD + 2 + 2 * L.lane);
       *d2 = make_float2(st.accS[x][0], st.accS[x][1]);
     }
   }
+  }  // tok0 < tok1
+  if constexpr (!BAL) {
+    break;
+  } else {  // the next request of this workgroup's range, if any
+    if (++b >= a.batch || pref_lds[b] >= g_hi) break;
+    pg0 = 0;
+    pg_end = min(g_hi, pref_lds[b + 1]) - pref_lds[b];
+    slot = (size_t)blockIdx.x + b;
+    __syncthreads();  // LDS of the last segment is reused
+  }
+  }  // segments
 }
 
 // ---------------------------------------------------------------------------------------
@@ -692,13 +800,15 @@ decode_split_kernel(const SplitArgs a) {
 // does: the records of all n_split chunks (16-byte loads issued together, before the request
 // length is known; records past the visible chunks are ignored) and the thread's B_V row.
 // Then m* and the weights exp2(m_s - m*) come from the LDS copy, columns are summed over the
-// chunks in chunk order, and o[d] = (A_S[d] + A_R . B_V[h][d]) / L.
+// chunks in chunk order, and o[d] = (A_S[d] + A_R . B_V[h][d]) / L.  Balanced split: the
+// request's records are those of the workgroups whose page ranges meet it (slot w + b),
+// found from the lengths first; a workgroup skips nothing and the count is exact.
 // ---------------------------------------------------------------------------------------
-template <class S>
+template <class S, bool BAL>
 __global__ void __launch_bounds__(256)
 merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
                     const int32_t* __restrict__ seq_lens, int q_len, int n_split, int chunk,
-                    void* __restrict__ out) {
+                    int batch, int groups, int max_pages, void* __restrict__ out) {
   static_assert(S::DH + S::R + 1 <= 256, "one thread per column");
   constexpr int PP = S::PART_PAD;
   constexpr int MS_LDS = (48 * 1024) / (PP * 4);
@@ -718,6 +828,18 @@ merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
   const float* base = part + (row * n_split * S::H + h) * PP;
   const size_t stride = (size_t)S::H * PP;  // floats between chunks of the same head
   const float* tf = reinterpret_cast<const float*>(tile);
+  int cap = n_split;  // records that may be read
+  int n_bal = 0;      // balanced: this request's records
+  if constexpr (BAL) {
+    __shared__ int pref_s[kBalancedMaxBatch + 1];
+    __shared__ int wsum_s[4];
+    const int N = page_prefix<256, S::P>(seq_lens, batch, max_pages, pref_s, wsum_s, t);
+    const int p0 = pref_s[b], p1 = pref_s[b + 1];
+    const int w0 = p1 > p0 ? group_of_page(p0, N, groups) : 0;
+    n_bal = p1 > p0 ? group_of_page(p1 - 1, N, groups) - w0 + 1 : 0;
+    base = part + (((size_t)w0 + b) * S::H + h) * PP;
+    cap = n_bal;
+  }
 
   auto load_pass = [&](int s0, int cnt) {
     for (int i = t; i < cnt * (PP / 4); i += 256) {
@@ -726,7 +848,7 @@ merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
     }
   };
   // first pass and B_V row go out before the length is known
-  if (n_split <= MS) load_pass(0, n_split);
+  if (cap <= MS) load_pass(0, cap);
   constexpr int BVW = S::R * S::EB / 16;
   uint4 bvr[BVW];
   if (t < S::DH) {
@@ -736,7 +858,7 @@ merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
     for (int c = 0; c < BVW; ++c) bvr[c] = src[c];
   }
   const int vis = visible_tokens(seq_lens[b], q_len, qi);
-  const int n = (vis + chunk - 1) / chunk;
+  const int n = BAL ? n_bal : (vis + chunk - 1) / chunk;
   if (n == 0) {  // no visible token: zeros
     if (t < S::DH) {
       if constexpr (S::BF) static_cast<uint16_t*>(out)[out_off + t] = 0;
@@ -753,7 +875,7 @@ merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
   };
 
   float m_star;
-  if (n_split <= MS) {
+  if (cap <= MS) {
     __syncthreads();
     m_star = block_max(t < n ? tf[t * PP] : -INFINITY);
   } else {
@@ -765,7 +887,7 @@ merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
   float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
   for (int s0 = 0; s0 < n; s0 += MS) {
     const int cnt = min(MS, n - s0);
-    if (n_split > MS) {
+    if (cap > MS) {
       __syncthreads();  // previous pass done with tile
       load_pass(s0, cnt);
       __syncthreads();
@@ -835,11 +957,22 @@ hipError_t launch_decode(const DecodeArgs& a) {
   s.q_len = a.q_len;
   s.n_split = a.n_split;
   s.chunk = a.chunk;
+  s.batch = a.batch;
+  s.groups = a.groups;
   s.score_scale = 1.4426950408889634f / sqrtf((float)S::DH);
-  hipLaunchKernelGGL(decode_split_kernel<S>, dim3(a.n_split, a.q_len, a.batch),
-                     dim3(SplitCfg<S>::NT), 0, a.stream, s);
-  hipLaunchKernelGGL(merge_expand_kernel<S>, dim3(S::H, a.q_len, a.batch), dim3(256), 0, a.stream,
-                     a.part_ws, a.B_V, a.seq_lens, a.q_len, a.n_split, a.chunk, a.out);
+  if (a.groups > 0) {  // balanced split, one query row per request
+    hipLaunchKernelGGL((decode_split_kernel<S, true>), dim3(a.groups), dim3(SplitCfg<S>::NT), 0,
+                       a.stream, s);
+    hipLaunchKernelGGL((merge_expand_kernel<S, true>), dim3(S::H, 1, a.batch), dim3(256), 0,
+                       a.stream, a.part_ws, a.B_V, a.seq_lens, 1, 0, 0, a.batch, a.groups,
+                       a.max_pages, a.out);
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<S, false>), dim3(a.n_split, a.q_len, a.batch),
+                       dim3(SplitCfg<S>::NT), 0, a.stream, s);
+    hipLaunchKernelGGL((merge_expand_kernel<S, false>), dim3(S::H, a.q_len, a.batch), dim3(256), 0,
+                       a.stream, a.part_ws, a.B_V, a.seq_lens, a.q_len, a.n_split, a.chunk,
+                       a.batch, 0, a.max_pages, a.out);
+  }
   return hipGetLastError();
 }
 

@@ -25,8 +25,11 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   int n_split;   // chunks per (request, query row)
   int chunk;     // tokens per chunk, a multiple of the page size
+  int groups;    // > 0: balanced split over this many workgroups (q_len = 1)
   void* out;
-  float* part_ws;  // [batch][q_len][n_split][H][record of 2 + d_h + r floats, padded to 4]
+  // partial records of 2 + d_h + r floats (padded to 4) per head: [batch][q_len][n_split][H],
+  // or, balanced, [groups + batch][H]
+  float* part_ws;
   hipStream_t stream;
 };
 

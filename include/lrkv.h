@@ -141,11 +141,12 @@ size_t lrkv_decode_workspace_bytes(const lrkv_layout* L, int32_t batch, int32_t 
  *   page_table device, [batch][max_pages_per_req] int32
  *   seq_lens   device, [batch] int32, 0 <= seq_lens[b] <= max_seq_len
  *   max_seq_len  host value >= every seq_lens[b], and <= max_pages_per_req * P
- *   chunk_tokens host value: 0 picks the split size from batch * q_len * max_seq_len
- *              (one wave of 256 split workgroups, 64 to 2048 tokens: right for equal
- *              lengths); else a positive multiple of P up to 4096.  A ragged batch, sized
- *              by its longest request under 0, often runs faster with several waves of
- *              shorter chunks (e.g. 768 tokens for 32 lengths spread over 512..32768)
+ *   chunk_tokens host value: 0 picks the split.  With q_len == 1 and 16 to 1024 requests
+ *              the batch's pages (request after request, from the lengths on the device)
+ *              are cut into equal ranges, one per split workgroup, whatever the lengths;
+ *              otherwise chunks of batch * q_len * max_seq_len / 256 tokens (one wave of
+ *              256 split workgroups, 64 to 2048 tokens).  Else a positive multiple of P up
+ *              to 4096: chunks of that many tokens
  *   out        device, [batch][q_len][H][d_h]  in L->dtype
  *   workspace  device, >= lrkv_decode_workspace_bytes(L, batch, q_len, max_seq_len,
  *              chunk_tokens) bytes, 256-byte aligned; contents need not be initialised

@@ -82,6 +82,32 @@ def test_c1_shape_ragged_paged_nan_tails(chunk):
     check(case, case.run_f64(chunk_tokens=chunk), case.reference(), what=f"c1 ragged chunk {chunk}")
 
 
+@pytest.mark.parametrize("lens_kind", ["mixed", "short_many", "equal"])
+def test_balanced_split(lens_kind):
+    """Automatic splits of 16 or more single-row requests cut the batch's pages into equal
+    ranges per workgroup; ranges cross request boundaries (one segment and record per
+    request met), requests of 0 tokens own no pages.  Every output against the oracle, and
+    against the chunked split (explicit chunk_tokens) within the same bar."""
+    g = np.random.default_rng(120)
+    if lens_kind == "mixed":
+        lens = [0, 1, 15, 16, 17, 300, 1000, 33] + g.integers(0, 700, 16).tolist()
+    elif lens_kind == "short_many":  # 100 requests of 3 pages: ranges of 1-2 pages
+        lens = [48] * 100
+    else:  # 20 x 700 tokens: about 55 pages a range, several requests per range edge
+        lens = [700] * 20
+    log(f"balanced split, {len(lens)} requests, {sum(lens)} tokens ({lens_kind})")
+    case = iid_case(121 + len(lens), 16, 128, 56, O.BF16, lens, permute=True, fill=0x7FC0)
+    got = case.run_f64()
+    ref = case.reference()
+    for b, t in enumerate(lens):
+        if t == 0:
+            assert np.all(got[b] == 0.0)
+    live = np.array(lens) > 0
+    check(case, got[live], ref[live], what=f"balanced {lens_kind}")
+    chunked = case.run_f64(chunk_tokens=64)
+    check(case, chunked[live], ref[live], what=f"chunked {lens_kind}")
+
+
 def test_c3_shape_small():
     log("c3 shape (32 heads, r=32), ragged, permuted, NaN tails")
     case = iid_case(102, 32, 128, 32, O.BF16, [5, 64, 129], permute=True, fill=0x7FC0)

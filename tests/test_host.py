@@ -72,9 +72,19 @@ def test_workspace_sizes():
     # B=4, T=131072 also fills one wave: 2048-token chunks (the automatic maximum)
     assert F.lrkv_decode_workspace_bytes(C3, 4, 1, 131072, 0) == \
         F.lrkv_decode_workspace_bytes(C3, 4, 1, 131072, 2048)
-    # B=32 padded to 32768 tokens would want 4096: capped at 2048
+    # B=32 padded to 32768 tokens would want 4096: capped at 2048 when asked for explicitly
+    assert F.lrkv_decode_workspace_bytes(C1, 32, 1, 32768, 2048) == \
+        -(-32 * 16 * H * rec * 4 // 256) * 256
+    # automatic splits of 16 or more single-row requests are balanced: one record per
+    # (workgroup, request it meets), at most groups + batch of them; groups = 256, or more
+    # when the page ranges would outgrow 255 pages (B=32 x 2048 pages: 258)
     assert F.lrkv_decode_workspace_bytes(C1, 32, 1, 32768, 0) == \
-        F.lrkv_decode_workspace_bytes(C1, 32, 1, 32768, 2048)
+        -(-(258 + 32) * H * rec * 4 // 256) * 256
+    assert F.lrkv_decode_workspace_bytes(C1, 16, 1, 4096, 0) == \
+        -(-(256 + 16) * H * rec * 4 // 256) * 256
+    # several query rows keep the chunked split
+    assert F.lrkv_decode_workspace_bytes(C1, 32, 2, 4096, 0) == \
+        F.lrkv_decode_workspace_bytes(C1, 32, 2, 4096, 1024)
     assert F.lrkv_decode_workspace_bytes(C1, 8, 1, 4096, 4096 + 16) == 0  # chunk too long
     assert F.lrkv_decode_workspace_bytes(C1, 8, 1, 4096, 24) == 0  # not a multiple of P
     assert F.lrkv_decode_workspace_bytes(C1, 0, 1, 4096, 0) == 0
