@@ -72,7 +72,6 @@ int pick_chunk(const lrkv_layout* L, int batch, int q_len, int max_seq_len, int 
 // 500 µs for one wave of chunks sized by the longest request).  Smaller batches keep the
 // chunked split, whose four pages in flight per workgroup and shorter start suit them.
 constexpr int kBalancedMinBatch = 16;
-constexpr int kBalancedMaxBatch = 1024;  // as in the kernels
 constexpr int kBalancedGroups = 256;     // one wave of split workgroups
 
 struct DecodeSizes {

@@ -97,8 +97,8 @@ struct SplitArgs {
 // crossing requests is processed as one segment per request.  The segment of request b in
 // workgroup w writes its partial tuples at record slot w + b: slots are unique (ranges
 // are ordered, so w' > w implies b' >= b) and a request's slots are consecutive, in page
-// order.  Both kernels derive the ranges from the lengths on the device.
-constexpr int kBalancedMaxBatch = 1024;
+// order.  Both kernels derive the ranges from the lengths on the device (at most
+// kBalancedMaxBatch requests).
 
 // pref[b] = pages of requests 0..b-1 (pref[B] = all pages), one page per P tokens started,
 // at most max_pages per request; every thread of the block takes part, the result is in

@@ -55,6 +55,9 @@ hipError_t launch_decode(const DecodeArgs& a);
 template <class S>
 hipError_t launch_append(const AppendArgs& a);
 
+// Largest batch the balanced split handles (its kernels hold the batch's page counts in LDS).
+constexpr int kBalancedMaxBatch = 1024;
+
 // Query rows per request at or above which a bf16 lrkv_decode call takes the multi-query
 // (prefill) kernel; it needs no workspace.
 constexpr int kPrefillMinRows = 64;
