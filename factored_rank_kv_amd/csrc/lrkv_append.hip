@@ -181,7 +181,8 @@ append_few_rows_f32_kernel(AppendArgs a) {
 // ---------------------------------------------------------------------------------------
 // Many rows (prefill, cache build), bf16: the product on MFMA.  Workgroup = BM rows x 128
 // product columns (one 128-column slice of one weight matrix), 256 threads = 2 x 2
-// wavefronts of BM/2 x 64, K in steps of 32 through double-buffered LDS;
+// wavefronts of BM/2 x 64, K in steps of 32 through a ring of three LDS stages that direct
+// global->LDS loads fill two steps ahead of the products (no register staging);
 // v_mfma_f32_16x16x32_bf16 with float32 accumulation.  X tiles ([row][k]) and weight tiles
 // ([column][k], the weights being output-major) are stored alike, and each lane reads the
 // 8 consecutive k of one row (A operand) or of one column (B operand) as one 16-byte LDS
@@ -206,18 +207,36 @@ struct GemmCfg {
   static constexpr int X_BYTES = BM * XS;
   static constexpr int W_BYTES = BN * XS;
   static constexpr int STAGE = X_BYTES + W_BYTES;
-  static constexpr int KCH = BK * 2 / 16;        // 16-byte k-chunks per row and stage
-  static constexpr int XC = BM * KCH / NT;       // 16-byte X chunks staged per thread
-  static constexpr int WC = BN * KCH / NT;       // ... weight chunks
+  static constexpr int NSTAGE = 3;
   static constexpr int OS = BN * 2 + 16;         // bytes per output row in LDS (padded)
   static constexpr int NS_TILES = S::DH / BN;    // slices of W_SK (and of W_SV)
   static constexpr int NU_TILES = S::H * S::R / BN;  // slices of U_K (and of U_V)
   static constexpr int COL_TILES = 2 * NS_TILES + 2 * NU_TILES;
   static_assert(S::BF && S::DH % BN == 0 && (S::H * S::R) % BN == 0, "128-column slices");
-  static_assert(KCH == 4 && XC * NT == BM * KCH && WC * NT == BN * KCH, "whole chunks per thread");
+  // staging: 1 KiB (16 rows of 64 bytes) per wavefront load; 4 of X and 2 of weights
+  // per wavefront and stage
+  static_assert(BK == 32 && NT == 256 && X_BYTES == 4 * 4 * 1024 && W_BYTES == 4 * 2 * 1024,
+                "staging geometry");
   // the output tile reuses the stage buffers
-  static constexpr int SMEM = 2 * STAGE > BM * OS ? 2 * STAGE : BM * OS;
+  static constexpr int SMEM = NSTAGE * STAGE > BM * OS ? NSTAGE * STAGE : BM * OS;
 };
+
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): lane i
+// of the wavefront writes LDS bytes [lds + 16 i, lds + 16 i + 16); lds is wave-uniform.
+// Written as inline assembly, so the compiler's wait counters do not see these loads; the
+// caller waits for them with s_waitcnt vmcnt and a barrier before reading the bytes.
+// M0 (which holds the LDS address) is saved and restored around the load.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(g), "s"(lds)
+      : "memory");
+}
 
 template <class S>
 __global__ void __launch_bounds__(256, 2)
@@ -258,20 +277,37 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
     row_slot[i] = slot;
   }
 
-  // global -> register staging, X and weights alike: chunk c of a thread is row (or
-  // column) t/4 + 64 c, k-chunk t%4; rows past the end read a valid row whose result is
-  // dropped
+  // global -> LDS staging by direct loads (global_load_lds_dwordx4): one wavefront
+  // instruction fills 1 KiB = 16 rows x 64 bytes; lane i writes bytes [16 i, 16 i + 16) of
+  // it, i.e. row i/4, chunk position i%4, so it loads k-chunk (i%4) ^ f(i/4) of that row.
   const uint8_t* X = static_cast<const uint8_t*>(a.X);
   const size_t xrow = (size_t)a.d * 2;  // bytes per X row and per weight row
-  const uint8_t* xp = X + 16 * (t & 3);
-  const uint8_t* wp = W + (size_t)(t / 4) * xrow + 16 * (t & 3);
-  const int xlast = a.n_rows - 1 - row0 - t / 4;  // chunks with 64 c > xlast read row n-1
-  // LDS offset of this thread's chunk 0 (row t/4; the other chunks are 64 c rows below,
-  // with the same swizzle)
-  const int so = (t / 4) * G::XS + 16 * ((t & 3) ^ (((t / 4) ^ (t / 8)) & 3));
+  const int rr = lane >> 2;
+  const int kc = (lane & 3) ^ ((rr ^ (rr >> 1)) & 3);
+  // X rows of this lane: 16 (wave + 4 m) + rr, m = 0..3; rows past the end read row n-1
+  const uint8_t* xsrc[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int r = min(row0 + 16 * (wave + 4 * m) + rr, a.n_rows - 1);
+    xsrc[m] = X + (size_t)r * xrow + 16 * kc;
+  }
+  const uint8_t* wsrc[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) wsrc[m] = W + (size_t)(16 * (wave + 4 * m) + rr) * xrow + 16 * kc;
   const int lsw = 16 * (lg ^ ((li ^ (li >> 1)) & 3));  // operand reads: rows 16 x + li
-  typedef unsigned int stage_v __attribute__((ext_vector_type(4)));
-  stage_v xr[G::XC], wr[G::WC];
+  typedef __attribute__((address_space(3))) uint8_t* lds_p;
+  const uint32_t smem_base = (uint32_t)(size_t)(lds_p)smem;
+  auto issue = [&](int ks, int buf) {
+    const uint32_t st = smem_base + buf * G::STAGE;
+    const size_t ko = (size_t)ks * G::BK * 2;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      lds_dma16(xsrc[m] + ko, __builtin_amdgcn_readfirstlane(st + 1024 * (wave + 4 * m)));
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+      lds_dma16(wsrc[m] + ko,
+                __builtin_amdgcn_readfirstlane(st + G::X_BYTES + 1024 * (wave + 4 * m)));
+  };
   f32x4_v acc[G::IT][G::JT];
 #pragma unroll
   for (int i = 0; i < G::IT; ++i)
@@ -279,33 +315,15 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
     for (int j = 0; j < G::JT; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
 
   const int nk = a.d / G::BK;
-  {
-#pragma unroll
-    for (int c = 0; c < G::XC; ++c)
-      xr[c] = *reinterpret_cast<const stage_v*>(
-          xp + (size_t)(row0 + t / 4 + min(64 * c, xlast)) * xrow + 0);
-#pragma unroll
-    for (int c = 0; c < G::WC; ++c)
-      wr[c] = *reinterpret_cast<const stage_v*>(wp + (size_t)(64 * c) * xrow + 0);
-#pragma unroll
-    for (int c = 0; c < G::XC; ++c)
-      *reinterpret_cast<stage_v*>(smem + so + 64 * c * G::XS) = xr[c];
-#pragma unroll
-    for (int c = 0; c < G::WC; ++c)
-      *reinterpret_cast<stage_v*>(smem + G::X_BYTES + so + 64 * c * G::XS) = wr[c];
-  }
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  if (nk > 1) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  int buf = 0;
   for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nk) {
-#pragma unroll
-      for (int c = 0; c < G::XC; ++c)
-        xr[c] = *reinterpret_cast<const stage_v*>(
-            xp + (size_t)(row0 + t / 4 + min(64 * c, xlast)) * xrow + (size_t)((ks + 1) * G::BK) * 2);
-#pragma unroll
-      for (int c = 0; c < G::WC; ++c)
-        wr[c] = *reinterpret_cast<const stage_v*>(wp + (size_t)(64 * c) * xrow + (size_t)((ks + 1) * G::BK) * 2);
-    }
+    const int nb = buf == 0 ? 2 : buf - 1;  // (ks + 2) % 3
+    if (ks + 2 < nk) issue(ks + 2, nb);
     const uint8_t* st = smem + buf * G::STAGE;
     bf16x8_v bv[G::JT];
 #pragma unroll
@@ -320,16 +338,10 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
       for (int j = 0; j < G::JT; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[j], acc[i][j], 0, 0, 0);
     }
-    if (ks + 1 < nk) {
-#pragma unroll
-      for (int c = 0; c < G::XC; ++c)
-        *reinterpret_cast<stage_v*>(smem + (buf ^ 1) * G::STAGE + so + 64 * c * G::XS) = xr[c];
-#pragma unroll
-      for (int c = 0; c < G::WC; ++c)
-        *reinterpret_cast<stage_v*>(smem + (buf ^ 1) * G::STAGE + G::X_BYTES + so + 64 * c * G::XS) =
-            wr[c];
-    }
+    if (ks + 2 < nk) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    buf = buf == 2 ? 0 : buf + 1;
   }
 
   // result tile -> bf16 [row][column] in LDS (D[i][j] at lane 16*(i/4) + j, element i%4)
