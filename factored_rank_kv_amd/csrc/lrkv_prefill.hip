@@ -66,9 +66,13 @@ __device__ __forceinline__ void split4(const f32x4_p& x, short4_p& hi, short4_p&
   lo = pack4(l[0], l[1], l[2], l[3]);
 }
 
+// max over the four 16-lane rows that hold one query row's tokens: v_permlane16_swap
+// pairs rows 0-1 and 2-3, v_permlane32_swap the two halves (VALU, no LDS round trip)
 __device__ __forceinline__ float xor_max(float x) {
-  x = __builtin_fmaxf(x, __shfl_xor(x, 16));
-  return __builtin_fmaxf(x, __shfl_xor(x, 32));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __builtin_fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float xor_sum(float x) {
   x += __shfl_xor(x, 16);
@@ -250,11 +254,14 @@ prefill_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < C::RB; ++i) orr[w][i] = f32x4_p{0.f, 0.f, 0.f, 0.f};
   }
-  // m_run: running max of the row; l_part: this lane's 4-token share of its exp-sum
+  // m_run: running max of the row (scaled, base-2 units); l_part: this lane's 4-token share
+  // of its exp-sum.  The max starts at a finite floor far below any score, so exp2 of a
+  // masked score (-inf) minus it is exactly 0 with no select, and the first visible score
+  // always moves it.
   float m_run[RW], l_part[RW];
 #pragma unroll
   for (int w = 0; w < RW; ++w) {
-    m_run[w] = -INFINITY;
+    m_run[w] = -1e30f;
     l_part[w] = 0.f;
   }
 
@@ -355,22 +362,24 @@ prefill_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int w = 0; w < RW; ++w) {
       float mt = -INFINITY;
+      // token 16 tb + e of this lane's group is visible iff 16 tb + e <= lim (j < T follows
+      // from pos < T)
+      const int lim = row_ok[w] ? pos[w] - kt * C::BT - 4 * lg : -1;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int j = kt * C::BT + 16 * tb + 4 * lg + e;
-          const bool ok = row_ok[w] && j <= pos[w];  // j < T follows from pos < T
-          const float s = ok ? sc[w][tb][e] * a.score_scale : -INFINITY;
+          const bool ok = 16 * tb + e <= lim;
+          const float s = ok ? sc[w][tb][e] : -INFINITY;  // unscaled
           sc[w][tb][e] = s;
           mt = __builtin_fmaxf(mt, s);
         }
-      mt = xor_max(mt);
+      mt = xor_max(mt) * a.score_scale;
       const bool bump = mt > m_run[w] + 8.0f;
       if (__builtin_expect(__any(bump), 0)) {
         asm volatile("" ::: "memory");
         const float m_new = bump ? mt : m_run[w];
-        const float alpha = m_run[w] == m_new ? 1.f : exp2_fast(m_run[w] - m_new);
+        const float alpha = exp2_fast(m_run[w] - m_new);  // 1 if not bumped, 0 on the first
         l_part[w] *= alpha;
 #pragma unroll
         for (int i = 0; i < C::FB; ++i) os[w][i] *= alpha;
@@ -384,7 +393,7 @@ prefill_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float s = sc[w][2 * tp + e / 4][e % 4];
-          p[e] = s == -INFINITY ? 0.f : exp2_fast(s - m_run[w]);
+          p[e] = exp2_fast(fmaf(s, a.score_scale, -m_run[w]));  // 0 for a masked score
           l_part[w] += p[e];
         }
         pp[w][tp] = __builtin_bit_cast(
