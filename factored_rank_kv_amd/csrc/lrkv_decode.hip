@@ -421,9 +421,12 @@ struct SplitState {
   f32x4 accT[SplitCfg<S>::HT];                // bf16 cache: MFMA tiles of acc_S (see above)
 };
 
-// the partner lane of a (head, token) pair holds the other half of the features
+// the partner lane of a (head, token) pair (lane ^ 16) holds the other half of the
+// features; v_permlane16_swap hands each lane of the pair both values (VALU, no LDS round
+// trip), and both lanes form the same sum
 __device__ __forceinline__ float add_partner(float x) {
-  return x + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
 template <class S>
@@ -867,8 +870,11 @@ merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
     return;
   }
   auto block_max = [&](float m) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o));
+    m = r16_max(m);  // DPP inside each 16-lane row, then the rows by permlane swaps
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = __builtin_fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = __builtin_fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
     if ((t & 63) == 0) red[t >> 6] = m;
     __syncthreads();
     return __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
