@@ -67,6 +67,8 @@ def _load():
     lib.lrkv_decode_workspace_bytes.restype = SZ
     lib.lrkv_decode.argtypes = [LP, P, I32, I32, P, P, P, P, I32, P, I32, I32, P, P, SZ, P]
     lib.lrkv_decode.restype = ctypes.c_int
+    lib.lrkv_check_indices.argtypes = [LP, P, I32, I32, P, I32, P, P, I32, I64, P, P]
+    lib.lrkv_check_indices.restype = ctypes.c_int
     lib.lrkv_status_string.argtypes = [ctypes.c_int]
     lib.lrkv_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -74,7 +76,7 @@ def _load():
 
 
 EXPORTS = ("lrkv_page_bytes", "lrkv_append", "lrkv_decode_workspace_bytes", "lrkv_decode",
-           "lrkv_status_string")
+           "lrkv_check_indices", "lrkv_status_string")
 
 
 def library():
@@ -139,4 +141,15 @@ def lrkv_decode(layout, q, batch, q_len, B_K, B_V, pool, page_table, max_pages_p
                              workspace_bytes, _stream(stream))
     if check and st != LRKV_OK:
         raise LRKVError(st, "lrkv_decode")
+    return st
+
+
+def lrkv_check_indices(layout, page_table, batch, max_pages_per_req, seq_lens, max_seq_len,
+                       row_req, row_pos, n_rows, num_pages, errors, stream=None,
+                       check=True) -> int:
+    st = _load().lrkv_check_indices(_layout(layout), _ptr(page_table), batch, max_pages_per_req,
+                                    _ptr(seq_lens), max_seq_len, _ptr(row_req), _ptr(row_pos),
+                                    n_rows, num_pages, _ptr(errors), _stream(stream))
+    if check and st != LRKV_OK:
+        raise LRKVError(st, "lrkv_check_indices")
     return st

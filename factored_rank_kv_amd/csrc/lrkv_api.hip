@@ -238,4 +238,35 @@ int lrkv_append(const lrkv_layout* L, const void* X, int32_t n_rows, int32_t d,
   }
 }
 
+int lrkv_check_indices(const lrkv_layout* L, const int32_t* page_table, int32_t batch,
+                       int32_t max_pages_per_req, const int32_t* seq_lens, int32_t max_seq_len,
+                       const int32_t* row_req, const int32_t* row_pos, int32_t n_rows,
+                       int64_t num_pages, int32_t* errors, void* stream) {
+  if (!layout_valid(L)) return LRKV_ERR_INVALID_ARG;
+  if (batch <= 0 || max_pages_per_req <= 0 || max_seq_len < 0 || n_rows < 0 || num_pages <= 0)
+    return LRKV_ERR_INVALID_ARG;
+  if ((long long)max_seq_len > (long long)max_pages_per_req * L->page_size)
+    return LRKV_ERR_INVALID_ARG;
+  if ((long long)max_pages_per_req * L->page_size > 0x7fffffffLL) return LRKV_ERR_INVALID_ARG;
+  if (!page_table || !errors || (!row_req) != (!row_pos)) return LRKV_ERR_INVALID_ARG;
+  auto aligned4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+  if (!aligned4(page_table) || !aligned4(errors) || (seq_lens && !aligned4(seq_lens)) ||
+      (row_req && (!aligned4(row_req) || !aligned4(row_pos))))
+    return LRKV_ERR_INVALID_ARG;
+  CheckArgs a{};
+  a.page_table = page_table;
+  a.batch = batch;
+  a.max_pages = max_pages_per_req;
+  a.seq_lens = seq_lens;
+  a.max_seq_len = max_seq_len;
+  a.row_req = row_req;
+  a.row_pos = row_pos;
+  a.n_rows = row_req ? n_rows : 0;
+  a.num_pages = num_pages;
+  a.page_size = L->page_size;
+  a.errors = errors;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(launch_check(a));
+}
+
 }  // extern "C"

@@ -65,4 +65,22 @@ constexpr int kPrefillMinRows = 64;
 template <class S>
 hipError_t launch_prefill(const DecodeArgs& a);
 
+struct CheckArgs {
+  const int32_t* page_table;
+  int batch;
+  int max_pages;
+  const int32_t* seq_lens;  // may be null: lengths and their pages not checked
+  int max_seq_len;
+  const int32_t* row_req;   // may be null (then row_pos too): rows not checked
+  const int32_t* row_pos;
+  int n_rows;
+  long long num_pages;
+  int page_size;
+  int32_t* errors;
+  hipStream_t stream;
+};
+
+// Zeroes *errors, then adds the number of index values that break the layout's rules.
+hipError_t launch_check(const CheckArgs& a);
+
 }  // namespace lrkv

@@ -45,8 +45,9 @@
  *    asynchronous; the library never synchronizes.  Calls that share a workspace or write
  *    the same pool rows must be ordered by the caller (one stream does that).
  *  - Every argument check runs on the host before any launch.  Values that live in device
- *    memory (page ids, lengths, row positions) are not checked: out-of-range values are
- *    undefined behaviour.
+ *    memory (page ids, lengths, row positions) are not checked by lrkv_append and
+ *    lrkv_decode: out-of-range values are undefined behaviour.  lrkv_check_indices counts
+ *    them on the device for a caller who wants to validate first.
  *  - Return value: LRKV_OK, or a negative status (lrkv_status_string gives its text).
  *
  * Shapes with a kernel variant in this build, (H, d_h, r, dtype):
@@ -156,6 +157,34 @@ int lrkv_decode(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_le
                 int32_t max_pages_per_req, const int32_t* seq_lens, int32_t max_seq_len,
                 int32_t chunk_tokens, void* out, void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/* Counts the device-side index values that lrkv_append and lrkv_decode trust without
+ * checking them (they read them on the device; a check there would need a
+ * synchronization).  For callers who want to validate their tables first, for example in
+ * a debug run: enqueue this on the same stream before the calls it guards.  The rules
+ * are those of the page layout above (LRKV notes §3, one page table for shared and
+ * private rows):
+ *   lengths  (if seq_lens != NULL)  0 <= seq_lens[b] <= max_seq_len, for b < batch
+ *   pages    (if seq_lens != NULL)  for each b with a valid length and each page index
+ *            p < ceil(seq_lens[b] / P): 0 <= page_table[b * max_pages_per_req + p] < num_pages
+ *   rows     (if row_req != NULL)   0 <= row_req[n] < batch, 0 <= row_pos[n] <
+ *            max_pages_per_req * P, and the page holding (row_req[n], row_pos[n]) is in
+ *            [0, num_pages), for n < n_rows
+ * Distinctness of the appended (request, position) pairs is not checked.
+ *   page_table device, [batch][max_pages_per_req] int32
+ *   seq_lens   device, [batch] int32, or NULL
+ *   row_req, row_pos  device, [n_rows] int32 each, or both NULL
+ *   errors     device, one int32, written asynchronously on `stream`: the number of
+ *              violations found (0: every checked value is valid).  Device pointers need
+ *              4-byte alignment here.
+ * Returns LRKV_OK once the check is enqueued (two small kernels; nothing allocated), or
+ * LRKV_ERR_INVALID_ARG for host-side argument errors (batch, max_pages_per_req or
+ * num_pages <= 0, max_seq_len outside [0, max_pages_per_req * P], a NULL page_table or
+ * errors, one of row_req / row_pos NULL without the other). */
+int lrkv_check_indices(const lrkv_layout* L, const int32_t* page_table, int32_t batch,
+                       int32_t max_pages_per_req, const int32_t* seq_lens, int32_t max_seq_len,
+                       const int32_t* row_req, const int32_t* row_pos, int32_t n_rows,
+                       int64_t num_pages, int32_t* errors, void* stream);
 
 /* Text of a status code (static storage). */
 const char* lrkv_status_string(int status);

@@ -140,6 +140,28 @@ def test_append_rejects_bad_arguments_before_launch():
     assert append_status(n_rows=0) == F.LRKV_OK  # nothing to do, nothing launched
 
 
+def check_status(lay=C1, **over):
+    args = dict(page_table=FAKE, batch=2, max_pages_per_req=4, seq_lens=FAKE, max_seq_len=64,
+                row_req=FAKE, row_pos=FAKE, n_rows=3, num_pages=8, errors=FAKE)
+    args.update(over)
+    return F.lrkv_check_indices(lay, check=False, stream=0, **args)
+
+
+def test_check_indices_rejects_bad_arguments_before_launch():
+    bad = F.LRKV_ERR_INVALID_ARG
+    assert check_status(page_table=None) == bad
+    assert check_status(errors=None) == bad
+    assert check_status(row_pos=None) == bad  # one of the row arrays without the other
+    assert check_status(errors=FAKE + 2) == bad  # misaligned int32
+    assert check_status(batch=0) == bad
+    assert check_status(max_pages_per_req=0) == bad
+    assert check_status(num_pages=0) == bad
+    assert check_status(n_rows=-1) == bad
+    assert check_status(max_seq_len=65) == bad  # more than max_pages * P
+    assert check_status(max_seq_len=-1) == bad
+    assert check_status(F.lrkv_layout(16, 128, 56, 12, F.LRKV_BF16)) == bad
+
+
 def test_status_strings():
     for st in (F.LRKV_OK, F.LRKV_ERR_INVALID_ARG, F.LRKV_ERR_UNSUPPORTED, F.LRKV_ERR_HIP):
         assert F.lrkv_status_string(st).startswith("LRKV")
