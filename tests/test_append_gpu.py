@@ -90,11 +90,13 @@ def test_exact_inputs_small_widths(n_rows, d):
 
 
 @pytest.mark.parametrize("shape", [(16, 128, 56), (32, 128, 32)])
-@pytest.mark.parametrize("n_rows,d", [(64, 256), (300, 256), (300, 264), (470, 256)])
+@pytest.mark.parametrize("n_rows,d", [(64, 256), (300, 256), (300, 264), (470, 256), (96, 32),
+                                      (200, 64), (257, 96)])
 def test_exact_inputs_bit_exact_many_rows(shape, n_rows, d):
     """Prefill-sized appends (the MFMA product; d = 264 is not a multiple of its 32-wide K
-    step and takes the row kernel): exact arithmetic, bit-exact pool with sentinels, a
-    ragged last block of rows, permuted pages and scattered positions."""
+    step and takes the row kernel; d = 32, 64, 96 give one, two and three K steps, shorter
+    than the product's three-stage ring): exact arithmetic, bit-exact pool with sentinels,
+    a ragged last block of rows, permuted pages and scattered positions."""
     H, dh, r = shape
     L = O.Layout(H, dh, r, 16, O.BF16)
     g = np.random.default_rng(250 + n_rows + d)
