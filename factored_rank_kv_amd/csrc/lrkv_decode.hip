@@ -7,7 +7,7 @@
 //                            p = q B_K[h] of every head are formed while they travel (eq 6).
 //                            Loop: shared S_K/S_V tiles staged once in LDS for every head,
 //                            private R_K/R_V rows streamed per head straight into registers
-//                            (pages k+1..k+3 in flight while page k is used), one online
+//                            (page k+1 in flight while page k is used), one online
 //                            softmax with a shared and a private value accumulator (fused
 //                            blockwise paragraph after Algorithm 2).
 //                            Writes the chunk's (max, exp-sum, acc_S, acc_R) tuple per head.
@@ -61,8 +61,9 @@ __device__ __forceinline__ float r16_sum(float x) {
 // scores); for a float32 cache the wavefront switches to lanes over feature pairs
 // (2*lane, 2*lane+1) of its HPW heads, with the weights broadcast by readlane.
 //
-// Pipeline: four register buffers; pages pg+1..pg+3 are in flight while page pg is
-// consumed; the S tiles go through a double-buffered LDS stage.  Page bytes are read with
+// Pipeline: two register buffers; page pg+1 is in flight while page pg is consumed, and
+// the query row and private query of the lane stay in registers; the S tiles go through a
+// double-buffered LDS stage.  Page bytes are read with
 // non-temporal loads: the stream is used once and should not evict the small operands that
 // every workgroup re-reads (B_K, queries, page tables).
 //
@@ -159,6 +160,7 @@ struct SplitCfg {
   // room for SPLIT*RC_L chunks: the slots past RC hold zeros, so a lane whose half runs
   // past the last private chunk adds nothing for it
   static constexpr int P_STRIDE = (SPLIT * RC_L * P_PER_CHUNK) | 1;
+  static constexpr int PREG_N = RC_L * P_PER_CHUNK;  // uint4 of a lane's private query share
   // private queries: one job per (head, 16-byte chunk of p), d_h split over PQ_GROUPS
   static constexpr int PQ_JOBS = S::H * S::RC;
   static constexpr int PQ_GROUPS = NT / PQ_JOBS > 0 ? NT / PQ_JOBS : 1;
@@ -429,10 +431,11 @@ __device__ __forceinline__ float add_partner(float x) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-template <class S>
+template <class S, bool PREG>
 __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
                                              const uint4* __restrict__ sv,
-                                             const uint4* __restrict__ q_lds,
+                                             const uint4 (&qreg)[SplitCfg<S>::DHC_L],
+                                             const uint4 (&preg)[SplitCfg<S>::PREG_N],
                                              const uint4* __restrict__ p_lds,
                                              uint16_t* __restrict__ wl, float* __restrict__ al,
                                              const Lane<S>& L, int nvalid, float score_scale,
@@ -442,14 +445,13 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
   const bool valid = j < nvalid;
   // ---- score: q . S_K[j] + p . R_K[h, j]   (eq 6), this lane's half of the features
   float acc0 = 0.f, acc1 = 0.f;
-  const uint4* qh = q_lds + L.h * C::Q_STRIDE + L.half * C::DHC_L;
   const uint4* skh = sk + L.half * C::DHC_L * S::P;
 #pragma unroll
   for (int c = 0; c < C::DHC_L; ++c) {
     // at most four chunk pairs of LDS operands in registers at a time
     if (c % 4 == 0) __builtin_amdgcn_sched_barrier(0);
     const uint4 s4 = skh[c * S::P + j];
-    const uint4 q4 = qh[c];
+    const uint4 q4 = qreg[c];
     if constexpr (S::BF) {
       acc0 = dot2_bf16(q4.x, s4.x, acc0);
       acc1 = dot2_bf16(q4.y, s4.y, acc1);
@@ -468,7 +470,8 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
     const int cg = L.half * C::RC_L + c;  // slots past RC hold p = 0
     const uint4 k4 = r.rk[c];
     if constexpr (S::BF) {
-      const uint4 hi = ph[2 * cg], lo = ph[2 * cg + 1];
+      const uint4 hi = PREG ? preg[2 * c] : ph[2 * cg];
+      const uint4 lo = PREG ? preg[2 * c + 1] : ph[2 * cg + 1];
       acc0 = dot2_bf16(hi.x, k4.x, acc0);
       acc1 = dot2_bf16(hi.y, k4.y, acc1);
       acc0 = dot2_bf16(hi.z, k4.z, acc0);
@@ -478,7 +481,7 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
       acc0 = dot2_bf16(lo.z, k4.z, acc0);
       acc1 = dot2_bf16(lo.w, k4.w, acc1);
     } else {
-      const uint4 p4 = ph[cg];
+      const uint4 p4 = PREG ? preg[c] : ph[cg];
       acc0 = fmaf(__uint_as_float(p4.x), __uint_as_float(k4.x), acc0);
       acc1 = fmaf(__uint_as_float(p4.y), __uint_as_float(k4.y), acc1);
       acc0 = fmaf(__uint_as_float(p4.z), __uint_as_float(k4.z), acc0);
@@ -686,21 +689,29 @@ decode_split_kernel(const SplitArgs a) {
   auto page_ptr = [&](int pg) { return pool + (size_t)ids_lds[pg - pg0] * S::PAGE; };
   auto nvalid = [&](int pg) { return min(S::P, tok1 - pg * S::P); };
 
-  // register buffers of pages: four (pages k+1..k+3 in flight while k is consumed), or two
-  // in the balanced split, whose loop over segments leaves less room (page k+2 then goes in
-  // flight once page k is consumed)
-  constexpr int DEPTH = BAL ? 2 : 4;
-  PageRegs<S> r0, r1, r2, r3;
-  // pages pg0, pg0+1 go in flight while the private queries are formed (the B_K rows
-  // hold the registers of a further buffer until then); with four buffers page pg0+2
-  // follows right after, with three the first step issues it
+  // two register buffers of pages: page k+1 travels while page k is consumed, and page
+  // k+2 goes in flight into k's buffer once k is consumed (measured faster than three or
+  // four buffers: the registers hold the query row and the private query instead)
+  PageRegs<S> r0, r1;
+  // pages pg0, pg0+1 go in flight while the private queries are formed
   issue_page<S>(page_ptr(pg0), L, r0);
   if (pg0 + 1 < pg1) issue_page<S>(page_ptr(pg0 + 1), L, r1);
   form_private_queries<S>(bkr, q_lds, pacc, p_lds, tid);
-  if (DEPTH == 4 && pg0 + 2 < pg1) issue_page<S>(page_ptr(pg0 + 2), L, r2);
-  (void)r3;
   stage_shared<S>(sk_lds[0], sv_lds[0], svt_lds[0], tid, r0, nvalid(pg0));
   __syncthreads();
+
+  // this lane's half of its head's query row, and its share of the private query (hi and
+  // lo parts for bf16), in registers for the whole segment; the balanced split of the
+  // 32-head shape has no room for the private share, which stays in LDS there
+  constexpr bool PREG = !BAL || S::H <= 16;
+  uint4 qreg[C::DHC_L];
+#pragma unroll
+  for (int c = 0; c < C::DHC_L; ++c) qreg[c] = q_lds[L.h * C::Q_STRIDE + L.half * C::DHC_L + c];
+  uint4 preg[C::PREG_N];
+  if constexpr (PREG) {
+#pragma unroll
+    for (int c = 0; c < C::PREG_N; ++c) preg[c] = p_lds[L.h * C::P_STRIDE + L.half * C::PREG_N + c];
+  }
 
   SplitState<S> st;
   st.m_run = -INFINITY;
@@ -712,40 +723,30 @@ decode_split_kernel(const SplitArgs a) {
 #pragma unroll
   for (int x = 0; x < C::HT; ++x) st.accT[x] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // one pipeline step: page pg is in `cur` and LDS buffer `buf`, page pg+1 in `nxt`; with
-  // four buffers page pg+2 is in flight and page pg+3 goes in flight into `fre`, with three
-  // page pg+2 goes into `fre`.  bf16 cache: the shared value of page pg-1 (weights written
-  // last step) goes through MFMA first.  Returns false when pg was the last page.
-  auto step = [&](int pg, int buf, PageRegs<S>& cur, PageRegs<S>& nxt, PageRegs<S>& fre) {
-    if (DEPTH > 2 && pg + DEPTH - 1 < pg1) issue_page<S>(page_ptr(pg + DEPTH - 1), L, fre);
+  // one pipeline step: page pg is in `cur` and LDS buffer `buf`, page pg+1 in `nxt`; page
+  // pg+2 goes in flight into `cur` once pg is consumed.  bf16 cache: the shared value of
+  // page pg-1 (weights written last step) goes through MFMA first.  Returns false when pg
+  // was the last page.
+  auto step = [&](int pg, int buf, PageRegs<S>& cur, PageRegs<S>& nxt) {
     const int k = pg - pg0;
     if constexpr (C::MFMA_SV) {
       if (k > 0)
         shared_value_mfma<S>(st.accT, w_lds[buf ^ 1], al_lds[buf ^ 1], svt_lds[(k + 2) % 3],
                              L.wave, L.lane);
     }
-    consume_page<S>(sk_lds[buf], sv_lds[buf], q_lds, p_lds, w_lds[buf], al_lds[buf], L,
-                    nvalid(pg), a.score_scale, cur, st);
+    consume_page<S, PREG>(sk_lds[buf], sv_lds[buf], qreg, preg, p_lds, w_lds[buf], al_lds[buf],
+                          L, nvalid(pg), a.score_scale, cur, st);
     const bool more = pg + 1 < pg1;
     if (more)
       stage_shared<S>(sk_lds[buf ^ 1], sv_lds[buf ^ 1], svt_lds[C::MFMA_SV ? (k + 1) % 3 : 0],
                       tid, nxt, nvalid(pg + 1));
-    if (DEPTH == 2 && pg + 2 < pg1) issue_page<S>(page_ptr(pg + 2), L, fre);  // fre is cur
+    if (pg + 2 < pg1) issue_page<S>(page_ptr(pg + 2), L, cur);
     __syncthreads();
     return more;
   };
-  if constexpr (DEPTH == 4) {
-    for (int pg = pg0;; pg += 4) {
-      if (!step(pg, 0, r0, r1, r3)) break;
-      if (!step(pg + 1, 1, r1, r2, r0)) break;
-      if (!step(pg + 2, 0, r2, r3, r1)) break;
-      if (!step(pg + 3, 1, r3, r0, r2)) break;
-    }
-  } else {
-    for (int pg = pg0;; pg += 2) {
-      if (!step(pg, 0, r0, r1, r0)) break;
-      if (!step(pg + 1, 1, r1, r0, r1)) break;
-    }
+  for (int pg = pg0;; pg += 2) {
+    if (!step(pg, 0, r0, r1)) break;
+    if (!step(pg + 1, 1, r1, r0)) break;
   }
   if constexpr (C::MFMA_SV) {  // shared value of the last page
     const int kl = pg1 - 1 - pg0;
