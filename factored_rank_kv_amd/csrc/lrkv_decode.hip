@@ -2,7 +2,7 @@
 // factored paged cache, as two launches on the caller's stream:
 //   1. decode_split_kernel   one workgroup per (chunk of pages, query row, request) covering
 //                            all heads.  Prologue: the chunk's page ids, the request length
-//                            and the query row are fetched together with the B_K rows, the
+//                            and the query row are fetched first, then the B_K rows, the
 //                            first two pages are put in flight, and the private queries
 //                            p = q B_K[h] of every head are formed while they travel (eq 6).
 //                            Loop: shared S_K/S_V tiles staged once in LDS for every head,
@@ -662,11 +662,8 @@ decode_split_kernel(const SplitArgs a) {
     const int i = tid + k * C::NT;
     if (i < S::H * S::DHC) q_r[k] = qsrc[i];
   }
-  // the request length is read first (a scalar load); B_K rows, which depend on nothing,
-  // follow at once, ahead of every page load
+  // the request length is read first (a scalar load)
   const int len_b = a.seq_lens[b];
-  BKRows<S> bkr;
-  load_bk_rows<S>(a.BK, tid, bkr);
   const int vis = visible_tokens(len_b, a.q_len, qi);
   const int tok0 = pg0 * S::P;
   // pages past the table row are never read, whatever the lengths say
@@ -683,6 +680,11 @@ decode_split_kernel(const SplitArgs a) {
     if (i < S::H * S::DHC) q_lds[(i / S::DHC) * C::Q_STRIDE + i % S::DHC] = q_r[k];
   }
   __syncthreads();  // page ids and q in LDS
+  // B_K rows go out once the page ids are in (ahead of them they delay the ids: every
+  // workgroup reads all of B_K, 58 MB of L2 traffic at C1 sizes) and ahead of every page
+  // load, since loads return in issue order
+  BKRows<S> bkr;
+  load_bk_rows<S>(a.BK, tid, bkr);
 
   const int pg1 = (tok1 + S::P - 1) / S::P;
   const uint8_t* pool = a.pool;
