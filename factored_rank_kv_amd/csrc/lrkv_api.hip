@@ -173,6 +173,10 @@ int lrkv_decode(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_le
   const DecodeSizes z = decode_sizes(L, batch, q_len, max_seq_len, chunk_tokens);
   if (workspace_bytes < z.total) return LRKV_ERR_INVALID_ARG;
   if (z.n_split > 65535) return LRKV_ERR_INVALID_ARG;
+  // one-dimensional grids of the split and merge kernels (rounded up to 8 blocks)
+  if ((long long)batch * q_len * (z.n_split > L->num_heads ? z.n_split : L->num_heads) >
+      0x7fffffffLL - 8)
+    return LRKV_ERR_INVALID_ARG;
 
   DecodeArgs a{};
   a.q = q;

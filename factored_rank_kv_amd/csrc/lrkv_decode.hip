@@ -52,7 +52,10 @@ __device__ __forceinline__ float r16_sum(float x) {
 // ---------------------------------------------------------------------------------------
 // 1. split kernel
 //
-// Workgroup = (chunk, query row qi, request b); NW = H / HPW wavefronts, HPW heads each.
+// Workgroup = (chunk, query row qi, request b), numbered so that each XCD takes a
+// contiguous range of (request, row, chunk) (xcd_range_index): a request's records are
+// written by one XCD (or a few), and the merge workgroups of that request run there and
+// find them in its L2.  NW = H / HPW wavefronts, HPW heads each.
 // For the score, the softmax and the private value, lane = hl*(16*SPLIT) + half*16 + j
 // covers head h = HPW*wave + hl and token slot j of the page; with SPLIT = 2 the two
 // lanes (half = 0, 1) of a (head, token) pair each take half of the features of the dot
@@ -100,6 +103,15 @@ struct SplitArgs {
 // are ordered, so w' > w implies b' >= b) and a request's slots are consecutive, in page
 // order.  Both kernels derive the ranges from the lengths on the device (at most
 // kBalancedMaxBatch requests).
+
+// Blocks of a 1-D grid go to the 8 XCDs round robin (block L to XCD L % 8).  This maps
+// block L to index x * ceil(total / 8) + L / 8 (x = L % 8), so each XCD takes one
+// contiguous range of [0, total); the grid has 8 * ceil(total / 8) blocks, indices past
+// total are left idle.
+__device__ __forceinline__ int xcd_range_index(int total) {
+  const int per_xcd = (total + 7) / 8;
+  return (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+}
 
 // pref[b] = pages of requests 0..b-1 (pref[B] = all pages), one page per P tokens started,
 // at most max_pages per request; every thread of the block takes part, the result is in
@@ -628,11 +640,18 @@ decode_split_kernel(const SplitArgs a) {
     pg_end = min(g_hi, pref_lds[b + 1]) - pref_lds[b];
     slot = (size_t)blockIdx.x + b;
   } else {
-    qi = blockIdx.y;
-    b = blockIdx.z;
-    pg0 = blockIdx.x * (a.chunk / S::P);
+    // (request, row, chunk) index g in order; XCD x (blocks go to the 8 XCDs round robin)
+    // takes the contiguous range of g starting at x * per_xcd, so a request's records are
+    // written by as few XCDs as possible and the merge reads them there
+    const int total = a.batch * a.q_len * a.n_split;
+    const int g = xcd_range_index(total);
+    if (g >= total) return;  // uniform
+    const int split = g % a.n_split;
+    qi = (g / a.n_split) % a.q_len;
+    b = g / (a.n_split * a.q_len);
+    pg0 = split * (a.chunk / S::P);
     pg_end = pg0 + a.chunk / S::P;
-    slot = ((size_t)b * a.q_len + qi) * a.n_split + blockIdx.x;
+    slot = (size_t)g;
   }
   for (;;) {
   // the lane's geometry is derived anew for each segment: values computed from it are then
@@ -800,7 +819,8 @@ decode_split_kernel(const SplitArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// 2. merge + expand.  Workgroup = (head, query row, request), 256 threads.  Thread t owns
+// 2. merge + expand.  Workgroup = (head, query row, request), 256 threads, on the XCD that
+// wrote the request's records (chunked split; see xcd_range_index).  Thread t owns
 // one column of the partial record: t < DH -> acc_S[t], t < DH + R -> acc_R[t - DH],
 // t == DH + R -> l.  When every chunk fits in LDS (the usual case) one memory round trip
 // does: the records of all n_split chunks (16-byte loads issued together, before the request
@@ -824,9 +844,19 @@ merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
   __shared__ float red[4];
   __shared__ float accR_s[S::R];
   __shared__ float l_s;
-  const int h = blockIdx.x;
-  const int qi = blockIdx.y;
-  const int b = blockIdx.z;
+  int h, qi, b;
+  if constexpr (BAL) {
+    h = blockIdx.x;
+    qi = blockIdx.y;
+    b = blockIdx.z;
+  } else {  // (request, row, head) ranges per XCD, as the split kernel's chunks
+    const int total = batch * q_len * S::H;
+    const int g = xcd_range_index(total);
+    if (g >= total) return;
+    h = g % S::H;
+    qi = (g / S::H) % q_len;
+    b = g / (S::H * q_len);
+  }
   const int t = threadIdx.x;
   const size_t row = (size_t)b * q_len + qi;
   const size_t out_off = (row * S::H + h) * S::DH;
@@ -976,9 +1006,10 @@ hipError_t launch_decode(const DecodeArgs& a) {
                        a.stream, a.part_ws, a.B_V, a.seq_lens, 1, 0, 0, a.batch, a.groups,
                        a.max_pages, a.out);
   } else {
-    hipLaunchKernelGGL((decode_split_kernel<S, false>), dim3(a.n_split, a.q_len, a.batch),
+    const int split_blocks = (a.batch * a.q_len * a.n_split + 7) / 8 * 8;
+    hipLaunchKernelGGL((decode_split_kernel<S, false>), dim3(split_blocks),
                        dim3(SplitCfg<S>::NT), 0, a.stream, s);
-    hipLaunchKernelGGL((merge_expand_kernel<S, false>), dim3(S::H, a.q_len, a.batch), dim3(256), 0,
+    hipLaunchKernelGGL((merge_expand_kernel<S, false>), dim3((a.batch * a.q_len * S::H + 7) / 8 * 8), dim3(256), 0,
                        a.stream, a.part_ws, a.B_V, a.seq_lens, a.q_len, a.n_split, a.chunk,
                        a.batch, 0, a.max_pages, a.out);
   }
