@@ -460,8 +460,6 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
   const uint4* skh = sk + L.half * C::DHC_L * S::P;
 #pragma unroll
   for (int c = 0; c < C::DHC_L; ++c) {
-    // at most four chunk pairs of LDS operands in registers at a time
-    if (c % 4 == 0) __builtin_amdgcn_sched_barrier(0);
     const uint4 s4 = skh[c * S::P + j];
     const uint4 q4 = qreg[c];
     if constexpr (S::BF) {
