@@ -41,12 +41,40 @@ __device__ __forceinline__ float r16_max(float x) {
   x = __builtin_fmaxf(x, dpp_f<kMirror>(x));
   return x;
 }
+// One stage of a reduce-scatter inside a 16-lane row: v[0..2n) -> v[0..n).  The DPP
+// pattern pairs each lane with a partner; the lane keeps the lower or upper half (`upper`,
+// its partner the other), sends the other half and adds the partner's copy of its own.
+template <int CTRL, int N>
+__device__ __forceinline__ void rs_stage(float* v, bool upper) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float send = upper ? v[i] : v[i + N];
+    const float keep = upper ? v[i + N] : v[i];
+    v[i] = keep + dpp_f<CTRL>(send);
+  }
+}
+
+// Sums each of 32 values over the 16 lanes of a row; lane j ends with the sums of values
+// 2j (in v[0]) and 2j + 1 (in v[1]).  The four stages pair lane j with 15 - j, with
+// 7 - j inside its half, with j ^ 2 and with j ^ 1; lane j keeps the upper half at the
+// stages where bit 3, 2, 1, 0 of j is set, so the values left are 16 b3 + 8 b2 + 4 b1 +
+// 2 b0 = 2j and the next; each pairing joins two disjoint lane sets, so the sums cover
+// all 16 lanes.
+__device__ __forceinline__ void reduce_scatter_32(float* v, int j);
+
 __device__ __forceinline__ float r16_sum(float x) {
   x += dpp_f<kQuadSwap1>(x);
   x += dpp_f<kQuadSwap2>(x);
   x += dpp_f<kHalfMirror>(x);
   x += dpp_f<kMirror>(x);
   return x;
+}
+
+__device__ __forceinline__ void reduce_scatter_32(float* v, int j) {
+  rs_stage<kMirror, 16>(v, j >= 8);
+  rs_stage<kHalfMirror, 8>(v, (j & 7) >= 4);
+  rs_stage<kQuadSwap2, 4>(v, (j & 2) != 0);
+  rs_stage<kQuadSwap1, 2>(v, (j & 1) != 0);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -774,17 +802,27 @@ decode_split_kernel(const SplitArgs a) {
 
   // ---- partial tuple of this chunk: m, l, acc_S[DH], acc_R[R] per head
   const float l_tot = r16_sum(st.l_run);
-#pragma unroll
-  for (int k = 0; k < C::RC_L * S::CE; ++k) st.accR[k] = r16_sum(st.accR[k]);
   float* dst = a.part + (slot * S::H + L.h) * S::PART_PAD;
   if (L.j == 0 && L.half == 0) {
     dst[0] = st.m_run;
     dst[1] = l_tot;
   }
+  constexpr int NR = C::RC_L * S::CE;  // acc_R values per lane (its half of the features)
+  if constexpr (NR == 32) {
+    // reduce-scatter over the 16 token lanes of the row: lane j ends with the sums of
+    // values 2j and 2j + 1, stored as one float2
+    reduce_scatter_32(st.accR, L.j);
+    const int kg = L.half * NR + 2 * L.j;  // feature of R_V
+    if (kg < S::R)
+      *reinterpret_cast<float2*>(dst + 2 + S::DH + kg) = make_float2(st.accR[0], st.accR[1]);
+  } else {
 #pragma unroll
-  for (int k = 0; k < C::RC_L * S::CE; ++k) {
-    const int kg = L.half * C::RC_L * S::CE + k;  // feature of R_V
-    if ((k & 15) == L.j && kg < S::R) dst[2 + S::DH + kg] = st.accR[k];
+    for (int k = 0; k < NR; ++k) st.accR[k] = r16_sum(st.accR[k]);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      const int kg = L.half * NR + k;  // feature of R_V
+      if ((k & 15) == L.j && kg < S::R) dst[2 + S::DH + kg] = st.accR[k];
+    }
   }
   if constexpr (C::MFMA_SV) {
     // MFMA tile: lane holds heads 16*ht + 4*(lane/16) + e, feature 16*wave + lane%16
