@@ -361,17 +361,19 @@ struct BKRows {
 template <class S>
 __device__ __forceinline__ void load_bk_rows(const void* __restrict__ BK, int tid, BKRows<S>& r) {
   using C = SplitCfg<S>;
-  // threads past the last group load a valid row they never use: no branch, so the loads
-  // stay where they are written
+  // wavefronts wholly past the last group load nothing; a thread past it in a wavefront
+  // that does loads a valid row it never uses
   const int job = tid % C::PQ_JOBS;
   const int g = min(tid / C::PQ_JOBS, C::PQ_GROUPS - 1);
   const int h = job / S::RC;
   const int c = job - h * S::RC;
   const uint8_t* bk = static_cast<const uint8_t*>(BK) +
                       ((size_t)h * S::DH * S::R + (size_t)c * S::CE) * S::EB;
+  if (__builtin_amdgcn_readfirstlane(tid) < C::PQ_GROUPS * C::PQ_JOBS) {
 #pragma unroll
-  for (int dd = 0; dd < C::PQ_DSPAN; ++dd)
-    r.v[dd] = *reinterpret_cast<const uint4*>(bk + (size_t)(g * C::PQ_DSPAN + dd) * S::R * S::EB);
+    for (int dd = 0; dd < C::PQ_DSPAN; ++dd)
+      r.v[dd] = *reinterpret_cast<const uint4*>(bk + (size_t)(g * C::PQ_DSPAN + dd) * S::R * S::EB);
+  }
   asm volatile("" ::: "memory");  // keep them ahead of the page loads that follow
 }
 
