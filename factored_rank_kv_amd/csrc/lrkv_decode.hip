@@ -358,18 +358,20 @@ struct BKRows {
   uint4 v[SplitCfg<S>::PQ_DSPAN];
 };
 
-template <class S>
+// SKIP_IDLE: wavefronts wholly past the last group load nothing (the balanced split, whose
+// loop over segments leaves no registers to spare, keeps the loads unconditional: the
+// branch made it spill).  A thread past the last group in a wavefront that loads reads a
+// valid row it never uses.
+template <class S, bool SKIP_IDLE>
 __device__ __forceinline__ void load_bk_rows(const void* __restrict__ BK, int tid, BKRows<S>& r) {
   using C = SplitCfg<S>;
-  // wavefronts wholly past the last group load nothing; a thread past it in a wavefront
-  // that does loads a valid row it never uses
   const int job = tid % C::PQ_JOBS;
   const int g = min(tid / C::PQ_JOBS, C::PQ_GROUPS - 1);
   const int h = job / S::RC;
   const int c = job - h * S::RC;
   const uint8_t* bk = static_cast<const uint8_t*>(BK) +
                       ((size_t)h * S::DH * S::R + (size_t)c * S::CE) * S::EB;
-  if (__builtin_amdgcn_readfirstlane(tid) < C::PQ_GROUPS * C::PQ_JOBS) {
+  if (!SKIP_IDLE || __builtin_amdgcn_readfirstlane(tid) < C::PQ_GROUPS * C::PQ_JOBS) {
 #pragma unroll
     for (int dd = 0; dd < C::PQ_DSPAN; ++dd)
       r.v[dd] = *reinterpret_cast<const uint4*>(bk + (size_t)(g * C::PQ_DSPAN + dd) * S::R * S::EB);
@@ -731,7 +733,7 @@ decode_split_kernel(const SplitArgs a) {
   // workgroup reads all of B_K, 58 MB of L2 traffic at C1 sizes) and ahead of every page
   // load, since loads return in issue order
   BKRows<S> bkr;
-  load_bk_rows<S>(a.BK, tid, bkr);
+  load_bk_rows<S, !BAL>(a.BK, tid, bkr);
 
   const int pg1 = (tok1 + S::P - 1) / S::P;
   const uint8_t* pool = a.pool;
