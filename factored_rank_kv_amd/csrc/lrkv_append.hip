@@ -221,21 +221,37 @@ struct GemmCfg {
   static constexpr int SMEM = NSTAGE * STAGE > BM * OS ? NSTAGE * STAGE : BM * OS;
 };
 
-// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): lane i
-// of the wavefront writes LDS bytes [lds + 16 i, lds + 16 i + 16); lds is wave-uniform.
-// Written as inline assembly, so the compiler's wait counters do not see these loads; the
-// caller waits for them with s_waitcnt vmcnt and a barrier before reading the bytes.
-// M0 (which holds the LDS address) is saved and restored around the load.
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
+// One GEMM stage of direct global->LDS loads (global_load_lds_dwordx4, 16 bytes per lane:
+// lane i of the wavefront writes LDS bytes [m0 + 16 i, m0 + 16 i + 16), M0 wave-uniform):
+// four 1 KiB loads of X rows (global xb + xoff[m]) to x_lds + 4096 m, then two of weight
+// rows (wb + woff[m]) to w_lds + 4096 m.  The global bases are wave-uniform (scalar
+// registers), the per-lane parts 32-bit offsets; M0 is set once, stepped by 4 KiB, and
+// restored at the end.  Written as inline assembly, so the compiler's wait counters do
+// not see these loads (it would otherwise wait for all of them before any LDS read); the
+// caller waits with s_waitcnt vmcnt and a barrier before reading the bytes.
+__device__ __forceinline__ void lds_dma_stage(const void* xb, const void* wb,
+                                              const uint32_t (&xoff)[4], const uint32_t (&woff)[2],
+                                              uint32_t x_lds, uint32_t w_lds) {
   uint32_t keep;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %7\n\t"
+      "global_load_lds_dwordx4 %1, %9\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\t"
+      "global_load_lds_dwordx4 %2, %9\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\t"
+      "global_load_lds_dwordx4 %3, %9\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\t"
+      "global_load_lds_dwordx4 %4, %9\n\t"
+      "s_mov_b32 m0, %8\n\t"
+      "global_load_lds_dwordx4 %5, %10\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\t"
+      "global_load_lds_dwordx4 %6, %10\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(keep)
-      : "v"(g), "s"(lds)
-      : "memory");
+      : "v"(xoff[0]), "v"(xoff[1]), "v"(xoff[2]), "v"(xoff[3]), "v"(woff[0]), "v"(woff[1]),
+        "s"(x_lds), "s"(w_lds), "s"(xb), "s"(wb)
+      : "memory", "scc");
 }
 
 template <class S>
@@ -285,28 +301,24 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
   const int rr = lane >> 2;
   const int kc = (lane & 3) ^ ((rr ^ (rr >> 1)) & 3);
   // X rows of this lane: 16 (wave + 4 m) + rr, m = 0..3; rows past the end read row n-1
-  const uint8_t* xsrc[4];
+  // per-lane 32-bit offsets from the X and weight bases (loop invariant); rows past the
+  // end read row n-1
+  uint32_t xoff[4], woff[2];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int r = min(row0 + 16 * (wave + 4 * m) + rr, a.n_rows - 1);
-    xsrc[m] = X + (size_t)r * xrow + 16 * kc;
+    xoff[m] = (uint32_t)((size_t)r * xrow + 16 * kc);
   }
-  const uint8_t* wsrc[2];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) wsrc[m] = W + (size_t)(16 * (wave + 4 * m) + rr) * xrow + 16 * kc;
+  for (int m = 0; m < 2; ++m) woff[m] = (uint32_t)((size_t)(16 * (wave + 4 * m) + rr) * xrow + 16 * kc);
   const int lsw = 16 * (lg ^ ((li ^ (li >> 1)) & 3));  // operand reads: rows 16 x + li
   typedef __attribute__((address_space(3))) uint8_t* lds_p;
   const uint32_t smem_base = (uint32_t)(size_t)(lds_p)smem;
+  // one stage: 4 X and 2 weight loads of 1 KiB per wavefront, LDS addresses 4 KiB apart
   auto issue = [&](int ks, int buf) {
-    const uint32_t st = smem_base + buf * G::STAGE;
+    const uint32_t st = __builtin_amdgcn_readfirstlane(smem_base + buf * G::STAGE + 1024 * wave);
     const size_t ko = (size_t)ks * G::BK * 2;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      lds_dma16(xsrc[m] + ko, __builtin_amdgcn_readfirstlane(st + 1024 * (wave + 4 * m)));
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-      lds_dma16(wsrc[m] + ko,
-                __builtin_amdgcn_readfirstlane(st + G::X_BYTES + 1024 * (wave + 4 * m)));
+    lds_dma_stage(X + ko, W + ko, xoff, woff, st, st + G::X_BYTES);
   };
   f32x4_v acc[G::IT][G::JT];
 #pragma unroll
@@ -380,10 +392,22 @@ template <class S>
 hipError_t launch_append(const AppendArgs& a) {
   if constexpr (S::BF) {
     if (a.n_rows >= kGemmMinRows && a.d % GemmCfg<S>::BK == 0) {
-      const int row_tiles = (a.n_rows + GemmCfg<S>::BM - 1) / GemmCfg<S>::BM;
-      const int blocks = ((row_tiles + 7) / 8) * 8 * GemmCfg<S>::COL_TILES;
-      hipLaunchKernelGGL(append_gemm_kernel<S>, dim3(blocks), dim3(GemmCfg<S>::NT), 0, a.stream,
-                         a, row_tiles);
+      // the kernel addresses X rows by 32-bit byte offsets from X: batches of rows that span
+      // less than 4 GiB each
+      const size_t row_bytes = (size_t)a.d * 2;
+      size_t cap = (size_t)0xffffffffu / row_bytes / GemmCfg<S>::BM * GemmCfg<S>::BM;
+      if (cap > (size_t)a.n_rows) cap = a.n_rows;
+      for (int r0 = 0; r0 < a.n_rows; r0 += (int)cap) {
+        AppendArgs b = a;
+        b.X = static_cast<const uint8_t*>(a.X) + (size_t)r0 * row_bytes;
+        b.row_req = a.row_req + r0;
+        b.row_pos = a.row_pos + r0;
+        b.n_rows = a.n_rows - r0 < (int)cap ? a.n_rows - r0 : (int)cap;
+        const int row_tiles = (b.n_rows + GemmCfg<S>::BM - 1) / GemmCfg<S>::BM;
+        const int blocks = ((row_tiles + 7) / 8) * 8 * GemmCfg<S>::COL_TILES;
+        hipLaunchKernelGGL(append_gemm_kernel<S>, dim3(blocks), dim3(GemmCfg<S>::NT), 0,
+                           a.stream, b, row_tiles);
+      }
       return hipGetLastError();
     }
   }
