@@ -61,11 +61,11 @@ typedef float f32x4_v __attribute__((ext_vector_type(4)));
 // Workgroup = 8 product columns x 16 rows, 256 threads = 4 wavefronts that split k into
 // 32-wide blocks (wavefront w takes blocks w, w + 4, ...).  v_mfma_f32_16x16x32_bf16 with
 // A = X (lane 16*(k/8) + i: 8 consecutive k of row i) and B = the weight rows (lane
-// 16*(k/8) + j: 8 consecutive k of column j; lanes j and j + 8 hold the same column, whose
-// duplicate results are dropped): both operands are 16-byte loads straight from memory,
-// and a wavefront issues all of them for 16 blocks before the first product, so a pass
-// costs one memory round trip.  Rows past the last are read as the last row and their
-// results dropped (an output row of the product depends on its own A row only).  The
+// 16*(k/8) + j: 8 consecutive k of column j, j < 8; lanes j >= 8 hold zeros and their
+// results are dropped): both operands are 16-byte loads straight from memory, and a
+// wavefront issues all of them for 16 blocks before the first product, so a pass costs
+// one memory round trip.  Rows past the last are zeros and their results dropped (an
+// output row of the product depends on its own A row only).  The
 // destination (request, position, then page) of each stored element is requested before
 // and during the operand loads.  The four partial tiles add in a fixed order through LDS.
 // Each column's weights are one contiguous run of d values, so the workgroups need no
@@ -103,11 +103,12 @@ append_few_rows_mfma_kernel(AppendArgs a) {
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       // k past the end: a valid address, zero weights
+      // lanes j >= 8 (B) and rows past the last (A) load nothing: their products are
+      // dropped, and zeros keep them finite; k past the end: zero weights
       const int k = (kb0 + 4 * u) * 32 + 8 * lg;
       const int kc = min(k, a.d - 8) * 2;
-      bv[u] = *reinterpret_cast<const bf16x8_v*>(wr + kc);
-      av[u] = *reinterpret_cast<const bf16x8_v*>(xr + kc);
-      if (k >= a.d) bv[u] = bf16x8_v{};
+      bv[u] = (li < 8 && k < a.d) ? *reinterpret_cast<const bf16x8_v*>(wr + kc) : bf16x8_v{};
+      av[u] = li < nr ? *reinterpret_cast<const bf16x8_v*>(xr + kc) : bf16x8_v{};
     }
     if (!have_page && t < 128) {
       asm volatile("" ::: "memory");  // after the operand loads, not ahead of them
