@@ -101,8 +101,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the LRKV decode "
-              "path here is single-GPU, see DESIGN.md for how it would shard", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the LRKV decode "
+              "path is built and timed on a single GPU", file=sys.stderr)
         sys.exit(2)
 
     import torch
