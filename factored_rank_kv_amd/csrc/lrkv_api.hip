@@ -47,8 +47,8 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // B=4 x 131072 in 2048-token chunks, 84 % of 8 TB/s), at least 4 pages and at most
 // kAutoChunkTokens long.  The host does not see the lengths (they stay on the device), so a
 // ragged batch is sized by its longest request; such a batch does better with several
-// waves of shorter chunks (B=32, lengths 512..32768: 768 tokens, 418 µs, against 492 µs
-// for the automatic 2048), which a caller who knows the lengths can ask for.
+// waves of shorter chunks (B=32, lengths 512..32768: 768-token chunks, 405-420 µs), which
+// a caller who knows the lengths can ask for.
 constexpr long long kAutoChunkTokens = 2048;
 
 int pick_chunk(const lrkv_layout* L, int batch, int q_len, int max_seq_len, int chunk_tokens) {
@@ -68,9 +68,9 @@ int pick_chunk(const lrkv_layout* L, int batch, int q_len, int max_seq_len, int 
 
 // Automatic splits of a batch of at least this many single-row requests (and at most
 // kBalancedMaxBatch) take the balanced split: equal page ranges per workgroup whatever the
-// lengths (B=32, lengths 512..32768: 347 µs against 426 µs for the best chunk size and
-// 500 µs for one wave of chunks sized by the longest request).  Smaller batches keep the
-// chunked split, whose four pages in flight per workgroup and shorter start suit them.
+// lengths (B=32, lengths 512..32768: 310-340 µs against 405-420 µs for the best chunk
+// size).  Smaller batches keep the chunked split, whose shorter start (no length scan)
+// suits them.
 constexpr int kBalancedMinBatch = 16;
 constexpr int kBalancedGroups = 256;     // one wave of split workgroups
 
