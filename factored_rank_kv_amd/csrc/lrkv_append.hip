@@ -188,7 +188,9 @@ append_few_rows_f32_kernel(AppendArgs a) {
 // ([column][k], the weights being output-major) are stored alike, and each lane reads the
 // 8 consecutive k of one row (A operand) or of one column (B operand) as one 16-byte LDS
 // read; a wavefront's A and B reads serve (BM/32) x 4 products, so taller wavefront tiles
-// read less LDS per product.  The BM x 128 result is rounded to bf16 into LDS, then written
+// read less LDS per product.  The operand reads run one step ahead in registers: halfway
+// through a step's products the next stage is waited for (one barrier per step) and its
+// operands are read while the second half of the products runs.  The BM x 128 result is rounded to bf16 into LDS, then written
 // to the pages as 16-byte chunks (16 consecutive rows of one page fill 256 contiguous bytes
 // of a section).  Blocks are numbered so that the 128-column slices of one row block run
 // on one XCD (blocks go to the 8 XCDs round robin), where they share that row block's X in
@@ -333,29 +335,61 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
   if (nk > 1) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  int buf = 0;
-  for (int ks = 0; ks < nk; ++ks) {
-    const int nb = buf == 0 ? 2 : buf - 1;  // (ks + 2) % 3
-    if (ks + 2 < nk) issue(ks + 2, nb);
+  // operand fragments of one stage: B (JT columns blocks) and A (IT row blocks)
+  struct Frag {
+    bf16x8_v b[G::JT];
+    bf16x8_v a[G::IT];
+  };
+  auto load_frag = [&](int buf, Frag& f) {
     const uint8_t* st = smem + buf * G::STAGE;
-    bf16x8_v bv[G::JT];
 #pragma unroll
     for (int j = 0; j < G::JT; ++j)
-      bv[j] = *reinterpret_cast<const bf16x8_v*>(st + G::X_BYTES +
-                                                 (64 * wn + 16 * j + li) * G::XS + lsw);
+      f.b[j] = *reinterpret_cast<const bf16x8_v*>(st + G::X_BYTES +
+                                                  (64 * wn + 16 * j + li) * G::XS + lsw);
 #pragma unroll
-    for (int i = 0; i < G::IT; ++i) {
-      const bf16x8_v av =
-          *reinterpret_cast<const bf16x8_v*>(st + (G::WM * wm + 16 * i + li) * G::XS + lsw);
+    for (int i = 0; i < G::IT; ++i)
+      f.a[i] = *reinterpret_cast<const bf16x8_v*>(st + (G::WM * wm + 16 * i + li) * G::XS + lsw);
+  };
+  // step ks: stage ks's fragments are in fc; the first half of the products runs, then the
+  // stage ks + 1 bytes are waited for (own loads, then the barrier for every wavefront's),
+  // and its fragments are read into fn during the second half.  The barrier also orders
+  // every wavefront's reads of stage ks - 1 (done before this step) before the loads of
+  // step ks + 1 refill that stage.
+  auto step = [&](int ks, int buf, Frag& fc, Frag& fn) {
+    const int nb = buf == 0 ? 2 : buf - 1;  // (ks + 2) % 3
+    if (ks + 2 < nk) issue(ks + 2, nb);
+#pragma unroll
+    for (int i = 0; i < G::IT / 2; ++i)
 #pragma unroll
       for (int j = 0; j < G::JT; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fc.a[i], fc.b[j], acc[i][j], 0, 0, 0);
+    // every read of fc done here on both paths, so the products below wait on nothing the
+    // next stage's reads add (s_waitcnt lgkmcnt(0), other counters left alone)
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    if (ks + 1 < nk) {
+      if (ks + 2 < nk) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      load_frag(buf == 2 ? 0 : buf + 1, fn);
     }
-    if (ks + 2 < nk) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+#pragma unroll
+    for (int i = G::IT / 2; i < G::IT; ++i)
+#pragma unroll
+      for (int j = 0; j < G::JT; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fc.a[i], fc.b[j], acc[i][j], 0, 0, 0);
+  };
+  Frag f0, f1;
+  load_frag(0, f0);
+  int buf = 0;
+  for (int ks = 0; ks < nk; ks += 2) {
+    step(ks, buf, f0, f1);
     buf = buf == 2 ? 0 : buf + 1;
+    if (ks + 1 < nk) {
+      step(ks + 1, buf, f1, f0);
+      buf = buf == 2 ? 0 : buf + 1;
+    }
   }
+  __syncthreads();  // every wavefront's last products read their operands; LDS is reused
 
   // result tile -> bf16 [row][column] in LDS (D[i][j] at lane 16*(i/4) + j, element i%4)
   uint8_t* ot = smem;
