@@ -18,6 +18,8 @@
 // is exactly the B-operand layout of the value products, and each lane owns one query row
 // for the softmax rescale.  S_V^T and R_V^T operands come from ds_read_b64_tr_b16 on the
 // token-major rows.  P, A and the final O_R are held as bf16; P and O_R as hi + lo pairs.
+// Operand reads run ahead of the products in registers: two token blocks of the score
+// operands, six of the value operands (the first six issued before the softmax).
 //
 // MFMA lane layouts used (v_mfma_f32_16x16x32_bf16 / 16x16x16_bf16): A[i][k] at lane
 // 16*(k/KL) + i, element k%KL; B[k][j] at lane 16*(k/KL) + j; D[i][j] at lane 16*(i/4) + j,
@@ -327,33 +329,74 @@ prefill_kernel(const PrefillArgs a) {
     // ---- scores S^T for the 4 token blocks: lane (lg, li) gets tokens 16 tb + 4 lg + e of
     // row li of each row block; every operand read from LDS serves both row blocks
     f32x4_p sc[RW][4];
+    // operands of one token block: its S_K rows (K = 32 blocks) and R_K[h] rows (pairs of
+    // 16-rank blocks); two blocks are held ahead so the reads overlap the products
+    struct ScoreFrag {
+      bf16x8_p kv[C::KB];
+      bf16x8_p rk[C::RB / 2];
+    };
+    auto load_sf = [&](int tb, ScoreFrag& f) {
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+        f.kv[kb] = *reinterpret_cast<const bf16x8_p*>(lds + C::SK_OFF + sk_slot(16 * tb + li, 4 * kb + lg));
+#pragma unroll
+      for (int kp = 0; kp < C::RB / 2; ++kp) {
+        const uint8_t* rkrow = lds + C::RK_OFF + (16 * tb + li) * C::R_STRIDE + 64 * kp + 8 * lg;
+        f.rk[kp] = cat8(*reinterpret_cast<const short4_p*>(rkrow),
+                        *reinterpret_cast<const short4_p*>(rkrow + 32));
+      }
+    };
+    ScoreFrag sf[2];
+    load_sf(0, sf[0]);
+    load_sf(1, sf[1]);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
+      __builtin_amdgcn_sched_barrier(0);
+      ScoreFrag& f = sf[tb & 1];
       f32x4_p acc[RW];
 #pragma unroll
       for (int w = 0; w < RW; ++w) acc[w] = f32x4_p{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        const bf16x8_p kv = *reinterpret_cast<const bf16x8_p*>(
-            lds + C::SK_OFF + sk_slot(16 * tb + li, 4 * kb + lg));
+      for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int w = 0; w < RW; ++w) acc[w] = mfma32(kv, qv[w][kb], acc[w]);
-      }
+        for (int w = 0; w < RW; ++w) acc[w] = mfma32(f.kv[kb], qv[w][kb], acc[w]);
       // private part, K = 32 per product, ranks ordered as in pkh / pkl
 #pragma unroll
-      for (int kp = 0; kp < C::RB / 2; ++kp) {
-        const uint8_t* rkrow = lds + C::RK_OFF + (16 * tb + li) * C::R_STRIDE + 64 * kp + 8 * lg;
-        const bf16x8_p rk = cat8(*reinterpret_cast<const short4_p*>(rkrow),
-                                 *reinterpret_cast<const short4_p*>(rkrow + 32));
+      for (int kp = 0; kp < C::RB / 2; ++kp)
 #pragma unroll
         for (int w = 0; w < RW; ++w) {
-          acc[w] = mfma32(rk, pkh[w][kp], acc[w]);
-          acc[w] = mfma32(rk, pkl[w][kp], acc[w]);
+          acc[w] = mfma32(f.rk[kp], pkh[w][kp], acc[w]);
+          acc[w] = mfma32(f.rk[kp], pkl[w][kp], acc[w]);
         }
-      }
 #pragma unroll
       for (int w = 0; w < RW; ++w) sc[w][tb] = acc[w];
+      if (tb + 2 < 4) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_sf(tb + 2, f);
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // value operands, in product order: for each pair of token blocks tp, the FB S_V^T
+    // feature blocks then the RB R_V[h]^T rank blocks; VD of them are read ahead (the first
+    // VD before the softmax, which they do not depend on)
+    constexpr int VN = 2 * (C::FB + C::RB), VD = 6;
+    auto vfrag = [&](int f) -> bf16x8_p {
+      const int tp = f / (C::FB + C::RB), k = f % (C::FB + C::RB);
+      if (k < C::FB) {
+        const int svrow = 32 * tp + 4 * lg + li / 4;
+        // features 16 fb + 4 (li & 3) .. +3: chunk 2 fb + (li & 3) / 2, half li & 1
+        const uint8_t* v0 = lds + C::SV_OFF + sv_slot(svrow, 2 * k + ((li & 3) >> 1)) + 8 * (li & 1);
+        return cat8(read_tr(v0), read_tr(v0 + 16 * C::SV_STRIDE));
+      }
+      const uint8_t* v0 = lds + C::RV_OFF + (32 * tp + 4 * lg + li / 4) * C::R_STRIDE +
+                          (16 * (k - C::FB) + 4 * (li & 3)) * 2;
+      return cat8(read_tr(v0), read_tr(v0 + 16 * C::R_STRIDE));
+    };
+    bf16x8_p vf[VD];
+#pragma unroll
+    for (int f = 0; f < VD; ++f) vf[f] = vfrag(f);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- online softmax per row: scores are tokens j = kt*BT + 16 tb + 4 lg + e of row li
     // probabilities as the B operands of the value products: pp[w][tp] element e < 4 is
@@ -407,26 +450,17 @@ prefill_kernel(const PrefillArgs a) {
     // 4 + e: token 32 tp + 16 + 4 lg + e, in both operands); the A operand of block
     // (fb, tb) is S_V[16 tb + 4 lg' + e][16 fb + li'] by a transposing read
 #pragma unroll
-    for (int tp = 0; tp < 2; ++tp) {
-      const int svrow = 32 * tp + 4 * lg + li / 4;  // second read: row + 16, same position
-      const uint8_t* rvr = lds + C::RV_OFF + (32 * tp + 4 * lg + li / 4) * C::R_STRIDE;
+    for (int f = 0; f < VN; ++f) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int tp = f / (C::FB + C::RB), k = f % (C::FB + C::RB);
 #pragma unroll
-      for (int fb = 0; fb < C::FB; ++fb) {
-        // features 16 fb + 4 (li & 3) .. +3: chunk 2 fb + (li & 3) / 2, half li & 1
-        const uint8_t* v0 =
-            lds + C::SV_OFF + sv_slot(svrow, 2 * fb + ((li & 3) >> 1)) + 8 * (li & 1);
-        const bf16x8_p v = cat8(read_tr(v0), read_tr(v0 + 16 * C::SV_STRIDE));
-#pragma unroll
-        for (int w = 0; w < RW; ++w) os[w][fb] = mfma32(v, pp[w][tp], os[w][fb]);
+      for (int w = 0; w < RW; ++w) {
+        if (k < C::FB) os[w][k] = mfma32(vf[f % VD], pp[w][tp], os[w][k]);
+        else orr[w][k - C::FB] = mfma32(vf[f % VD], pp[w][tp], orr[w][k - C::FB]);
       }
-#pragma unroll
-      for (int rb = 0; rb < C::RB; ++rb) {
-        const uint8_t* v0 = rvr + (16 * rb + 4 * (li & 3)) * 2;
-        const bf16x8_p v = cat8(read_tr(v0), read_tr(v0 + 16 * C::R_STRIDE));
-#pragma unroll
-        for (int w = 0; w < RW; ++w) orr[w][rb] = mfma32(v, pp[w][tp], orr[w][rb]);
-      }
+      if (f + VD < VN) vf[f % VD] = vfrag(f + VD);
     }
+    __builtin_amdgcn_sched_barrier(0);
     if (kt + 1 < n_tiles) {
       if ((kt + 1) % C::TPB == 0) {  // next block of page ids (uniform over the workgroup)
         __syncthreads();
