@@ -975,6 +975,8 @@ merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
     __syncthreads();
     if (col >= 0) {
       int s = 0;
+      // unrolled: the reads of 16 records go out before the first sum waits on them
+#pragma unroll 4
       for (; s + 4 <= cnt; s += 4) {
         v0 = fmaf(wts[s], tf[s * PP + col], v0);
         v1 = fmaf(wts[s + 1], tf[(s + 1) * PP + col], v1);
