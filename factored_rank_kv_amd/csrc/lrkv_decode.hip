@@ -879,7 +879,8 @@ merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
   constexpr int PP = S::PART_PAD;
   constexpr int MS_LDS = (48 * 1024) / (PP * 4);
   constexpr int MS = MS_LDS < 256 ? MS_LDS : 256;  // chunks per pass held in LDS
-  __shared__ float4 tile[MS * PP / 4];
+  constexpr int LP = (MS * (PP / 4) + 255) / 256;  // 16-byte loads per thread and pass
+  __shared__ float4 tile[LP * 256];                // records, then padding
   __shared__ float wts[MS];
   __shared__ float red[4];
   __shared__ float accR_s[S::R];
@@ -917,14 +918,23 @@ merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
     cap = n_bal;
   }
 
+  // a pass of cnt <= MS records into LDS: every load of the thread goes out before the
+  // first LDS write (one memory round trip, not one per 16 bytes); lanes past the pass
+  // read its last 16 bytes again and write them past its records (never read), so
+  // neither the loads nor the writes need a branch
   auto load_pass = [&](int s0, int cnt) {
-    for (int i = t; i < cnt * (PP / 4); i += 256) {
+    const int last = cnt * (PP / 4) - 1;
+    float4 v[LP];
+#pragma unroll
+    for (int k = 0; k < LP; ++k) {
+      const int i = min(t + 256 * k, last);
       const int s = i / (PP / 4), c4 = i - s * (PP / 4);
-      tile[i] = reinterpret_cast<const float4*>(base + (size_t)(s0 + s) * stride)[c4];
+      v[k] = reinterpret_cast<const float4*>(base + (size_t)(s0 + s) * stride)[c4];
     }
+#pragma unroll
+    for (int k = 0; k < LP; ++k) tile[t + 256 * k] = v[k];
   };
-  // first pass and B_V row go out before the length is known
-  if (cap <= MS) load_pass(0, cap);
+  // B_V row and first pass go out before the length is known
   constexpr int BVW = S::R * S::EB / 16;
   uint4 bvr[BVW];
   if (t < S::DH) {
@@ -933,6 +943,7 @@ merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
 #pragma unroll
     for (int c = 0; c < BVW; ++c) bvr[c] = src[c];
   }
+  if (cap > 0 && cap <= MS) load_pass(0, cap);
   const int vis = visible_tokens(seq_lens[b], q_len, qi);
   const int n = BAL ? n_bal : (vis + chunk - 1) / chunk;
   if (n == 0) {  // no visible token: zeros
