@@ -142,6 +142,17 @@ def test_permuted_pool_is_bit_identical_to_identity():
         assert torch.equal(oa, ob)
 
 
+@pytest.mark.parametrize("shape", [(16, 128, 56), (32, 128, 32)])
+def test_merge_in_several_passes(shape):
+    """More chunk records per query row than the merge holds in LDS at once (65 at H=16,
+    74 at H=32): 2100 tokens in 16-token chunks are 132 records, merged in passes of that
+    many; the weights of every pass are taken against the row's global max."""
+    H, dh, r = shape
+    log(f"merge in passes, shape {shape}")
+    case = iid_case(130 + H, H, dh, r, O.BF16, [2100, 1100, 5], permute=True, fill=0x7FC0)
+    check(case, case.run_f64(chunk_tokens=16), case.reference(), what=f"merge passes {shape}")
+
+
 def test_chunk_sizes_agree():
     case = iid_case(106, 16, 128, 56, O.BF16, [300, 77], permute=True)
     ref = case.reference()
