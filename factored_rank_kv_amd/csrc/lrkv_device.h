@@ -6,7 +6,7 @@
 
 namespace lrkv {
 
-constexpr int kPage = 16;  // tokens per page in this build
+constexpr int kPage = 16;  // tokens per page of every compiled variant
 
 // Compile-time description of one kernel variant.  Page layout as in include/lrkv.h:
 // sections S_K, S_V, R_K[0..H-1], R_V[0..H-1], each chunk-major ([chunk][token][16 B]).

@@ -8,7 +8,7 @@
 
 namespace lrkv {
 
-// The kernel variants of this build: (H, d_h, r, dtype).
+// The compiled kernel variants: (H, d_h, r, dtype).
 using ShapeC0 = Shape<4, 16, 4, false>;    // float32 single-layer check
 using ShapeC1 = Shape<16, 128, 56, true>;  // bf16, 16 heads, rank 56 (half the dense cache)
 using ShapeC3 = Shape<32, 128, 32, true>;  // bf16, 32 heads, rank 32

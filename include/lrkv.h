@@ -16,7 +16,7 @@
  * paragraph after Algorithm 1 asking that both kinds of page share token numbering and
  * lifetime).
  *
- *   P   = page_size tokens per page (16 in this build)
+ *   P   = page_size tokens per page (16 for every compiled variant)
  *   b   = element bytes (4 for LRKV_F32, 2 for LRKV_BF16)
  *   C   = 16 / b elements per 16-byte chunk; d_h and r must be multiples of C
  *   page_bytes = P * 2 * (d_h + H*r) * b     (eq 9 of LRKV notes §4, per page)
@@ -50,7 +50,7 @@
  *    them on the device for a caller who wants to validate first.
  *  - Return value: LRKV_OK, or a negative status (lrkv_status_string gives its text).
  *
- * Shapes with a kernel variant in this build, (H, d_h, r, dtype):
+ * Shapes with a compiled kernel variant, (H, d_h, r, dtype):
  *   (4, 16, 4, LRKV_F32), (16, 128, 56, LRKV_BF16), (32, 128, 32, LRKV_BF16); P = 16.
  * Any other shape returns LRKV_ERR_UNSUPPORTED.
  */

@@ -1,8 +1,8 @@
 """Plain float64 CPU oracle for Low-Rank Key Value attention (LRKV).
 
-TEST INFRASTRUCTURE ONLY.  This module is the checker, not the product.  It may be
-imported only by ``tests/``, by ``__graft_entry__.smoke()`` and by the CPU-baseline leg
-of ``bench.py``.  The library in ``factored_rank_kv_amd/`` never imports, links or runs
+TEST INFRASTRUCTURE ONLY.  This module is what the tests compare the library against,
+not the product.  It may be imported only by ``tests/``, by ``__graft_entry__.smoke()``
+and by the CPU-baseline leg of ``bench.py``.  The library in ``factored_rank_kv_amd/`` never imports, links or runs
 it, and it shares no code with that library.
 
 What it follows

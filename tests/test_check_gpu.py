@@ -82,7 +82,7 @@ def test_each_planted_violation_is_counted():
 
 
 def test_large_table_many_blocks():
-    """A table larger than one dispatch wave of the checker (grid-stride loop), with the
+    """A table larger than one dispatch wave of the index-check kernel (grid-stride loop), with the
     violations spread over it."""
     B, max_pages = 64, 4096
     npg = B * max_pages
