@@ -85,10 +85,17 @@ def library():
 
 
 def _ptr(x):
+    """Address of a buffer argument: a device tensor's data_ptr(), an int address, or None.
+    Host tensors and strided views are refused here: the kernels would read a host address
+    as device memory, or a view's storage as if it were dense."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if not x.is_cuda:
+        raise ValueError("LRKV buffers live in device memory; got a host tensor")
+    if not x.is_contiguous():
+        raise ValueError("LRKV buffers are dense; got a non-contiguous tensor view")
     return x.data_ptr()
 
 

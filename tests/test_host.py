@@ -190,3 +190,15 @@ def test_header_is_plain_c():
                            text=True)
         assert r.returncode == 0, r.stderr
     assert ctypes.sizeof(F.lrkv_layout) == 20
+
+
+def test_binding_refuses_host_tensors():
+    """A host tensor never reaches the library (its address would be read as device memory)."""
+    import torch
+
+    host = torch.zeros(64, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        F.lrkv_check_indices(C1, host, 2, 4, None, 64, None, None, 0, 8, host, stream=0)
+    with pytest.raises(ValueError):
+        F.lrkv_decode(C1, host, 1, 1, FAKE, FAKE, FAKE, FAKE, 1, FAKE, 16, 0, FAKE, FAKE, 1 << 20,
+                      stream=0)
