@@ -284,17 +284,6 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
   const int wm = wave >> 1, wn = wave & 1;
   const int li = lane & 15, lg = lane >> 4;
 
-  for (int i = t; i < G::BM; i += G::NT) {
-    const int r = row0 + i;
-    int page = 0, slot = 0;
-    if (r < a.n_rows) {
-      const int req = a.row_req[r], pos = a.row_pos[r];
-      page = a.page_table[(size_t)req * a.max_pages + pos / S::P];
-      slot = pos % S::P;
-    }
-    row_page[i] = page;
-    row_slot[i] = slot;
-  }
 
   // global -> LDS staging by direct loads (global_load_lds_dwordx4): one wavefront
   // instruction fills 1 KiB = 16 rows x 64 bytes; lane i writes bytes [16 i, 16 i + 16) of
@@ -332,6 +321,18 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
   const int nk = a.d / G::BK;
   issue(0, 0);
   if (nk > 1) issue(1, 1);
+  // destinations of the tile's rows, looked up while the first two stages travel
+  for (int i = t; i < G::BM; i += G::NT) {
+    const int r = row0 + i;
+    int page = 0, slot = 0;
+    if (r < a.n_rows) {
+      const int req = a.row_req[r], pos = a.row_pos[r];
+      page = a.page_table[(size_t)req * a.max_pages + pos / S::P];
+      slot = pos % S::P;
+    }
+    row_page[i] = page;
+    row_slot[i] = slot;
+  }
   if (nk > 1) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
