@@ -19,7 +19,7 @@
 // for the softmax rescale.  S_V^T and R_V^T operands come from ds_read_b64_tr_b16 on the
 // token-major rows.  P, A and the final O_R are held as bf16; P and O_R as hi + lo pairs.
 // Operand reads run ahead of the products in registers: two token blocks of the score
-// operands, six of the value operands (the first six issued before the softmax).
+// operands, five of the value operands (the first five issued before the softmax).
 //
 // MFMA lane layouts used (v_mfma_f32_16x16x32_bf16 / 16x16x16_bf16): A[i][k] at lane
 // 16*(k/KL) + i, element k%KL; B[k][j] at lane 16*(k/KL) + j; D[i][j] at lane 16*(i/4) + j,
@@ -379,8 +379,8 @@ prefill_kernel(const PrefillArgs a) {
 
     // value operands, in product order: for each pair of token blocks tp, the FB S_V^T
     // feature blocks then the RB R_V[h]^T rank blocks; VD of them are read ahead (the first
-    // VD before the softmax, which they do not depend on)
-    constexpr int VN = 2 * (C::FB + C::RB), VD = 6;
+    // VD before the softmax, which they do not depend on; 5 measured best of 3 to 8)
+    constexpr int VN = 2 * (C::FB + C::RB), VD = 5;
     auto vfrag = [&](int f) -> bf16x8_p {
       const int tp = f / (C::FB + C::RB), k = f % (C::FB + C::RB);
       if (k < C::FB) {
