@@ -271,3 +271,51 @@ def test_reappend_after_wipe_is_bit_identical():
     a = run_append(L, X, wc, np.zeros(48, int), np.arange(48), table, npg, start)
     b = run_append(L, X, wc, np.zeros(48, int), np.arange(48), table, npg, start)
     assert np.array_equal(a, b)
+
+
+def test_rows_spanning_more_than_4_gib_of_x():
+    """X rows spanning more than 4 GiB (d = 8192: 262,656 rows of 16 KiB, 4.3 GB) go out in
+    several launches, the product addressing X rows by 32-bit offsets.  One-hot rows (each
+    projected value is one weight entry, so the result is exact); every 5th row of the last
+    1,600 (the region holding the launch boundary) and a spread of earlier rows are compared
+    with the oracle: its projection of those rows, written over a copy of the library's
+    pages that hold them, must leave those pages unchanged byte for byte."""
+    L = O.Layout(16, 128, 56, 16, O.BF16)
+    d, n = 8192, 262_656
+    assert n * d * 2 > 2**32
+    g = np.random.default_rng(410)
+    idx = g.integers(0, d, n)
+    neg = g.random(n) < 0.5
+    dev = torch.device("cuda")
+    log(f"append of {n} one-hot rows, d = {d} ({n * d * 2 / 1e9:.2f} GB of X)")
+    X = torch.zeros((n, d), dtype=torch.int16, device=dev)
+    one = torch.from_numpy(np.where(neg, np.int16(-16512), np.int16(0x3F80))).to(dev)  # -1.0, 1.0
+    X[torch.arange(n, device=dev), torch.from_numpy(idx).to(dev)] = one
+    w = synth.projection_weights(411, d, L.num_heads, L.head_dim, L.rank)
+    wc = {k: as_codes(v, O.BF16) for k, v in w.items() if k in ("W_SK", "W_SV", "U_K", "U_V")}
+    table, npg = synth.page_assignment(412, [n], 16, True)
+    pb = O.page_bytes(L)
+    pool = torch.full((npg * pb // 2,), SENTINEL_BF16, dtype=torch.int16, device=dev)
+    pool = pool.view(torch.uint8)
+    wdev = {k: to_dev(output_major(v)) for k, v in wc.items()}
+    req = torch.zeros(n, dtype=torch.int32, device=dev)
+    pos = torch.arange(n, dtype=torch.int32, device=dev)
+    F.lrkv_append(layout_c(L), X, n, d, wdev["W_SK"], wdev["W_SV"], wdev["U_K"], wdev["U_V"], req,
+                  pos, to_dev(np.ascontiguousarray(table, np.int32)), table.shape[1], pool, npg)
+    torch.cuda.synchronize()
+    del X
+    rows = np.unique(np.concatenate([np.arange(n - 1600, n, 5), g.integers(0, n - 1600, 64),
+                                     [0, n - 1]]))
+    pages = table[0, rows // 16]
+    uniq, inv = np.unique(pages, return_inverse=True)
+    got = pool.view(npg, pb)[torch.from_numpy(uniq.astype(np.int64)).to(dev)].cpu().numpy()
+    got = got.reshape(-1)
+    table_c = np.zeros_like(table)
+    table_c[0, rows // 16] = inv
+    Xs = np.zeros((len(rows), d), np.float64)
+    Xs[np.arange(len(rows)), idx[rows]] = np.where(neg[rows], -1.0, 1.0)
+    w64 = {k: codes_f64(v, O.BF16) for k, v in wc.items()}
+    log(f"oracle projection of {len(rows)} sampled rows over {len(uniq)} pages")
+    exp = O.append_reference(got.copy(), L, Xs, w64["W_SK"], w64["W_SV"], w64["U_K"], w64["U_V"],
+                             np.zeros(len(rows), np.int64), rows, table_c)
+    assert np.array_equal(got, exp)
