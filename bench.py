@@ -168,7 +168,8 @@ def main():
     stream = torch.cuda.current_stream()
 
     def timed(fn, n, use_graph):
-        """Average ms per call of fn over n calls, HIP events on the launch stream."""
+        """Average ms per call of fn over exactly n calls (call k reads pool copy k mod the
+        number of copies), HIP events on the launch stream around one graph replay."""
         if use_graph:
             g = torch.cuda.CUDAGraph()
             s = torch.cuda.Stream()
@@ -177,19 +178,17 @@ def main():
                 fn(0)  # warm the capture stream
             torch.cuda.synchronize()
             with torch.cuda.graph(g, stream=s):
-                for k in range(len(pools)):
+                for k in range(n):
                     fn(k)
-            reps = max(1, n // len(pools))
-            n = reps * len(pools)
             torch.cuda.synchronize()
-            g.replay()
+            g.replay()  # untimed: first replay uploads the graph
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            for _ in range(reps):
-                g.replay()
+            g.replay()
             e1.record(stream)
             torch.cuda.synchronize()
+            del g
             return e0.elapsed_time(e1) / n, n
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -200,6 +199,20 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n, n
 
+    def per_call_us(fn, n):
+        """Durations of n single calls, each between two HIP events on the launch stream.  A
+        spin kernel first holds the stream while every call is enqueued, so the calls run back
+        to back and no event pair spans host launch time."""
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(200_000_000)  # ~0.1 s of spinning on one wavefront
+        for k in range(n):
+            evs[k].record(stream)
+            fn(k)
+        evs[n].record(stream)
+        torch.cuda.synchronize()
+        return np.array([evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(n)])
+
     # ---------------- warmup + timed steps ----------------
     for k in range(args.warmup):
         step(k)
@@ -209,7 +222,11 @@ def main():
     ms_decode, _ = timed(decode, args.steps, use_graph)
     ms_append, _ = timed(append, args.steps, use_graph)
     log(f"step {ms_step * 1e3:.2f} us (decode {ms_decode * 1e3:.2f} us, append "
-        f"{ms_append * 1e3:.2f} us), graph={use_graph}")
+        f"{ms_append * 1e3:.2f} us), graph={use_graph}, {n_steps} steps")
+    calls = per_call_us(decode, max(240, args.steps))
+    pct = {p: float(np.percentile(calls, p)) for p in (10, 50, 90)}
+    log(f"decode call by event pairs over {len(calls)} calls: p10 {pct[10]:.2f} p50 "
+        f"{pct[50]:.2f} p90 {pct[90]:.2f} us")
 
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -242,6 +259,9 @@ def main():
         "traffic": None if trec is None else trec["hbm_bytes_per_call"],
         "algorithmic_bytes": alg_bytes,
         "avg_call_us": round(ms_decode * 1e3, 3),
+        "call_us_p10_p50_p90": [round(pct[10], 3), round(pct[50], 3), round(pct[90], 3)],
+        "calls_in_distribution": int(len(calls)),
+        "achieved_at_p50": round(alg_bytes / (pct[50] * 1e-6) / 1e9, 1),
     }
 
     result = {
@@ -439,17 +459,45 @@ def cpu_baseline(work, weights, target_s):
         passes += 1
     per_pass = t_total / passes
     sample_bytes = 2 * 2 * n_req * T * (work.d_h + work.H * work.r)
-    threads = os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count())
-    log(f"cpu baseline: {passes} passes, {per_pass:.3f} s each")
+    blas = blas_info()
+    threads = blas.get("threads") or int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
+    log(f"cpu baseline: {passes} passes, {per_pass:.3f} s each ({blas})")
     return {
         "value": round(sample_bytes / per_pass / 1e9, 4),
         "unit": "GB/s",
         "cores": int(threads),
+        "cpu_model": cpu_model(),
+        "blas": blas,
         "kind": "oracle",
         "sample": (f"{n_req} of the {work.B} requests (T={T}, all {work.H} heads), float64 numpy "
                    f"oracle, {passes} timed passes ({t_total:.1f} s), same eq-9 bytes metric"),
         "query_head_tokens_per_s": round(work.H * n_req * T / per_pass, 1),
     }
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_info() -> dict:
+    """numpy's BLAS library and the threads it runs (threadpoolctl's report)."""
+    try:
+        import threadpoolctl
+
+        for rec in threadpoolctl.threadpool_info():
+            if rec.get("user_api") == "blas":
+                return {"vendor": rec.get("internal_api"), "version": rec.get("version"),
+                        "threads": rec.get("num_threads")}
+    except Exception:  # the report is informational only
+        pass
+    return {}
 
 
 if __name__ == "__main__":

@@ -124,8 +124,9 @@ struct SplitArgs {
   float score_scale;
 };
 
-// Balanced split (single query row per request): the batch's pages, request after request,
-// are cut into `groups` equal ranges, one per split workgroup, whatever the lengths; a range
+// Balanced split (single query row per request): the batch's N pages, request after request,
+// are cut into G = min(groups, N) equal ranges, one per split workgroup (workgroups past G
+// have no range), whatever the lengths; every range holds at least one page; a range
 // crossing requests is processed as one segment per request.  The segment of request b in
 // workgroup w writes its partial tuples at record slot w + b: slots are unique (ranges
 // are ordered, so w' > w implies b' >= b) and a request's slots are consecutive, in page
@@ -655,9 +656,12 @@ decode_split_kernel(const SplitArgs a) {
   if constexpr (BAL) {
     const int N = page_prefix<C::NT, S::P>(a.seq_lens, a.batch, a.max_pages, pref_lds, wsum_lds,
                                            (int)threadIdx.x);
-    const int g_lo = (int)((long long)blockIdx.x * N / a.groups);
-    g_hi = (int)((long long)(blockIdx.x + 1) * N / a.groups);
-    if (g_lo >= g_hi) return;  // uniform for the whole workgroup
+    // ranges over at most N workgroups, so that every range holds at least one page (the
+    // merge takes every slot between a request's first and last range as written)
+    const int G = min(a.groups, N);
+    if ((int)blockIdx.x >= G) return;  // uniform for the whole workgroup
+    const int g_lo = (int)((long long)blockIdx.x * N / G);
+    g_hi = (int)((long long)(blockIdx.x + 1) * N / G);
     int lo = 0, hi = a.batch - 1;  // the request holding page g_lo
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
@@ -911,9 +915,10 @@ merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
     __shared__ int pref_s[kBalancedMaxBatch + 1];
     __shared__ int wsum_s[4];
     const int N = page_prefix<256, S::P>(seq_lens, batch, max_pages, pref_s, wsum_s, t);
+    const int G = min(groups, N);  // the split kernel's ranges: each holds a page
     const int p0 = pref_s[b], p1 = pref_s[b + 1];
-    const int w0 = p1 > p0 ? group_of_page(p0, N, groups) : 0;
-    n_bal = p1 > p0 ? group_of_page(p1 - 1, N, groups) - w0 + 1 : 0;
+    const int w0 = p1 > p0 ? group_of_page(p0, N, G) : 0;
+    n_bal = p1 > p0 ? group_of_page(p1 - 1, N, G) - w0 + 1 : 0;
     base = part + (((size_t)w0 + b) * S::H + h) * PP;
     cap = n_bal;
   }

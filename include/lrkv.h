@@ -98,8 +98,15 @@ size_t lrkv_page_bytes(const lrkv_layout* L);
  * slot row_pos[n] % P, in the four sections.  No other byte of the pool changes.  Prefill
  * (all rows of a prompt) and single-token append are the same call.
  *
- * The weights are held output-major (the [out][in] order of a linear layer's weight): the
- * d weights that produce one output coordinate are contiguous.
+ * WEIGHT ORIENTATION - read this before passing weights.  The page writes the products as
+ * X W_S with W_S of shape [d][d_h] and X U_h with U_h of shape [d][r].  This call does NOT
+ * take them in that order: every weight is held OUTPUT-MAJOR, the [out][in] order of a
+ * linear layer's weight matrix, i.e. the transposes [d_h][d] and [H][r][d].  Weights held
+ * [d][d_h] / [d][H][r] must be transposed (made contiguous in the order below) first; passing
+ * them untransposed is not detected and gives wrong rows.  The reason: the d weights that
+ * produce one output coordinate are then contiguous, so both operands of the product are
+ * read along d in 16-byte runs (the decode-step append reads each column's weights as one
+ * run; held [d][out], a column's weights sit d rows apart).
  *   X        device, [n_rows][d]     in L->dtype
  *   W_SK     device, [d_h][d]        in L->dtype, element [c][k] = W_SK[k][c]
  *   W_SV     device, [d_h][d]        in L->dtype, element [c][k] = W_SV[k][c]
@@ -116,7 +123,8 @@ int lrkv_append(const lrkv_layout* L, const void* X, int32_t n_rows, int32_t d,
                 const int32_t* row_req, const int32_t* row_pos, const int32_t* page_table,
                 int32_t max_pages_per_req, void* pool, int64_t num_pages, void* stream);
 
-/* Workspace bytes lrkv_decode needs for these sizes (private queries and split partials). */
+/* Infrastructure of this library, not an operation of the method: the workspace bytes
+ * lrkv_decode needs for these sizes (the split partial tuples).  0 for invalid arguments. */
 size_t lrkv_decode_workspace_bytes(const lrkv_layout* L, int32_t batch, int32_t q_len,
                                    int32_t max_seq_len, int32_t chunk_tokens);
 
@@ -186,7 +194,8 @@ int lrkv_check_indices(const lrkv_layout* L, const int32_t* page_table, int32_t 
                        const int32_t* row_req, const int32_t* row_pos, int32_t n_rows,
                        int64_t num_pages, int32_t* errors, void* stream);
 
-/* Text of a status code (static storage). */
+/* Infrastructure of this library, not an operation of the method: the text of a status
+ * code (static storage). */
 const char* lrkv_status_string(int status);
 
 #ifdef __cplusplus

@@ -95,15 +95,21 @@ class Case:
         return self._dev
 
     def run(self, chunk_tokens: int = 0, max_seq_len: int | None = None, table=None,
-            pool=None) -> torch.Tensor:
-        """lrkv_decode on the device; returns the output codes tensor."""
+            pool=None, ws_fill: int | None = 0xFF) -> torch.Tensor:
+        """lrkv_decode on the device; returns the output codes tensor.
+
+        The workspace is pre-filled with the byte `ws_fill` (0xFF: every float32 there is a
+        NaN), so an output that depends on a record the call did not write is caught."""
         d = self.dev
         L = self.L
         msl = int(self.lens.max()) if max_seq_len is None else max_seq_len
         lay = layout_c(L)
         ws_bytes = F.lrkv_decode_workspace_bytes(lay, self.B, self.q_len, msl, chunk_tokens)
         assert ws_bytes > 0
-        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+        if ws_fill is None:
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+        else:
+            ws = torch.full((ws_bytes,), ws_fill, dtype=torch.uint8, device=DEV)
         out = torch.empty(self.q_codes.shape, dtype=d["q"].dtype, device=DEV)
         tab = d["table"] if table is None else table
         F.lrkv_decode(lay, d["q"], self.B, self.q_len, d["BK"], d["BV"],
@@ -179,3 +185,100 @@ def projected_case(seed, work: synth.Workload, lens=None, q_len=1, permute=False
                               req, pos, table)
     q = synth.queries(seed + 3, len(lens), q_len, work.H, work.d_h, q_scale)
     return Case(L, pool, table, lens, as_codes(q, L.dtype), wc["B_K"], wc["B_V"], npg)
+
+
+# --------------------------------------------------------------------------------------
+# large workloads: rows generated and packed on the device by torch (harness code; the
+# library is not involved), then copied to the host where the oracle walks the pages
+# --------------------------------------------------------------------------------------
+
+
+def _pack_pages_torch(L: O.Layout, table: np.ndarray, lens, rows: dict, num_pages: int,
+                      fill: int) -> torch.Tensor:
+    """Place rows (device int16 codes: SK, SV [n, d_h]; RK, RV [n, H, r]) into a fresh pool
+    in the page layout: sections S_K, S_V, R_K[0..H-1], R_V[0..H-1], each chunk-major
+    ([chunk][token][16 bytes]).  Slots no request owns hold `fill`."""
+    P, dh, r, H, C = L.page_size, L.head_dim, L.rank, L.num_heads, L.chunk
+    pe = O.page_elems(L)
+    fill16 = fill - 65536 if fill >= 32768 else fill  # the code as a signed 16-bit value
+    pool = torch.full((num_pages, pe), fill16, dtype=torch.int16, device=DEV)
+    tab = torch.from_numpy(np.ascontiguousarray(table, np.int64)).to(DEV)
+    off = 0
+    for b, T in enumerate(lens):
+        T = int(T)
+        n_pages = -(-T // P)
+        if n_pages == 0:
+            continue
+        ids = tab[b, :n_pages]
+
+        def blocks(x, heads, width):
+            padded = torch.full((n_pages * P, heads, width), fill16, dtype=torch.int16,
+                                device=DEV)
+            padded[:T] = x.reshape(T, heads, width)
+            y = padded.view(n_pages, P, heads, width // C, C).permute(0, 2, 3, 1, 4)
+            return y.reshape(n_pages, heads * width * P)
+
+        pool[ids, 0:P * dh] = blocks(rows["SK"][off:off + T], 1, dh)
+        pool[ids, P * dh:2 * P * dh] = blocks(rows["SV"][off:off + T], 1, dh)
+        base = 2 * P * dh
+        pool[ids, base:base + H * P * r] = blocks(rows["RK"][off:off + T], H, r)
+        pool[ids, base + H * P * r:base + 2 * H * P * r] = blocks(rows["RV"][off:off + T], H, r)
+        off += T
+    return pool
+
+
+def projected_case_device(seed, work: synth.Workload, lens=None, permute=True, fill=0x7FC0,
+                          q_scale=1.0, chunk_rows=32768):
+    """A bf16 workload whose cached rows are projections of X ~ N(0,1) through N(0, 1/d)
+    weights (the workloads' recipe), computed on the device by torch: X drawn by torch's
+    seeded generator and rounded to bf16, weights from `synth.projection_weights` rounded to
+    bf16, the four products in float32 (torch.matmul, row chunks), rounded to bf16 (nearest
+    even), packed into a (permuted) pool.  The host copy of the pool is what the oracle
+    reads; the device copy is what the library reads."""
+    assert work.dtype == O.BF16
+    lens = list(work.lens if lens is None else lens)
+    L = O.Layout(work.H, work.d_h, work.r, work.page_size, O.BF16)
+    H, dh, r, d = work.H, work.d_h, work.r, work.d
+    w = synth.projection_weights(seed, d, H, dh, r)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(DEV).to(torch.bfloat16)
+    Wcat = torch.cat([bf(w["W_SK"]), bf(w["W_SV"]), bf(w["U_K"].reshape(d, H * r)),
+                      bf(w["U_V"].reshape(d, H * r))], dim=1).float()
+    n = int(sum(lens))
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed + 1)
+    outs = {k: torch.empty(shape, dtype=torch.int16, device=DEV) for k, shape in
+            (("SK", (n, dh)), ("SV", (n, dh)), ("RK", (n, H, r)), ("RV", (n, H, r)))}
+    for a in range(0, n, chunk_rows):
+        m = min(chunk_rows, n - a)
+        X = torch.randn(m, d, device=DEV, generator=gen).to(torch.bfloat16).float()
+        Y = (X @ Wcat).to(torch.bfloat16).view(torch.int16)
+        outs["SK"][a:a + m] = Y[:, :dh]
+        outs["SV"][a:a + m] = Y[:, dh:2 * dh]
+        outs["RK"][a:a + m] = Y[:, 2 * dh:2 * dh + H * r].reshape(m, H, r)
+        outs["RV"][a:a + m] = Y[:, 2 * dh + H * r:].reshape(m, H, r)
+        del X, Y
+    table, npg = synth.page_assignment(seed + 2, lens, work.page_size, permute)
+    pool_dev = _pack_pages_torch(L, table, lens, outs, npg, fill).view(torch.uint8).reshape(-1)
+    del outs
+    torch.cuda.synchronize()
+    pool = pool_dev.cpu().numpy()
+    q = synth.queries(seed + 3, len(lens), 1, H, dh, q_scale)
+    case = Case(L, pool, table, lens, as_codes(q, O.BF16), as_codes(w["B_K"], O.BF16),
+                as_codes(w["B_V"], O.BF16), npg)
+    case._dev = dict(pool=pool_dev, table=to_dev(case.table), lens=to_dev(case.lens),
+                     q=to_dev(case.q_codes), BK=to_dev(case.BK_codes), BV=to_dev(case.BV_codes))
+    return case
+
+
+def reference_by_request(case: Case, what: str) -> np.ndarray:
+    """The oracle's output for every (request, row, head), one request at a time with a
+    progress line each (long workloads)."""
+    out = np.full((case.B, case.q_len, case.L.num_heads, case.L.head_dim), np.nan)
+    t0 = time.time()
+    for b in range(case.B):
+        sample = [(b, i, h) for i in range(case.q_len) for h in range(case.L.num_heads)]
+        ref = case.reference(sample=sample)
+        out[b] = ref[b]
+        log(f"{what}: oracle request {b + 1}/{case.B} (T={int(case.lens[b])}) done, "
+            f"{time.time() - t0:.0f} s")
+    return out

@@ -82,30 +82,50 @@ def test_c1_shape_ragged_paged_nan_tails(chunk):
     check(case, case.run_f64(chunk_tokens=chunk), case.reference(), what=f"c1 ragged chunk {chunk}")
 
 
-@pytest.mark.parametrize("lens_kind", ["mixed", "short_many", "equal"])
-def test_balanced_split(lens_kind):
+BALANCED_SHAPES = [(16, 128, 56, O.BF16), (32, 128, 32, O.BF16), (4, 16, 4, O.F32)]
+
+
+def balanced_lens(kind):
+    g = np.random.default_rng(120)
+    if kind == "mixed":  # zero, one, page edges, long and short requests
+        return [0, 1, 15, 16, 17, 300, 1000, 33] + g.integers(0, 700, 16).tolist()
+    if kind == "short_many":  # 100 requests of 3 pages: ranges of 1-2 pages
+        return [48] * 100
+    if kind == "equal":  # 20 x 700 tokens: about 55 pages a range
+        return [700] * 20
+    if kind == "few_pages_100":  # 16 x 7 pages = 112 pages, fewer than the 256 ranges
+        return [100] * 16
+    if kind == "few_pages_48":  # 16 x 3 pages = 48 pages
+        return [48] * 16
+    if kind == "few_pages_ragged":  # 20 requests, 0..3 pages each, some empty
+        return [0, 1, 17, 48, 0, 33, 16, 2, 47, 0, 5, 31, 32, 18, 0, 9, 40, 1, 16, 3]
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("shape", BALANCED_SHAPES, ids=["h16r56", "h32r32", "h4r4f32"])
+@pytest.mark.parametrize("lens_kind", ["mixed", "short_many", "equal", "few_pages_100",
+                                       "few_pages_48", "few_pages_ragged"])
+def test_balanced_split(shape, lens_kind):
     """Automatic splits of 16 or more single-row requests cut the batch's pages into equal
     ranges per workgroup; ranges cross request boundaries (one segment and record per
-    request met), requests of 0 tokens own no pages.  Every output against the oracle, and
-    against the chunked split (explicit chunk_tokens) within the same bar."""
-    g = np.random.default_rng(120)
-    if lens_kind == "mixed":
-        lens = [0, 1, 15, 16, 17, 300, 1000, 33] + g.integers(0, 700, 16).tolist()
-    elif lens_kind == "short_many":  # 100 requests of 3 pages: ranges of 1-2 pages
-        lens = [48] * 100
-    else:  # 20 x 700 tokens: about 55 pages a range, several requests per range edge
-        lens = [700] * 20
-    log(f"balanced split, {len(lens)} requests, {sum(lens)} tokens ({lens_kind})")
-    case = iid_case(121 + len(lens), 16, 128, 56, O.BF16, lens, permute=True, fill=0x7FC0)
+    request met), requests of 0 tokens own no pages, and a batch of fewer pages than
+    workgroups gets one range per page.  The workspace starts as NaN bytes, so a merged
+    record the split did not write shows.  Every output against the oracle, and against
+    the chunked split (explicit chunk_tokens) within the same bar."""
+    H, dh, r, dt = shape
+    lens = balanced_lens(lens_kind)
+    nan_fill = 0x7FC0 if dt == O.BF16 else 0x7FC00000
+    log(f"balanced split {shape}, {len(lens)} requests, {sum(lens)} tokens ({lens_kind})")
+    case = iid_case(121 + len(lens) + H, H, dh, r, dt, lens, permute=True, fill=nan_fill)
     got = case.run_f64()
     ref = case.reference()
     for b, t in enumerate(lens):
         if t == 0:
             assert np.all(got[b] == 0.0)
     live = np.array(lens) > 0
-    check(case, got[live], ref[live], what=f"balanced {lens_kind}")
+    check(case, got[live], ref[live], what=f"balanced {shape} {lens_kind}")
     chunked = case.run_f64(chunk_tokens=64)
-    check(case, chunked[live], ref[live], what=f"chunked {lens_kind}")
+    check(case, chunked[live], ref[live], what=f"chunked {shape} {lens_kind}")
 
 
 def test_c3_shape_small():
@@ -201,3 +221,39 @@ def test_multi_row_queries_causal(shape):
     case = iid_case(109, H, dh, r, dt, [40, 7, 16], q_len=5, permute=True,
                     fill=0x7FC0 if dt == O.BF16 else 0x7FC00000)
     check(case, case.run_f64(chunk_tokens=16), case.reference(), what=f"multi-row {shape}")
+
+
+@pytest.mark.parametrize("shape", [(16, 128, 56, O.BF16), (32, 128, 32, O.BF16)])
+def test_near_cancelling_shared_and_private(shape):
+    """LRKV notes §9 asks for small inputs where the shared key and the private correction
+    nearly cancel.  Head 0's shared rows are set to -R[0] B[0]^T plus a small term (keys and
+    values alike), so its full keys and values are ~1/100 of either branch; the factored
+    sums cancel in float32.  Bar: 1e-2 of max|ref| over all outputs, and also over head 0's
+    own outputs alone (a hundred times smaller)."""
+    H, dh, r, dt = shape
+    lens = [300, 1000, 17]
+    g = np.random.default_rng(140 + H)
+    L = O.Layout(H, dh, r, 16, dt)
+    n = sum(lens)
+    bf = lambda x: O.round_to_dtype(np.asarray(x, np.float64), dt)
+    RK = bf(g.standard_normal((n, H, r)))
+    RV = bf(g.standard_normal((n, H, r)))
+    BK = bf(g.standard_normal((H, dh, r)) / np.sqrt(r))
+    BV = bf(g.standard_normal((H, dh, r)) / np.sqrt(r))
+    SK = bf(-RK[:, 0] @ BK[0].T + 0.01 * g.standard_normal((n, dh)))
+    SV = bf(-RV[:, 0] @ BV[0].T + 0.01 * g.standard_normal((n, dh)))
+    table, npg = synth.page_assignment(141, lens, 16, True)
+    enc = lambda a: O.f64_to_bf16_bits(a)
+    pool = O.pack_pool(L, table, lens, enc(SK), enc(SV), enc(RK), enc(RV), npg, fill=0x7FC0)
+    q = synth.queries(142, len(lens), 1, H, dh)
+    case = Case(L, pool, table, lens, as_codes(q, dt), enc(BK), enc(BV), npg)
+    ref = case.reference()
+    k0 = O.reconstruct(SK, np.transpose(RK, (1, 0, 2))[:1], BK[:1])[0]
+    assert np.abs(k0).max() < 0.1 * np.abs(SK).max()  # the cancellation is real
+    for chunk in (0, 16):
+        got = case.run_f64(chunk_tokens=chunk)
+        check(case, got, ref, what=f"near-cancel {shape} chunk {chunk}, all heads")
+        err0 = max_rel_err(got[:, :, 0], ref[:, :, 0])
+        log(f"near-cancel {shape} chunk {chunk}: head 0 alone max rel err {err0:.3e}, "
+            f"max|ref| {np.abs(ref[:, :, 0]).max():.2e} vs {np.abs(ref).max():.2e} overall")
+        assert err0 <= tolerance(dt)

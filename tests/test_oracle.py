@@ -402,7 +402,19 @@ def test_cost_models():
     for row in g["tp_replication"]:
         assert _pct(O.tp_replicated_ratio(row["P"], row["H"], row["r"], row["d_h"]), 1) == \
             row["percent"]
-    assert O.roofline_time(8e9, 1e12, 8e12, 1e15) == 1e-3
+
+
+def test_roofline_time_takes_the_larger_term():
+    """t >= max(bytes / bandwidth, flops / rate) (LRKV notes §4): with unequal terms the
+    bound is the larger one, whichever it is (a min, a sum or a swapped pair fails)."""
+    # bandwidth-bound: 1.6e9 B at 8e12 B/s = 0.2 ms against 1e11 FLOP at 2.5e15/s = 0.04 ms
+    assert O.roofline_time(1.6e9, 1e11, 8e12, 2.5e15) == pytest.approx(2e-4, rel=1e-15)
+    # compute-bound: 8e8 B = 0.1 ms against 1e12 FLOP = 0.4 ms
+    assert O.roofline_time(8e8, 1e12, 8e12, 2.5e15) == pytest.approx(4e-4, rel=1e-15)
+    # the workload's own numbers: 134,217,728 B at 8 TB/s is 16.78 us; 389,545,984 FLOP at
+    # 157.3 TFLOP/s is 2.48 us, so the bytes decide
+    assert O.roofline_time(134217728, 389545984, 8e12, 157.3e12) == pytest.approx(
+        134217728 / 8e12, rel=1e-15)
 
 
 @pytest.mark.parametrize("shape", [(4, 16, 4, O.F32), (16, 128, 56, O.BF16),
@@ -571,3 +583,79 @@ def test_append_rne_ties():
     rows = O.gather_request(got, L, table[0], 2)
     assert rows["SK"][:, 0].tolist() == [256.0, 260.0]
     assert rows["RV"][0, :, 7].tolist() == [256.0, 260.0]
+
+
+# --------------------------------------------------------------------------------------
+# planted mistakes in the oracle itself (on the CPU): each must make a pin above fail
+# --------------------------------------------------------------------------------------
+
+
+def _drop_private(S, R, Bm):
+    S = np.asarray(S, np.float64)
+    return np.broadcast_to(S[None], (np.shape(R)[0],) + S.shape).copy()
+
+
+def _untransposed_basis(S, R, Bm):
+    return np.asarray(S, np.float64)[None] + np.matmul(np.asarray(R, np.float64),
+                                                       np.asarray(Bm, np.float64))
+
+
+def test_full_rank_random_basis_matches_full_projection():
+    """r = d_h with a random (non-symmetric) basis: the oracle over the factored cache equals
+    textbook attention over keys and values projected straight through W_h = W_S + U_h B_h^T
+    (eq 2), so an oracle that applied B_h instead of B_h^T would miss."""
+    H, d_h, d, n = 2, 8, 24, 19
+    w = synth.projection_weights(90, d, H, d_h, d_h, with_wq=True)
+    X = synth.activations(91, n, d).astype(np.float64)
+    L = O.Layout(H, d_h, d_h, 16, O.F32)
+    SK, SV, RK, RV = O.project_rows(X, w["W_SK"], w["W_SV"], w["U_K"], w["U_V"])
+    f32 = lambda a: np.ascontiguousarray(a, np.float32).view(np.uint32)
+    table, npg = synth.page_assignment(92, [n], 16, True)
+    pool = O.pack_pool(L, table, [n], f32(SK), f32(SV), f32(RK), f32(RV), npg)
+    rnd = lambda a: np.asarray(a, np.float32).astype(np.float64)
+    q = X[-1] @ w["W_q"].astype(np.float64)
+    q = q.reshape(1, 1, H, d_h)
+    out = O.decode_reference(L, q, w["B_K"], w["B_V"], pool, table, [n])
+    # keys and values straight from the stored (float32) factors and the full per-head weight
+    for h in range(H):
+        K = rnd(SK) + rnd(RK[:, h]) @ w["B_K"][h].astype(np.float64).T
+        V = rnd(SV) + rnd(RV[:, h]) @ w["B_V"][h].astype(np.float64).T
+        assert rel_err(out[0, 0, h], sdpa(q[0, 0, h], K, V)) < 1e-12
+    # and the factors themselves equal the projection through W_h (eq 2-5)
+    Kfull = O.full_projection_kv(X, w["W_SK"], w["U_K"], w["B_K"])
+    Kfac = O.reconstruct(SK, np.transpose(RK, (1, 0, 2)), w["B_K"])
+    assert rel_err(Kfac, Kfull) < 1e-12
+
+
+def test_mutant_dropped_private_term_fails(monkeypatch):
+    """Planted mistake: reconstruct returns the shared rows only.  The worked example's full
+    key (5, -1) and the full-rank pin must both fail."""
+    monkeypatch.setattr(O, "reconstruct", _drop_private)
+    with pytest.raises(AssertionError):
+        test_worked_example_scores()
+    with pytest.raises(AssertionError):
+        test_full_rank_random_basis_matches_full_projection()
+
+
+def test_mutant_untransposed_basis_fails(monkeypatch):
+    """Planted mistake: R_h B_h instead of R_h B_h^T.  With r < d_h the shapes do not even
+    agree; with r = d_h (a square, non-symmetric basis) the full-rank pin must fail."""
+    monkeypatch.setattr(O, "reconstruct", _untransposed_basis)
+    with pytest.raises((AssertionError, ValueError)):
+        test_factored_rows_equal_full_projection()
+    with pytest.raises(AssertionError):
+        test_full_rank_random_basis_matches_full_projection()
+
+
+def test_mutant_wrong_slot_index_fails(monkeypatch):
+    """Planted mistake: token slot t placed at slot t + 1 (mod P) inside each chunk column.
+    The hand-worked byte map must fail (the page walk and the packer share the rule, so
+    their round trip alone could not see it)."""
+    good = O.in_block_index
+
+    def shifted(L, width, t, k):
+        return good(L, width, (np.asarray(t) + 1) % L.page_size, k)
+
+    monkeypatch.setattr(O, "in_block_index", shifted)
+    with pytest.raises(AssertionError):
+        test_page_layout_byte_map()
