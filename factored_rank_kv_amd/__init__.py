@@ -24,6 +24,7 @@ LRKV_OK = 0
 LRKV_ERR_INVALID_ARG = -1
 LRKV_ERR_UNSUPPORTED = -2
 LRKV_ERR_HIP = -3
+LRKV_ERR_SCRATCH = -4
 
 
 class lrkv_layout(ctypes.Structure):
@@ -67,6 +68,8 @@ def _load():
     lib.lrkv_decode_workspace_bytes.restype = SZ
     lib.lrkv_decode.argtypes = [LP, P, I32, I32, P, P, P, P, I32, P, I32, I32, P, P, SZ, P]
     lib.lrkv_decode.restype = ctypes.c_int
+    lib.lrkv_decode_noalloc.argtypes = [LP, P, I32, I32, P, P, P, P, I32, P, I32, I32, P, P]
+    lib.lrkv_decode_noalloc.restype = ctypes.c_int
     lib.lrkv_check_indices.argtypes = [LP, P, I32, I32, P, I32, P, P, I32, I64, P, P]
     lib.lrkv_check_indices.restype = ctypes.c_int
     lib.lrkv_status_string.argtypes = [ctypes.c_int]
@@ -76,7 +79,7 @@ def _load():
 
 
 EXPORTS = ("lrkv_page_bytes", "lrkv_append", "lrkv_decode_workspace_bytes", "lrkv_decode",
-           "lrkv_check_indices", "lrkv_status_string")
+           "lrkv_decode_noalloc", "lrkv_check_indices", "lrkv_status_string")
 
 
 def library():
@@ -148,6 +151,18 @@ def lrkv_decode(layout, q, batch, q_len, B_K, B_V, pool, page_table, max_pages_p
                              workspace_bytes, _stream(stream))
     if check and st != LRKV_OK:
         raise LRKVError(st, "lrkv_decode")
+    return st
+
+
+def lrkv_decode_noalloc(layout, q, batch, q_len, B_K, B_V, pool, page_table, max_pages_per_req,
+                        seq_lens, max_seq_len, chunk_tokens, out, stream=None,
+                        check=True) -> int:
+    st = _load().lrkv_decode_noalloc(_layout(layout), _ptr(q), batch, q_len, _ptr(B_K),
+                                     _ptr(B_V), _ptr(pool), _ptr(page_table), max_pages_per_req,
+                                     _ptr(seq_lens), max_seq_len, chunk_tokens, _ptr(out),
+                                     _stream(stream))
+    if check and st != LRKV_OK:
+        raise LRKVError(st, "lrkv_decode_noalloc")
     return st
 
 

@@ -5,8 +5,17 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/lrkv.h"
 #include "lrkv_launch.h"
+
+// Fixed scratch of lrkv_decode_noalloc: one array per GPU, in the library's device code, held
+// until the process ends.  On the host, `scratch` names a host-side stand-in, not device
+// memory: its device address on a GPU is found once per device by hipGetSymbolAddress (with
+// that device current) and only that address is ever passed to a kernel or copy.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -121,6 +130,91 @@ DecodeSizes decode_sizes(const lrkv_layout* L, int batch, int q_len, int max_seq
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LRKV_OK : LRKV_ERR_HIP; }
 
+// Host-side checks of a decode call (everything but the workspace); fills the split sizes.
+int decode_check(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_len,
+                 const void* B_K, const void* B_V, const void* pool, const int32_t* page_table,
+                 int32_t max_pages_per_req, const int32_t* seq_lens, int32_t max_seq_len,
+                 int32_t chunk_tokens, void* out, DecodeSizes* z) {
+  if (!layout_valid(L)) return LRKV_ERR_INVALID_ARG;
+  if (batch <= 0 || q_len <= 0 || max_pages_per_req <= 0 || max_seq_len < 0)
+    return LRKV_ERR_INVALID_ARG;
+  if (batch > 65535 || q_len > 65535) return LRKV_ERR_INVALID_ARG;
+  if ((long long)max_seq_len > (long long)max_pages_per_req * L->page_size)
+    return LRKV_ERR_INVALID_ARG;
+  if (chunk_tokens < 0 || chunk_tokens % L->page_size || chunk_tokens > kMaxChunkTokens)
+    return LRKV_ERR_INVALID_ARG;
+  if (!q || !B_K || !B_V || !pool || !page_table || !seq_lens || !out)
+    return LRKV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(B_K) || !aligned16(B_V) || !aligned16(pool) ||
+      !aligned16(page_table) || !aligned16(seq_lens) || !aligned16(out))
+    return LRKV_ERR_INVALID_ARG;
+  if (find_variant(L) == V_NONE) return LRKV_ERR_UNSUPPORTED;
+  *z = decode_sizes(L, batch, q_len, max_seq_len, chunk_tokens);
+  if (z->n_split > 65535) return LRKV_ERR_INVALID_ARG;
+  // one-dimensional grids of the split and merge kernels (rounded up to 8 blocks)
+  if ((long long)batch * q_len * (z->n_split > L->num_heads ? z->n_split : L->num_heads) >
+      0x7fffffffLL - 8)
+    return LRKV_ERR_INVALID_ARG;
+  return LRKV_OK;
+}
+
+// Launches of a checked decode call on `workspace` (at least z.total bytes, 256-aligned).
+int decode_launch(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_len,
+                  const void* B_K, const void* B_V, const void* pool, const int32_t* page_table,
+                  int32_t max_pages_per_req, const int32_t* seq_lens, void* out,
+                  void* workspace, const DecodeSizes& z, void* stream) {
+  DecodeArgs a{};
+  a.q = q;
+  a.batch = batch;
+  a.q_len = q_len;
+  a.B_K = B_K;
+  a.B_V = B_V;
+  a.pool = pool;
+  a.page_table = page_table;
+  a.max_pages = max_pages_per_req;
+  a.seq_lens = seq_lens;
+  a.n_split = z.n_split;
+  a.chunk = z.chunk;
+  a.groups = z.groups;
+  a.out = out;
+  a.part_ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + z.p_bytes);
+  a.stream = static_cast<hipStream_t>(stream);
+  switch (find_variant(L)) {
+    case V_C0: return hip_status(launch_decode<ShapeC0>(a));
+    case V_C1: return hip_status(launch_decode<ShapeC1>(a));
+    case V_C3: return hip_status(launch_decode<ShapeC3>(a));
+    default: return LRKV_ERR_UNSUPPORTED;
+  }
+}
+
+// ---- fixed scratch of the no-allocation decode (the array is declared above the namespace)
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // device address of `scratch`, per device, once found
+
+int scratch_address(hipStream_t stream, void** ws) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return LRKV_ERR_HIP;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t sd = 0;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return LRKV_ERR_HIP;
+    dev = (int)sd;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return LRKV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return LRKV_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) return LRKV_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *ws = g_scratch_dev[dev];
+  return LRKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -137,6 +231,9 @@ const char* lrkv_status_string(int status) {
     case LRKV_ERR_INVALID_ARG: return "LRKV_ERR_INVALID_ARG: invalid argument";
     case LRKV_ERR_UNSUPPORTED: return "LRKV_ERR_UNSUPPORTED: no kernel variant for this shape";
     case LRKV_ERR_HIP: return "LRKV_ERR_HIP: HIP runtime error at launch";
+    case LRKV_ERR_SCRATCH:
+      return "LRKV_ERR_SCRATCH: the call needs more workspace than the 16 MiB fixed scratch of "
+             "lrkv_decode_noalloc holds (use lrkv_decode with a caller workspace)";
     default: return "LRKV: unknown status";
   }
 }
@@ -154,52 +251,31 @@ int lrkv_decode(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_le
                 int32_t max_pages_per_req, const int32_t* seq_lens, int32_t max_seq_len,
                 int32_t chunk_tokens, void* out, void* workspace, size_t workspace_bytes,
                 void* stream) {
-  if (!layout_valid(L)) return LRKV_ERR_INVALID_ARG;
-  if (batch <= 0 || q_len <= 0 || max_pages_per_req <= 0 || max_seq_len < 0)
-    return LRKV_ERR_INVALID_ARG;
-  if (batch > 65535 || q_len > 65535) return LRKV_ERR_INVALID_ARG;
-  if ((long long)max_seq_len > (long long)max_pages_per_req * L->page_size)
-    return LRKV_ERR_INVALID_ARG;
-  if (chunk_tokens < 0 || chunk_tokens % L->page_size || chunk_tokens > kMaxChunkTokens)
-    return LRKV_ERR_INVALID_ARG;
-  if (!q || !B_K || !B_V || !pool || !page_table || !seq_lens || !out || !workspace)
-    return LRKV_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(B_K) || !aligned16(B_V) || !aligned16(pool) ||
-      !aligned16(page_table) || !aligned16(seq_lens) || !aligned16(out))
-    return LRKV_ERR_INVALID_ARG;
-  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return LRKV_ERR_INVALID_ARG;
-  const Variant v = find_variant(L);
-  if (v == V_NONE) return LRKV_ERR_UNSUPPORTED;
-  const DecodeSizes z = decode_sizes(L, batch, q_len, max_seq_len, chunk_tokens);
+  DecodeSizes z{};
+  const int st = decode_check(L, q, batch, q_len, B_K, B_V, pool, page_table, max_pages_per_req,
+                              seq_lens, max_seq_len, chunk_tokens, out, &z);
+  if (st != LRKV_OK) return st;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return LRKV_ERR_INVALID_ARG;
   if (workspace_bytes < z.total) return LRKV_ERR_INVALID_ARG;
-  if (z.n_split > 65535) return LRKV_ERR_INVALID_ARG;
-  // one-dimensional grids of the split and merge kernels (rounded up to 8 blocks)
-  if ((long long)batch * q_len * (z.n_split > L->num_heads ? z.n_split : L->num_heads) >
-      0x7fffffffLL - 8)
-    return LRKV_ERR_INVALID_ARG;
+  return decode_launch(L, q, batch, q_len, B_K, B_V, pool, page_table, max_pages_per_req,
+                       seq_lens, out, workspace, z, stream);
+}
 
-  DecodeArgs a{};
-  a.q = q;
-  a.batch = batch;
-  a.q_len = q_len;
-  a.B_K = B_K;
-  a.B_V = B_V;
-  a.pool = pool;
-  a.page_table = page_table;
-  a.max_pages = max_pages_per_req;
-  a.seq_lens = seq_lens;
-  a.n_split = z.n_split;
-  a.chunk = z.chunk;
-  a.groups = z.groups;
-  a.out = out;
-  a.part_ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + z.p_bytes);
-  a.stream = static_cast<hipStream_t>(stream);
-  switch (v) {
-    case V_C0: return hip_status(launch_decode<ShapeC0>(a));
-    case V_C1: return hip_status(launch_decode<ShapeC1>(a));
-    case V_C3: return hip_status(launch_decode<ShapeC3>(a));
-    default: return LRKV_ERR_UNSUPPORTED;
-  }
+int lrkv_decode_noalloc(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_len,
+                        const void* B_K, const void* B_V, const void* pool,
+                        const int32_t* page_table, int32_t max_pages_per_req,
+                        const int32_t* seq_lens, int32_t max_seq_len, int32_t chunk_tokens,
+                        void* out, void* stream) {
+  DecodeSizes z{};
+  const int st = decode_check(L, q, batch, q_len, B_K, B_V, pool, page_table, max_pages_per_req,
+                              seq_lens, max_seq_len, chunk_tokens, out, &z);
+  if (st != LRKV_OK) return st;
+  if (z.total > kScratchBytes) return LRKV_ERR_SCRATCH;  // before any device call
+  void* ws = nullptr;
+  const int sst = scratch_address(static_cast<hipStream_t>(stream), &ws);
+  if (sst != LRKV_OK) return sst;
+  return decode_launch(L, q, batch, q_len, B_K, B_V, pool, page_table, max_pages_per_req,
+                       seq_lens, out, ws, z, stream);
 }
 
 int lrkv_append(const lrkv_layout* L, const void* X, int32_t n_rows, int32_t d,

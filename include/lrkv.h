@@ -70,7 +70,9 @@ enum {
   LRKV_OK = 0,
   LRKV_ERR_INVALID_ARG = -1, /* null / misaligned pointer, bad size, workspace too small */
   LRKV_ERR_UNSUPPORTED = -2, /* (H, d_h, r, dtype, P) without a kernel variant          */
-  LRKV_ERR_HIP = -3          /* the HIP runtime reported an error at launch            */
+  LRKV_ERR_HIP = -3,         /* the HIP runtime reported an error at launch            */
+  LRKV_ERR_SCRATCH = -4      /* lrkv_decode_noalloc: the call needs more than its fixed */
+                             /* scratch holds                                           */
 };
 
 /* Description of the cache.  Physical rank = logical rank: no padding of r (LRKV notes §4
@@ -165,6 +167,25 @@ int lrkv_decode(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_le
                 int32_t max_pages_per_req, const int32_t* seq_lens, int32_t max_seq_len,
                 int32_t chunk_tokens, void* out, void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/* lrkv_decode without a workspace argument, for callers that cannot allocate device memory
+ * for it (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, semantics and kernels as lrkv_decode, minus workspace and
+ * workspace_bytes: the split partials go to a fixed scratch array of 16 MiB (16,777,216
+ * bytes) compiled into the library, one per GPU, held by each GPU the library runs on until
+ * the process ends.  Nothing is allocated or freed by this call.
+ *  - A call whose lrkv_decode_workspace_bytes(...) exceeds 16 MiB returns LRKV_ERR_SCRATCH
+ *    before touching the device (at B=8, T=4096 with the automatic split: 3 MiB).
+ *  - Every call on one GPU uses that GPU's one array, which keeps the last call's contents
+ *    (nothing in it needs to start at any value).  Calls that may overlap on one GPU (other
+ *    streams, other host threads) race on it and must be ordered by the caller.
+ *  - The first call on a GPU looks up the array's device address on that GPU (the device
+ *    of `stream`, else the current device) and keeps it for the process. */
+int lrkv_decode_noalloc(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_len,
+                        const void* B_K, const void* B_V, const void* pool,
+                        const int32_t* page_table, int32_t max_pages_per_req,
+                        const int32_t* seq_lens, int32_t max_seq_len, int32_t chunk_tokens,
+                        void* out, void* stream);
 
 /* Counts the device-side index values that lrkv_append and lrkv_decode trust without
  * checking them (they read them on the device; a check there would need a

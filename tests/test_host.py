@@ -121,6 +121,24 @@ def test_decode_rejects_bad_arguments_before_launch():
     assert decode_status(F.lrkv_layout(16, 128, 56, 16, F.LRKV_F32)) == unsupported
 
 
+def test_decode_noalloc_rejects_before_any_device_call():
+    """Argument errors and calls whose partials exceed the fixed 16 MiB scratch are refused
+    on the host (no GPU here: a device call would fail with LRKV_ERR_HIP instead)."""
+    def st(**over):
+        args = dict(q=FAKE, batch=8, q_len=1, B_K=FAKE, B_V=FAKE, pool=FAKE, page_table=FAKE,
+                    max_pages_per_req=256, seq_lens=FAKE, max_seq_len=4096, chunk_tokens=16,
+                    out=FAKE)
+        args.update(over)
+        return F.lrkv_decode_noalloc(C1, check=False, stream=0, **args)
+
+    # 8 requests x 256 chunks x 16 heads x 752 B = 24 MiB of partials
+    assert F.lrkv_decode_workspace_bytes(C1, 8, 1, 4096, 16) > 16 << 20
+    assert st() == F.LRKV_ERR_SCRATCH
+    assert st(q=None) == F.LRKV_ERR_INVALID_ARG
+    assert st(chunk_tokens=24) == F.LRKV_ERR_INVALID_ARG
+    assert F.lrkv_status_string(F.LRKV_ERR_SCRATCH).startswith("LRKV_ERR_SCRATCH")
+
+
 def append_status(lay=C1, **over):
     args = dict(X=FAKE, n_rows=4, d=2048, W_SK=FAKE, W_SV=FAKE, U_K=FAKE, U_V=FAKE,
                 row_req=FAKE, row_pos=FAKE, page_table=FAKE, max_pages_per_req=4, pool=FAKE,
@@ -163,7 +181,8 @@ def test_check_indices_rejects_bad_arguments_before_launch():
 
 
 def test_status_strings():
-    for st in (F.LRKV_OK, F.LRKV_ERR_INVALID_ARG, F.LRKV_ERR_UNSUPPORTED, F.LRKV_ERR_HIP):
+    for st in (F.LRKV_OK, F.LRKV_ERR_INVALID_ARG, F.LRKV_ERR_UNSUPPORTED, F.LRKV_ERR_HIP,
+               F.LRKV_ERR_SCRATCH):
         assert F.lrkv_status_string(st).startswith("LRKV")
     with pytest.raises(F.LRKVError) as e:
         F.lrkv_decode(C1, None, 1, 1, FAKE, FAKE, FAKE, FAKE, 1, FAKE, 16, 0, FAKE, FAKE, 1 << 20,
