@@ -459,6 +459,84 @@ def full_projection_kv(X, W_S, U, Bm):
 
 
 # ---------------------------------------------------------------------------------------
+# Rotary position encoding over the factored cache (LRKV notes §8, "can RoPE's rotation pass
+# through the low-rank basis").  The rotation D_j of position j acts on the row vector of a
+# key: feature pairs (2m, 2m+1) turn by the angle whose cosine and sine are the table's
+# entry (j, m):  (x_2m, x_2m+1) D = (x_2m c - x_2m+1 s,  x_2m s + x_2m+1 c).  The key at
+# position j is the reconstructed key turned by D_j, k_j = (s_j + z_j B_h^T) D_j; the query
+# comes already turned at its own position (q~).  The cache holds the unrotated rows.
+# ---------------------------------------------------------------------------------------
+
+
+def rotate_rows(X: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """Row vectors X [n, d] turned pair by pair: row i, pair m by (cos[i, m], sin[i, m])."""
+    X = np.asarray(X, np.float64)
+    c = np.asarray(cos, np.float64)
+    s = np.asarray(sin, np.float64)
+    out = np.empty_like(X)
+    out[:, 0::2] = X[:, 0::2] * c - X[:, 1::2] * s
+    out[:, 1::2] = X[:, 0::2] * s + X[:, 1::2] * c
+    return out
+
+
+def rope_keys(S, R, Bm, cos, sin) -> np.ndarray:
+    """Full rotated keys of a history, by the plain definition: reconstruct every head's
+    keys S + R_h B_h^T (eq 2-5), then turn row j by D_j.
+
+    S [T, d_h]; R [H, T, r]; Bm [H, d_h, r]; cos, sin [T, d_h/2] (row j: position j)."""
+    K = reconstruct(S, R, Bm)
+    return np.stack([rotate_rows(K[h], cos, sin) for h in range(K.shape[0])])
+
+
+def decode_reference_rope(L: Layout, q, B_K, B_V, pool, page_table, seq_lens, rope_cs,
+                          sample=None):
+    """Expected output of the rotary decode: textbook attention of the turned query q~ over
+    the turned keys (S_K[j] + R_K[h, j] B_K[h]^T) D_j, values unrotated.
+
+    rope_cs [rows, d_h/2, 2] holds (cos, sin) of position j at row j.  Other arguments as
+    in `decode_reference`."""
+    q = np.asarray(q, np.float64)
+    Bn, q_len, H, dh = q.shape
+    cs = np.asarray(rope_cs, np.float64)
+    out = np.full((Bn, q_len, H, dh), np.nan)
+    want = {}
+    if sample is None:
+        for b in range(Bn):
+            want[b] = {(i, h) for i in range(q_len) for h in range(H)}
+    else:
+        for b, i, h in sample:
+            want.setdefault(int(b), set()).add((int(i), int(h)))
+    scale = 1.0 / math.sqrt(dh)
+    BK = np.asarray(B_K, np.float64)
+    BV = np.asarray(B_V, np.float64)
+    for b, items in sorted(want.items()):
+        T = int(seq_lens[b])
+        SK, SV = gather_shared(pool, L, page_table[b], T)
+        for h in sorted({h for _, h in items}):
+            RK, RV = gather_private(pool, L, page_table[b], T, h)
+            K = rope_keys(SK, RK[None], BK[h:h + 1], cs[:T, :, 0], cs[:T, :, 1])[0]
+            V = reconstruct(SV, RV[None], BV[h:h + 1])[0]
+            for i, hh in sorted(items):
+                if hh != h:
+                    continue
+                n = visible_count(T, q_len, i)
+                out[b, i, h] = softmax_attention(q[b, i, h], K[:n], V[:n], scale)
+    return out
+
+
+def rope_scores_per_position(q_rot, S, R_h, B_h, cos, sin) -> np.ndarray:
+    """Second coding of the rotary scores, used only to check `rope_keys`: the page's exact
+    path with a private query formed anew for every key position,
+        score_j = (q~ D_j^T) . s_j + ((q~ D_j^T) B_h) . z_j,
+    D_j^T being the turn by the opposite angle.  Unscaled; S [T, d_h], R_h [T, r]."""
+    q_rot = np.asarray(q_rot, np.float64)
+    T = np.shape(S)[0]
+    qj = rotate_rows(np.broadcast_to(q_rot, (T, q_rot.shape[0])), cos, -np.asarray(sin))
+    p = qj @ np.asarray(B_h, np.float64)  # one private query per position
+    return np.sum(qj * np.asarray(S, np.float64), axis=1) + np.sum(p * np.asarray(R_h, np.float64), axis=1)
+
+
+# ---------------------------------------------------------------------------------------
 # Blockwise online softmax and the merge of partial results (LRKV notes §3, the fused
 # blockwise paragraph after Algorithm 2: running max, exp-sum and two value accumulators,
 # all rescaled by one factor when the max moves; division by the exp-sum at the end)

@@ -150,3 +150,14 @@ def page_assignment(seed: int, lens, page_size: int, permute: bool):
         table[b, :n] = ids[off:off + n]
         off += n
     return table, max(total, 1)
+
+
+def rope_table(n_pos: int, d_h: int, base: float = 10000.0) -> np.ndarray:
+    """Rotary table [n_pos, d_h/2, 2] float32: (cos, sin) of the angle j * base^(-2m/d_h)
+    for position j and feature pair m (the usual rotary frequencies; the factored-cache
+    method takes whatever table the model was trained with).  Angles in float64, then
+    rounded to float32; the table itself is the input both sides read."""
+    j = np.arange(n_pos, dtype=np.float64)[:, None]
+    theta = base ** (-2.0 * np.arange(d_h // 2, dtype=np.float64) / d_h)
+    ang = j * theta[None, :]
+    return np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)

@@ -659,3 +659,98 @@ def test_mutant_wrong_slot_index_fails(monkeypatch):
     monkeypatch.setattr(O, "in_block_index", shifted)
     with pytest.raises(AssertionError):
         test_page_layout_byte_map()
+
+
+# --------------------------------------------------------------------------------------
+# rotary position encoding over the factored cache (LRKV notes §8)
+# --------------------------------------------------------------------------------------
+
+
+def test_rope_two_dimensional_counterexample():
+    """The page's counterexample: the exact path turns the reconstructed key to the vertical
+    axis (score 1 with a vertical query); any low-dimensional turn of the single private
+    coordinate keeps the key horizontal (score 0), whatever the turn."""
+    g = gold("rope_counterexample.json")
+    S = np.array([g["shared_key"]])
+    R = np.array([[[g["private_coordinate"]]]])
+    Bm = np.array(g["basis_column"], float).reshape(1, 2, 1)
+    c, s = g["rotation_cos_sin"]
+    K = O.rope_keys(S, R, Bm, np.array([[c]]), np.array([[s]]))[0, 0]
+    assert O.reconstruct(S, R, Bm)[0, 0].tolist() == g["reconstructed_key"]
+    assert K.tolist() == g["turned_key"]
+    q = np.array(g["query_turned"])
+    assert q @ K == g["exact_score_unscaled"]
+    sc = O.rope_scores_per_position(q, S, R[0], Bm[0], np.array([[c]]), np.array([[s]]))
+    assert sc.tolist() == [g["exact_score_unscaled"]]
+    for e in (-3.0, -1.0, 0.0, 0.5, 1.0, 7.0):  # E_j z B^T for any scalar turn E_j = e
+        low = O.reconstruct(S, R * e, Bm)[0, 0]
+        assert q @ low == g["low_dimensional_path_score_unscaled"]
+
+
+def test_rope_zero_angle_is_plain_decode():
+    L, pool, table, lens, q, BK, BV = random_case(81, 4, 16, 4, O.F32, [40, 0, 17])
+    cs = np.zeros((64, 8, 2), np.float32)
+    cs[..., 0] = 1.0
+    a = O.decode_reference_rope(L, q, BK, BV, pool, table, lens, cs)
+    b = O.decode_reference(L, q, BK, BV, pool, table, lens)
+    assert np.array_equal(a, b)
+
+
+def _complex_turn(x, cs):
+    """x [T, d] turned by complex multiplication: pair (x_2m, x_2m+1) as x_2m + i x_2m+1,
+    times cos + i sin (an independent coding of the row-vector turn)."""
+    z = torch.view_as_complex(torch.from_numpy(np.ascontiguousarray(x, np.float64)).reshape(
+        x.shape[0], -1, 2))
+    w = torch.view_as_complex(torch.from_numpy(np.asarray(cs, np.float64)))
+    return torch.view_as_real(z * w).reshape(x.shape[0], -1).numpy()
+
+
+def test_rope_full_rank_identity_basis_is_rotary_mha():
+    """r = d_h, S = 0, B = I: every head's keys are its private rows, and the rotary decode
+    equals torch's float64 attention over those rows turned by complex multiplication."""
+    H, d_h, n = 2, 8, 37
+    L = O.Layout(H, d_h, d_h, 16, O.F32)
+    g = np.random.default_rng(82)
+    RK = g.standard_normal((n, H, d_h)).astype(np.float32)
+    RV = g.standard_normal((n, H, d_h)).astype(np.float32)
+    z = np.zeros((n, d_h), np.float32)
+    table, npg = synth.page_assignment(83, [n], 16, True)
+    pool = O.pack_pool(L, table, [n], z.view(np.uint32), z.view(np.uint32),
+                       RK.view(np.uint32), RV.view(np.uint32), npg)
+    cs = synth.rope_table(48, d_h)
+    q = g.standard_normal((1, 1, H, d_h))
+    eye = np.stack([np.eye(d_h)] * H)
+    out = O.decode_reference_rope(L, q, eye, eye, pool, table, [n], cs)
+    for h in range(H):
+        K = _complex_turn(RK[:, h].astype(np.float64), cs[:n])
+        ref = sdpa(q[0, 0, h], K, RV[:, h].astype(np.float64))
+        assert rel_err(out[0, 0, h], ref) < 1e-13
+
+
+def test_rope_per_position_private_query_agrees():
+    """The page's exact path, a private query (q~ D_j^T B_h) per key position, equals the
+    turned reconstructed keys (second coding against the first), on random factors."""
+    g = np.random.default_rng(84)
+    T, d_h, r = 50, 16, 4
+    S = g.standard_normal((T, d_h))
+    R = g.standard_normal((1, T, r))
+    Bm = g.standard_normal((1, d_h, r))
+    cs = synth.rope_table(T, d_h)
+    q = g.standard_normal(d_h)
+    K = O.rope_keys(S, R, Bm, cs[:, :, 0], cs[:, :, 1])[0]
+    sc = O.rope_scores_per_position(q, S, R[0], Bm[0], cs[:, :, 0], cs[:, :, 1])
+    assert rel_err(sc, K @ q) < 1e-13
+
+
+def test_rope_mutant_low_dimensional_turn_fails(monkeypatch):
+    """Planted mistake: turning only the shared rows and leaving the private term in the
+    basis's span (the low-dimensional path the page shows to be wrong) must fail the
+    counterexample."""
+    def shared_only(S, R, Bm, cos, sin):
+        Sr = O.rotate_rows(S, cos, sin)
+        return Sr[None] + np.matmul(np.asarray(R, np.float64),
+                                    np.transpose(np.asarray(Bm, np.float64), (0, 2, 1)))
+
+    monkeypatch.setattr(O, "rope_keys", shared_only)
+    with pytest.raises(AssertionError):
+        test_rope_two_dimensional_counterexample()
