@@ -68,6 +68,11 @@ def _load():
     lib.lrkv_decode_workspace_bytes.restype = SZ
     lib.lrkv_decode.argtypes = [LP, P, I32, I32, P, P, P, P, I32, P, I32, I32, P, P, SZ, P]
     lib.lrkv_decode.restype = ctypes.c_int
+    lib.lrkv_decode_rope.argtypes = [LP, P, I32, I32, P, P, P, P, I32, P, I32, I32, P, I32, P,
+                                     P, SZ, P]
+    lib.lrkv_decode_rope.restype = ctypes.c_int
+    lib.lrkv_decode_rope_workspace_bytes.argtypes = [LP, I32, I32, I32, I32]
+    lib.lrkv_decode_rope_workspace_bytes.restype = SZ
     lib.lrkv_decode_noalloc.argtypes = [LP, P, I32, I32, P, P, P, P, I32, P, I32, I32, P, P]
     lib.lrkv_decode_noalloc.restype = ctypes.c_int
     lib.lrkv_check_indices.argtypes = [LP, P, I32, I32, P, I32, P, P, I32, I64, P, P]
@@ -79,7 +84,8 @@ def _load():
 
 
 EXPORTS = ("lrkv_page_bytes", "lrkv_append", "lrkv_decode_workspace_bytes", "lrkv_decode",
-           "lrkv_decode_noalloc", "lrkv_check_indices", "lrkv_status_string")
+           "lrkv_decode_noalloc", "lrkv_decode_rope", "lrkv_decode_rope_workspace_bytes",
+           "lrkv_check_indices", "lrkv_status_string")
 
 
 def library():
@@ -151,6 +157,24 @@ def lrkv_decode(layout, q, batch, q_len, B_K, B_V, pool, page_table, max_pages_p
                              workspace_bytes, _stream(stream))
     if check and st != LRKV_OK:
         raise LRKVError(st, "lrkv_decode")
+    return st
+
+
+def lrkv_decode_rope_workspace_bytes(layout, batch, q_len, max_seq_len, chunk_tokens) -> int:
+    return int(_load().lrkv_decode_rope_workspace_bytes(_layout(layout), batch, q_len,
+                                                         max_seq_len, chunk_tokens))
+
+
+def lrkv_decode_rope(layout, q, batch, q_len, B_K, B_V, pool, page_table, max_pages_per_req,
+                     seq_lens, max_seq_len, chunk_tokens, rope_cs, rope_rows, out, workspace,
+                     workspace_bytes, stream=None, check=True) -> int:
+    st = _load().lrkv_decode_rope(_layout(layout), _ptr(q), batch, q_len, _ptr(B_K), _ptr(B_V),
+                                  _ptr(pool), _ptr(page_table), max_pages_per_req,
+                                  _ptr(seq_lens), max_seq_len, chunk_tokens, _ptr(rope_cs),
+                                  rope_rows, _ptr(out), _ptr(workspace), workspace_bytes,
+                                  _stream(stream))
+    if check and st != LRKV_OK:
+        raise LRKVError(st, "lrkv_decode_rope")
     return st
 
 

@@ -130,6 +130,35 @@ DecodeSizes decode_sizes(const lrkv_layout* L, int batch, int q_len, int max_seq
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LRKV_OK : LRKV_ERR_HIP; }
 
+// Rotary decode: always the chunked split.  Its workgroups take 4 heads each and two fit a
+// compute unit, so for 0 the batch's padded work over 512 / (H/4) chunks, 64 to 2048
+// tokens, else the caller's multiple of P.
+DecodeSizes rope_sizes(const lrkv_layout* L, int batch, int q_len, int max_seq_len,
+                       int chunk_tokens) {
+  DecodeSizes z{};
+  const int P = L->page_size;
+  long long c = chunk_tokens;
+  if (c == 0) {
+    const long long groups = L->num_heads / 4 > 0 ? L->num_heads / 4 : 1;
+    const long long per_wave = 512 / groups > 0 ? 512 / groups : 1;
+    const long long work = (long long)batch * q_len * (long long)max_seq_len;
+    c = (work + per_wave - 1) / per_wave;
+    c = (c + P - 1) / P * P;
+    if (c < 4LL * P) c = 4LL * P;
+    if (c > kAutoChunkTokens) c = kAutoChunkTokens;
+    const long long cap = ((long long)max_seq_len + P - 1) / P * P;
+    if (c > cap && cap > 0) c = cap;
+    if (c < P) c = P;
+  }
+  z.chunk = (int)c;
+  z.n_split = max_seq_len > 0 ? (max_seq_len + z.chunk - 1) / z.chunk : 1;
+  const size_t rec = ((size_t)2 + L->head_dim + L->rank + 3) / 4 * 4;
+  z.part_bytes = align_up((size_t)batch * q_len * (size_t)z.n_split * L->num_heads * rec *
+                              sizeof(float), 256);
+  z.total = z.part_bytes;
+  return z;
+}
+
 // Host-side checks of a decode call (everything but the workspace); fills the split sizes.
 int decode_check(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_len,
                  const void* B_K, const void* B_V, const void* pool, const int32_t* page_table,
@@ -259,6 +288,54 @@ int lrkv_decode(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_le
   if (workspace_bytes < z.total) return LRKV_ERR_INVALID_ARG;
   return decode_launch(L, q, batch, q_len, B_K, B_V, pool, page_table, max_pages_per_req,
                        seq_lens, out, workspace, z, stream);
+}
+
+size_t lrkv_decode_rope_workspace_bytes(const lrkv_layout* L, int32_t batch, int32_t q_len,
+                                        int32_t max_seq_len, int32_t chunk_tokens) {
+  if (!layout_valid(L) || batch <= 0 || q_len <= 0 || max_seq_len < 0 || chunk_tokens < 0)
+    return 0;
+  if (chunk_tokens % L->page_size || chunk_tokens > kMaxChunkTokens) return 0;
+  return rope_sizes(L, batch, q_len, max_seq_len, chunk_tokens).total;
+}
+
+int lrkv_decode_rope(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_len,
+                     const void* B_K, const void* B_V, const void* pool,
+                     const int32_t* page_table, int32_t max_pages_per_req,
+                     const int32_t* seq_lens, int32_t max_seq_len, int32_t chunk_tokens,
+                     const float* rope_cs, int32_t rope_rows, void* out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  DecodeSizes z{};
+  int st = decode_check(L, q, batch, q_len, B_K, B_V, pool, page_table, max_pages_per_req,
+                        seq_lens, max_seq_len, chunk_tokens, out, &z);
+  if (st != LRKV_OK) return st;
+  if (!rope_cs || !aligned16(rope_cs) || rope_rows < max_seq_len || rope_rows <= 0)
+    return LRKV_ERR_INVALID_ARG;
+  const Variant v = find_variant(L);
+  if (v != V_C1 && v != V_C3) return LRKV_ERR_UNSUPPORTED;  // bf16 variants only
+  z = rope_sizes(L, batch, q_len, max_seq_len, chunk_tokens);
+  if (z.n_split > 65535) return LRKV_ERR_INVALID_ARG;
+  if ((long long)batch * q_len * z.n_split * (L->num_heads / 4) > 0x7fffffffLL - 8)
+    return LRKV_ERR_INVALID_ARG;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return LRKV_ERR_INVALID_ARG;
+  if (workspace_bytes < z.total) return LRKV_ERR_INVALID_ARG;
+  DecodeArgs a{};
+  a.q = q;
+  a.batch = batch;
+  a.q_len = q_len;
+  a.B_K = B_K;
+  a.B_V = B_V;
+  a.pool = pool;
+  a.page_table = page_table;
+  a.max_pages = max_pages_per_req;
+  a.seq_lens = seq_lens;
+  a.n_split = z.n_split;
+  a.chunk = z.chunk;
+  a.groups = 0;
+  a.out = out;
+  a.part_ws = static_cast<float*>(workspace);
+  a.stream = static_cast<hipStream_t>(stream);
+  if (v == V_C1) return hip_status(launch_decode_rope<ShapeC1>(a, rope_cs, rope_rows));
+  return hip_status(launch_decode_rope<ShapeC3>(a, rope_cs, rope_rows));
 }
 
 int lrkv_decode_noalloc(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_len,

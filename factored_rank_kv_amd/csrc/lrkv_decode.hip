@@ -22,25 +22,6 @@
 
 namespace lrkv {
 
-// ---------------------------------------------------------------------------------------
-// DPP reductions inside a row of 16 lanes (one head per row)
-// ---------------------------------------------------------------------------------------
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-constexpr int kQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
-constexpr int kQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
-constexpr int kHalfMirror = 0x141; // lane i <-> 7-i inside each half row
-constexpr int kMirror = 0x140;     // lane i <-> 15-i inside the row
-
-__device__ __forceinline__ float r16_max(float x) {
-  x = __builtin_fmaxf(x, dpp_f<kQuadSwap1>(x));
-  x = __builtin_fmaxf(x, dpp_f<kQuadSwap2>(x));
-  x = __builtin_fmaxf(x, dpp_f<kHalfMirror>(x));
-  x = __builtin_fmaxf(x, dpp_f<kMirror>(x));
-  return x;
-}
 // One stage of a reduce-scatter inside a 16-lane row: v[0..2n) -> v[0..n).  The DPP
 // pattern pairs each lane with a partner; the lane keeps the lower or upper half (`upper`,
 // its partner the other), sends the other half and adds the partner's copy of its own.
@@ -61,14 +42,6 @@ __device__ __forceinline__ void rs_stage(float* v, bool upper) {
 // 2 b0 = 2j and the next; each pairing joins two disjoint lane sets, so the sums cover
 // all 16 lanes.
 __device__ __forceinline__ void reduce_scatter_32(float* v, int j);
-
-__device__ __forceinline__ float r16_sum(float x) {
-  x += dpp_f<kQuadSwap1>(x);
-  x += dpp_f<kQuadSwap2>(x);
-  x += dpp_f<kHalfMirror>(x);
-  x += dpp_f<kMirror>(x);
-  return x;
-}
 
 __device__ __forceinline__ void reduce_scatter_32(float* v, int j) {
   rs_stage<kMirror, 16>(v, j >= 8);
@@ -1067,12 +1040,21 @@ hipError_t launch_decode(const DecodeArgs& a) {
     const int split_blocks = (a.batch * a.q_len * a.n_split + 7) / 8 * 8;
     hipLaunchKernelGGL((decode_split_kernel<S, false>), dim3(split_blocks),
                        dim3(SplitCfg<S>::NT), 0, a.stream, s);
-    hipLaunchKernelGGL((merge_expand_kernel<S, false>), dim3((a.batch * a.q_len * S::H + 7) / 8 * 8), dim3(256), 0,
-                       a.stream, a.part_ws, a.B_V, a.seq_lens, a.q_len, a.n_split, a.chunk,
-                       a.batch, 0, a.max_pages, a.out);
+    return launch_merge<S>(a);
   }
   return hipGetLastError();
 }
+
+template <class S>
+hipError_t launch_merge(const DecodeArgs& a) {
+  hipLaunchKernelGGL((merge_expand_kernel<S, false>), dim3((a.batch * a.q_len * S::H + 7) / 8 * 8),
+                     dim3(256), 0, a.stream, a.part_ws, a.B_V, a.seq_lens, a.q_len, a.n_split,
+                     a.chunk, a.batch, 0, a.max_pages, a.out);
+  return hipGetLastError();
+}
+
+template hipError_t launch_merge<ShapeC1>(const DecodeArgs&);
+template hipError_t launch_merge<ShapeC3>(const DecodeArgs&);
 
 template hipError_t launch_decode<ShapeC0>(const DecodeArgs&);
 template hipError_t launch_decode<ShapeC1>(const DecodeArgs&);

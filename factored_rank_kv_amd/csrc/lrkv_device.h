@@ -76,6 +76,46 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// ---- DPP reductions inside a row of 16 lanes ----------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141; // lane i <-> 7-i inside each half row
+constexpr int kMirror = 0x140;     // lane i <-> 15-i inside the row
+
+__device__ __forceinline__ float r16_max(float x) {
+  x = __builtin_fmaxf(x, dpp_f<kQuadSwap1>(x));
+  x = __builtin_fmaxf(x, dpp_f<kQuadSwap2>(x));
+  x = __builtin_fmaxf(x, dpp_f<kHalfMirror>(x));
+  x = __builtin_fmaxf(x, dpp_f<kMirror>(x));
+  return x;
+}
+__device__ __forceinline__ float r16_sum(float x) {
+  x += dpp_f<kQuadSwap1>(x);
+  x += dpp_f<kQuadSwap2>(x);
+  x += dpp_f<kHalfMirror>(x);
+  x += dpp_f<kMirror>(x);
+  return x;
+}
+
+// max over the four 16-lane rows of a wavefront (v_permlane16_swap pairs rows 0-1 and 2-3,
+// v_permlane32_swap the two halves); every lane gets the result
+__device__ __forceinline__ float rows4_max(float m) {
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  m = __builtin_fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return __builtin_fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+}
+__device__ __forceinline__ float rows4_sum(float m) {
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  m = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+}
+
 __device__ __forceinline__ float readlane_f(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }

@@ -52,6 +52,19 @@ struct AppendArgs {
 template <class S>
 hipError_t launch_decode(const DecodeArgs& a);
 
+// The merge + expansion of a chunked split's partial records (records [batch][q_len]
+// [n_split][H], chunk tokens a.chunk), on a.stream.
+template <class S>
+hipError_t launch_merge(const DecodeArgs& a);
+
+// Rotary decode (chunked split, then launch_merge); rope_cs is [rope_rows][d_h/2][2] float32.
+template <class S>
+hipError_t launch_decode_rope(const DecodeArgs& a, const float* rope_cs, int rope_rows);
+
+// Head groups (workgroups per chunk) of the rotary decode.
+template <class S>
+int rope_groups();
+
 template <class S>
 hipError_t launch_append(const AppendArgs& a);
 

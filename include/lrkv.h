@@ -168,6 +168,36 @@ int lrkv_decode(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_le
                 int32_t chunk_tokens, void* out, void* workspace, size_t workspace_bytes,
                 void* stream);
 
+/* Rotary decode: the exact path of LRKV notes §8 for a model whose keys and queries carry
+ * rotary position encoding.  Same cache, same arguments and the same output as lrkv_decode,
+ * but the key of head h at position j is the reconstructed key turned by the rotation D_j of
+ * position j, and q holds the query already turned at its own position (q~):
+ *   k_j      = (S_K[j] + R_K[h, j] B_K[h]^T) D_j
+ *   s_j      = q~ . k_j / sqrt(d_h) = ((q~ D_j^T) . S_K[j] + ((q~ D_j^T) B_K[h]) . R_K[h, j]) / sqrt(d_h)
+ *   out[b,i,h] = softmax over the visible j, applied to S_V + R_V[h] B_V[h]^T (values unturned)
+ * The cache holds unrotated rows (lrkv_append as usual).  Because D_j depends on the key
+ * position, the private query (q~ D_j^T) B_K[h] cannot be formed once (eq 6): this call forms
+ * each page's unrotated key block on the matrix cores and dots it with the query turned
+ * back by each key's angle, so it does more arithmetic than lrkv_decode.
+ * D_j turns feature pairs (2m, 2m+1) of a row vector:
+ *   (x_2m, x_2m+1) D_j = (x_2m c - x_2m+1 s,  x_2m s + x_2m+1 c),  (c, s) = rope_cs[j][m]
+ *   rope_cs    device, float32 [rope_rows][d_h/2][2], (cos, sin) of position j in row j;
+ *              rope_rows >= max_seq_len; 16-byte aligned
+ *   workspace  >= lrkv_decode_rope_workspace_bytes(...) bytes, 256-byte aligned
+ * Chunked split only (chunk_tokens 0 = automatic, else a multiple of P up to 4096), any
+ * q_len.  bf16 variants only: (16, 128, 56) and (32, 128, 32); others return
+ * LRKV_ERR_UNSUPPORTED. */
+int lrkv_decode_rope(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_len,
+                     const void* B_K, const void* B_V, const void* pool,
+                     const int32_t* page_table, int32_t max_pages_per_req,
+                     const int32_t* seq_lens, int32_t max_seq_len, int32_t chunk_tokens,
+                     const float* rope_cs, int32_t rope_rows, void* out, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Infrastructure of this library: the workspace bytes lrkv_decode_rope needs. */
+size_t lrkv_decode_rope_workspace_bytes(const lrkv_layout* L, int32_t batch, int32_t q_len,
+                                        int32_t max_seq_len, int32_t chunk_tokens);
+
 /* lrkv_decode without a workspace argument, for callers that cannot allocate device memory
  * for it (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation).  Same arguments, semantics and kernels as lrkv_decode, minus workspace and

@@ -121,6 +121,27 @@ class Case:
     def run_f64(self, **kw) -> np.ndarray:
         return from_dev(self.run(**kw), self.L.dtype)
 
+    def run_rope(self, rope_cs: np.ndarray, chunk_tokens: int = 0, ws_fill: int = 0xFF):
+        """lrkv_decode_rope on the device with the (cos, sin) table rope_cs [rows][d_h/2][2];
+        returns float64 outputs."""
+        d = self.dev
+        lay = layout_c(self.L)
+        msl = int(self.lens.max())
+        ws_bytes = F.lrkv_decode_rope_workspace_bytes(lay, self.B, self.q_len, msl, chunk_tokens)
+        assert ws_bytes > 0
+        ws = torch.full((ws_bytes,), ws_fill, dtype=torch.uint8, device=DEV)
+        out = torch.empty(self.q_codes.shape, dtype=d["q"].dtype, device=DEV)
+        cs = torch.from_numpy(np.ascontiguousarray(rope_cs, np.float32)).to(DEV)
+        F.lrkv_decode_rope(lay, d["q"], self.B, self.q_len, d["BK"], d["BV"], d["pool"],
+                           d["table"], self.table.shape[1], d["lens"], msl, chunk_tokens, cs,
+                           rope_cs.shape[0], out, ws, ws_bytes)
+        torch.cuda.synchronize()
+        return from_dev(out, self.L.dtype)
+
+    def reference_rope(self, rope_cs, sample=None) -> np.ndarray:
+        return O.decode_reference_rope(self.L, self.q64, self.BK64, self.BV64, self.pool,
+                                       self.table, self.lens, rope_cs, sample=sample)
+
     def reference(self, sample=None) -> np.ndarray:
         return O.decode_reference(self.L, self.q64, self.BK64, self.BV64, self.pool, self.table,
                                   self.lens, sample=sample)

@@ -139,6 +139,28 @@ def test_decode_noalloc_rejects_before_any_device_call():
     assert F.lrkv_status_string(F.LRKV_ERR_SCRATCH).startswith("LRKV_ERR_SCRATCH")
 
 
+def test_decode_rope_rejects_bad_arguments_before_launch():
+    def st(lay=C1, **over):
+        args = dict(q=FAKE, batch=2, q_len=1, B_K=FAKE, B_V=FAKE, pool=FAKE, page_table=FAKE,
+                    max_pages_per_req=4, seq_lens=FAKE, max_seq_len=64, chunk_tokens=0,
+                    rope_cs=FAKE, rope_rows=64, out=FAKE, workspace=FAKE,
+                    workspace_bytes=1 << 30)
+        args.update(over)
+        return F.lrkv_decode_rope(lay, check=False, stream=0, **args)
+
+    bad = F.LRKV_ERR_INVALID_ARG
+    assert st(rope_cs=None) == bad
+    assert st(rope_cs=FAKE + 4) == bad
+    assert st(rope_rows=63) == bad  # fewer table rows than positions
+    assert st(workspace_bytes=256) == bad
+    assert st(chunk_tokens=8) == bad
+    assert st(C0) == F.LRKV_ERR_UNSUPPORTED  # bf16 variants only
+    n = F.lrkv_decode_rope_workspace_bytes(C1, 8, 1, 4096, 0)
+    # 16 chunks of 256 tokens x 8 requests x 16 heads x 188 floats
+    assert n == 16 * 8 * 16 * 188 * 4
+    assert F.lrkv_decode_rope_workspace_bytes(C1, 8, 1, 4096, 24) == 0
+
+
 def append_status(lay=C1, **over):
     args = dict(X=FAKE, n_rows=4, d=2048, W_SK=FAKE, W_SV=FAKE, U_K=FAKE, U_V=FAKE,
                 row_req=FAKE, row_pos=FAKE, page_table=FAKE, max_pages_per_req=4, pool=FAKE,
