@@ -96,6 +96,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--prefill", type=int, default=1,
                     help="also time the B=4 x 8192 prefill (append + multi-query attention)")
+    ap.add_argument("--rope", type=int, default=1,
+                    help="also time the rotary decode (lrkv_decode_rope) on the same workload")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration runs)")
     args = ap.parse_args()
@@ -292,6 +294,44 @@ def main():
         "cpu_baseline": None,
     }
 
+    if args.rope:
+        # rotary decode (LRKV notes §8) on the same rotating pools and queries
+        cs = torch.from_numpy(synth.rope_table(T, dh)).to(dev)
+        rws = F.lrkv_decode_rope_workspace_bytes(lay, B, 1, T, 0)
+        rws_t = torch.empty(rws, dtype=torch.uint8, device=dev)
+
+        def rope_decode(k):
+            F.lrkv_decode_rope(lay, qd, B, 1, wd["B_K"], wd["B_V"], pools[k % len(pools)], tab,
+                               table.shape[1], lens, T, 0, cs, T, out, rws_t, rws)
+
+        for k in range(5):
+            rope_decode(k)
+        ms_rope, n_rope = timed(rope_decode, 96, use_graph)
+        rope_calls = per_call_us(rope_decode, 96)
+        pairs = B * T * H
+        # per (token, head): key block on MFMA 2 d_h r; turn + dot 4 d_h; values 2 (d_h + r) x 2
+        fl_mfma = pairs * 2 * dh * r
+        fl_valu = pairs * (4 * dh + 4 * (dh + r))
+        table_bytes = T * dh * 4
+        t_s = ms_rope * 1e-3
+        terms = {"hbm": (alg_bytes + table_bytes) / (PEAK_HBM_GBS * 1e9),
+                 "mfma": fl_mfma / (PEAK_BF16_TFLOPS * 1e12),
+                 "alu": fl_valu / (PEAK_FP32_TFLOPS * 1e12)}
+        bound = max(terms, key=terms.get)
+        result["rope_decode"] = {
+            "workload": work.name + "_rope", "call_us": round(ms_rope * 1e3, 3),
+            "call_us_p10_p50_p90": [round(float(np.percentile(rope_calls, p)), 3)
+                                    for p in (10, 50, 90)],
+            "achieved_gbs": round(alg_bytes / t_s / 1e9, 1),
+            "roofline": {"bound": bound, "terms_us": {k: round(v * 1e6, 3) for k, v in terms.items()},
+                         "frac_of_bound": round(terms[bound] / t_s, 4),
+                         "mfma_flop": fl_mfma, "valu_flop": fl_valu,
+                         "bytes": alg_bytes + table_bytes},
+        }
+        log(f"rope decode: {ms_rope * 1e3:.2f} us per call ({alg_bytes / t_s / 1e9:.0f} GB/s), "
+            f"bound {bound} {terms[bound] * 1e6:.2f} us")
+        del rws_t
+
     if args.prefill:
         result["prefill"] = prefill_bench(torch, F, synth, dev)
     if args.other_decodes:
@@ -304,6 +344,7 @@ def main():
 
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3  # MI355X fp32 vector
 
 
 def prefill_bench(torch, F, synth, dev):

@@ -139,6 +139,9 @@ class Layout:
     rank: int  # r, width of a private row R_K[h, j], R_V[h, j]
     page_size: int  # P tokens per page
     dtype: int  # F32 or BF16
+    # LRKV notes §8 (RMSNorm paragraph): one stored reciprocal of the joint key denominator
+    # per head and position, in the cache dtype, as a fifth section N[h][t] of each page
+    key_norm: bool = False
 
     @property
     def elem_bytes(self) -> int:
@@ -151,8 +154,10 @@ class Layout:
 
 
 def page_elems(L: Layout) -> int:
-    """Elements in one page: P tokens x (2 shared rows of d_h + 2H private rows of r)."""
-    return L.page_size * 2 * (L.head_dim + L.num_heads * L.rank)
+    """Elements in one page: P tokens x (2 shared rows of d_h + 2H private rows of r), plus
+    P x H key-norm reciprocals when the layout keeps them."""
+    extra = L.page_size * L.num_heads if L.key_norm else 0
+    return L.page_size * 2 * (L.head_dim + L.num_heads * L.rank) + extra
 
 
 def page_bytes(L: Layout) -> int:
@@ -174,6 +179,8 @@ def section_base(L: Layout, section: str, head: int = 0) -> int:
         return 2 * P * dh + head * P * r
     if section == "RV":
         return 2 * P * dh + H * P * r + head * P * r
+    if section == "N" and L.key_norm:  # head h's P reciprocals, token after token
+        return 2 * P * dh + 2 * H * P * r + head * P
     raise ValueError(section)
 
 
@@ -225,6 +232,15 @@ def gather_private(pool, L: Layout, table_row, n_tokens: int, h: int):
             _read_block(pool, L, pages, t, "RV", h, L.rank))
 
 
+def gather_norms(pool, L: Layout, table_row, n_tokens: int, h: int):
+    """Page walk for head h's stored key-norm reciprocals of tokens 0..n_tokens-1 [n]."""
+    pool = np.asarray(pool, dtype=np.uint8).reshape(-1)
+    pages, t = _positions_to_pages(L, table_row, n_tokens)
+    idx = pages * page_elems(L) + section_base(L, "N", h) + t
+    byte_idx = (idx[:, None] * L.elem_bytes + np.arange(L.elem_bytes)).reshape(-1)
+    return decode_elems(pool[byte_idx], L.dtype).reshape(n_tokens)
+
+
 def gather_request(pool: np.ndarray, L: Layout, table_row: np.ndarray, n_tokens: int) -> dict:
     """Page walk over every section: S_K, S_V [n, d_h] and R_K, R_V [H, n, r], float64."""
     SK, SV = gather_shared(pool, L, table_row, n_tokens)
@@ -239,7 +255,8 @@ def storage_dtype(L: Layout):
     return np.uint16 if L.dtype == BF16 else np.uint32
 
 
-def pack_pool(L: Layout, page_table, lens, SK, SV, RK, RV, num_pages: int, fill: int = 0):
+def pack_pool(L: Layout, page_table, lens, SK, SV, RK, RV, num_pages: int, fill: int = 0,
+              NR=None):
     """Bulk placement of whole requests into a fresh pool (the placement rule of
     `write_rows`, coded separately as a reshape per page so the two check each other).
 
@@ -279,6 +296,14 @@ def pack_pool(L: Layout, page_table, lens, SK, SV, RK, RV, num_pages: int, fill:
             base = 2 * P * dh
             pool[ids, base:base + H * P * r] = blocks(rk, r, H)
             pool[ids, base + H * P * r:base + 2 * H * P * r] = blocks(rv, r, H)
+        if L.key_norm and NR is not None:  # [T, H] codes -> N[h][t] of each page
+            nr = np.asarray(NR[off:off + T])
+            nr = nr.view(st) if nr.dtype != st else nr
+            padded = np.full((n_pages * P, H), fill, dtype=st)
+            padded[:T] = nr
+            base = 2 * P * dh + 2 * H * P * r
+            pool[ids, base:base + H * P] = padded.reshape(n_pages, P, H).transpose(0, 2, 1).reshape(
+                n_pages, H * P)
         off += T
     return pool.view(np.uint8).reshape(-1)
 
@@ -344,6 +369,51 @@ def append_reference(pool, L: Layout, X, W_SK, W_SV, U_K, U_V, row_req, row_pos,
 
 
 # ---------------------------------------------------------------------------------------
+# RMSNorm of the full key (LRKV notes §8, "RMSNorm has one more per-head joint quantity"):
+# the key k = s + z B_h^T is normalised by n = sqrt(|k|^2 / d_h + eps), a quantity of the
+# full key that neither branch knows alone; its reciprocal is computed when the token is
+# appended and stored per head and position, and scoring multiplies it onto the summed
+# score.  A fixed per-channel gain moves to the query side and is not the cache's concern.
+# ---------------------------------------------------------------------------------------
+
+
+def key_rms_reciprocal(s_row, z_rows, Bm, eps: float) -> np.ndarray:
+    """1 / n_h for one token: s_row [d_h], z_rows [H, r], Bm [H, d_h, r] -> [H], float64,
+    with n_h = sqrt(|s + z_h B_h^T|^2 / d_h + eps) (the full key, reconstructed)."""
+    s_row = np.asarray(s_row, np.float64)
+    K = s_row[None, :] + np.einsum("hr,hdr->hd", np.asarray(z_rows, np.float64),
+                                   np.asarray(Bm, np.float64))
+    d_h = s_row.shape[0]
+    return 1.0 / np.sqrt(np.sum(K * K, axis=1) / d_h + eps)
+
+
+def key_norms_reference(pool, L: Layout, B_K, eps: float, row_req, row_pos, page_table):
+    """Expected pool after the key-norm step of an append: for every appended row and head,
+    the reciprocal of the joint denominator of the key as stored (the row's S_K and R_K[h]
+    read back from the pool), rounded to nearest even in the cache dtype and written at
+    N[h][slot] of the row's page; every other byte keeps its value."""
+    assert L.key_norm
+    out = np.array(pool, dtype=np.uint8, copy=True).reshape(-1)
+    elems = out.view(storage_dtype(L))
+    pe = page_elems(L)
+    table = np.asarray(page_table, np.int64)
+    for req, pos in zip(np.asarray(row_req, np.int64), np.asarray(row_pos, np.int64)):
+        page = table[req, pos // L.page_size]
+        t = pos % L.page_size
+        pg, sl = np.array([page]), np.array([t])
+        src = np.asarray(pool, dtype=np.uint8).reshape(-1)
+        # the stored rows of this position, read back through the page layout
+        s_row = _read_block(src, L, pg, sl, "SK", 0, L.head_dim)[0]
+        z = np.stack([_read_block(src, L, pg, sl, "RK", h, L.rank)[0]
+                      for h in range(L.num_heads)])
+        inv = key_rms_reciprocal(s_row, z, B_K, eps)
+        for h in range(L.num_heads):
+            elems[page * pe + section_base(L, "N", h) + t] = encode_elems(
+                inv[h:h + 1], L.dtype).view(storage_dtype(L))[0]
+    return out
+
+
+# ---------------------------------------------------------------------------------------
 # Plain attention over reconstructed keys / values (LRKV notes §2 and eq 2-5)
 # ---------------------------------------------------------------------------------------
 
@@ -404,6 +474,8 @@ def decode_reference(L: Layout, q, B_K, B_V, pool, page_table, seq_lens, sample=
         for h in sorted({h for _, h in items}):
             RK, RV = gather_private(pool, L, page_table[b], T, h)
             K = reconstruct(SK, RK[None], BK[h:h + 1])[0]
+            if L.key_norm:  # normalised key: the full key times its stored reciprocal
+                K = K * gather_norms(pool, L, page_table[b], T, h)[:, None]
             V = reconstruct(SV, RV[None], BV[h:h + 1])[0]
             for i, hh in sorted(items):
                 if hh != h:
@@ -437,6 +509,8 @@ def decode_algorithm2(L: Layout, q, B_K, B_V, pool, page_table, seq_lens):
                 shared = rows["SK"][:n] @ qh
                 private = rows["RK"][h, :n] @ p
                 s = (shared + private) / math.sqrt(dh)  # one score per position, then softmax
+                if L.key_norm:  # the stored reciprocal multiplies the summed score
+                    s = s * gather_norms(pool, L, page_table[b], T, h)[:n]
                 w = np.exp(s - s.max())
                 a = w / w.sum()
                 red_shared = a @ rows["SV"][:n]

@@ -754,3 +754,144 @@ def test_rope_mutant_low_dimensional_turn_fails(monkeypatch):
     monkeypatch.setattr(O, "rope_keys", shared_only)
     with pytest.raises(AssertionError):
         test_rope_two_dimensional_counterexample()
+
+
+# --------------------------------------------------------------------------------------
+# RMSNorm joint denominator (LRKV notes §8)
+# --------------------------------------------------------------------------------------
+
+
+def test_key_norm_expansion_of_the_page():
+    """The page expands the squared norm of k = s + z B^T into its shared, cross and private
+    terms: d_h n^2 = |s|^2 + 2 s B z^T + z B^T B z^T + d_h eps.  The oracle's reciprocal
+    (which reconstructs k) must equal 1 / n from that expansion, coded here term by term."""
+    g = np.random.default_rng(85)
+    H, d_h, r, eps = 3, 16, 4, 1e-6
+    s_row = g.standard_normal(d_h)
+    z = g.standard_normal((H, r))
+    Bm = g.standard_normal((H, d_h, r))
+    got = O.key_rms_reciprocal(s_row, z, Bm, eps)
+    for h in range(H):
+        Bh = Bm[h]
+        dn2 = (s_row @ s_row + 2 * s_row @ Bh @ z[h] + z[h] @ (Bh.T @ Bh) @ z[h] + d_h * eps)
+        assert abs(got[h] - 1 / math.sqrt(dn2 / d_h)) < 1e-14 * got[h]
+
+
+def test_key_norm_exact_values():
+    """Keys of all entries +-2 have n = 2 exactly (eps = 0): reciprocal 0.5 in any dtype; a
+    key scaled by 4 has a reciprocal 4 times smaller (the norm is homogeneous)."""
+    d_h = 16
+    s_row = 2.0 * np.where(np.arange(d_h) % 3 == 0, -1.0, 1.0)
+    assert O.key_rms_reciprocal(s_row, np.zeros((1, 4)), np.ones((1, d_h, 4)), 0.0).tolist() == [0.5]
+    g = np.random.default_rng(86)
+    s2, z2, B2 = g.standard_normal(d_h), g.standard_normal((2, 4)), g.standard_normal((2, d_h, 4))
+    a = O.key_rms_reciprocal(s2, z2, B2, 0.0)
+    b = O.key_rms_reciprocal(4 * s2, 4 * z2, B2, 0.0)
+    assert np.allclose(b, a / 4, rtol=1e-15, atol=0)
+
+
+def test_key_norm_page_bytes_add_one_over_two_dh():
+    """One stored reciprocal per head and position costs 1/(2 d_h) of the dense K/V cache on
+    top of eq 9's 1/H + r/d_h (LRKV notes §8)."""
+    for H, d_h, r, dt in ((16, 128, 56, O.BF16), (32, 128, 32, O.BF16), (4, 16, 4, O.F32)):
+        L = O.Layout(H, d_h, r, 16, dt, key_norm=True)
+        dense = 16 * 2 * H * d_h * L.elem_bytes
+        assert Fraction(O.page_bytes(L), dense) == O.cache_ratio(H, r, d_h) + Fraction(1, 2 * d_h)
+
+
+def _norm_case(seed, H, d_h, r, dtype, lens, eps, permute=True):
+    """Random cached rows; the reciprocals written by the oracle's own key-norm step."""
+    L = O.Layout(H, d_h, r, 16, dtype, key_norm=True)
+    _, pool, table, lens, q, BK, BV = random_case(seed, H, d_h, r, dtype, lens, permute=permute)
+    # repack into the key-norm layout (same rows), then fill N by the key-norm step
+    L0 = O.Layout(H, d_h, r, 16, dtype)
+    n = int(sum(lens))
+    SK, SV, RK, RV = [], [], [], []
+    for b, T in enumerate(lens):
+        rows = O.gather_request(pool, L0, table[b], T)
+        SK.append(rows["SK"]); SV.append(rows["SV"])
+        RK.append(np.transpose(rows["RK"], (1, 0, 2))); RV.append(np.transpose(rows["RV"], (1, 0, 2)))
+    enc = lambda a: O.encode_elems(np.concatenate(a), dtype).view(O.storage_dtype(L))
+    npg = int(table.max()) + 1
+    pool_n = O.pack_pool(L, table, lens, enc(SK).reshape(n, d_h), enc(SV).reshape(n, d_h),
+                         enc(RK).reshape(n, H, r), enc(RV).reshape(n, H, r), npg)
+    req = np.repeat(np.arange(len(lens)), lens)
+    pos = np.concatenate([np.arange(t) for t in lens])
+    pool_n = O.key_norms_reference(pool_n, L, BK, eps, req, pos, table)
+    return L, pool_n, table, lens, q, BK, BV
+
+
+def test_key_norm_decode_is_attention_over_normalised_keys():
+    """r = d_h, S = 0, B = I: the normalised keys are the private rows divided by their RMS;
+    the decode equals torch's float64 attention over those, and Algorithm 2 with the stored
+    reciprocal multiplied into the summed score agrees."""
+    H, d_h, n, eps = 2, 8, 21, 1e-5
+    L = O.Layout(H, d_h, d_h, 16, O.F32, key_norm=True)
+    g = np.random.default_rng(87)
+    RK = g.standard_normal((n, H, d_h)).astype(np.float32)
+    RV = g.standard_normal((n, H, d_h)).astype(np.float32)
+    z = np.zeros((n, d_h), np.float32)
+    table, npg = synth.page_assignment(88, [n], 16, True)
+    pool = O.pack_pool(L, table, [n], z.view(np.uint32), z.view(np.uint32),
+                       RK.view(np.uint32), RV.view(np.uint32), npg)
+    eye = np.stack([np.eye(d_h)] * H)
+    pool = O.key_norms_reference(pool, L, eye, eps, np.zeros(n, int), np.arange(n), table)
+    q = g.standard_normal((1, 1, H, d_h))
+    out = O.decode_reference(L, q, eye, eye, pool, table, [n])
+    for h in range(H):
+        k = RK[:, h].astype(np.float64)
+        inv = np.float32(1.0) / np.sqrt(np.mean(k * k, axis=1) + eps)  # in the cache dtype
+        inv = inv.astype(np.float32).astype(np.float64)
+        ref = sdpa(q[0, 0, h], k * inv[:, None], RV[:, h].astype(np.float64))
+        assert rel_err(out[0, 0, h], ref) < 1e-6  # the stored reciprocal is float32-rounded
+    out2 = O.decode_algorithm2(L, q, eye, eye, pool, table, [n])
+    assert rel_err(out2, out) < 1e-13
+
+
+def test_key_norm_makes_scores_scale_free():
+    """With eps = 0 the normalised key does not depend on the key's length: scaling every
+    cached row of one token by 4 (exact in bf16) leaves the decode output unchanged."""
+    L, pool, table, lens, q, BK, BV = _norm_case(89, 3, 16, 8, O.BF16, [37], 0.0, permute=False)
+    base = O.decode_reference(L, q, BK, BV, pool, table, lens)
+    rows = O.gather_request(pool, L, table[0], 37)
+    j = 11
+    scaled = O.write_rows(pool, L, table, [0], [j], 4 * rows["SK"][j:j + 1], rows["SV"][j:j + 1],
+                          4 * np.transpose(rows["RK"][:, j:j + 1], (1, 0, 2)),
+                          np.transpose(rows["RV"][:, j:j + 1], (1, 0, 2)))
+    scaled = O.key_norms_reference(scaled, L, BK, 0.0, [0], [j], table)
+    assert not np.array_equal(scaled, pool)
+    after = O.decode_reference(L, q, BK, BV, scaled, table, lens)
+    assert rel_err(after, base) < 1e-14
+
+
+def test_key_norm_step_writes_only_the_norm_section():
+    L, pool, table, lens, q, BK, BV = _norm_case(90, 2, 16, 8, O.BF16, [20, 35], 1e-6)
+    sentinel = pool.copy()
+    pe = O.page_elems(L)
+    el = sentinel.view(np.uint16).reshape(-1, pe)
+    base = O.section_base(L, "N", 0)
+    el[:, base:base + L.num_heads * 16] = 0xBEEF  # wipe the norm section
+    redo = O.key_norms_reference(sentinel, L, BK, 1e-6, np.repeat([0, 1], lens),
+                                 np.concatenate([np.arange(t) for t in lens]), table)
+    # every appended (page, slot) restored; slots past a request's end keep the sentinel
+    expect = pool.copy()
+    ex = expect.view(np.uint16).reshape(-1, pe)
+    for b, T in enumerate(lens):
+        for j in range(T, -(-T // 16) * 16):
+            for h in range(L.num_heads):
+                ex[table[b, j // 16], O.section_base(L, "N", h) + j % 16] = 0xBEEF
+    assert np.array_equal(redo, expect)
+
+
+def test_key_norm_mutant_without_cross_term_fails(monkeypatch):
+    """Planted mistake: the squared norm taken as |s|^2 + |z B^T|^2 (branches normalised as if
+    orthogonal, the cross term 2 s B z^T dropped) must fail the page's expansion."""
+    def no_cross(s_row, z_rows, Bm, eps):
+        s_row = np.asarray(s_row, np.float64)
+        P_ = np.einsum("hr,hdr->hd", np.asarray(z_rows, np.float64), np.asarray(Bm, np.float64))
+        d_h = s_row.shape[0]
+        return 1.0 / np.sqrt((s_row @ s_row + np.sum(P_ * P_, axis=1)) / d_h + eps)
+
+    monkeypatch.setattr(O, "key_rms_reciprocal", no_cross)
+    with pytest.raises(AssertionError):
+        test_key_norm_expansion_of_the_page()
