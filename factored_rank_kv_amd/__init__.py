@@ -34,11 +34,13 @@ class lrkv_layout(ctypes.Structure):
         ("rank", ctypes.c_int32),
         ("page_size", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("key_norm", ctypes.c_int32),
     ]
 
     def __repr__(self):
         return (f"lrkv_layout(H={self.num_heads}, d_h={self.head_dim}, r={self.rank}, "
-                f"P={self.page_size}, dtype={'bf16' if self.dtype == LRKV_BF16 else 'f32'})")
+                f"P={self.page_size}, dtype={'bf16' if self.dtype == LRKV_BF16 else 'f32'}, "
+                f"key_norm={self.key_norm})")
 
 
 class LRKVError(RuntimeError):
@@ -73,6 +75,8 @@ def _load():
     lib.lrkv_decode_rope.restype = ctypes.c_int
     lib.lrkv_decode_rope_workspace_bytes.argtypes = [LP, I32, I32, I32, I32]
     lib.lrkv_decode_rope_workspace_bytes.restype = SZ
+    lib.lrkv_key_norms.argtypes = [LP, P, ctypes.c_float, P, P, I32, P, I32, P, I64, P]
+    lib.lrkv_key_norms.restype = ctypes.c_int
     lib.lrkv_decode_noalloc.argtypes = [LP, P, I32, I32, P, P, P, P, I32, P, I32, I32, P, P]
     lib.lrkv_decode_noalloc.restype = ctypes.c_int
     lib.lrkv_check_indices.argtypes = [LP, P, I32, I32, P, I32, P, P, I32, I64, P, P]
@@ -85,6 +89,7 @@ def _load():
 
 EXPORTS = ("lrkv_page_bytes", "lrkv_append", "lrkv_decode_workspace_bytes", "lrkv_decode",
            "lrkv_decode_noalloc", "lrkv_decode_rope", "lrkv_decode_rope_workspace_bytes",
+           "lrkv_key_norms",
            "lrkv_check_indices", "lrkv_status_string")
 
 
@@ -157,6 +162,16 @@ def lrkv_decode(layout, q, batch, q_len, B_K, B_V, pool, page_table, max_pages_p
                              workspace_bytes, _stream(stream))
     if check and st != LRKV_OK:
         raise LRKVError(st, "lrkv_decode")
+    return st
+
+
+def lrkv_key_norms(layout, B_K, eps, row_req, row_pos, n_rows, page_table, max_pages_per_req,
+                   pool, num_pages, stream=None, check=True) -> int:
+    st = _load().lrkv_key_norms(_layout(layout), _ptr(B_K), float(eps), _ptr(row_req),
+                                _ptr(row_pos), n_rows, _ptr(page_table), max_pages_per_req,
+                                _ptr(pool), num_pages, _stream(stream))
+    if check and st != LRKV_OK:
+        raise LRKVError(st, "lrkv_key_norms")
     return st
 
 

@@ -21,7 +21,7 @@ namespace {
 
 using namespace lrkv;
 
-enum Variant { V_NONE = -1, V_C0 = 0, V_C1 = 1, V_C3 = 2 };
+enum Variant { V_NONE = -1, V_C0 = 0, V_C1 = 1, V_C3 = 2, V_C1N = 3, V_C3N = 4 };
 
 // The split kernel holds one chunk's page ids in LDS (256 pages of 16 tokens).
 constexpr int kMaxChunkTokens = 256 * 16;
@@ -33,15 +33,20 @@ bool layout_valid(const lrkv_layout* L) {
   if (L->page_size < 16 || (L->page_size & (L->page_size - 1))) return false;
   const int chunk = L->dtype == LRKV_BF16 ? 8 : 4;
   if (L->head_dim % chunk || L->rank % chunk) return false;
+  if (L->key_norm != 0 && L->key_norm != 1) return false;
+  // the norm section (H x P elements) keeps pages whole 16-byte units
+  if (L->key_norm && ((long long)L->num_heads * L->page_size * (L->dtype == LRKV_BF16 ? 2 : 4)) % 16)
+    return false;
   return true;
 }
 
 Variant find_variant(const lrkv_layout* L) {
   if (L->page_size != kPage) return V_NONE;
   const int H = L->num_heads, dh = L->head_dim, r = L->rank;
-  if (L->dtype == LRKV_F32 && H == 4 && dh == 16 && r == 4) return V_C0;
-  if (L->dtype == LRKV_BF16 && H == 16 && dh == 128 && r == 56) return V_C1;
-  if (L->dtype == LRKV_BF16 && H == 32 && dh == 128 && r == 32) return V_C3;
+  const bool nk = L->key_norm != 0;
+  if (L->dtype == LRKV_F32 && H == 4 && dh == 16 && r == 4 && !nk) return V_C0;
+  if (L->dtype == LRKV_BF16 && H == 16 && dh == 128 && r == 56) return nk ? V_C1N : V_C1;
+  if (L->dtype == LRKV_BF16 && H == 32 && dh == 128 && r == 32) return nk ? V_C3N : V_C3;
   return V_NONE;
 }
 
@@ -95,7 +100,7 @@ struct DecodeSizes {
 DecodeSizes decode_sizes(const lrkv_layout* L, int batch, int q_len, int max_seq_len,
                          int chunk_tokens) {
   DecodeSizes z{};
-  if (L->dtype == LRKV_BF16 && q_len >= kPrefillMinRows) {
+  if (L->dtype == LRKV_BF16 && !L->key_norm && q_len >= kPrefillMinRows) {
     // multi-query kernel: no split, no workspace (one 256-byte block keeps the pointer
     // contract uniform)
     z.chunk = chunk_tokens > 0 ? chunk_tokens : L->page_size;
@@ -212,6 +217,8 @@ int decode_launch(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_
     case V_C0: return hip_status(launch_decode<ShapeC0>(a));
     case V_C1: return hip_status(launch_decode<ShapeC1>(a));
     case V_C3: return hip_status(launch_decode<ShapeC3>(a));
+    case V_C1N: return hip_status(launch_decode<ShapeC1N>(a));
+    case V_C3N: return hip_status(launch_decode<ShapeC3N>(a));
     default: return LRKV_ERR_UNSUPPORTED;
   }
 }
@@ -251,7 +258,9 @@ extern "C" {
 size_t lrkv_page_bytes(const lrkv_layout* L) {
   if (!layout_valid(L)) return 0;
   const size_t b = L->dtype == LRKV_BF16 ? 2 : 4;
-  return (size_t)L->page_size * 2 * ((size_t)L->head_dim + (size_t)L->num_heads * L->rank) * b;
+  const size_t norm = L->key_norm ? (size_t)L->page_size * L->num_heads * b : 0;
+  return (size_t)L->page_size * 2 * ((size_t)L->head_dim + (size_t)L->num_heads * L->rank) * b +
+         norm;
 }
 
 const char* lrkv_status_string(int status) {
@@ -311,7 +320,7 @@ int lrkv_decode_rope(const lrkv_layout* L, const void* q, int32_t batch, int32_t
   if (!rope_cs || !aligned16(rope_cs) || rope_rows < max_seq_len || rope_rows <= 0)
     return LRKV_ERR_INVALID_ARG;
   const Variant v = find_variant(L);
-  if (v != V_C1 && v != V_C3) return LRKV_ERR_UNSUPPORTED;  // bf16 variants only
+  if (v == V_C0 || v == V_NONE) return LRKV_ERR_UNSUPPORTED;  // bf16 variants only
   z = rope_sizes(L, batch, q_len, max_seq_len, chunk_tokens);
   if (z.n_split > 65535) return LRKV_ERR_INVALID_ARG;
   if ((long long)batch * q_len * z.n_split * (L->num_heads / 4) > 0x7fffffffLL - 8)
@@ -334,8 +343,13 @@ int lrkv_decode_rope(const lrkv_layout* L, const void* q, int32_t batch, int32_t
   a.out = out;
   a.part_ws = static_cast<float*>(workspace);
   a.stream = static_cast<hipStream_t>(stream);
-  if (v == V_C1) return hip_status(launch_decode_rope<ShapeC1>(a, rope_cs, rope_rows));
-  return hip_status(launch_decode_rope<ShapeC3>(a, rope_cs, rope_rows));
+  switch (v) {
+    case V_C1: return hip_status(launch_decode_rope<ShapeC1>(a, rope_cs, rope_rows));
+    case V_C3: return hip_status(launch_decode_rope<ShapeC3>(a, rope_cs, rope_rows));
+    case V_C1N: return hip_status(launch_decode_rope<ShapeC1N>(a, rope_cs, rope_rows));
+    case V_C3N: return hip_status(launch_decode_rope<ShapeC3N>(a, rope_cs, rope_rows));
+    default: return LRKV_ERR_UNSUPPORTED;
+  }
 }
 
 int lrkv_decode_noalloc(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_len,
@@ -391,8 +405,37 @@ int lrkv_append(const lrkv_layout* L, const void* X, int32_t n_rows, int32_t d,
     case V_C0: return hip_status(launch_append<ShapeC0>(a));
     case V_C1: return hip_status(launch_append<ShapeC1>(a));
     case V_C3: return hip_status(launch_append<ShapeC3>(a));
+    case V_C1N: return hip_status(launch_append<ShapeC1N>(a));
+    case V_C3N: return hip_status(launch_append<ShapeC3N>(a));
     default: return LRKV_ERR_UNSUPPORTED;
   }
+}
+
+int lrkv_key_norms(const lrkv_layout* L, const void* B_K, float eps, const int32_t* row_req,
+                   const int32_t* row_pos, int32_t n_rows, const int32_t* page_table,
+                   int32_t max_pages_per_req, void* pool, int64_t num_pages, void* stream) {
+  if (!layout_valid(L) || !L->key_norm) return LRKV_ERR_INVALID_ARG;
+  if (n_rows < 0 || max_pages_per_req <= 0 || num_pages <= 0) return LRKV_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f) || eps > 1e30f) return LRKV_ERR_INVALID_ARG;  // also refuses NaN
+  if (!B_K || !row_req || !row_pos || !page_table || !pool) return LRKV_ERR_INVALID_ARG;
+  if (!aligned16(B_K) || !aligned16(pool) || (reinterpret_cast<uintptr_t>(row_req) & 3u) ||
+      (reinterpret_cast<uintptr_t>(row_pos) & 3u) || (reinterpret_cast<uintptr_t>(page_table) & 3u))
+    return LRKV_ERR_INVALID_ARG;
+  const Variant v = find_variant(L);
+  if (v != V_C1N && v != V_C3N) return LRKV_ERR_UNSUPPORTED;
+  if (n_rows == 0) return LRKV_OK;
+  NormArgs a{};
+  a.B_K = B_K;
+  a.eps = eps;
+  a.row_req = row_req;
+  a.row_pos = row_pos;
+  a.n_rows = n_rows;
+  a.page_table = page_table;
+  a.max_pages = max_pages_per_req;
+  a.pool = pool;
+  a.stream = static_cast<hipStream_t>(stream);
+  if (v == V_C1N) return hip_status(launch_key_norms<ShapeC1N>(a));
+  return hip_status(launch_key_norms<ShapeC3N>(a));
 }
 
 int lrkv_check_indices(const lrkv_layout* L, const int32_t* page_table, int32_t batch,

@@ -463,5 +463,7 @@ hipError_t launch_append(const AppendArgs& a) {
 template hipError_t launch_append<ShapeC0>(const AppendArgs&);
 template hipError_t launch_append<ShapeC1>(const AppendArgs&);
 template hipError_t launch_append<ShapeC3>(const AppendArgs&);
+template hipError_t launch_append<ShapeC1N>(const AppendArgs&);
+template hipError_t launch_append<ShapeC3N>(const AppendArgs&);
 
 }  // namespace lrkv

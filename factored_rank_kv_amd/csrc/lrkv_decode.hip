@@ -203,6 +203,7 @@ struct PageRegs {
   uint4 rk[SplitCfg<S>::RC_L];
   uint4 rv[SplitCfg<S>::RC_L];
   uint4 st[SplitCfg<S>::SPT];
+  uint32_t nrm;  // key-norm layouts: the stored reciprocal of the lane's (head, token)
 };
 
 // Lane geometry inside the workgroup.
@@ -244,6 +245,12 @@ __device__ __forceinline__ void issue_page(const uint8_t* __restrict__ page, con
   for (int c = 0; c < C::RC_L; ++c) {
     const int cg = min(L.half * C::RC_L + c, S::RC - 1);
     r.rv[c] = load_stream(rvp + cg * S::P);
+  }
+  if constexpr (S::NORM) {
+    if constexpr (S::BF)
+      r.nrm = *reinterpret_cast<const uint16_t*>(page + S::OFF_N + (L.h * S::P + L.j) * 2);
+    else
+      r.nrm = *reinterpret_cast<const uint32_t*>(page + S::OFF_N + (L.h * S::P + L.j) * 4);
   }
 }
 
@@ -506,8 +513,11 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
   }
   float full = acc0 + acc1;
   if constexpr (C::SPLIT == 2) full = add_partner(full);
+  float scale = score_scale;
+  if constexpr (S::NORM)  // the key's stored joint-norm reciprocal multiplies the summed score
+    scale *= S::BF ? bf16_to_f32((uint16_t)r.nrm) : __uint_as_float(r.nrm);
   // masked slots leave by selection, never by multiplying with zero
-  const float s = valid ? full * score_scale : -INFINITY;
+  const float s = valid ? full * scale : -INFINITY;
 
   // ---- online softmax: the reference moves (and rescales l, acc_S, acc_R by one factor)
   // only when the page's max clears it by more than the slack
@@ -729,9 +739,10 @@ decode_split_kernel(const SplitArgs a) {
   __syncthreads();
 
   // this lane's half of its head's query row, and its share of the private query (hi and
-  // lo parts for bf16), in registers for the whole segment; the balanced split of the
-  // 32-head shape has no room for the private share, which stays in LDS there
-  constexpr bool PREG = !BAL || S::H <= 16;
+  // lo parts for bf16), in registers for the whole segment; the balanced split and the
+  // key-norm layout of the 32-head shape have no room for the private share, which stays
+  // in LDS there
+  constexpr bool PREG = (!BAL && !S::NORM) || S::H <= 16;
   uint4 qreg[C::DHC_L];
 #pragma unroll
   for (int c = 0; c < C::DHC_L; ++c) qreg[c] = q_lds[L.h * C::Q_STRIDE + L.half * C::DHC_L + c];
@@ -1013,7 +1024,7 @@ merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
 // ---------------------------------------------------------------------------------------
 template <class S>
 hipError_t launch_decode(const DecodeArgs& a) {
-  if constexpr (S::BF) {
+  if constexpr (S::BF && !S::NORM) {  // key-norm layouts: every row through the split
     if (a.q_len >= kPrefillMinRows) return launch_prefill<S>(a);
   }
   SplitArgs s{};
@@ -1055,9 +1066,13 @@ hipError_t launch_merge(const DecodeArgs& a) {
 
 template hipError_t launch_merge<ShapeC1>(const DecodeArgs&);
 template hipError_t launch_merge<ShapeC3>(const DecodeArgs&);
+template hipError_t launch_merge<ShapeC1N>(const DecodeArgs&);
+template hipError_t launch_merge<ShapeC3N>(const DecodeArgs&);
 
 template hipError_t launch_decode<ShapeC0>(const DecodeArgs&);
 template hipError_t launch_decode<ShapeC1>(const DecodeArgs&);
 template hipError_t launch_decode<ShapeC3>(const DecodeArgs&);
+template hipError_t launch_decode<ShapeC1N>(const DecodeArgs&);
+template hipError_t launch_decode<ShapeC3N>(const DecodeArgs&);
 
 }  // namespace lrkv

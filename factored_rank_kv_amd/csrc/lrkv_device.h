@@ -10,12 +10,15 @@ constexpr int kPage = 16;  // tokens per page of every compiled variant
 
 // Compile-time description of one kernel variant.  Page layout as in include/lrkv.h:
 // sections S_K, S_V, R_K[0..H-1], R_V[0..H-1], each chunk-major ([chunk][token][16 B]).
-template <int H_, int DH_, int R_, bool BF16_>
+// NORM_: the page also keeps, after R_V, one key-norm reciprocal per head and token slot,
+// section N[h][t] (the joint RMSNorm denominator of the full key, LRKV notes §8).
+template <int H_, int DH_, int R_, bool BF16_, bool NORM_ = false>
 struct Shape {
   static constexpr int H = H_;
   static constexpr int DH = DH_;
   static constexpr int R = R_;
   static constexpr bool BF = BF16_;
+  static constexpr bool NORM = NORM_;
   static constexpr int EB = BF ? 2 : 4;         // element bytes
   static constexpr int CE = 16 / EB;            // elements per 16-byte chunk
   static constexpr int DHC = DH / CE;           // chunks in a shared row
@@ -23,10 +26,12 @@ struct Shape {
   static constexpr int P = kPage;
   static constexpr int SEC_S = P * DH * EB;     // bytes of a shared section
   static constexpr int SEC_R = P * R * EB;      // bytes of one head's private block
-  static constexpr int PAGE = 2 * SEC_S + 2 * H * SEC_R;
+  static constexpr int SEC_N = NORM ? H * P * EB : 0;  // bytes of the key-norm section
+  static constexpr int PAGE = 2 * SEC_S + 2 * H * SEC_R + SEC_N;
   static constexpr int OFF_SV = SEC_S;
   static constexpr int OFF_RK = 2 * SEC_S;
   static constexpr int OFF_RV = 2 * SEC_S + H * SEC_R;
+  static constexpr int OFF_N = 2 * SEC_S + 2 * H * SEC_R;  // N[h][t] at OFF_N + (h P + t) EB
   static constexpr int PART = 2 + DH + R;       // floats of a chunk's partial tuple per head
   static constexpr int PART_PAD = (PART + 3) / 4 * 4;  // record stride (16-byte rows)
   static_assert(DH % CE == 0 && R % CE == 0, "widths must be whole 16-byte chunks");

@@ -12,6 +12,9 @@ namespace lrkv {
 using ShapeC0 = Shape<4, 16, 4, false>;    // float32 single-layer check
 using ShapeC1 = Shape<16, 128, 56, true>;  // bf16, 16 heads, rank 56 (half the dense cache)
 using ShapeC3 = Shape<32, 128, 32, true>;  // bf16, 32 heads, rank 32
+// the same bf16 shapes with the key-norm section in every page
+using ShapeC1N = Shape<16, 128, 56, true, true>;
+using ShapeC3N = Shape<32, 128, 32, true, true>;
 
 struct DecodeArgs {
   const void* q;
@@ -92,6 +95,22 @@ struct CheckArgs {
   int32_t* errors;
   hipStream_t stream;
 };
+
+// Key-norm step of an append: reciprocal joint RMS denominators of the appended rows' keys.
+struct NormArgs {
+  const void* B_K;
+  float eps;
+  const int32_t* row_req;
+  const int32_t* row_pos;
+  int n_rows;
+  const int32_t* page_table;
+  int max_pages;
+  void* pool;
+  hipStream_t stream;
+};
+
+template <class S>
+hipError_t launch_key_norms(const NormArgs& a);
 
 // Zeroes *errors, then adds the number of index values that break the layout's rules.
 hipError_t launch_check(const CheckArgs& a);

@@ -72,6 +72,7 @@ struct RopeRegs {
   uint4 cs[RopeCfg<S>::CPT];  // (cos, sin) rows of the page's 16 positions
   uint4 rk[RopeCfg<S>::KB];   // MFMA A operand: R_K[h] chunk 4kb + lane/16, token lane%16
   uint4 rv[RopeCfg<S>::RVL];  // R_V[h] chunk lane/16 + 4j, token lane%16
+  uint2 nrm;                  // key-norm layouts: stored reciprocals of tokens 4(lane/16)..+3
 };
 
 __device__ __forceinline__ uint4 ld_stream(const void* p) {
@@ -109,6 +110,8 @@ __device__ __forceinline__ void rope_issue(const uint8_t* __restrict__ page, con
     const int c = g + 4 * j;
     r.rv[j] = c < S::RC ? ld_stream(rv + (c * S::P + t) * 16) : make_uint4(0u, 0u, 0u, 0u);
   }
+  if constexpr (S::NORM)
+    r.nrm = *reinterpret_cast<const uint2*>(page + S::OFF_N + (h * S::P + 4 * g) * 2);
 }
 
 // Page bytes to LDS: S_K transposed to feature rows skt[f][t] (the layout of the MFMA
@@ -153,8 +156,7 @@ __device__ __forceinline__ void rope_consume(const uint16_t* __restrict__ skt,
                                              const uint4* __restrict__ sv,
                                              const float2* __restrict__ csl,
                                              float* __restrict__ wl, const uint4 (&bk)[RopeCfg<S>::KB][RopeCfg<S>::NTILE],
-                                             const float (&qf)[RopeCfg<S>::NTILE],
-                                             const float (&qp)[RopeCfg<S>::NTILE], int lane,
+                                             const float (&qf)[RopeCfg<S>::NTILE], int lane,
                                              int nvalid, float score_scale, const RopeRegs<S>& r,
                                              RopeState<S>& st) {
   using C = RopeCfg<S>;
@@ -177,23 +179,33 @@ __device__ __forceinline__ void rope_consume(const uint16_t* __restrict__ skt,
   }
   // ---- score: key row t dotted with the query turned back by t's angle, q~ D_t^T:
   // (q~ D^T)_f = cos * q~_f + sin * qp_f, qp_f = q~_(f+1) for even f, -q~_(f-1) for odd f
+  // (the pair partner f ^ 1 sits in lane ^ 1: one DPP swap)
   float sc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int nt = 0; nt < C::NTILE; ++nt) {
     const int m = 8 * nt + (n >> 1);
+    const float partner = dpp_f<kQuadSwap1>(qf[nt]);
+    const float qp = (n & 1) ? -partner : partner;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float2 c = csl[(4 * g + e) * C::PAIRS + m];
-      const float qr = fmaf(c.x, qf[nt], c.y * qp[nt]);
+      const float qr = fmaf(c.x, qf[nt], c.y * qp);
       sc[e] = fmaf(acc[nt][e], qr, sc[e]);
     }
   }
   float s[4];
   float pm = -INFINITY;
+  float nrm[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (S::NORM) {  // the keys' stored joint-norm reciprocals (RMSNorm of §8)
+    nrm[0] = bf16_lo(r.nrm.x);
+    nrm[1] = bf16_hi(r.nrm.x);
+    nrm[2] = bf16_lo(r.nrm.y);
+    nrm[3] = bf16_hi(r.nrm.y);
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const float d = r16_sum(sc[e]);  // over the 16 features of each tile row
-    s[e] = (4 * g + e) < nvalid ? d * score_scale : -INFINITY;  // selection, never x 0
+    s[e] = (4 * g + e) < nvalid ? d * (score_scale * nrm[e]) : -INFINITY;  // selection
     pm = fmaxf(pm, s[e]);
   }
   pm = rows4_max(pm);
@@ -282,18 +294,13 @@ __global__ void __launch_bounds__(RopeCfg<S>::NT, 2) decode_rope_kernel(const Ro
       bk[kb][nt] = k0 < S::R ? *reinterpret_cast<const uint4*>(bkh + ((size_t)(16 * nt + n) * S::R + k0) * 2)
                              : make_uint4(0u, 0u, 0u, 0u);
     }
-  float qf[C::NTILE], qp[C::NTILE];
+  float qf[C::NTILE];  // q~ at feature 16nt + lane%16
   {
     const size_t row = (size_t)b * a.q_len + qi;
-    const uint32_t* qrow = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.q) +
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(a.q) +
                                                              (row * S::H + h) * S::DH * 2);
 #pragma unroll
-    for (int nt = 0; nt < C::NTILE; ++nt) {
-      const uint32_t pr = qrow[8 * nt + (n >> 1)];  // pair (2m, 2m+1)
-      const float q0 = bf16_lo(pr), q1 = bf16_hi(pr);
-      qf[nt] = (n & 1) ? q1 : q0;
-      qp[nt] = (n & 1) ? -q0 : q1;
-    }
+    for (int nt = 0; nt < C::NTILE; ++nt) qf[nt] = bf16_to_f32(qrow[16 * nt + n]);
   }
   __syncthreads();  // page ids in LDS
 
@@ -318,7 +325,7 @@ __global__ void __launch_bounds__(RopeCfg<S>::NT, 2) decode_rope_kernel(const Ro
 
   auto step = [&](int pg, int buf, RopeRegs<S>& cur, RopeRegs<S>& nxt) {
     rope_consume<S>(skt_lds[buf], sv_lds[buf], reinterpret_cast<const float2*>(cs_lds[buf]),
-                    w_lds[wave], bk, qf, qp, lane, nvalid(pg), a.score_scale, cur, st);
+                    w_lds[wave], bk, qf, lane, nvalid(pg), a.score_scale, cur, st);
     const bool more = pg + 1 < pg1;
     if (more) rope_stage<S>(skt_lds[buf ^ 1], sv_lds[buf ^ 1], cs_lds[buf ^ 1], tid, nxt, nvalid(pg + 1));
     if (pg + 2 < pg1)
@@ -390,5 +397,7 @@ template int rope_groups<ShapeC1>();
 template int rope_groups<ShapeC3>();
 template hipError_t launch_decode_rope<ShapeC1>(const DecodeArgs&, const float*, int);
 template hipError_t launch_decode_rope<ShapeC3>(const DecodeArgs&, const float*, int);
+template hipError_t launch_decode_rope<ShapeC1N>(const DecodeArgs&, const float*, int);
+template hipError_t launch_decode_rope<ShapeC3N>(const DecodeArgs&, const float*, int);
 
 }  // namespace lrkv

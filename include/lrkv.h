@@ -31,8 +31,11 @@
  * i.e. chunk-major: the 16-byte chunk column c holds the P tokens' features [cC, cC+C)
  * back to back.  One 1 KiB load of a wavefront then hands lane (c, t) one token's chunk.
  *
+ * With key_norm = 1 a fifth section follows R_V (LRKV notes §8, RMSNorm paragraph):
+ *   N[h]         at 2*P*d_h + 2*H*P*r + h*P   P elements: 1/n of head h for slots 0..P-1
+ *
  * Token position j of request b lives in page page_table[b * max_pages_per_req + j / P],
- * slot j % P, in all four sections.  Page ids index a pool of num_pages * page_bytes bytes.
+ * slot j % P, in all sections.  Page ids index a pool of num_pages * page_bytes bytes.
  *
  * ---------------------------------------------------------------------------------------
  * Conventions for every entry point:
@@ -51,7 +54,9 @@
  *  - Return value: LRKV_OK, or a negative status (lrkv_status_string gives its text).
  *
  * Shapes with a compiled kernel variant, (H, d_h, r, dtype):
- *   (4, 16, 4, LRKV_F32), (16, 128, 56, LRKV_BF16), (32, 128, 32, LRKV_BF16); P = 16.
+ *   (4, 16, 4, LRKV_F32), (16, 128, 56, LRKV_BF16), (32, 128, 32, LRKV_BF16); P = 16;
+ *   the two bf16 shapes also with key_norm = 1 (their multi-query calls then run through
+ *   the split decode kernels rather than the prefill kernel).
  * Any other shape returns LRKV_ERR_UNSUPPORTED.
  */
 #ifndef LRKV_H
@@ -84,11 +89,13 @@ typedef struct lrkv_layout {
   int32_t rank;      /* r   */
   int32_t page_size; /* P   */
   int32_t dtype;     /* LRKV_F32 or LRKV_BF16 */
+  int32_t key_norm;  /* 0, or 1: pages keep the key-norm section N (see lrkv_key_norms) */
 } lrkv_layout;
 
-/* Bytes of one page: P * 2 * (d_h + H*r) * b.  With P tokens the dense multi-head cache
- * would take P * 2 * H * d_h * b, so page_bytes over that is exactly 1/H + r/d_h (LRKV
- * notes §4, eq 9).  Returns 0 if L is NULL or describes no valid layout. */
+/* Bytes of one page: P * 2 * (d_h + H*r) * b, plus P * H * b with key_norm.  With P tokens
+ * the dense multi-head cache would take P * 2 * H * d_h * b, so page_bytes over that is
+ * exactly 1/H + r/d_h (LRKV notes §4, eq 9), plus 1/(2 d_h) with key_norm (§8).  Returns 0
+ * if L is NULL or describes no valid layout. */
 size_t lrkv_page_bytes(const lrkv_layout* L);
 
 /* Algorithm 1 of LRKV notes §3: build or append the factored cache.
@@ -124,6 +131,25 @@ int lrkv_append(const lrkv_layout* L, const void* X, int32_t n_rows, int32_t d,
                 const void* W_SK, const void* W_SV, const void* U_K, const void* U_V,
                 const int32_t* row_req, const int32_t* row_pos, const int32_t* page_table,
                 int32_t max_pages_per_req, void* pool, int64_t num_pages, void* stream);
+
+/* Key-norm step of an append (LRKV notes §8, RMSNorm paragraph), for layouts with
+ * key_norm = 1.  An RMSNorm of the key divides the full key k = S_K + R_K[h] B_K[h]^T by
+ *   n_h = sqrt(|S_K + R_K[h] B_K[h]^T|^2 / d_h + eps),
+ * a quantity of the full key that neither branch has alone (its square holds the cross
+ * term 2 S_K B_K[h] R_K[h]^T).  For each appended row n and head h this reads the row's
+ * stored S_K and R_K[h] (written by lrkv_append: enqueue this after it, on the same stream),
+ * forms n_h with float32 accumulation and writes 1/n_h, rounded to nearest even in
+ * L->dtype, at N[h][row_pos[n] % P] of the row's page; no other byte changes.  lrkv_decode
+ * and lrkv_decode_rope then multiply each summed score by its key's stored 1/n_h.  A fixed
+ * per-channel gain of the norm belongs on the query side (the caller's q).
+ *   B_K        device, [H][d_h][r] in L->dtype
+ *   eps        host value >= 0
+ *   row_req, row_pos, page_table, max_pages_per_req, pool, num_pages: as in lrkv_append
+ * bf16 layouts (16, 128, 56) and (32, 128, 32) with key_norm = 1; others return
+ * LRKV_ERR_UNSUPPORTED (key_norm = 0: LRKV_ERR_INVALID_ARG).  n_rows == 0: no-op. */
+int lrkv_key_norms(const lrkv_layout* L, const void* B_K, float eps, const int32_t* row_req,
+                   const int32_t* row_pos, int32_t n_rows, const int32_t* page_table,
+                   int32_t max_pages_per_req, void* pool, int64_t num_pages, void* stream);
 
 /* Infrastructure of this library, not an operation of the method: the workspace bytes
  * lrkv_decode needs for these sizes (the split partial tuples).  0 for invalid arguments. */

@@ -589,6 +589,8 @@ def decode_reference_rope(L: Layout, q, B_K, B_V, pool, page_table, seq_lens, ro
         for h in sorted({h for _, h in items}):
             RK, RV = gather_private(pool, L, page_table[b], T, h)
             K = rope_keys(SK, RK[None], BK[h:h + 1], cs[:T, :, 0], cs[:T, :, 1])[0]
+            if L.key_norm:  # a turn keeps the key's length: the same stored reciprocal
+                K = K * gather_norms(pool, L, page_table[b], T, h)[:, None]
             V = reconstruct(SV, RV[None], BV[h:h + 1])[0]
             for i, hh in sorted(items):
                 if hh != h:

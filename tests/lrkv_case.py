@@ -24,7 +24,8 @@ def log(msg):
 
 
 def layout_c(L: O.Layout) -> F.lrkv_layout:
-    return F.lrkv_layout(L.num_heads, L.head_dim, L.rank, L.page_size, L.dtype)
+    return F.lrkv_layout(L.num_heads, L.head_dim, L.rank, L.page_size, L.dtype,
+                         1 if L.key_norm else 0)
 
 
 def as_codes(x: np.ndarray, dtype: int) -> np.ndarray:
@@ -174,15 +175,22 @@ def bases_and_queries(seed, L: O.Layout, B, q_len, q_scale=1.0):
     return as_codes(q, L.dtype), as_codes(BK, L.dtype), as_codes(BV, L.dtype)
 
 
-def iid_case(seed, H, dh, r, dtype, lens, q_len=1, permute=True, q_scale=1.0, fill=0):
-    """Cached rows drawn i.i.d. N(0,1), packed by the oracle's bulk placement."""
-    L = O.Layout(H, dh, r, 16, dtype)
+def iid_case(seed, H, dh, r, dtype, lens, q_len=1, permute=True, q_scale=1.0, fill=0,
+             key_norm_eps=None):
+    """Cached rows drawn i.i.d. N(0,1), packed by the oracle's bulk placement.  With
+    key_norm_eps, the layout keeps the key-norm section, filled by the oracle's key-norm step
+    (its reciprocals of the stored keys)."""
+    L = O.Layout(H, dh, r, 16, dtype, key_norm=key_norm_eps is not None)
     n = int(sum(lens))
     SK, SV, RK, RV = synth.factored_rows(seed, n, H, dh, r)
     table, npg = synth.page_assignment(seed + 7, lens, 16, permute)
     pool = O.pack_pool(L, table, lens, as_codes(SK, dtype), as_codes(SV, dtype),
                        as_codes(RK, dtype), as_codes(RV, dtype), npg, fill=fill)
     qc, bk, bv = bases_and_queries(seed + 13, L, len(lens), q_len, q_scale)
+    if key_norm_eps is not None and n:
+        req = np.repeat(np.arange(len(lens)), lens)
+        pos = np.concatenate([np.arange(t) for t in lens])
+        pool = O.key_norms_reference(pool, L, codes_f64(bk, dtype), key_norm_eps, req, pos, table)
     return Case(L, pool, table, lens, qc, bk, bv, npg)
 
 

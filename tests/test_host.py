@@ -161,6 +161,28 @@ def test_decode_rope_rejects_bad_arguments_before_launch():
     assert F.lrkv_decode_rope_workspace_bytes(C1, 8, 1, 4096, 24) == 0
 
 
+def test_key_norm_layouts_and_argument_checks():
+    C1N = F.lrkv_layout(16, 128, 56, 16, F.LRKV_BF16, 1)
+    L = O.Layout(16, 128, 56, 16, O.BF16, key_norm=True)
+    assert F.lrkv_page_bytes(C1N) == O.page_bytes(L) == 65536 + 16 * 16 * 2
+    assert F.lrkv_page_bytes(F.lrkv_layout(16, 128, 56, 16, F.LRKV_BF16, 2)) == 0
+
+    def st(lay=C1N, **over):
+        args = dict(B_K=FAKE, eps=1e-6, row_req=FAKE, row_pos=FAKE, n_rows=4, page_table=FAKE,
+                    max_pages_per_req=4, pool=FAKE, num_pages=8)
+        args.update(over)
+        return F.lrkv_key_norms(lay, check=False, stream=0, **args)
+
+    bad = F.LRKV_ERR_INVALID_ARG
+    assert st(C1) == bad  # a layout without the norm section
+    assert st(B_K=None) == bad
+    assert st(eps=-1.0) == bad
+    assert st(eps=float("nan")) == bad
+    assert st(pool=FAKE + 8) == bad
+    assert st(F.lrkv_layout(4, 16, 4, 16, F.LRKV_F32, 1)) == F.LRKV_ERR_UNSUPPORTED
+    assert st(n_rows=0) == F.LRKV_OK
+
+
 def append_status(lay=C1, **over):
     args = dict(X=FAKE, n_rows=4, d=2048, W_SK=FAKE, W_SV=FAKE, U_K=FAKE, U_V=FAKE,
                 row_req=FAKE, row_pos=FAKE, page_table=FAKE, max_pages_per_req=4, pool=FAKE,
@@ -224,13 +246,13 @@ def test_header_is_plain_c():
     with tempfile.TemporaryDirectory() as d:
         src = os.path.join(d, "t.c")
         with open(src, "w") as f:
-            f.write('#include "lrkv.h"\nint main(void){lrkv_layout L={16,128,56,16,LRKV_BF16};'
-                    'return (int)sizeof(L) - 20;}\n')
+            f.write('#include "lrkv.h"\nint main(void){lrkv_layout L={16,128,56,16,LRKV_BF16,0};'
+                    'return (int)sizeof(L) - 24;}\n')
         r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
                             "-c", src, "-o", os.path.join(d, "t.o")], capture_output=True,
                            text=True)
         assert r.returncode == 0, r.stderr
-    assert ctypes.sizeof(F.lrkv_layout) == 20
+    assert ctypes.sizeof(F.lrkv_layout) == 24
 
 
 def test_binding_refuses_host_tensors():

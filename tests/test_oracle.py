@@ -895,3 +895,25 @@ def test_key_norm_mutant_without_cross_term_fails(monkeypatch):
     monkeypatch.setattr(O, "key_rms_reciprocal", no_cross)
     with pytest.raises(AssertionError):
         test_key_norm_expansion_of_the_page()
+
+
+def test_rope_with_key_norm():
+    """Rotary keys over a key-norm layout: with zero angles the rotary decode equals the plain
+    key-norm decode; with a real table, the reciprocal stored from the unturned key is the
+    turned key's too (a turn keeps the length), checked against attention over the turned
+    keys divided by their own RMS."""
+    L, pool, table, lens, q, BK, BV = _norm_case(91, 2, 16, 8, O.F32, [37, 5], 0.0)
+    cs0 = np.zeros((40, 8, 2), np.float32)
+    cs0[..., 0] = 1.0
+    a = O.decode_reference_rope(L, q, BK, BV, pool, table, lens, cs0)
+    assert rel_err(a, O.decode_reference(L, q, BK, BV, pool, table, lens)) < 1e-14
+    cs = synth.rope_table(40, 16)
+    got = O.decode_reference_rope(L, q, BK, BV, pool, table, lens, cs)
+    rows = O.gather_request(pool, L, table[0], 37)
+    for h in range(2):
+        K = O.rope_keys(rows["SK"], rows["RK"][h:h + 1], BK[h:h + 1], cs[:37, :, 0],
+                        cs[:37, :, 1])[0]
+        K = K / np.sqrt(np.mean(K * K, axis=1))[:, None]
+        V = O.reconstruct(rows["SV"], rows["RV"][h:h + 1], BV[h:h + 1])[0]
+        ref = sdpa(q[0, 0, h], K, V)
+        assert rel_err(got[0, 0, h], ref) < 1e-6  # table rows are float32-rounded turns
