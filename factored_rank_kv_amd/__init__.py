@@ -25,6 +25,7 @@ LRKV_ERR_INVALID_ARG = -1
 LRKV_ERR_UNSUPPORTED = -2
 LRKV_ERR_HIP = -3
 LRKV_ERR_SCRATCH = -4
+LRKV_ERR_NO_PAGES = -5
 
 
 class lrkv_layout(ctypes.Structure):
@@ -41,6 +42,15 @@ class lrkv_layout(ctypes.Structure):
         return (f"lrkv_layout(H={self.num_heads}, d_h={self.head_dim}, r={self.rank}, "
                 f"P={self.page_size}, dtype={'bf16' if self.dtype == LRKV_BF16 else 'f32'}, "
                 f"key_norm={self.key_norm})")
+
+
+class lrkv_page_pool(ctypes.Structure):
+    _fields_ = [
+        ("num_pages", ctypes.c_int64),
+        ("num_free", ctypes.c_int64),
+        ("refcount", ctypes.POINTER(ctypes.c_int32)),
+        ("free_stack", ctypes.POINTER(ctypes.c_int32)),
+    ]
 
 
 class LRKVError(RuntimeError):
@@ -75,6 +85,16 @@ def _load():
     lib.lrkv_decode_rope.restype = ctypes.c_int
     lib.lrkv_decode_rope_workspace_bytes.argtypes = [LP, I32, I32, I32, I32]
     lib.lrkv_decode_rope_workspace_bytes.restype = SZ
+    PP = ctypes.POINTER(lrkv_page_pool)
+    lib.lrkv_pages_init.argtypes = [PP, P, P, I64]
+    lib.lrkv_pages_alloc.argtypes = [PP, I32, P]
+    lib.lrkv_pages_retain.argtypes = [PP, P, I32]
+    lib.lrkv_pages_release.argtypes = [PP, P, I32]
+    lib.lrkv_fork_prefix.argtypes = [LP, PP, P, I32, P, I32, P, P]
+    lib.lrkv_copy_pages.argtypes = [LP, P, P, P, I32, P]
+    for fn in ("lrkv_pages_init", "lrkv_pages_alloc", "lrkv_pages_retain", "lrkv_pages_release",
+               "lrkv_fork_prefix", "lrkv_copy_pages"):
+        getattr(lib, fn).restype = ctypes.c_int
     lib.lrkv_key_norms.argtypes = [LP, P, ctypes.c_float, P, P, I32, P, I32, P, I64, P]
     lib.lrkv_key_norms.restype = ctypes.c_int
     lib.lrkv_decode_noalloc.argtypes = [LP, P, I32, I32, P, P, P, P, I32, P, I32, I32, P, P]
@@ -89,7 +109,8 @@ def _load():
 
 EXPORTS = ("lrkv_page_bytes", "lrkv_append", "lrkv_decode_workspace_bytes", "lrkv_decode",
            "lrkv_decode_noalloc", "lrkv_decode_rope", "lrkv_decode_rope_workspace_bytes",
-           "lrkv_key_norms",
+           "lrkv_key_norms", "lrkv_pages_init", "lrkv_pages_alloc", "lrkv_pages_retain",
+           "lrkv_pages_release", "lrkv_fork_prefix", "lrkv_copy_pages",
            "lrkv_check_indices", "lrkv_status_string")
 
 
@@ -162,6 +183,81 @@ def lrkv_decode(layout, q, batch, q_len, B_K, B_V, pool, page_table, max_pages_p
                              workspace_bytes, _stream(stream))
     if check and st != LRKV_OK:
         raise LRKVError(st, "lrkv_decode")
+    return st
+
+
+def _host_i32(a):
+    """Address of a host numpy int32 array (the page allocator works on host memory)."""
+    import numpy as np
+
+    if a is None:
+        return None
+    if not (isinstance(a, np.ndarray) and a.dtype == np.int32 and a.flags.c_contiguous):
+        raise ValueError("page bookkeeping arrays are contiguous host numpy int32 arrays")
+    return a.ctypes.data
+
+
+def lrkv_pages_init(pp: "lrkv_page_pool", refcount, free_stack, num_pages: int,
+                    check=True) -> int:
+    st = _load().lrkv_pages_init(ctypes.byref(pp), _host_i32(refcount), _host_i32(free_stack),
+                                 num_pages)
+    if check and st != LRKV_OK:
+        raise LRKVError(st, "lrkv_pages_init")
+    return st
+
+
+class PagePool:
+    """Caller-owned page bookkeeping (lrkv_page_pool over two host int32 arrays)."""
+
+    def __init__(self, num_pages: int):
+        import numpy as np
+
+        self.refcount = np.zeros(num_pages, np.int32)
+        self.free_stack = np.zeros(num_pages, np.int32)
+        self.c = lrkv_page_pool()
+        lrkv_pages_init(self.c, self.refcount, self.free_stack, num_pages)
+
+    @property
+    def num_free(self) -> int:
+        return int(self.c.num_free)
+
+
+def lrkv_pages_alloc(pool: PagePool, n: int, ids, check=True) -> int:
+    st = _load().lrkv_pages_alloc(ctypes.byref(pool.c), n, _host_i32(ids))
+    if check and st != LRKV_OK:
+        raise LRKVError(st, "lrkv_pages_alloc")
+    return st
+
+
+def lrkv_pages_retain(pool: PagePool, ids, n: int, check=True) -> int:
+    st = _load().lrkv_pages_retain(ctypes.byref(pool.c), _host_i32(ids), n)
+    if check and st != LRKV_OK:
+        raise LRKVError(st, "lrkv_pages_retain")
+    return st
+
+
+def lrkv_pages_release(pool: PagePool, ids, n: int, check=True) -> int:
+    st = _load().lrkv_pages_release(ctypes.byref(pool.c), _host_i32(ids), n)
+    if check and st != LRKV_OK:
+        raise LRKVError(st, "lrkv_pages_release")
+    return st
+
+
+def lrkv_fork_prefix(layout, pool: PagePool, parent_row, prefix_len, child_row,
+                     max_pages_per_req, dev_pool, stream=None, check=True) -> int:
+    st = _load().lrkv_fork_prefix(_layout(layout), ctypes.byref(pool.c), _host_i32(parent_row),
+                                  prefix_len, _host_i32(child_row), max_pages_per_req,
+                                  _ptr(dev_pool), _stream(stream))
+    if check and st != LRKV_OK:
+        raise LRKVError(st, "lrkv_fork_prefix")
+    return st
+
+
+def lrkv_copy_pages(layout, dev_pool, src_ids, dst_ids, n, stream=None, check=True) -> int:
+    st = _load().lrkv_copy_pages(_layout(layout), _ptr(dev_pool), _ptr(src_ids), _ptr(dst_ids),
+                                 n, _stream(stream))
+    if check and st != LRKV_OK:
+        raise LRKVError(st, "lrkv_copy_pages")
     return st
 
 

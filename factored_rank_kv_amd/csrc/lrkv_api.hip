@@ -269,6 +269,7 @@ const char* lrkv_status_string(int status) {
     case LRKV_ERR_INVALID_ARG: return "LRKV_ERR_INVALID_ARG: invalid argument";
     case LRKV_ERR_UNSUPPORTED: return "LRKV_ERR_UNSUPPORTED: no kernel variant for this shape";
     case LRKV_ERR_HIP: return "LRKV_ERR_HIP: HIP runtime error at launch";
+    case LRKV_ERR_NO_PAGES: return "LRKV_ERR_NO_PAGES: not enough free pages in the page pool";
     case LRKV_ERR_SCRATCH:
       return "LRKV_ERR_SCRATCH: the call needs more workspace than the 16 MiB fixed scratch of "
              "lrkv_decode_noalloc holds (use lrkv_decode with a caller workspace)";

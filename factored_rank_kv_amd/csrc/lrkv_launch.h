@@ -112,6 +112,12 @@ struct NormArgs {
 template <class S>
 hipError_t launch_key_norms(const NormArgs& a);
 
+// Copies whole pages of `page_bytes` bytes: page src[i] to dst[i] for i < n, or, with
+// null id arrays, the one page single_src to single_dst.
+hipError_t launch_copy_pages(uint8_t* pool, const int32_t* src, const int32_t* dst, int n,
+                             long long page_bytes, int single_src, int single_dst,
+                             hipStream_t stream);
+
 // Zeroes *errors, then adds the number of index values that break the layout's rules.
 hipError_t launch_check(const CheckArgs& a);
 

@@ -76,8 +76,9 @@ enum {
   LRKV_ERR_INVALID_ARG = -1, /* null / misaligned pointer, bad size, workspace too small */
   LRKV_ERR_UNSUPPORTED = -2, /* (H, d_h, r, dtype, P) without a kernel variant          */
   LRKV_ERR_HIP = -3,         /* the HIP runtime reported an error at launch            */
-  LRKV_ERR_SCRATCH = -4      /* lrkv_decode_noalloc: the call needs more than its fixed */
+  LRKV_ERR_SCRATCH = -4,     /* lrkv_decode_noalloc: the call needs more than its fixed */
                              /* scratch holds                                           */
+  LRKV_ERR_NO_PAGES = -5     /* the page pool has fewer free pages than asked for       */
 };
 
 /* Description of the cache.  Physical rank = logical rank: no padding of r (LRKV notes §4
@@ -270,6 +271,51 @@ int lrkv_check_indices(const lrkv_layout* L, const int32_t* page_table, int32_t 
                        int32_t max_pages_per_req, const int32_t* seq_lens, int32_t max_seq_len,
                        const int32_t* row_req, const int32_t* row_pos, int32_t n_rows,
                        int64_t num_pages, int32_t* errors, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Shared-prefix page reuse and reclamation (LRKV notes §3, the note after Algorithm 1:
+ * shared and private pages must keep the same token numbering and reclamation lifetime, or
+ * reusing a prefix or releasing a request can leave the two paths of one position pointing
+ * at different histories).  One page id holds every section of its tokens, so a page shared,
+ * copied or freed moves its shared rows, private rows (and key-norm reciprocals) together.
+ *
+ * The allocator is host code over caller-owned host arrays; it keeps no other state.  It is
+ * not thread-safe: one caller at a time per lrkv_page_pool. */
+typedef struct lrkv_page_pool {
+  int64_t num_pages;   /* pages of the pool */
+  int64_t num_free;    /* free page ids on the stack */
+  int32_t* refcount;   /* host, [num_pages]: requests holding each page (0: free) */
+  int32_t* free_stack; /* host, [num_pages]: free ids; the next allocation takes
+                          free_stack[num_free - 1] */
+} lrkv_page_pool;
+
+/* Every page free; allocations then return ids 0, 1, 2, ... in order. */
+int lrkv_pages_init(lrkv_page_pool* pp, int32_t* refcount, int32_t* free_stack,
+                    int64_t num_pages);
+/* Takes n free pages (reference count 1) into ids[0..n); LRKV_ERR_NO_PAGES, with nothing
+ * taken, if fewer than n are free. */
+int lrkv_pages_alloc(lrkv_page_pool* pp, int32_t n, int32_t* ids);
+/* One more reference to each listed page (a request that shares it); every page must be in
+ * use, else LRKV_ERR_INVALID_ARG and nothing changes. */
+int lrkv_pages_retain(lrkv_page_pool* pp, const int32_t* ids, int32_t n);
+/* Drops one reference per listed page (an id listed twice drops two); pages left with none
+ * return to the free stack in list order.  A page with fewer references than listings:
+ * LRKV_ERR_INVALID_ARG and nothing changes. */
+int lrkv_pages_release(lrkv_page_pool* pp, const int32_t* ids, int32_t n);
+/* A new request that continues the first prefix_len tokens of another (shared prefix):
+ * child_row[k] = parent_row[k] for the prefix_len / P full pages (one more reference each,
+ * never written again: later tokens go to later pages); if prefix_len % P != 0 the page
+ * holding the prefix's last tokens is copied, every section of it, into a newly allocated
+ * page (enqueued on `stream`), which becomes the child's, so both requests can append past
+ * the prefix without touching each other's rows.  Host rows, device pool; child_row
+ * entries past the prefix are not written.  LRKV_ERR_NO_PAGES if the copy has no page. */
+int lrkv_fork_prefix(const lrkv_layout* L, lrkv_page_pool* pp, const int32_t* parent_row,
+                     int32_t prefix_len, int32_t* child_row, int32_t max_pages_per_req,
+                     void* pool, void* stream);
+/* Copies whole pages (every section) src_ids[i] -> dst_ids[i], i < n, on the device.
+ * src_ids, dst_ids: device int32 [n]; pool: device, 16-byte aligned. */
+int lrkv_copy_pages(const lrkv_layout* L, void* pool, const int32_t* src_ids,
+                    const int32_t* dst_ids, int32_t n, void* stream);
 
 /* Infrastructure of this library, not an operation of the method: the text of a status
  * code (static storage). */

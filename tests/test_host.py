@@ -265,3 +265,79 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         F.lrkv_decode(C1, host, 1, 1, FAKE, FAKE, FAKE, FAKE, 1, FAKE, 16, 0, FAKE, FAKE, 1 << 20,
                       stream=0)
+
+
+def test_page_allocator_matches_reference_model():
+    """Seeded random sequences of alloc / retain / release / fork (whole-page prefixes, no
+    device copy) on the C allocator and on the oracle's reference model: the same status,
+    ids, reference counts and free stack after every operation."""
+    import numpy as np
+
+    from oracle.page_pool import PagePoolModel
+
+    g = np.random.default_rng(600)
+    lay = F.lrkv_layout(16, 128, 56, 16, F.LRKV_BF16)
+    for trial in range(20):
+        n = int(g.integers(1, 40))
+        pool, model = F.PagePool(n), PagePoolModel(n)
+        held = []  # page lists of live "requests"
+        for step in range(200):
+            op = g.integers(0, 4)
+            if op == 0:
+                k = int(g.integers(0, 6))
+                ids = np.zeros(max(k, 1), np.int32)
+                st = F.lrkv_pages_alloc(pool, k, ids, check=False)
+                mst, mids = model.alloc(k)
+                assert st == mst and list(ids[:k] if st == 0 else []) == (mids if st == 0 else [])
+                if st == 0 and k:
+                    held.append(list(mids))
+            elif op == 1 and held:
+                ids = held[int(g.integers(0, len(held)))]
+                if g.random() < 0.2:
+                    ids = ids + [int(g.integers(-2, n + 2))]  # sometimes an invalid id
+                a = np.array(ids, np.int32)
+                st = F.lrkv_pages_retain(pool, a, len(ids), check=False)
+                assert st == model.retain(ids)
+                if st == 0:
+                    held.append(list(ids))
+            elif op == 2 and held:
+                ids = held.pop(int(g.integers(0, len(held))))
+                if g.random() < 0.2:
+                    ids = ids + ids[:1]  # sometimes one listing too many
+                a = np.array(ids, np.int32)
+                st = F.lrkv_pages_release(pool, a, len(ids), check=False)
+                assert st == model.release(ids)
+                if st != 0:
+                    held.append(ids[:-1])
+            elif op == 3 and held:
+                parent = held[int(g.integers(0, len(held)))]
+                plen = 16 * int(g.integers(0, len(parent) + 1))  # whole pages: no copy
+                row = np.array(parent + [0], np.int32)
+                child = np.full(len(parent) + 1, -7, np.int32)
+                st = F.lrkv_fork_prefix(lay, pool, row, plen, child, len(row), 16, check=False)
+                mst, mchild, mcopy = model.fork(parent, plen, 16)
+                assert st == mst and mcopy is None
+                if st == 0:
+                    assert list(child[:len(mchild)]) == mchild
+                    if mchild:
+                        held.append(mchild)
+            assert pool.refcount.tolist() == model.ref
+            assert pool.num_free == len(model.free)
+            assert pool.free_stack[:pool.num_free].tolist() == model.free
+
+
+def test_page_allocator_host_errors():
+    import numpy as np
+
+    pool = F.PagePool(3)
+    ids = np.zeros(4, np.int32)
+    assert F.lrkv_pages_alloc(pool, 4, ids, check=False) == F.LRKV_ERR_NO_PAGES
+    assert pool.num_free == 3  # nothing taken
+    assert F.lrkv_pages_alloc(pool, 2, ids) == 0 and ids[:2].tolist() == [0, 1]
+    assert F.lrkv_pages_retain(pool, np.array([2], np.int32), 1, check=False) == \
+        F.LRKV_ERR_INVALID_ARG  # a free page cannot gain a holder
+    assert F.lrkv_pages_release(pool, np.array([0, 0], np.int32), 2, check=False) == \
+        F.LRKV_ERR_INVALID_ARG
+    assert pool.refcount.tolist() == [1, 1, 0]  # the failed release changed nothing
+    with pytest.raises(ValueError):
+        F.lrkv_pages_retain(pool, [0], 1)  # host numpy int32 arrays only
