@@ -142,6 +142,12 @@ class Layout:
     # LRKV notes §8 (RMSNorm paragraph): one stored reciprocal of the joint key denominator
     # per head and position, in the cache dtype, as a fifth section N[h][t] of each page
     key_norm: bool = False
+    # LRKV notes §3 (after the gradient formulas): one shared block per group of heads.
+    # Heads h of group g = h // (H / groups) use S_K[g], S_V[g]; 1 = one block for all heads
+    groups: int = 1
+
+    def group_of(self, h: int) -> int:
+        return h // (self.num_heads // self.groups)
 
     @property
     def elem_bytes(self) -> int:
@@ -154,10 +160,10 @@ class Layout:
 
 
 def page_elems(L: Layout) -> int:
-    """Elements in one page: P tokens x (2 shared rows of d_h + 2H private rows of r), plus
-    P x H key-norm reciprocals when the layout keeps them."""
+    """Elements in one page: P tokens x (2 shared rows of d_h per group + 2H private rows of
+    r), plus P x H key-norm reciprocals when the layout keeps them."""
     extra = L.page_size * L.num_heads if L.key_norm else 0
-    return L.page_size * 2 * (L.head_dim + L.num_heads * L.rank) + extra
+    return L.page_size * 2 * (L.groups * L.head_dim + L.num_heads * L.rank) + extra
 
 
 def page_bytes(L: Layout) -> int:
@@ -165,21 +171,27 @@ def page_bytes(L: Layout) -> int:
 
 
 def section_base(L: Layout, section: str, head: int = 0) -> int:
-    """Element offset, inside a page, of a section (per head for the private ones).
+    """Element offset, inside a page, of a section: `head` is the group for the shared
+    sections "SK", "SV" and the head for the private ones.
 
-    Order inside a page: S_K block, S_V block, R_K blocks for heads 0..H-1, R_V blocks for
-    heads 0..H-1.  A shared block holds P x d_h elements, a private block P x r.
+    A page is one block per group of heads, in group order; block g holds S_K[g], S_V[g]
+    (P x d_h each), then R_K of the group's heads, then R_V of the group's heads (P x r
+    each), so with one group: S_K, S_V, R_K[0..H-1], R_V[0..H-1].  The key-norm section
+    (one group only) follows: N[h], P elements per head.
     """
-    P, dh, r, H = L.page_size, L.head_dim, L.rank, L.num_heads
+    P, dh, r, H, G = L.page_size, L.head_dim, L.rank, L.num_heads, L.groups
+    Hg = H // G
+    block = P * 2 * (dh + Hg * r)
     if section == "SK":
-        return 0
+        return head * block
     if section == "SV":
-        return P * dh
+        return head * block + P * dh
+    g, j = divmod(head, Hg)  # private sections: group and place of the head in it
     if section == "RK":
-        return 2 * P * dh + head * P * r
+        return g * block + 2 * P * dh + j * P * r
     if section == "RV":
-        return 2 * P * dh + H * P * r + head * P * r
-    if section == "N" and L.key_norm:  # head h's P reciprocals, token after token
+        return g * block + 2 * P * dh + Hg * P * r + j * P * r
+    if section == "N" and L.key_norm and G == 1:  # head h's P reciprocals, token after token
         return 2 * P * dh + 2 * H * P * r + head * P
     raise ValueError(section)
 
@@ -211,15 +223,16 @@ def _read_block(pool, L: Layout, pages, t, section, head, width):
     return decode_elems(pool[byte_idx], L.dtype).reshape(len(pages), width)
 
 
-def gather_shared(pool, L: Layout, table_row, n_tokens: int):
-    """Page walk for the shared rows of tokens 0..n_tokens-1: S_K, S_V as [n, d_h] float64.
+def gather_shared(pool, L: Layout, table_row, n_tokens: int, group: int = 0):
+    """Page walk for the shared rows of tokens 0..n_tokens-1 (of one group of heads): S_K,
+    S_V as [n, d_h] float64.
 
     Token j lives in page table_row[j // P], slot j % P.
     """
     pool = np.asarray(pool, dtype=np.uint8).reshape(-1)
     pages, t = _positions_to_pages(L, table_row, n_tokens)
-    return (_read_block(pool, L, pages, t, "SK", 0, L.head_dim),
-            _read_block(pool, L, pages, t, "SV", 0, L.head_dim))
+    return (_read_block(pool, L, pages, t, "SK", group, L.head_dim),
+            _read_block(pool, L, pages, t, "SV", group, L.head_dim))
 
 
 def gather_private(pool, L: Layout, table_row, n_tokens: int, h: int):
@@ -242,8 +255,13 @@ def gather_norms(pool, L: Layout, table_row, n_tokens: int, h: int):
 
 
 def gather_request(pool: np.ndarray, L: Layout, table_row: np.ndarray, n_tokens: int) -> dict:
-    """Page walk over every section: S_K, S_V [n, d_h] and R_K, R_V [H, n, r], float64."""
-    SK, SV = gather_shared(pool, L, table_row, n_tokens)
+    """Page walk over every section: S_K, S_V [n, d_h] (grouped layouts: [G, n, d_h]) and
+    R_K, R_V [H, n, r], float64."""
+    if L.groups == 1:
+        SK, SV = gather_shared(pool, L, table_row, n_tokens)
+    else:
+        sh = [gather_shared(pool, L, table_row, n_tokens, g) for g in range(L.groups)]
+        SK, SV = np.stack([a for a, _ in sh]), np.stack([b for _, b in sh])
     priv = [gather_private(pool, L, table_row, n_tokens, h) for h in range(L.num_heads)]
     return {"SK": SK, "SV": SV,
             "RK": np.stack([p[0] for p in priv]) if priv else np.zeros((0, n_tokens, L.rank)),
@@ -263,11 +281,14 @@ def pack_pool(L: Layout, page_table, lens, SK, SV, RK, RV, num_pages: int, fill:
     SK, SV [sum(lens), d_h] and RK, RV [sum(lens), H, r] hold element *codes* (uint16
     bfloat16 codes, or uint32 float32 bit patterns), requests back to back in order.
     Every slot not written (pages no request owns, slots past a request's last token) holds
-    the code `fill`.  Returns the pool as uint8 [num_pages * page_bytes].
+    the code `fill`.  Returns the pool as uint8 [num_pages * page_bytes].  Grouped layouts
+    take SK, SV as [sum(lens), G, d_h].
     """
     st = storage_dtype(L)
     P, dh, r, H, C = L.page_size, L.head_dim, L.rank, L.num_heads, L.chunk
     pe = page_elems(L)
+    if L.groups > 1:
+        return _pack_pool_grouped(L, page_table, lens, SK, SV, RK, RV, num_pages, fill)
     pool = np.full((num_pages, pe), fill, dtype=st)
     off = 0
     for b, T in enumerate(lens):
@@ -308,6 +329,22 @@ def pack_pool(L: Layout, page_table, lens, SK, SV, RK, RV, num_pages: int, fill:
     return pool.view(np.uint8).reshape(-1)
 
 
+def _pack_pool_grouped(L: Layout, page_table, lens, SK, SV, RK, RV, num_pages, fill):
+    """Grouped layouts: each group's block is placed like a one-group page of its heads."""
+    G, H = L.groups, L.num_heads
+    Hg = H // G
+    Lg = Layout(Hg, L.head_dim, L.rank, L.page_size, L.dtype)
+    st = storage_dtype(L)
+    blk = page_elems(Lg)
+    pool = np.full((num_pages, page_elems(L)), fill, dtype=st)
+    for g in range(G):
+        part = pack_pool(Lg, page_table, lens, np.asarray(SK)[:, g], np.asarray(SV)[:, g],
+                         np.asarray(RK)[:, g * Hg:(g + 1) * Hg],
+                         np.asarray(RV)[:, g * Hg:(g + 1) * Hg], num_pages, fill)
+        pool[:, g * blk:(g + 1) * blk] = part.view(st).reshape(num_pages, blk)
+    return pool.view(np.uint8).reshape(-1)
+
+
 def write_rows(pool: np.ndarray, L: Layout, page_table: np.ndarray, row_req, row_pos,
                SK, SV, RK, RV) -> np.ndarray:
     """Place already-rounded rows at their (request, position) in a copy of the pool.
@@ -330,8 +367,13 @@ def write_rows(pool: np.ndarray, L: Layout, page_table: np.ndarray, row_req, row
                + in_block_index(L, width, t[:, None], np.arange(width)[None, :]))
         elems[idx.reshape(-1)] = encode_elems(vals, L.dtype).view(storage_dtype(L))
 
-    put("SK", 0, dh, np.asarray(SK))
-    put("SV", 0, dh, np.asarray(SV))
+    if L.groups == 1:
+        put("SK", 0, dh, np.asarray(SK))
+        put("SV", 0, dh, np.asarray(SV))
+    else:  # SK, SV [n, G, d_h]
+        for g in range(L.groups):
+            put("SK", g, dh, np.asarray(SK)[:, g])
+            put("SV", g, dh, np.asarray(SV)[:, g])
     for h in range(H if r else 0):
         put("RK", h, r, np.asarray(RK)[:, h])
         put("RV", h, r, np.asarray(RV)[:, h])
@@ -346,12 +388,17 @@ def write_rows(pool: np.ndarray, L: Layout, page_table: np.ndarray, row_req, row
 def project_rows(X, W_SK, W_SV, U_K, U_V):
     """Factored projections of new rows, float64 (eq 2-5; Algorithm 1 steps 02, 04, 05).
 
-    X [n, d]; W_SK, W_SV [d, d_h]; U_K, U_V [d, H, r].
-    Returns S_K, S_V [n, d_h] and R_K, R_V [n, H, r].
+    X [n, d]; W_SK, W_SV [d, d_h] (one shared block per group of heads: [G, d, d_h]);
+    U_K, U_V [d, H, r].
+    Returns S_K, S_V [n, d_h] (grouped: [n, G, d_h]) and R_K, R_V [n, H, r].
     """
     X = np.asarray(X, np.float64)
-    SK = X @ np.asarray(W_SK, np.float64)
-    SV = X @ np.asarray(W_SV, np.float64)
+    if np.ndim(W_SK) == 3:
+        SK = np.stack([X @ np.asarray(w, np.float64) for w in W_SK], axis=1)
+        SV = np.stack([X @ np.asarray(w, np.float64) for w in W_SV], axis=1)
+    else:
+        SK = X @ np.asarray(W_SK, np.float64)
+        SV = X @ np.asarray(W_SV, np.float64)
     d, H, r = np.shape(U_K)
     RK = (X @ np.asarray(U_K, np.float64).reshape(d, H * r)).reshape(-1, H, r)
     RV = (X @ np.asarray(U_V, np.float64).reshape(d, H * r)).reshape(-1, H, r)
@@ -470,8 +517,9 @@ def decode_reference(L: Layout, q, B_K, B_V, pool, page_table, seq_lens, sample=
     BV = np.asarray(B_V, np.float64)
     for b, items in sorted(want.items()):
         T = int(seq_lens[b])
-        SK, SV = gather_shared(pool, L, page_table[b], T)
+        shared = [gather_shared(pool, L, page_table[b], T, g) for g in range(L.groups)]
         for h in sorted({h for _, h in items}):
+            SK, SV = shared[L.group_of(h)]  # the shared block of the head's group
             RK, RV = gather_private(pool, L, page_table[b], T, h)
             K = reconstruct(SK, RK[None], BK[h:h + 1])[0]
             if L.key_norm:  # normalised key: the full key times its stored reciprocal
@@ -505,15 +553,17 @@ def decode_algorithm2(L: Layout, q, B_K, B_V, pool, page_table, seq_lens):
                 continue
             for h in range(H):
                 qh = q[b, i, h]
+                SKh = rows["SK"] if L.groups == 1 else rows["SK"][L.group_of(h)]
+                SVh = rows["SV"] if L.groups == 1 else rows["SV"][L.group_of(h)]
                 p = qh @ BK[h]  # private query, formed once for the whole history
-                shared = rows["SK"][:n] @ qh
+                shared = SKh[:n] @ qh
                 private = rows["RK"][h, :n] @ p
                 s = (shared + private) / math.sqrt(dh)  # one score per position, then softmax
                 if L.key_norm:  # the stored reciprocal multiplies the summed score
                     s = s * gather_norms(pool, L, page_table[b], T, h)[:n]
                 w = np.exp(s - s.max())
                 a = w / w.sum()
-                red_shared = a @ rows["SV"][:n]
+                red_shared = a @ SVh[:n]
                 red_private = a @ rows["RV"][h, :n]  # same weights as the shared branch
                 out[b, i, h] = red_shared + red_private @ BV[h].T  # expand once
     return out
@@ -585,8 +635,9 @@ def decode_reference_rope(L: Layout, q, B_K, B_V, pool, page_table, seq_lens, ro
     BV = np.asarray(B_V, np.float64)
     for b, items in sorted(want.items()):
         T = int(seq_lens[b])
-        SK, SV = gather_shared(pool, L, page_table[b], T)
+        shared = [gather_shared(pool, L, page_table[b], T, g) for g in range(L.groups)]
         for h in sorted({h for _, h in items}):
+            SK, SV = shared[L.group_of(h)]
             RK, RV = gather_private(pool, L, page_table[b], T, h)
             K = rope_keys(SK, RK[None], BK[h:h + 1], cs[:T, :, 0], cs[:T, :, 1])[0]
             if L.key_norm:  # a turn keeps the key's length: the same stored reciprocal
@@ -678,6 +729,12 @@ def param_ratio(H: int, r: int, d_h: int, d: int) -> Fraction:
 def decode_arith_ratio(T: int, r: int, d_h: int) -> Fraction:
     """Decode multiply-adds relative to dense: (2 T d_h + 2 T r + 2 r d_h) / (2 T d_h)."""
     return Fraction(2 * T * d_h + 2 * T * r + 2 * r * d_h, 2 * T * d_h)
+
+
+def grouped_cache_bytes(b: int, N: int, tokens: int, d_h: int, H: int, r: int, G: int) -> int:
+    """One shared block per group of heads (LRKV notes §3): the shared features are stored
+    G times, 2 b N (B T) (G d_h + H r)."""
+    return 2 * b * N * tokens * (G * d_h + H * r)
 
 
 def tp_replicated_ratio(P: int, H: int, r: int, d_h: int) -> Fraction:

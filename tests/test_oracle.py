@@ -917,3 +917,116 @@ def test_rope_with_key_norm():
         V = O.reconstruct(rows["SV"], rows["RV"][h:h + 1], BV[h:h + 1])[0]
         ref = sdpa(q[0, 0, h], K, V)
         assert rel_err(got[0, 0, h], ref) < 1e-6  # table rows are float32-rounded turns
+
+
+# --------------------------------------------------------------------------------------
+# one shared block per group of heads (LRKV notes §3, after the gradient formulas)
+# --------------------------------------------------------------------------------------
+
+
+def _grouped_case(seed, H, d_h, r, G, dtype, lens, permute=True):
+    g = np.random.default_rng(seed)
+    L = O.Layout(H, d_h, r, 16, dtype, groups=G)
+    n = int(sum(lens))
+    code = (lambda x: synth.to_bf16_bits(x.astype(np.float32))) if dtype == O.BF16 else \
+        (lambda x: x.astype(np.float32).view(np.uint32))
+    SK, SV = code(g.standard_normal((n, G, d_h))), code(g.standard_normal((n, G, d_h)))
+    RK, RV = code(g.standard_normal((n, H, r))), code(g.standard_normal((n, H, r)))
+    table, npg = synth.page_assignment(seed + 1, lens, 16, permute)
+    pool = O.pack_pool(L, table, lens, SK, SV, RK, RV, npg)
+    q = g.standard_normal((len(lens), 1, H, d_h))
+    BK = g.standard_normal((H, d_h, r)) / math.sqrt(r)
+    BV = g.standard_normal((H, d_h, r)) / math.sqrt(r)
+    return L, pool, table, lens, q, BK, BV, (SK, SV, RK, RV)
+
+
+def test_grouped_cache_size_is_the_replicated_shared_formula():
+    """G shared blocks store the shared features G times: page bytes over the dense page is
+    G/H + r/d_h, the page's own formula for shared rows held in P copies (LRKV notes §4,
+    tensor-parallel replication, with P = G), and eq 9's bytes with G d_h in place of d_h."""
+    for H, d_h, r, G in ((32, 128, 32, 2), (16, 128, 56, 4), (32, 128, 32, 32), (4, 16, 4, 2)):
+        L = O.Layout(H, d_h, r, 16, O.BF16, groups=G)
+        dense = 16 * 2 * H * d_h * 2
+        assert Fraction(O.page_bytes(L), dense) == O.tp_replicated_ratio(G, H, r, d_h)
+        assert O.grouped_cache_bytes(2, 1, 16, d_h, H, r, G) == O.page_bytes(L)
+    assert O.grouped_cache_bytes(2, 1, 16, 128, 16, 56, 1) == O.lrkv_cache_bytes(2, 1, 16, 128,
+                                                                                  16, 56)
+
+
+def test_one_group_is_the_plain_layout():
+    L, pool, table, lens, q, BK, BV, rows = _grouped_case(92, 4, 16, 4, 1, O.F32, [37, 5])
+    L1 = O.Layout(4, 16, 4, 16, O.F32)
+    SK, SV, RK, RV = rows
+    plain = O.pack_pool(L1, table, lens, SK[:, 0], SV[:, 0], RK, RV, int(table.max()) + 1)
+    assert np.array_equal(pool, plain)
+
+
+def test_grouped_decode_is_each_groups_own_lrkv():
+    """A grouped cache decodes, head by head, exactly as G independent one-group caches, one
+    per group holding that group's shared rows and its heads' private rows (packed and
+    decoded on their own)."""
+    H, d_h, r, G = 4, 16, 4, 2
+    L, pool, table, lens, q, BK, BV, rows = _grouped_case(93, H, d_h, r, G, O.F32, [37, 5, 16])
+    got = O.decode_reference(L, q, BK, BV, pool, table, lens)
+    got2 = O.decode_algorithm2(L, q, BK, BV, pool, table, lens)
+    assert rel_err(got2, got) < 1e-13
+    SK, SV, RK, RV = rows
+    Hg = H // G
+    Lg = O.Layout(Hg, d_h, r, 16, O.F32)
+    for g in range(G):
+        hs = slice(g * Hg, (g + 1) * Hg)
+        sub = O.pack_pool(Lg, table, lens, SK[:, g], SV[:, g], RK[:, hs], RV[:, hs],
+                          int(table.max()) + 1)
+        ref = O.decode_reference(Lg, q[:, :, hs], BK[hs], BV[hs], sub, table, lens)
+        assert np.array_equal(got[:, :, hs], ref)
+
+
+def test_one_group_per_head_rank_zero_is_mha():
+    """G = H and r = 0: every head has its own shared block, i.e. plain multi-head attention
+    over it (torch float64 attention)."""
+    H, d_h, n = 3, 8, 19
+    g = np.random.default_rng(94)
+    L = O.Layout(H, d_h, 0, 16, O.F32, groups=H)
+    SK = g.standard_normal((n, H, d_h)).astype(np.float32)
+    SV = g.standard_normal((n, H, d_h)).astype(np.float32)
+    z = np.zeros((n, H, 0), np.float32)
+    table, npg = synth.page_assignment(95, [n], 16, True)
+    pool = O.pack_pool(L, table, [n], SK.view(np.uint32), SV.view(np.uint32), z.view(np.uint32),
+                       z.view(np.uint32), npg)
+    q = g.standard_normal((1, 1, H, d_h))
+    none = np.zeros((H, d_h, 0))
+    out = O.decode_reference(L, q, none, none, pool, table, [n])
+    for h in range(H):
+        assert rel_err(out[0, 0, h], sdpa(q[0, 0, h], SK[:, h].astype(np.float64),
+                                          SV[:, h].astype(np.float64))) < 1e-13
+
+
+def test_grouped_mutant_wrong_group_fails(monkeypatch):
+    """Planted mistake: heads assigned to groups round robin (h mod G) instead of in
+    contiguous runs must fail the per-group decomposition."""
+    monkeypatch.setattr(O.Layout, "group_of", lambda self, h: h % self.groups)
+    with pytest.raises(AssertionError):
+        test_grouped_decode_is_each_groups_own_lrkv()
+
+
+def test_grouped_append_places_each_groups_projection():
+    """Algorithm 1 with one shared projection per group: S_K[g] = X W_SK[g], placed in group
+    g's block; exact-integer inputs, compared with the per-group one-group append."""
+    H, d_h, r, G, d = 4, 16, 8, 2, 64
+    g = np.random.default_rng(96)
+    L = O.Layout(H, d_h, r, 16, O.BF16, groups=G)
+    X = g.integers(-1, 2, (5, d)).astype(np.float64)
+    WK, WV = g.integers(-1, 2, (G, d, d_h)), g.integers(-1, 2, (G, d, d_h))
+    UK, UV = g.integers(-1, 2, (d, H, r)), g.integers(-1, 2, (d, H, r))
+    table, npg = synth.page_assignment(97, [20, 9], 16, True)
+    req, pos = np.array([0, 1, 0, 1, 0]), np.array([19, 0, 16, 8, 3])
+    start = np.zeros(npg * O.page_elems(L), np.uint16).view(np.uint8)
+    got = O.append_reference(start, L, X, WK, WV, UK, UV, req, pos, table)
+    Lg = O.Layout(H // G, d_h, r, 16, O.BF16)
+    blk = O.page_elems(Lg)
+    el = got.view(np.uint16).reshape(npg, -1)
+    for gg in range(G):
+        hs = slice(gg * 2, gg * 2 + 2)
+        sub = O.append_reference(np.zeros(npg * blk, np.uint16).view(np.uint8), Lg, X, WK[gg],
+                                 WV[gg], UK[:, hs], UV[:, hs], req, pos, table)
+        assert np.array_equal(el[:, gg * blk:(gg + 1) * blk], sub.view(np.uint16).reshape(npg, blk))
