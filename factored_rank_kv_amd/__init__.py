@@ -36,12 +36,13 @@ class lrkv_layout(ctypes.Structure):
         ("page_size", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("key_norm", ctypes.c_int32),
+        ("groups", ctypes.c_int32),
     ]
 
     def __repr__(self):
         return (f"lrkv_layout(H={self.num_heads}, d_h={self.head_dim}, r={self.rank}, "
                 f"P={self.page_size}, dtype={'bf16' if self.dtype == LRKV_BF16 else 'f32'}, "
-                f"key_norm={self.key_norm})")
+                f"key_norm={self.key_norm}, groups={self.groups})")
 
 
 class lrkv_page_pool(ctypes.Structure):

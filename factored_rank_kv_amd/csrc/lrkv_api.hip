@@ -21,7 +21,10 @@ namespace {
 
 using namespace lrkv;
 
-enum Variant { V_NONE = -1, V_C0 = 0, V_C1 = 1, V_C3 = 2, V_C1N = 3, V_C3N = 4 };
+enum Variant { V_NONE = -1, V_C0 = 0, V_C1 = 1, V_C3 = 2, V_C1N = 3, V_C3N = 4, V_C3G2 = 5 };
+
+// shared blocks of a layout (0 and 1 both mean one block for all heads)
+int groups_of(const lrkv_layout* L) { return L->groups > 1 ? L->groups : 1; }
 
 // The split kernel holds one chunk's page ids in LDS (256 pages of 16 tokens).
 constexpr int kMaxChunkTokens = 256 * 16;
@@ -34,6 +37,7 @@ bool layout_valid(const lrkv_layout* L) {
   const int chunk = L->dtype == LRKV_BF16 ? 8 : 4;
   if (L->head_dim % chunk || L->rank % chunk) return false;
   if (L->key_norm != 0 && L->key_norm != 1) return false;
+  if (L->groups < 0 || L->num_heads % groups_of(L)) return false;
   // the norm section (H x P elements) keeps pages whole 16-byte units
   if (L->key_norm && ((long long)L->num_heads * L->page_size * (L->dtype == LRKV_BF16 ? 2 : 4)) % 16)
     return false;
@@ -44,6 +48,9 @@ Variant find_variant(const lrkv_layout* L) {
   if (L->page_size != kPage) return V_NONE;
   const int H = L->num_heads, dh = L->head_dim, r = L->rank;
   const bool nk = L->key_norm != 0;
+  const int G = groups_of(L);
+  if (G == 2 && !nk && L->dtype == LRKV_BF16 && H == 32 && dh == 128 && r == 32) return V_C3G2;
+  if (G != 1) return V_NONE;
   if (L->dtype == LRKV_F32 && H == 4 && dh == 16 && r == 4 && !nk) return V_C0;
   if (L->dtype == LRKV_BF16 && H == 16 && dh == 128 && r == 56) return nk ? V_C1N : V_C1;
   if (L->dtype == LRKV_BF16 && H == 32 && dh == 128 && r == 32) return nk ? V_C3N : V_C3;
@@ -100,7 +107,7 @@ struct DecodeSizes {
 DecodeSizes decode_sizes(const lrkv_layout* L, int batch, int q_len, int max_seq_len,
                          int chunk_tokens) {
   DecodeSizes z{};
-  if (L->dtype == LRKV_BF16 && !L->key_norm && q_len >= kPrefillMinRows) {
+  if (L->dtype == LRKV_BF16 && !L->key_norm && groups_of(L) == 1 && q_len >= kPrefillMinRows) {
     // multi-query kernel: no split, no workspace (one 256-byte block keeps the pointer
     // contract uniform)
     z.chunk = chunk_tokens > 0 ? chunk_tokens : L->page_size;
@@ -219,6 +226,7 @@ int decode_launch(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_
     case V_C3: return hip_status(launch_decode<ShapeC3>(a));
     case V_C1N: return hip_status(launch_decode<ShapeC1N>(a));
     case V_C3N: return hip_status(launch_decode<ShapeC3N>(a));
+    case V_C3G2: return hip_status(launch_decode_grouped<ShapeC3G, ShapeC3>(a, 2));
     default: return LRKV_ERR_UNSUPPORTED;
   }
 }
@@ -259,7 +267,8 @@ size_t lrkv_page_bytes(const lrkv_layout* L) {
   if (!layout_valid(L)) return 0;
   const size_t b = L->dtype == LRKV_BF16 ? 2 : 4;
   const size_t norm = L->key_norm ? (size_t)L->page_size * L->num_heads * b : 0;
-  return (size_t)L->page_size * 2 * ((size_t)L->head_dim + (size_t)L->num_heads * L->rank) * b +
+  return (size_t)L->page_size * 2 *
+             ((size_t)groups_of(L) * L->head_dim + (size_t)L->num_heads * L->rank) * b +
          norm;
 }
 
@@ -321,7 +330,7 @@ int lrkv_decode_rope(const lrkv_layout* L, const void* q, int32_t batch, int32_t
   if (!rope_cs || !aligned16(rope_cs) || rope_rows < max_seq_len || rope_rows <= 0)
     return LRKV_ERR_INVALID_ARG;
   const Variant v = find_variant(L);
-  if (v == V_C0 || v == V_NONE) return LRKV_ERR_UNSUPPORTED;  // bf16 variants only
+  if (v == V_C0 || v == V_NONE || v == V_C3G2) return LRKV_ERR_UNSUPPORTED;  // bf16, one group
   z = rope_sizes(L, batch, q_len, max_seq_len, chunk_tokens);
   if (z.n_split > 65535) return LRKV_ERR_INVALID_ARG;
   if ((long long)batch * q_len * z.n_split * (L->num_heads / 4) > 0x7fffffffLL - 8)
@@ -408,6 +417,21 @@ int lrkv_append(const lrkv_layout* L, const void* X, int32_t n_rows, int32_t d,
     case V_C3: return hip_status(launch_append<ShapeC3>(a));
     case V_C1N: return hip_status(launch_append<ShapeC1N>(a));
     case V_C3N: return hip_status(launch_append<ShapeC3N>(a));
+    case V_C3G2: {  // each group's block as a one-group page of its 16 heads
+      for (int g = 0; g < 2; ++g) {
+        AppendArgs b = a;
+        const size_t wsh = (size_t)L->head_dim * d * 2, wpr = (size_t)16 * L->rank * d * 2;
+        b.W_SK = static_cast<const uint8_t*>(W_SK) + g * wsh;
+        b.W_SV = static_cast<const uint8_t*>(W_SV) + g * wsh;
+        b.U_K = static_cast<const uint8_t*>(U_K) + g * wpr;
+        b.U_V = static_cast<const uint8_t*>(U_V) + g * wpr;
+        b.page_elems = 2 * (ShapeC3G::PAGE / 2);
+        b.elem_off = (long long)g * (ShapeC3G::PAGE / 2);
+        const int st = hip_status(launch_append<ShapeC3G>(b));
+        if (st != LRKV_OK) return st;
+      }
+      return LRKV_OK;
+    }
     default: return LRKV_ERR_UNSUPPORTED;
   }
 }

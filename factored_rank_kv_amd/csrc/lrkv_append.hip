@@ -128,7 +128,7 @@ append_few_rows_mfma_kernel(AppendArgs a) {
   if (storer) {
     const int r = t >> 3, c = t & 7;
     const float sum = (red[0][r][c] + red[1][r][c]) + (red[2][r][c] + red[3][r][c]);
-    store_elem<S>(a.pool, (size_t)page * (S::PAGE / S::EB) + append_dest<S>(col0 + c, pos % S::P),
+    store_elem<S>(a.pool, (size_t)page * a.page_elems + a.elem_off + append_dest<S>(col0 + c, pos % S::P),
                   sum);
   }
 }
@@ -172,7 +172,8 @@ append_few_rows_f32_kernel(AppendArgs a) {
       const int req = a.row_req[r];
       const int pos = a.row_pos[r];
       const int page = a.page_table[(size_t)req * a.max_pages + pos / S::P];
-      store_elem<S>(a.pool, (size_t)page * (S::PAGE / S::EB) + append_dest<S>(col0 + cc, pos % S::P),
+      store_elem<S>(a.pool, (size_t)page * a.page_elems + a.elem_off +
+                                append_dest<S>(col0 + cc, pos % S::P),
                     sum);
     }
   }
@@ -414,7 +415,7 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
     const int cc = idx / G::BM;  // column chunk 0..15
     if (row0 + r < a.n_rows) {
       const uint4 v = *reinterpret_cast<const uint4*>(ot + r * G::OS + 16 * cc);
-      const size_t e = (size_t)row_page[r] * (S::PAGE / 2) +
+      const size_t e = (size_t)row_page[r] * a.page_elems + a.elem_off +
                        append_dest<S>(col0 + 8 * cc, row_slot[r]);
       *reinterpret_cast<uint4*>(pool + e) = v;
     }
@@ -425,7 +426,9 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
 constexpr int kGemmMinRows = 64;
 
 template <class S>
-hipError_t launch_append(const AppendArgs& a) {
+hipError_t launch_append(const AppendArgs& a_in) {
+  AppendArgs a = a_in;
+  if (a.page_elems == 0) a.page_elems = S::PAGE / S::EB;  // one group: the page is the block
   if constexpr (S::BF) {
     if (a.n_rows >= kGemmMinRows && a.d % GemmCfg<S>::BK == 0) {
       // the kernel addresses X rows by 32-bit byte offsets from X: batches of rows that span
@@ -465,5 +468,6 @@ template hipError_t launch_append<ShapeC1>(const AppendArgs&);
 template hipError_t launch_append<ShapeC3>(const AppendArgs&);
 template hipError_t launch_append<ShapeC1N>(const AppendArgs&);
 template hipError_t launch_append<ShapeC3N>(const AppendArgs&);
+template hipError_t launch_append<ShapeC3G>(const AppendArgs&);
 
 }  // namespace lrkv

@@ -95,6 +95,14 @@ struct SplitArgs {
   int batch;
   int groups;  // balanced mode: split workgroups (0: one workgroup per chunk)
   float score_scale;
+  // grouped pages: bytes from page to page and to this group's block; heads of a query
+  // row and of a partial record in memory (the whole layout's), and this group's first
+  // head.  A one-group page: S::PAGE, 0, S::H, S::H, 0.
+  long long page_stride;
+  long long page_off;
+  int q_heads;
+  int rec_heads;
+  int head0;
 };
 
 // Balanced split (single query row per request): the batch's N pages, request after request,
@@ -692,7 +700,7 @@ decode_split_kernel(const SplitArgs a) {
   constexpr int QCH = (S::H * S::DHC + C::NT - 1) / C::NT;
   uint4 q_r[QCH];
   const uint4* qsrc = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.q) +
-                                                     row * S::H * S::DH * S::EB);
+                                                     (row * a.q_heads + a.head0) * S::DH * S::EB);
 #pragma unroll
   for (int k = 0; k < QCH; ++k) {
     const int i = tid + k * C::NT;
@@ -724,7 +732,9 @@ decode_split_kernel(const SplitArgs a) {
 
   const int pg1 = (tok1 + S::P - 1) / S::P;
   const uint8_t* pool = a.pool;
-  auto page_ptr = [&](int pg) { return pool + (size_t)ids_lds[pg - pg0] * S::PAGE; };
+  auto page_ptr = [&](int pg) {
+    return pool + (size_t)ids_lds[pg - pg0] * (size_t)a.page_stride + (size_t)a.page_off;
+  };
   auto nvalid = [&](int pg) { return min(S::P, tok1 - pg * S::P); };
 
   // two register buffers of pages: page k+1 travels while page k is consumed, and page
@@ -794,7 +804,7 @@ decode_split_kernel(const SplitArgs a) {
 
   // ---- partial tuple of this chunk: m, l, acc_S[DH], acc_R[R] per head
   const float l_tot = r16_sum(st.l_run);
-  float* dst = a.part + (slot * S::H + L.h) * S::PART_PAD;
+  float* dst = a.part + (slot * a.rec_heads + a.head0 + L.h) * S::PART_PAD;
   if (L.j == 0 && L.half == 0) {
     dst[0] = st.m_run;
     dst[1] = l_tot;
@@ -818,7 +828,7 @@ decode_split_kernel(const SplitArgs a) {
   }
   if constexpr (C::MFMA_SV) {
     // MFMA tile: lane holds heads 16*ht + 4*(lane/16) + e, feature 16*wave + lane%16
-    float* rec = a.part + slot * S::H * S::PART_PAD;
+    float* rec = a.part + (slot * a.rec_heads + a.head0) * S::PART_PAD;
 #pragma unroll
     for (int ht = 0; ht < C::HT; ++ht)
 #pragma unroll
@@ -829,7 +839,8 @@ decode_split_kernel(const SplitArgs a) {
 #pragma unroll
     for (int x = 0; x < C::HPW; ++x) {
       float2* d2 = reinterpret_cast<float2*>(
-          a.part + (slot * S::H + C::HPW * L.wave + x) * S::PART_PAD + 2 + 2 * L.lane);
+          a.part + (slot * a.rec_heads + a.head0 + C::HPW * L.wave + x) * S::PART_PAD + 2 +
+          2 * L.lane);
       *d2 = make_float2(st.accS[x][0], st.accS[x][1]);
     }
   }
@@ -1023,10 +1034,7 @@ merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
 // host launcher
 // ---------------------------------------------------------------------------------------
 template <class S>
-hipError_t launch_decode(const DecodeArgs& a) {
-  if constexpr (S::BF && !S::NORM) {  // key-norm layouts: every row through the split
-    if (a.q_len >= kPrefillMinRows) return launch_prefill<S>(a);
-  }
+SplitArgs split_args(const DecodeArgs& a) {
   SplitArgs s{};
   s.q = a.q;
   s.BK = a.B_K;
@@ -1041,20 +1049,62 @@ hipError_t launch_decode(const DecodeArgs& a) {
   s.batch = a.batch;
   s.groups = a.groups;
   s.score_scale = 1.4426950408889634f / sqrtf((float)S::DH);
-  if (a.groups > 0) {  // balanced split, one query row per request
+  s.page_stride = S::PAGE;
+  s.page_off = 0;
+  s.q_heads = S::H;
+  s.rec_heads = S::H;
+  s.head0 = 0;
+  return s;
+}
+
+template <class S>
+void launch_split(const DecodeArgs& a, const SplitArgs& s) {
+  if (a.groups > 0)
     hipLaunchKernelGGL((decode_split_kernel<S, true>), dim3(a.groups), dim3(SplitCfg<S>::NT), 0,
                        a.stream, s);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<S, false>), dim3((a.batch * a.q_len * a.n_split + 7) / 8 * 8),
+                       dim3(SplitCfg<S>::NT), 0, a.stream, s);
+}
+
+template <class S>
+hipError_t launch_decode(const DecodeArgs& a) {
+  if constexpr (S::BF && !S::NORM) {  // key-norm layouts: every row through the split
+    if (a.q_len >= kPrefillMinRows) return launch_prefill<S>(a);
+  }
+  launch_split<S>(a, split_args<S>(a));
+  if (a.groups > 0) {  // balanced split, one query row per request
     hipLaunchKernelGGL((merge_expand_kernel<S, true>), dim3(S::H, 1, a.batch), dim3(256), 0,
                        a.stream, a.part_ws, a.B_V, a.seq_lens, 1, 0, 0, a.batch, a.groups,
                        a.max_pages, a.out);
-  } else {
-    const int split_blocks = (a.batch * a.q_len * a.n_split + 7) / 8 * 8;
-    hipLaunchKernelGGL((decode_split_kernel<S, false>), dim3(split_blocks),
-                       dim3(SplitCfg<S>::NT), 0, a.stream, s);
-    return launch_merge<S>(a);
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  return launch_merge<S>(a);
 }
+
+template <class Sg, class S>
+hipError_t launch_decode_grouped(const DecodeArgs& a, int G) {
+  static_assert(Sg::DH == S::DH && Sg::R == S::R && Sg::BF == S::BF && !S::NORM, "group blocks");
+  for (int g = 0; g < G; ++g) {
+    SplitArgs s = split_args<Sg>(a);
+    s.BK = static_cast<const uint8_t*>(a.B_K) + (size_t)g * Sg::H * Sg::DH * Sg::R * Sg::EB;
+    s.page_stride = (long long)G * Sg::PAGE;
+    s.page_off = (long long)g * Sg::PAGE;
+    s.q_heads = S::H;
+    s.rec_heads = S::H;
+    s.head0 = g * Sg::H;
+    launch_split<Sg>(a, s);
+  }
+  if (a.groups > 0) {
+    hipLaunchKernelGGL((merge_expand_kernel<S, true>), dim3(S::H, 1, a.batch), dim3(256), 0,
+                       a.stream, a.part_ws, a.B_V, a.seq_lens, 1, 0, 0, a.batch, a.groups,
+                       a.max_pages, a.out);
+    return hipGetLastError();
+  }
+  return launch_merge<S>(a);
+}
+
+template hipError_t launch_decode_grouped<ShapeC3G, ShapeC3>(const DecodeArgs&, int);
 
 template <class S>
 hipError_t launch_merge(const DecodeArgs& a) {

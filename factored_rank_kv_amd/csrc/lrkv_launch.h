@@ -15,6 +15,8 @@ using ShapeC3 = Shape<32, 128, 32, true>;  // bf16, 32 heads, rank 32
 // the same bf16 shapes with the key-norm section in every page
 using ShapeC1N = Shape<16, 128, 56, true, true>;
 using ShapeC3N = Shape<32, 128, 32, true, true>;
+// one block of a grouped page: 16 heads of rank 32 (the 32-head layout in 2 groups)
+using ShapeC3G = Shape<16, 128, 32, true>;
 
 struct DecodeArgs {
   const void* q;
@@ -50,10 +52,19 @@ struct AppendArgs {
   int max_pages;
   void* pool;
   hipStream_t stream;
+  // grouped pages: elements from page to page, and the group block's first element (0 and
+  // 0: a one-group page of shape S)
+  long long page_elems;
+  long long elem_off;
 };
 
 template <class S>
 hipError_t launch_decode(const DecodeArgs& a);
+
+// Grouped layout of G blocks of shape Sg (G * Sg::H = S::H heads): the split kernels run
+// per group on its block, one merge of shape S covers every head.
+template <class Sg, class S>
+hipError_t launch_decode_grouped(const DecodeArgs& a, int G);
 
 // The merge + expansion of a chunked split's partial records (records [batch][q_len]
 // [n_split][H], chunk tokens a.chunk), on a.stream.

@@ -34,6 +34,12 @@
  * With key_norm = 1 a fifth section follows R_V (LRKV notes §8, RMSNorm paragraph):
  *   N[h]         at 2*P*d_h + 2*H*P*r + h*P   P elements: 1/n of head h for slots 0..P-1
  *
+ * Grouped pages (LRKV notes §3, after the gradient formulas: one shared block per group of
+ * heads, groups = G > 1, H a multiple of G): head h belongs to group g = h / (H/G) and uses
+ * that group's shared rows S_K[g], S_V[g].  A page is G blocks in group order, block g laid
+ * out exactly like a one-group page of the group's H/G heads (S_K[g], S_V[g], then R_K and
+ * R_V of heads g*H/G .. (g+1)*H/G - 1); page_bytes = P * 2 * (G*d_h + H*r) * b.
+ *
  * Token position j of request b lives in page page_table[b * max_pages_per_req + j / P],
  * slot j % P, in all sections.  Page ids index a pool of num_pages * page_bytes bytes.
  *
@@ -56,7 +62,9 @@
  * Shapes with a compiled kernel variant, (H, d_h, r, dtype):
  *   (4, 16, 4, LRKV_F32), (16, 128, 56, LRKV_BF16), (32, 128, 32, LRKV_BF16); P = 16;
  *   the two bf16 shapes also with key_norm = 1 (their multi-query calls then run through
- *   the split decode kernels rather than the prefill kernel).
+ *   the split decode kernels rather than the prefill kernel); (32, 128, 32, LRKV_BF16)
+ *   also with groups = 2 (lrkv_append and lrkv_decode; multi-query calls through the split
+ *   kernels).
  * Any other shape returns LRKV_ERR_UNSUPPORTED.
  */
 #ifndef LRKV_H
@@ -91,6 +99,7 @@ typedef struct lrkv_layout {
   int32_t page_size; /* P   */
   int32_t dtype;     /* LRKV_F32 or LRKV_BF16 */
   int32_t key_norm;  /* 0, or 1: pages keep the key-norm section N (see lrkv_key_norms) */
+  int32_t groups;    /* shared blocks G (0 or 1: one for all heads); see "Grouped pages" */
 } lrkv_layout;
 
 /* Bytes of one page: P * 2 * (d_h + H*r) * b, plus P * H * b with key_norm.  With P tokens
@@ -127,6 +136,7 @@ size_t lrkv_page_bytes(const lrkv_layout* L);
  *                                    distinct (request, position) pairs
  *   page_table device, [*][max_pages_per_req] int32; the caller assigns the pages
  *   pool     device, num_pages * lrkv_page_bytes(L) bytes
+ * Grouped layouts take one shared projection per group: W_SK and W_SV as [G][d_h][d].
  * d must be a positive multiple of 8.  n_rows == 0 is a no-op returning LRKV_OK. */
 int lrkv_append(const lrkv_layout* L, const void* X, int32_t n_rows, int32_t d,
                 const void* W_SK, const void* W_SV, const void* U_K, const void* U_V,

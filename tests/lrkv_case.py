@@ -25,7 +25,7 @@ def log(msg):
 
 def layout_c(L: O.Layout) -> F.lrkv_layout:
     return F.lrkv_layout(L.num_heads, L.head_dim, L.rank, L.page_size, L.dtype,
-                         1 if L.key_norm else 0)
+                         1 if L.key_norm else 0, L.groups)
 
 
 def as_codes(x: np.ndarray, dtype: int) -> np.ndarray:

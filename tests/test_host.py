@@ -246,13 +246,13 @@ def test_header_is_plain_c():
     with tempfile.TemporaryDirectory() as d:
         src = os.path.join(d, "t.c")
         with open(src, "w") as f:
-            f.write('#include "lrkv.h"\nint main(void){lrkv_layout L={16,128,56,16,LRKV_BF16,0};'
-                    'return (int)sizeof(L) - 24;}\n')
+            f.write('#include "lrkv.h"\nint main(void){lrkv_layout L={16,128,56,16,LRKV_BF16,0,1};'
+                    'return (int)sizeof(L) - 28;}\n')
         r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
                             "-c", src, "-o", os.path.join(d, "t.o")], capture_output=True,
                            text=True)
         assert r.returncode == 0, r.stderr
-    assert ctypes.sizeof(F.lrkv_layout) == 24
+    assert ctypes.sizeof(F.lrkv_layout) == 28
 
 
 def test_binding_refuses_host_tensors():
