@@ -230,6 +230,21 @@ def main():
     log(f"decode call by event pairs over {len(calls)} calls: p10 {pct[10]:.2f} p50 "
         f"{pct[50]:.2f} p90 {pct[90]:.2f} us")
 
+    # achievable read bound: a plain streaming read (lrkv_read_probe) of the same bytes, on
+    # the same rotating pool copies, best over a few grid sizes
+    sink = torch.empty(2048 * 16, dtype=torch.uint8, device=dev)
+    probe = {}
+    for wg in (256, 512, 1024, 2048):
+        def read_all(k, wg=wg):
+            F.lrkv_read_probe(pools[k % len(pools)], alg_bytes, wg, sink)
+        read_all(0)
+        probe[wg] = timed(read_all, args.steps, use_graph)[0] * 1e3
+    wg_best = min(probe, key=probe.get)
+    read_us = probe[wg_best]
+    log("read probe over the call's bytes: " +
+        ", ".join(f"{wg} wg {us:.2f} us" for wg, us in probe.items()) +
+        f"; decode call = {ms_decode * 1e3 / read_us:.3f} x the best read")
+
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -264,6 +279,11 @@ def main():
         "call_us_p10_p50_p90": [round(pct[10], 3), round(pct[50], 3), round(pct[90], 3)],
         "calls_in_distribution": int(len(calls)),
         "achieved_at_p50": round(alg_bytes / (pct[50] * 1e-6) / 1e9, 1),
+        "read_probe": {"what": "plain streaming read of the same bytes (lrkv_read_probe)",
+                       "us": round(read_us, 3), "workgroups": wg_best,
+                       "GB/s": round(alg_bytes / (read_us * 1e-6) / 1e9, 1),
+                       "frac": round(alg_bytes / (read_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                       "call_over_probe": round(ms_decode * 1e3 / read_us, 4)},
     }
 
     result = {

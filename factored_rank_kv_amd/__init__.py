@@ -102,6 +102,8 @@ def _load():
     lib.lrkv_decode_noalloc.restype = ctypes.c_int
     lib.lrkv_check_indices.argtypes = [LP, P, I32, I32, P, I32, P, P, I32, I64, P, P]
     lib.lrkv_check_indices.restype = ctypes.c_int
+    lib.lrkv_read_probe.argtypes = [P, ctypes.c_uint64, I32, P, P]
+    lib.lrkv_read_probe.restype = ctypes.c_int
     lib.lrkv_status_string.argtypes = [ctypes.c_int]
     lib.lrkv_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -112,7 +114,7 @@ EXPORTS = ("lrkv_page_bytes", "lrkv_append", "lrkv_decode_workspace_bytes", "lrk
            "lrkv_decode_noalloc", "lrkv_decode_rope", "lrkv_decode_rope_workspace_bytes",
            "lrkv_key_norms", "lrkv_pages_init", "lrkv_pages_alloc", "lrkv_pages_retain",
            "lrkv_pages_release", "lrkv_fork_prefix", "lrkv_copy_pages",
-           "lrkv_check_indices", "lrkv_status_string")
+           "lrkv_check_indices", "lrkv_read_probe", "lrkv_status_string")
 
 
 def library():
@@ -299,6 +301,14 @@ def lrkv_decode_noalloc(layout, q, batch, q_len, B_K, B_V, pool, page_table, max
                                      _stream(stream))
     if check and st != LRKV_OK:
         raise LRKVError(st, "lrkv_decode_noalloc")
+    return st
+
+
+def lrkv_read_probe(buf, nbytes, workgroups, sink, stream=None, check=True) -> int:
+    """Streaming read of nbytes of `buf` (measurement only; see include/lrkv.h)."""
+    st = _load().lrkv_read_probe(_ptr(buf), nbytes, workgroups, _ptr(sink), _stream(stream))
+    if check and st != LRKV_OK:
+        raise LRKVError(st, "lrkv_read_probe")
     return st
 
 

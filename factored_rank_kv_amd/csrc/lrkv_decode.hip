@@ -13,7 +13,7 @@
 //                            Writes the chunk's (max, exp-sum, acc_S, acc_R) tuple per head.
 //   2. merge_expand_kernel   merges the chunks' tuples with one rescale factor per chunk,
 //                            expands acc_R through B_V[h]^T once and divides by the exp-sum
-//                            (Algorithm 2 steps 08-09 without W_O).
+//                            (the output steps of Algorithm 2, without W_O).
 //
 // This file is compiled with -fno-honor-nans (max reductions fuse into DPP ops); masked
 // page slots are removed by integer selects, so NaN bytes there never reach arithmetic.

@@ -437,11 +437,14 @@ prefill_kernel(const PrefillArgs a) {
         for (int e = 0; e < 8; ++e) {
           const float s = sc[w][2 * tp + e / 4][e % 4];
           p[e] = exp2_fast(fmaf(s, a.score_scale, -m_run[w]));  // 0 for a masked score
-          l_part[w] += p[e];
         }
-        pp[w][tp] = __builtin_bit_cast(
-            bf16x8_p, make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                 pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
+        const uint4 pw = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                    pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+        // the exp-sum takes the same bf16-rounded weights the value products use, so the
+        // normalisation divides by exactly the weights that were summed
+        l_part[w] += ((bf16_lo(pw.x) + bf16_hi(pw.x)) + (bf16_lo(pw.y) + bf16_hi(pw.y))) +
+                     ((bf16_lo(pw.z) + bf16_hi(pw.z)) + (bf16_lo(pw.w) + bf16_hi(pw.w)));
+        pp[w][tp] = __builtin_bit_cast(bf16x8_p, pw);
       }
     }
 

@@ -12,7 +12,7 @@
 //   score_j = (q~ D_j^T) . (s_j + z_j B_K[h]^T) = (q~ D_j^T) . s_j + ((q~ D_j^T) B_K[h]) . z_j.
 // Values carry no rotation: the same online softmax, both value accumulators with one
 // weight per position, and the same partial records, merged and expanded once through
-// B_V[h]^T by the split decode's merge kernel (Algorithm 2 steps 06-09).
+// B_V[h]^T by the split decode's merge kernel (the softmax, value and output steps of Algorithm 2).
 //
 // Workgroup = (chunk of pages, group of 4 heads, query row, request), 4 wavefronts, one head
 // each; the chunk's S_K/S_V pages and (cos, sin) rows are staged once in LDS for the 4 heads

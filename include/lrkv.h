@@ -167,7 +167,7 @@ int lrkv_key_norms(const lrkv_layout* L, const void* B_K, float eps, const int32
 size_t lrkv_decode_workspace_bytes(const lrkv_layout* L, int32_t batch, int32_t q_len,
                                    int32_t max_seq_len, int32_t chunk_tokens);
 
-/* Algorithm 2 of LRKV notes §3 (steps 02-09 without the output projection W_O), read
+/* Algorithm 2 of LRKV notes §3 (every step but the output projection W_O), read
  * straight from the factored paged cache.
  *
  * For request b, query row i and head h, with T_b = seq_lens[b] cached tokens (the new
@@ -326,6 +326,17 @@ int lrkv_fork_prefix(const lrkv_layout* L, lrkv_page_pool* pp, const int32_t* pa
  * src_ids, dst_ids: device int32 [n]; pool: device, 16-byte aligned. */
 int lrkv_copy_pages(const lrkv_layout* L, void* pool, const int32_t* src_ids,
                     const int32_t* dst_ids, int32_t n, void* stream);
+
+/* Infrastructure of this library (measurement), not an operation of the method: a plain
+ * streaming read of `bytes` bytes of device memory at `buf` by `workgroups` workgroups of
+ * 256 threads (16-byte loads), the bound for any kernel that must read those bytes once.
+ *   buf   device, 16-byte aligned, bytes > 0 a multiple of 16
+ *   sink  device, workgroups * 16 bytes, 16-byte aligned: each workgroup writes the XOR
+ *         fold of what it read (written so that no read can be elided)
+ * Enqueued on `stream`; LRKV_ERR_INVALID_ARG for bad arguments, LRKV_ERR_HIP if the launch
+ * fails. */
+int lrkv_read_probe(const void* buf, uint64_t bytes, int32_t workgroups, void* sink,
+                    void* stream);
 
 /* Infrastructure of this library, not an operation of the method: the text of a status
  * code (static storage). */

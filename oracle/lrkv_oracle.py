@@ -386,7 +386,7 @@ def write_rows(pool: np.ndarray, L: Layout, page_table: np.ndarray, row_req, row
 
 
 def project_rows(X, W_SK, W_SV, U_K, U_V):
-    """Factored projections of new rows, float64 (eq 2-5; Algorithm 1 steps 02, 04, 05).
+    """Factored projections of new rows, float64 (eq 2-5; the projection and cache-write steps of Algorithm 1).
 
     X [n, d]; W_SK, W_SV [d, d_h] (one shared block per group of heads: [G, d, d_h]);
     U_K, U_V [d, H, r].
@@ -691,7 +691,7 @@ def merge_states(states):
 
 
 def finish_state(state, BV_h):
-    """o = (acc_S + acc_R B_V[h]^T) / l (Algorithm 2 steps 08-09 without W_O)."""
+    """o = (acc_S + acc_R B_V[h]^T) / l (the output steps of Algorithm 2, without W_O)."""
     _, l, acc_s, acc_r = state
     return (acc_s + acc_r @ np.asarray(BV_h, np.float64).T) / l
 

@@ -96,21 +96,23 @@ class Case:
         return self._dev
 
     def run(self, chunk_tokens: int = 0, max_seq_len: int | None = None, table=None,
-            pool=None, ws_fill: int | None = 0xFF) -> torch.Tensor:
+            pool=None, ws_fill: int | None = 0xFF, ws=None) -> torch.Tensor:
         """lrkv_decode on the device; returns the output codes tensor.
 
-        The workspace is pre-filled with the byte `ws_fill` (0xFF: every float32 there is a
-        NaN), so an output that depends on a record the call did not write is caught."""
+        A fresh workspace is filled with the byte `ws_fill` (0xFF: every float32 there is a
+        NaN, so an output that depends on a record the call did not write is caught); `ws`
+        reuses a workspace as the earlier calls left it."""
         d = self.dev
         L = self.L
         msl = int(self.lens.max()) if max_seq_len is None else max_seq_len
         lay = layout_c(L)
         ws_bytes = F.lrkv_decode_workspace_bytes(lay, self.B, self.q_len, msl, chunk_tokens)
         assert ws_bytes > 0
-        if ws_fill is None:
-            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+        if ws is not None:
+            assert ws.numel() >= ws_bytes
+            ws_bytes = ws.numel()
         else:
-            ws = torch.full((ws_bytes,), ws_fill, dtype=torch.uint8, device=DEV)
+            ws = fresh_workspace(ws_bytes, ws_fill)
         out = torch.empty(self.q_codes.shape, dtype=d["q"].dtype, device=DEV)
         tab = d["table"] if table is None else table
         F.lrkv_decode(lay, d["q"], self.B, self.q_len, d["BK"], d["BV"],
@@ -130,7 +132,7 @@ class Case:
         msl = int(self.lens.max())
         ws_bytes = F.lrkv_decode_rope_workspace_bytes(lay, self.B, self.q_len, msl, chunk_tokens)
         assert ws_bytes > 0
-        ws = torch.full((ws_bytes,), ws_fill, dtype=torch.uint8, device=DEV)
+        ws = fresh_workspace(ws_bytes, ws_fill)
         out = torch.empty(self.q_codes.shape, dtype=d["q"].dtype, device=DEV)
         cs = torch.from_numpy(np.ascontiguousarray(rope_cs, np.float32)).to(DEV)
         F.lrkv_decode_rope(lay, d["q"], self.B, self.q_len, d["BK"], d["BV"], d["pool"],
@@ -146,6 +148,13 @@ class Case:
     def reference(self, sample=None) -> np.ndarray:
         return O.decode_reference(self.L, self.q64, self.BK64, self.BV64, self.pool, self.table,
                                   self.lens, sample=sample)
+
+
+def fresh_workspace(nbytes: int, fill: int | None = 0xFF) -> torch.Tensor:
+    """A decode workspace filled with the byte `fill` (None: left as allocated)."""
+    if fill is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    return torch.full((nbytes,), fill, dtype=torch.uint8, device=DEV)
 
 
 def tolerance(dtype: int) -> float:

@@ -205,6 +205,37 @@ def test_peaked_softmax_max_in_last_chunk():
         check(case, case.run_f64(chunk_tokens=chunk), ref, what=f"peaked chunk {chunk}")
 
 
+def test_one_workspace_across_calls():
+    """One workspace, NaN-filled once and sized for the largest call, serves calls of
+    different batches, lengths, layouts and splits in a row, as each left it: in the
+    one-launch form the merge of a row waits until every chunk of the row has marked its
+    record done for this very call, so neither an earlier call's records and marks (other
+    layouts put them at other offsets) nor the NaN fill can pass for this call's.  Every
+    output against the oracle."""
+    from lrkv_case import fresh_workspace, layout_c
+    import factored_rank_kv_amd as F
+
+    big = iid_case(150, 16, 128, 56, O.BF16, [2100, 1100, 5, 700], permute=True, fill=0x7FC0)
+    small = iid_case(151, 16, 128, 56, O.BF16, [90, 17], permute=True, fill=0x7FC0)
+    many = iid_case(152, 16, 128, 56, O.BF16, [48] * 20 + [300], permute=True, fill=0x7FC0)
+    wide = iid_case(153, 32, 128, 32, O.BF16, [64, 129, 700], permute=True, fill=0x7FC0)
+    tiny = iid_case(154, 4, 16, 4, O.F32, [1, 15, 90], permute=True, fill=0x7FC00000)
+    cases = (big, small, many, wide, tiny)
+    nbytes = max(F.lrkv_decode_workspace_bytes(layout_c(c.L), c.B, c.q_len, int(c.lens.max()), ch)
+                 for c in cases for ch in (0, 16))
+    ws = fresh_workspace(nbytes)
+    for c, chunk, what in ((big, 16, "big chunk 16"), (small, 32, "small chunk 32"),
+                           (wide, 16, "32 heads chunk 16"), (small, 16, "small chunk 16"),
+                           (many, 0, "many automatic"), (many, 16, "many chunk 16"),
+                           (tiny, 16, "fp32 chunk 16"), (big, 48, "big chunk 48"),
+                           (wide, 0, "32 heads automatic"), (small, 0, "small automatic"),
+                           (big, 16, "big chunk 16 again")):
+        log(f"shared workspace: {what}")
+        got = c.run_f64(chunk_tokens=chunk, ws=ws)
+        live = np.array(c.lens) > 0
+        check(c, got[live], c.reference()[live], what=what)
+
+
 def test_repeat_runs_are_bitwise_equal():
     case = iid_case(108, 16, 128, 56, O.BF16, [513, 1000, 31], permute=True)
     log("determinism")

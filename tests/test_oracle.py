@@ -104,7 +104,7 @@ def test_worked_example_values_through_softmax():
     V = O.reconstruct(S_V, R_V, col)[0]
     o = O.softmax_attention(q, K, V, 1.0 / math.sqrt(d_h))
     assert np.allclose(o, g["output"], rtol=0, atol=1e-12)
-    # the same through block state + one expansion (Algorithm 2 steps 06-09)
+    # the same through block state + one expansion (the softmax, value and output steps of Algorithm 2)
     s = (S_K @ q + (R_K[0] @ (q @ col[0]))) / math.sqrt(d_h)
     st = O.block_state(s, S_V, R_V[0])
     w = np.exp(s - st[0]) / st[1]
