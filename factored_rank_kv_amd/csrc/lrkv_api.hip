@@ -142,17 +142,19 @@ DecodeSizes decode_sizes(const lrkv_layout* L, int batch, int q_len, int max_seq
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LRKV_OK : LRKV_ERR_HIP; }
 
-// Rotary decode: always the chunked split.  Its workgroups take 4 heads each and two fit a
-// compute unit, so for 0 the batch's padded work over 512 / (H/4) chunks, 64 to 2048
-// tokens, else the caller's multiple of P.
+// Rotary decode: always the chunked split.  Its workgroups take kRopeHeadsPerWorkgroup heads
+// each and two fit a compute unit, so for 0 the batch's padded work over
+// kRopeWaveWorkgroups / (H / kRopeHeadsPerWorkgroup) chunks, 64 to 2048 tokens, else the
+// caller's multiple of P.
 DecodeSizes rope_sizes(const lrkv_layout* L, int batch, int q_len, int max_seq_len,
                        int chunk_tokens) {
   DecodeSizes z{};
   const int P = L->page_size;
   long long c = chunk_tokens;
   if (c == 0) {
-    const long long groups = L->num_heads / 4 > 0 ? L->num_heads / 4 : 1;
-    const long long per_wave = 512 / groups > 0 ? 512 / groups : 1;
+    const long long groups = L->num_heads / kRopeHeadsPerWorkgroup > 0
+                                 ? L->num_heads / kRopeHeadsPerWorkgroup : 1;
+    const long long per_wave = kRopeWaveWorkgroups / groups > 0 ? kRopeWaveWorkgroups / groups : 1;
     const long long work = (long long)batch * q_len * (long long)max_seq_len;
     c = (work + per_wave - 1) / per_wave;
     c = (c + P - 1) / P * P;
@@ -333,7 +335,8 @@ int lrkv_decode_rope(const lrkv_layout* L, const void* q, int32_t batch, int32_t
   if (v == V_C0 || v == V_NONE || v == V_C3G2) return LRKV_ERR_UNSUPPORTED;  // bf16, one group
   z = rope_sizes(L, batch, q_len, max_seq_len, chunk_tokens);
   if (z.n_split > 65535) return LRKV_ERR_INVALID_ARG;
-  if ((long long)batch * q_len * z.n_split * (L->num_heads / 4) > 0x7fffffffLL - 8)
+  if ((long long)batch * q_len * z.n_split * (L->num_heads / kRopeHeadsPerWorkgroup) >
+      0x7fffffffLL - 8)
     return LRKV_ERR_INVALID_ARG;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return LRKV_ERR_INVALID_ARG;
   if (workspace_bytes < z.total) return LRKV_ERR_INVALID_ARG;

@@ -89,6 +89,11 @@ constexpr int kBalancedMaxBatch = 1024;
 // (prefill) kernel; it needs no workspace.
 constexpr int kPrefillMinRows = 64;
 
+// Rotary decode: heads per workgroup (one wavefront each) and the workgroups one wave of the
+// grid holds (two per compute unit: the kernel's registers allow two wavefronts per SIMD).
+constexpr int kRopeHeadsPerWorkgroup = 4;
+constexpr int kRopeWaveWorkgroups = 512;
+
 template <class S>
 hipError_t launch_prefill(const DecodeArgs& a);
 

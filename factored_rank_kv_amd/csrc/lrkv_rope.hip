@@ -33,7 +33,7 @@ constexpr int kRopeMaxChunkPages = 256;  // page ids of one chunk held in LDS
 
 template <class S>
 struct RopeCfg {
-  static constexpr int HG = 4;                     // heads per workgroup (one per wavefront)
+  static constexpr int HG = kRopeHeadsPerWorkgroup;  // heads per workgroup (one per wavefront)
   static constexpr int NT = 64 * HG;
   static constexpr int NG = S::H / HG;             // head groups
   static constexpr int NTILE = S::DH / 16;         // 16-feature MFMA tiles of a key row
@@ -44,6 +44,11 @@ struct RopeCfg {
   static constexpr int PAIRS = S::DH / 2;          // rotation pairs per row
   static constexpr int CS_CHUNKS = S::P * PAIRS * 8 / 16;  // 16-byte chunks of a page's table rows
   static constexpr int CPT = CS_CHUNKS / NT;
+  // LDS strides padded by one 16-byte slot so that a wavefront's reads spread over the
+  // banks: S_V chunk columns of P + 1 slots (lanes read 16 columns of one token), table rows
+  // of d_h/4 + 1 slots (lanes read four rows of one pair block)
+  static constexpr int SV_STRIDE = S::P + 1;
+  static constexpr int CS_ROW = PAIRS / 2 + 1;
   static_assert(S::BF && S::P == 16 && S::DH % 16 == 0 && S::H % HG == 0, "bf16 pages of 16");
   static_assert(S_CHUNKS % NT == 0 && CS_CHUNKS % NT == 0, "whole chunks per thread");
   static_assert(S::DH == 2 * 64, "lane l owns value features 2l, 2l+1");
@@ -135,11 +140,15 @@ __device__ __forceinline__ void rope_stage(uint16_t* __restrict__ skt, uint4* __
       }
     } else {
       const int cc = c - S::DHC * S::P;
-      sv[cc] = (cc % S::P) < nvalid ? r.st[i] : make_uint4(0u, 0u, 0u, 0u);
+      sv[(cc / S::P) * C::SV_STRIDE + cc % S::P] =
+          (cc % S::P) < nvalid ? r.st[i] : make_uint4(0u, 0u, 0u, 0u);
     }
   }
 #pragma unroll
-  for (int i = 0; i < C::CPT; ++i) csl[tid + i * C::NT] = r.cs[i];
+  for (int i = 0; i < C::CPT; ++i) {
+    const int c = tid + i * C::NT;  // chunk c % (d_h/4) of table row c / (d_h/4)
+    csl[(c / (C::PAIRS / 2)) * C::CS_ROW + c % (C::PAIRS / 2)] = r.cs[i];
+  }
 }
 
 template <class S>
@@ -188,7 +197,7 @@ __device__ __forceinline__ void rope_consume(const uint16_t* __restrict__ skt,
     const float qp = (n & 1) ? -partner : partner;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float2 c = csl[(4 * g + e) * C::PAIRS + m];
+      const float2 c = csl[(4 * g + e) * (2 * C::CS_ROW) + m];
       const float qr = fmaf(c.x, qf[nt], c.y * qp);
       sc[e] = fmaf(acc[nt][e], qr, sc[e]);
     }
@@ -209,23 +218,35 @@ __device__ __forceinline__ void rope_consume(const uint16_t* __restrict__ skt,
     pm = fmaxf(pm, s[e]);
   }
   pm = rows4_max(pm);
-  // ---- online softmax (base 2): one rescale factor for l, acc_S and acc_R
-  const float m_new = fmaxf(st.m_run, pm);
-  const float alpha = exp2_fast(st.m_run - m_new);  // 0 on the first page
+  // ---- online softmax (base 2) with a lazy reference: the reference max moves only when a
+  // page's max exceeds it by more than 8, and then l, acc_S and acc_R are rescaled together
+  // by one factor (a wave-uniform branch, rare after the first page); weights stay <= 2^8
+  if (__builtin_expect(pm > st.m_run + 8.0f, 0)) {
+    const float alpha = exp2_fast(st.m_run - pm);  // 0 on the first page
+    st.l_run *= alpha;
+    st.accS0 *= alpha;
+    st.accS1 *= alpha;
+#pragma unroll
+    for (int j = 0; j < C::RVL; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st.accR[j][e] *= alpha;
+    st.m_run = pm;
+  }
+  const float m_new = st.m_run;
   float w[4], ws = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     w[e] = exp2_fast(s[e] - m_new);
     ws += w[e];
   }
-  st.l_run = st.l_run * alpha + rows4_sum(ws);
-  st.m_run = m_new;
+  st.l_run += rows4_sum(ws);
   if (n == 0) *reinterpret_cast<float4*>(wl + 4 * g) = make_float4(w[0], w[1], w[2], w[3]);
   __builtin_amdgcn_wave_barrier();
   asm volatile("" ::: "memory");
   // ---- shared value: lane owns features 2*lane, 2*lane + 1 (chunk lane/4 of S_V)
-  float a0 = st.accS0 * alpha, a1 = st.accS1 * alpha;
-  const uint32_t* svw = reinterpret_cast<const uint32_t*>(sv) + (lane >> 2) * S::P * 4 + (lane & 3);
+  float a0 = st.accS0, a1 = st.accS1;
+  const uint32_t* svw =
+      reinterpret_cast<const uint32_t*>(sv) + (lane >> 2) * C::SV_STRIDE * 4 + (lane & 3);
 #pragma unroll
   for (int t = 0; t < S::P; ++t) {
     const float wt = wl[t];
@@ -243,8 +264,8 @@ __device__ __forceinline__ void rope_consume(const uint16_t* __restrict__ skt,
     const uint32_t v4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      st.accR[j][2 * e] = fmaf(wi, bf16_lo(v4[e]), st.accR[j][2 * e] * alpha);
-      st.accR[j][2 * e + 1] = fmaf(wi, bf16_hi(v4[e]), st.accR[j][2 * e + 1] * alpha);
+      st.accR[j][2 * e] = fmaf(wi, bf16_lo(v4[e]), st.accR[j][2 * e]);
+      st.accR[j][2 * e + 1] = fmaf(wi, bf16_hi(v4[e]), st.accR[j][2 * e + 1]);
     }
   }
   __builtin_amdgcn_wave_barrier();  // wl is rewritten by the next page
@@ -254,8 +275,8 @@ template <class S>
 __global__ void __launch_bounds__(RopeCfg<S>::NT, 2) decode_rope_kernel(const RopeArgs a) {
   using C = RopeCfg<S>;
   __shared__ __align__(16) uint16_t skt_lds[2][S::DH * S::P];
-  __shared__ uint4 sv_lds[2][S::DHC * S::P];
-  __shared__ uint4 cs_lds[2][C::CS_CHUNKS];
+  __shared__ uint4 sv_lds[2][S::DHC * C::SV_STRIDE];
+  __shared__ uint4 cs_lds[2][S::P * C::CS_ROW];
   __shared__ __align__(16) float w_lds[C::HG][S::P];
   __shared__ int ids_lds[kRopeMaxChunkPages];
 
