@@ -39,13 +39,17 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
+# the sources that decide the decode call's kernels and launches (the traffic record holds
+# for them only)
+DECODE_SOURCES = ("lrkv_api.hip", "lrkv_decode.hip", "lrkv_device.h", "lrkv_launch.h")
+
+
 def source_digest() -> str:
     csrc = os.path.join(ROOT, "factored_rank_kv_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+    for f in DECODE_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -414,16 +418,27 @@ def prefill_bench(torch, F, synth, dev):
 
     ms_app = ms_of(append, 10)
     ms_att = ms_of(attend, 10)
+    # the vendor library (hipBLASLt through torch.matmul) on the same plain product, X times
+    # the stacked [d x (2 d_h + 2 H r)] weights, without the scatter into pages: context
+    # for the append kernel, timed in the same process
+    Xb = X.view(torch.bfloat16)
+    Wcat = torch.randn(d, 2 * dh + 2 * H * r, device=dev, generator=g).to(torch.bfloat16)
+    Yb = torch.empty(n, Wcat.shape[1], dtype=torch.bfloat16, device=dev)
+    ms_blas = ms_of(lambda: torch.matmul(Xb, Wcat, out=Yb), 10)
+    del Wcat, Yb
     fl_app = 2.0 * n * d * (2 * dh + 2 * H * r)
     pairs = B * T * (T + 1) / 2
     fl_att = pairs * H * 4 * (dh + r) + B * T * H * 4 * dh * r  # scores + values, p + expansion
     tf_app = fl_app / (ms_app * 1e-3) / 1e12
     tf_att = fl_att / (ms_att * 1e-3) / 1e12
-    log(f"prefill: append {ms_app:.3f} ms ({tf_app:.0f} TFLOP/s), attention {ms_att:.3f} ms "
+    log(f"prefill: append {ms_app:.3f} ms ({tf_app:.0f} TFLOP/s; hipBLASLt plain product "
+        f"{ms_blas:.3f} ms, ratio {ms_app / ms_blas:.3f}), attention {ms_att:.3f} ms "
         f"({tf_att:.0f} TFLOP/s)")
     return {
         "workload": work.name, "B": B, "T": T, "d": d,
         "append_ms": round(ms_app, 4), "append_tflops": round(tf_app, 1),
+        "hipblaslt_plain_product_ms": round(ms_blas, 4),
+        "append_over_hipblaslt": round(ms_app / ms_blas, 4),
         "attention_ms": round(ms_att, 4), "attention_tflops": round(tf_att, 1),
         "roofline_append": {"bound": "mfma", "achieved": round(tf_app, 1),
                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
