@@ -181,27 +181,30 @@ append_few_rows_f32_kernel(AppendArgs a) {
 
 
 // ---------------------------------------------------------------------------------------
-// Many rows (prefill, cache build), bf16: the product on MFMA.  Workgroup = BM rows x 128
-// product columns (one 128-column slice of one weight matrix), 256 threads = 2 x 2
-// wavefronts of BM/2 x 64, K in steps of 32 through a ring of three LDS stages that direct
-// global->LDS loads fill two steps ahead of the products (no register staging);
-// v_mfma_f32_16x16x32_bf16 with float32 accumulation.  X tiles ([row][k]) and weight tiles
-// ([column][k], the weights being output-major) are stored alike, and each lane reads the
-// 8 consecutive k of one row (A operand) or of one column (B operand) as one 16-byte LDS
-// read; a wavefront's A and B reads serve (BM/32) x 4 products, so taller wavefront tiles
-// read less LDS per product.  The operand reads run one step ahead in registers: halfway
+// Many rows (prefill, cache build), bf16: the product on MFMA.  Workgroup = 256 rows x 256
+// product columns, 512 threads = 2 x 4 wavefronts of 128 x 64, K in steps of 32 through a
+// ring of three LDS stages that direct global->LDS loads fill two steps ahead of the
+// products (no register staging); v_mfma_f32_16x16x32_bf16 with float32 accumulation.  A
+// 256 x 256 tile reads (256 + 256) x d operands for 256^2 outputs, a third less L2 -> LDS
+// traffic per product than 256 x 128.  The 256 columns may span weight matrices (W_SK and
+// W_SV, U_K and U_V): each 16-column group of the staging loads is one matrix's rows, with a
+// base of its own.  X tiles ([row][k]) and weight tiles ([column][k], the weights being
+// output-major) are stored alike, and each lane reads the 8 consecutive k of one row (A
+// operand) or of one column (B operand) as one 16-byte LDS read; a wavefront's A and B
+// reads serve 8 x 4 products.  The operand reads run one step ahead in registers: halfway
 // through a step's products the next stage is waited for (one barrier per step) and its
-// operands are read while the second half of the products runs.  The BM x 128 result is rounded to bf16 into LDS, then written
-// to the pages as 16-byte chunks (16 consecutive rows of one page fill 256 contiguous bytes
-// of a section).  Blocks are numbered so that the 128-column slices of one row block run
-// on one XCD (blocks go to the 8 XCDs round robin), where they share that row block's X in
-// L2.
+// operands are read while the second half of the products runs.  The result is rounded to
+// bf16 into LDS, 128 rows at a time, then written to the pages as 16-byte chunks (16
+// consecutive rows of one page fill 256 contiguous bytes of a section).  Blocks are
+// numbered so that the column tiles of one row block run on one XCD (blocks go to the 8
+// XCDs round robin), where they share that row block's X in L2.
 // ---------------------------------------------------------------------------------------
 template <class S>
 struct GemmCfg {
-  static constexpr int BM = 256, BN = 128, BK = 32, NT = 256;
-  static constexpr int WM = BM / 2;              // rows per wavefront
-  static constexpr int IT = WM / 16, JT = 4;     // 16 x 16 product tiles per wavefront
+  static constexpr int BM = 256, BN = 256, BK = 32, NT = 512;
+  static constexpr int NWN = 4;                  // wavefronts across the columns
+  static constexpr int WM = BM / 2, WN = BN / NWN;  // rows and columns per wavefront
+  static constexpr int IT = WM / 16, JT = WN / 16;  // 16 x 16 product tiles per wavefront
   // bytes per X row / weight column in LDS: the 64 bytes of k, the four 16-byte chunks of
   // row r at positions c ^ ((r ^ r >> 1) & 3).  Measured with the LDS bank-conflict counter
   // on this part: both the operand reads (16 consecutive rows, one chunk per 16 lanes) and
@@ -212,54 +215,53 @@ struct GemmCfg {
   static constexpr int W_BYTES = BN * XS;
   static constexpr int STAGE = X_BYTES + W_BYTES;
   static constexpr int NSTAGE = 3;
+  static constexpr int OUT_ROWS = 128;           // result rows staged in LDS at a time
   static constexpr int OS = BN * 2 + 16;         // bytes per output row in LDS (padded)
-  static constexpr int NS_TILES = S::DH / BN;    // slices of W_SK (and of W_SV)
-  static constexpr int NU_TILES = S::H * S::R / BN;  // slices of U_K (and of U_V)
-  static constexpr int COL_TILES = 2 * NS_TILES + 2 * NU_TILES;
-  static_assert(S::BF && S::DH % BN == 0 && (S::H * S::R) % BN == 0, "128-column slices");
-  // staging: 1 KiB (16 rows of 64 bytes) per wavefront load; 4 of X and 2 of weights
+  static constexpr int N = 2 * S::DH + 2 * S::H * S::R;  // product columns
+  static constexpr int COL_TILES = N / BN;
+  static_assert(S::BF && N % BN == 0, "256-column tiles");
+  static_assert(S::DH % 16 == 0 && (S::H * S::R) % 16 == 0,
+                "16-column staging groups never straddle two weight matrices");
+  // staging: 1 KiB (16 rows of 64 bytes) per wavefront load; 2 of X and 2 of weights
   // per wavefront and stage
-  static_assert(BK == 32 && NT == 256 && X_BYTES == 4 * 4 * 1024 && W_BYTES == 4 * 2 * 1024,
+  static_assert(BK == 32 && NT == 512 && X_BYTES == 2 * 8 * 1024 && W_BYTES == 2 * 8 * 1024,
                 "staging geometry");
-  // the output tile reuses the stage buffers
-  static constexpr int SMEM = NSTAGE * STAGE > BM * OS ? NSTAGE * STAGE : BM * OS;
+  static constexpr int SMEM = NSTAGE * STAGE;    // the output tile reuses the stage buffers
+  static_assert(OUT_ROWS * OS <= SMEM && BM % OUT_ROWS == 0 && OUT_ROWS == WM, "output staging");
 };
 
 // One GEMM stage of direct global->LDS loads (global_load_lds_dwordx4, 16 bytes per lane:
 // lane i of the wavefront writes LDS bytes [m0 + 16 i, m0 + 16 i + 16), M0 wave-uniform):
-// four 1 KiB loads of X rows (global xb + xoff[m]) to x_lds + 4096 m, then two of weight
-// rows (wb + woff[m]) to w_lds + 4096 m.  The global bases are wave-uniform (scalar
-// registers), the per-lane parts 32-bit offsets; M0 is set once, stepped by 4 KiB, and
-// restored at the end.  Written as inline assembly, so the compiler's wait counters do
-// not see these loads (it would otherwise wait for all of them before any LDS read); the
-// caller waits with s_waitcnt vmcnt and a barrier before reading the bytes.
-__device__ __forceinline__ void lds_dma_stage(const void* xb, const void* wb,
-                                              const uint32_t (&xoff)[4], const uint32_t (&woff)[2],
+// two 1 KiB loads of X rows (global xb + xoff[m]) to x_lds and x_lds + 8 KiB, then two of
+// weight rows (global wb0 + woff, wb1 + woff: two 16-column groups, each of one weight
+// matrix) to w_lds and w_lds + 8 KiB.  The global bases are wave-uniform (scalar
+// registers), the per-lane parts 32-bit offsets; M0 is set, stepped by 8 KiB, and restored
+// at the end.  Written as inline assembly, so the compiler's wait counters do not see
+// these loads (it would otherwise wait for all of them before any LDS read); the caller
+// waits with s_waitcnt vmcnt and a barrier before reading the bytes.
+__device__ __forceinline__ void lds_dma_stage(const void* xb, const void* wb0, const void* wb1,
+                                              const uint32_t (&xoff)[2], uint32_t woff,
                                               uint32_t x_lds, uint32_t w_lds) {
   uint32_t keep;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %7\n\t"
-      "global_load_lds_dwordx4 %1, %9\n\t"
-      "s_add_u32 m0, m0, 0x1000\n\t"
-      "global_load_lds_dwordx4 %2, %9\n\t"
-      "s_add_u32 m0, m0, 0x1000\n\t"
-      "global_load_lds_dwordx4 %3, %9\n\t"
-      "s_add_u32 m0, m0, 0x1000\n\t"
-      "global_load_lds_dwordx4 %4, %9\n\t"
-      "s_mov_b32 m0, %8\n\t"
-      "global_load_lds_dwordx4 %5, %10\n\t"
-      "s_add_u32 m0, m0, 0x1000\n\t"
-      "global_load_lds_dwordx4 %6, %10\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "global_load_lds_dwordx4 %1, %6\n\t"
+      "s_add_u32 m0, m0, 0x2000\n\t"
+      "global_load_lds_dwordx4 %2, %6\n\t"
+      "s_mov_b32 m0, %5\n\t"
+      "global_load_lds_dwordx4 %3, %7\n\t"
+      "s_add_u32 m0, m0, 0x2000\n\t"
+      "global_load_lds_dwordx4 %3, %8\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(keep)
-      : "v"(xoff[0]), "v"(xoff[1]), "v"(xoff[2]), "v"(xoff[3]), "v"(woff[0]), "v"(woff[1]),
-        "s"(x_lds), "s"(w_lds), "s"(xb), "s"(wb)
+      : "v"(xoff[0]), "v"(xoff[1]), "v"(woff), "s"(x_lds), "s"(w_lds), "s"(xb), "s"(wb0),
+        "s"(wb1)
       : "memory", "scc");
 }
 
 template <class S>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(512, 2)
 append_gemm_kernel(AppendArgs a, int row_tiles) {
   using G = GemmCfg<S>;
   __shared__ __align__(16) uint8_t smem[G::SMEM];
@@ -274,44 +276,40 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
   const int rt = (L & 7) + 8 * (jx / G::COL_TILES);
   if (rt >= row_tiles) return;
   const int row0 = rt * G::BM;
-
-  // first product column of this column tile; its weights are BN consecutive rows of one
-  // output-major matrix
-  const int col0 = ct * G::BN;
-  const uint8_t* W = weight_row<S>(a, col0);
+  const int col0 = ct * G::BN;  // first product column of this column tile
 
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform: scalar addresses
+  const int wm = wave / G::NWN, wn = wave % G::NWN;
   const int li = lane & 15, lg = lane >> 4;
-
 
   // global -> LDS staging by direct loads (global_load_lds_dwordx4): one wavefront
   // instruction fills 1 KiB = 16 rows x 64 bytes; lane i writes bytes [16 i, 16 i + 16) of
   // it, i.e. row i/4, chunk position i%4, so it loads k-chunk (i%4) ^ f(i/4) of that row.
+  // Wavefront w stages X rows and weight columns 16 (w + 8 m) + i/4, m = 0, 1.
   const uint8_t* X = static_cast<const uint8_t*>(a.X);
   const size_t xrow = (size_t)a.d * 2;  // bytes per X row and per weight row
   const int rr = lane >> 2;
   const int kc = (lane & 3) ^ ((rr ^ (rr >> 1)) & 3);
-  // X rows of this lane: 16 (wave + 4 m) + rr, m = 0..3; rows past the end read row n-1
   // per-lane 32-bit offsets from the X and weight bases (loop invariant); rows past the
   // end read row n-1
-  uint32_t xoff[4], woff[2];
+  uint32_t xoff[2];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int r = min(row0 + 16 * (wave + 4 * m) + rr, a.n_rows - 1);
+  for (int m = 0; m < 2; ++m) {
+    const int r = min(row0 + 16 * (wave + 8 * m) + rr, a.n_rows - 1);
     xoff[m] = (uint32_t)((size_t)r * xrow + 16 * kc);
   }
-#pragma unroll
-  for (int m = 0; m < 2; ++m) woff[m] = (uint32_t)((size_t)(16 * (wave + 4 * m) + rr) * xrow + 16 * kc);
+  const uint32_t woff = (uint32_t)((size_t)rr * xrow + 16 * kc);
+  const uint8_t* W0 = weight_row<S>(a, col0 + 16 * wave);
+  const uint8_t* W1 = weight_row<S>(a, col0 + 16 * (wave + 8));
   const int lsw = 16 * (lg ^ ((li ^ (li >> 1)) & 3));  // operand reads: rows 16 x + li
   typedef __attribute__((address_space(3))) uint8_t* lds_p;
   const uint32_t smem_base = (uint32_t)(size_t)(lds_p)smem;
-  // one stage: 4 X and 2 weight loads of 1 KiB per wavefront, LDS addresses 4 KiB apart
   auto issue = [&](int ks, int buf) {
-    const uint32_t st = __builtin_amdgcn_readfirstlane(smem_base + buf * G::STAGE + 1024 * wave);
+    const uint32_t st = smem_base + buf * G::STAGE + 1024 * wave;
     const size_t ko = (size_t)ks * G::BK * 2;
-    lds_dma_stage(X + ko, W + ko, xoff, woff, st, st + G::X_BYTES);
+    lds_dma_stage(X + ko, W0 + ko, W1 + ko, xoff, woff, st, st + G::X_BYTES);
   };
   f32x4_v acc[G::IT][G::JT];
 #pragma unroll
@@ -334,7 +332,7 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
     row_page[i] = page;
     row_slot[i] = slot;
   }
-  if (nk > 1) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  if (nk > 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   // operand fragments of one stage: B (JT columns blocks) and A (IT row blocks)
@@ -347,7 +345,7 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
 #pragma unroll
     for (int j = 0; j < G::JT; ++j)
       f.b[j] = *reinterpret_cast<const bf16x8_v*>(st + G::X_BYTES +
-                                                  (64 * wn + 16 * j + li) * G::XS + lsw);
+                                                  (G::WN * wn + 16 * j + li) * G::XS + lsw);
 #pragma unroll
     for (int i = 0; i < G::IT; ++i)
       f.a[i] = *reinterpret_cast<const bf16x8_v*>(st + (G::WM * wm + 16 * i + li) * G::XS + lsw);
@@ -369,7 +367,7 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
     // next stage's reads add (s_waitcnt lgkmcnt(0), other counters left alone)
     __builtin_amdgcn_s_waitcnt(0xc07f);
     if (ks + 1 < nk) {
-      if (ks + 2 < nk) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      if (ks + 2 < nk) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       load_frag(buf == 2 ? 0 : buf + 1, fn);
@@ -391,33 +389,40 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
       buf = buf == 2 ? 0 : buf + 1;
     }
   }
-  __syncthreads();  // every wavefront's last products read their operands; LDS is reused
 
-  // result tile -> bf16 [row][column] in LDS (D[i][j] at lane 16*(i/4) + j, element i%4)
+  // result tile -> bf16 [row][column] in LDS, one wavefront row (128 rows) at a time
+  // (D[i][j] at lane 16*(i/4) + j, element i%4), then 16-byte chunks to the pages: chunk
+  // idx -> row idx % 128, column chunk idx / 128
   uint8_t* ot = smem;
-#pragma unroll
-  for (int i = 0; i < G::IT; ++i)
-#pragma unroll
-    for (int j = 0; j < G::JT; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = G::WM * wm + 16 * i + 4 * lg + e;
-        const int c = 64 * wn + 16 * j + li;
-        *reinterpret_cast<uint16_t*>(ot + r * G::OS + 2 * c) = (uint16_t)f32_to_bf16_rne(acc[i][j][e]);
-      }
-  __syncthreads();
-  // 16-byte chunks to the pages: chunk idx -> row idx % BM, column chunk idx / BM
   uint16_t* pool = static_cast<uint16_t*>(a.pool);
 #pragma unroll
-  for (int k = 0; k < (G::BM * G::BN / 8) / G::NT; ++k) {
-    const int idx = t + k * G::NT;
-    const int r = idx % G::BM;
-    const int cc = idx / G::BM;  // column chunk 0..15
-    if (row0 + r < a.n_rows) {
-      const uint4 v = *reinterpret_cast<const uint4*>(ot + r * G::OS + 16 * cc);
-      const size_t e = (size_t)row_page[r] * a.page_elems + a.elem_off +
-                       append_dest<S>(col0 + 8 * cc, row_slot[r]);
-      *reinterpret_cast<uint4*>(pool + e) = v;
+  for (int half = 0; half < G::BM / G::OUT_ROWS; ++half) {
+    __syncthreads();  // the last products (or the last half's chunk reads) are done with LDS
+    if (wm == half) {
+#pragma unroll
+      for (int i = 0; i < G::IT; ++i)
+#pragma unroll
+        for (int j = 0; j < G::JT; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * i + 4 * lg + e;
+            const int c = G::WN * wn + 16 * j + li;
+            *reinterpret_cast<uint16_t*>(ot + r * G::OS + 2 * c) = (uint16_t)f32_to_bf16_rne(acc[i][j][e]);
+          }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < (G::OUT_ROWS * G::BN / 8) / G::NT; ++k) {
+      const int idx = t + k * G::NT;
+      const int r = idx % G::OUT_ROWS;
+      const int cc = idx / G::OUT_ROWS;  // column chunk 0..BN/8-1
+      const int rt_row = G::OUT_ROWS * half + r;
+      if (row0 + rt_row < a.n_rows) {
+        const uint4 v = *reinterpret_cast<const uint4*>(ot + r * G::OS + 16 * cc);
+        const size_t e = (size_t)row_page[rt_row] * a.page_elems + a.elem_off +
+                         append_dest<S>(col0 + 8 * cc, row_slot[rt_row]);
+        *reinterpret_cast<uint4*>(pool + e) = v;
+      }
     }
   }
 }
