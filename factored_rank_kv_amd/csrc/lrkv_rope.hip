@@ -28,6 +28,18 @@ namespace {
 typedef __bf16 bf16x8_r __attribute__((ext_vector_type(8)));
 typedef float f32x4_r __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_r __attribute__((ext_vector_type(4)));
+// The B operand of a 16 x 16 x 32 product whose first 16 rows are the identity and the
+// rest zero: lane 16 (k/8) + j holds B[k][j] for k = 8 (lane/16) .. +7, j = lane % 16
+// (bf16 1.0 = 0x3f80 where k == j).
+__device__ __forceinline__ uint4 make_ident8(int lane) {
+  const int j = lane & 15, k0 = 8 * (lane >> 4);
+  unsigned short b[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) b[e] = (unsigned short)(k0 + e == j ? 0x3f80 : 0);
+  const uint4 w = make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16),
+                             b[6] | (b[7] << 16));
+  return w;
+}
 
 constexpr int kRopeMaxChunkPages = 256;  // page ids of one chunk held in LDS
 
@@ -119,11 +131,12 @@ __device__ __forceinline__ void rope_issue(const uint8_t* __restrict__ page, con
     r.nrm = *reinterpret_cast<const uint2*>(page + S::OFF_N + (h * S::P + 4 * g) * 2);
 }
 
-// Page bytes to LDS: S_K transposed to feature rows skt[f][t] (the layout of the MFMA
-// accumulator's start), S_V as loaded (chunk-major) with empty slots zeroed (their weights
-// are exactly 0, and 0 x NaN would not be), the table rows as loaded.
+// Page bytes to LDS: S_K as loaded (chunk-major: the A operand of the product that starts
+// the key block's accumulator; bytes of empty slots only reach their own token's row, whose
+// score is removed by selection), S_V as loaded with empty slots zeroed (their weights are
+// exactly 0, and 0 x NaN would not be), the table rows as loaded.
 template <class S>
-__device__ __forceinline__ void rope_stage(uint16_t* __restrict__ skt, uint4* __restrict__ sv,
+__device__ __forceinline__ void rope_stage(uint4* __restrict__ skc, uint4* __restrict__ sv,
                                            uint4* __restrict__ csl, int tid,
                                            const RopeRegs<S>& r, int nvalid) {
   using C = RopeCfg<S>;
@@ -131,13 +144,7 @@ __device__ __forceinline__ void rope_stage(uint16_t* __restrict__ skt, uint4* __
   for (int i = 0; i < C::SPT; ++i) {
     const int c = tid + i * C::NT;
     if (c < S::DHC * S::P) {
-      const int fc = c / S::P, t = c % S::P;  // features 8fc..8fc+7 of token t
-      const uint32_t w4[4] = {r.st[i].x, r.st[i].y, r.st[i].z, r.st[i].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        skt[(8 * fc + 2 * e) * S::P + t] = (uint16_t)(w4[e] & 0xffffu);
-        skt[(8 * fc + 2 * e + 1) * S::P + t] = (uint16_t)(w4[e] >> 16);
-      }
+      skc[c] = r.st[i];  // features 8 (c / P) .. +7 of token c % P
     } else {
       const int cc = c - S::DHC * S::P;
       sv[(cc / S::P) * C::SV_STRIDE + cc % S::P] =
@@ -161,22 +168,31 @@ struct RopeState {
 
 // One page of one head (this wavefront's).
 template <class S>
-__device__ __forceinline__ void rope_consume(const uint16_t* __restrict__ skt,
+__device__ __forceinline__ void rope_consume(const uint4* __restrict__ skc,
                                              const uint4* __restrict__ sv,
                                              const float2* __restrict__ csl,
-                                             float* __restrict__ wl, const uint4 (&bk)[RopeCfg<S>::KB][RopeCfg<S>::NTILE],
+                                             float* __restrict__ wl, const uint4* __restrict__ idl,
+                                             const uint4 (&bk)[RopeCfg<S>::KB][RopeCfg<S>::NTILE],
                                              const float (&qf)[RopeCfg<S>::NTILE], int lane,
                                              int nvalid, float score_scale, const RopeRegs<S>& r,
                                              RopeState<S>& st) {
   using C = RopeCfg<S>;
   const int n = lane & 15, g = lane >> 4;
   // ---- unrotated keys of the page: K[t][f] = S_K[t][f] + sum_k R_K[h][t][k] B_K[h][f][k]
-  // (lane holds tokens 4g..4g+3 of feature 16nt + n)
+  // (lane holds tokens 4g..4g+3 of feature 16nt + n).  The accumulator starts from S_K by a
+  // product with the identity, of the same shape as the private products below
+  // (v_mfma_f32_16x16x32_bf16, K = 32 of which the last 16 are zero: lanes g < 2 hold
+  // A = S_K[token n][features 16nt + 8g .. +7], one 16-byte read of a chunk-major row, and
+  // B[k][j] = (k == j)); exact, and with no conversion of S_K on the VALU
   f32x4_r acc[C::NTILE];
+  {
+    const bf16x8_r ident = __builtin_bit_cast(bf16x8_r, idl[lane]);
 #pragma unroll
-  for (int nt = 0; nt < C::NTILE; ++nt) {
-    const uint2 v = *reinterpret_cast<const uint2*>(skt + (16 * nt + n) * S::P + 4 * g);
-    acc[nt] = f32x4_r{bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+    for (int nt = 0; nt < C::NTILE; ++nt) {
+      const uint4 v = g < 2 ? skc[(2 * nt + g) * S::P + n] : make_uint4(0u, 0u, 0u, 0u);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_r, v), ident,
+                                                        f32x4_r{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    }
   }
 #pragma unroll
   for (int kb = 0; kb < C::KB; ++kb) {
@@ -274,11 +290,12 @@ __device__ __forceinline__ void rope_consume(const uint16_t* __restrict__ skt,
 template <class S>
 __global__ void __launch_bounds__(RopeCfg<S>::NT, 2) decode_rope_kernel(const RopeArgs a) {
   using C = RopeCfg<S>;
-  __shared__ __align__(16) uint16_t skt_lds[2][S::DH * S::P];
+  __shared__ uint4 skc_lds[2][S::DHC * S::P];
   __shared__ uint4 sv_lds[2][S::DHC * C::SV_STRIDE];
   __shared__ uint4 cs_lds[2][S::P * C::CS_ROW];
   __shared__ __align__(16) float w_lds[C::HG][S::P];
   __shared__ int ids_lds[kRopeMaxChunkPages];
+  __shared__ uint4 ident_lds[64];  // the identity B operand, read per page (not held)
 
   // (request, row, chunk, head group) in order, each XCD a contiguous range (blocks go to
   // the 8 XCDs round robin), so the head groups of a chunk share an L2
@@ -301,6 +318,7 @@ __global__ void __launch_bounds__(RopeCfg<S>::NT, 2) decode_rope_kernel(const Ro
   const int pg1 = (tok1 + S::P - 1) / S::P;
   const int n_pg = pg1 - pg0;
   for (int i = tid; i < n_pg; i += C::NT) ids_lds[i] = a.page_table[(size_t)b * a.max_pages + pg0 + i];
+  if (tid < 64) ident_lds[tid] = make_ident8(tid);
 
   // this wavefront's head: B_K[h]^T as the MFMA B operand (lane: feature 16nt + lane%16,
   // rank 32kb + 8(lane/16) .. +8; zero past r), and the turned query's pair elements
@@ -341,14 +359,14 @@ __global__ void __launch_bounds__(RopeCfg<S>::NT, 2) decode_rope_kernel(const Ro
   rope_issue<S>(page_ptr(pg0), a.rope_cs, a.rope_rows, tok0, h, tid, lane, r0);
   if (pg0 + 1 < pg1)
     rope_issue<S>(page_ptr(pg0 + 1), a.rope_cs, a.rope_rows, tok0 + S::P, h, tid, lane, r1);
-  rope_stage<S>(skt_lds[0], sv_lds[0], cs_lds[0], tid, r0, nvalid(pg0));
+  rope_stage<S>(skc_lds[0], sv_lds[0], cs_lds[0], tid, r0, nvalid(pg0));
   __syncthreads();
 
   auto step = [&](int pg, int buf, RopeRegs<S>& cur, RopeRegs<S>& nxt) {
-    rope_consume<S>(skt_lds[buf], sv_lds[buf], reinterpret_cast<const float2*>(cs_lds[buf]),
-                    w_lds[wave], bk, qf, lane, nvalid(pg), a.score_scale, cur, st);
+    rope_consume<S>(skc_lds[buf], sv_lds[buf], reinterpret_cast<const float2*>(cs_lds[buf]),
+                    w_lds[wave], ident_lds, bk, qf, lane, nvalid(pg), a.score_scale, cur, st);
     const bool more = pg + 1 < pg1;
-    if (more) rope_stage<S>(skt_lds[buf ^ 1], sv_lds[buf ^ 1], cs_lds[buf ^ 1], tid, nxt, nvalid(pg + 1));
+    if (more) rope_stage<S>(skc_lds[buf ^ 1], sv_lds[buf ^ 1], cs_lds[buf ^ 1], tid, nxt, nvalid(pg + 1));
     if (pg + 2 < pg1)
       rope_issue<S>(page_ptr(pg + 2), a.rope_cs, a.rope_rows, (pg + 2) * S::P, h, tid, lane, cur);
     __syncthreads();
