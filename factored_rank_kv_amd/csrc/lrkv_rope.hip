@@ -89,7 +89,6 @@ struct RopeRegs {
   uint4 cs[RopeCfg<S>::CPT];  // (cos, sin) rows of the page's 16 positions
   uint4 rk[RopeCfg<S>::KB];   // MFMA A operand: R_K[h] chunk 4kb + lane/16, token lane%16
   uint4 rv[RopeCfg<S>::RVL];  // R_V[h] chunk lane/16 + 4j, token lane%16
-  uint2 nrm;                  // key-norm layouts: stored reciprocals of tokens 4(lane/16)..+3
 };
 
 __device__ __forceinline__ uint4 ld_stream(const void* p) {
@@ -127,8 +126,6 @@ __device__ __forceinline__ void rope_issue(const uint8_t* __restrict__ page, con
     const int c = g + 4 * j;
     r.rv[j] = c < S::RC ? ld_stream(rv + (c * S::P + t) * 16) : make_uint4(0u, 0u, 0u, 0u);
   }
-  if constexpr (S::NORM)
-    r.nrm = *reinterpret_cast<const uint2*>(page + S::OFF_N + (h * S::P + 4 * g) * 2);
 }
 
 // Page bytes to LDS: S_K as loaded (chunk-major: the A operand of the product that starts
@@ -175,7 +172,7 @@ __device__ __forceinline__ void rope_consume(const uint4* __restrict__ skc,
                                              const uint4 (&bk)[RopeCfg<S>::KB][RopeCfg<S>::NTILE],
                                              const float (&qf)[RopeCfg<S>::NTILE], int lane,
                                              int nvalid, float score_scale, const RopeRegs<S>& r,
-                                             RopeState<S>& st) {
+                                             uint2 nrm_w, RopeState<S>& st) {
   using C = RopeCfg<S>;
   const int n = lane & 15, g = lane >> 4;
   // ---- unrotated keys of the page: K[t][f] = S_K[t][f] + sum_k R_K[h][t][k] B_K[h][f][k]
@@ -209,12 +206,13 @@ __device__ __forceinline__ void rope_consume(const uint4* __restrict__ skc,
 #pragma unroll
   for (int nt = 0; nt < C::NTILE; ++nt) {
     const int m = 8 * nt + (n >> 1);
-    const float partner = dpp_f<kQuadSwap1>(qf[nt]);
+    const float qn = qf[nt];
+    const float partner = dpp_f<kQuadSwap1>(qn);
     const float qp = (n & 1) ? -partner : partner;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float2 c = csl[(4 * g + e) * (2 * C::CS_ROW) + m];
-      const float qr = fmaf(c.x, qf[nt], c.y * qp);
+      const float qr = fmaf(c.x, qn, c.y * qp);
       sc[e] = fmaf(acc[nt][e], qr, sc[e]);
     }
   }
@@ -222,10 +220,10 @@ __device__ __forceinline__ void rope_consume(const uint4* __restrict__ skc,
   float pm = -INFINITY;
   float nrm[4] = {1.f, 1.f, 1.f, 1.f};
   if constexpr (S::NORM) {  // the keys' stored joint-norm reciprocals (RMSNorm of §8)
-    nrm[0] = bf16_lo(r.nrm.x);
-    nrm[1] = bf16_hi(r.nrm.x);
-    nrm[2] = bf16_lo(r.nrm.y);
-    nrm[3] = bf16_hi(r.nrm.y);
+    nrm[0] = bf16_lo(nrm_w.x);
+    nrm[1] = bf16_hi(nrm_w.x);
+    nrm[2] = bf16_lo(nrm_w.y);
+    nrm[3] = bf16_hi(nrm_w.y);
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -359,14 +357,28 @@ __global__ void __launch_bounds__(RopeCfg<S>::NT, 2) decode_rope_kernel(const Ro
   rope_issue<S>(page_ptr(pg0), a.rope_cs, a.rope_rows, tok0, h, tid, lane, r0);
   if (pg0 + 1 < pg1)
     rope_issue<S>(page_ptr(pg0 + 1), a.rope_cs, a.rope_rows, tok0 + S::P, h, tid, lane, r1);
+  // key-norm layouts: the stored reciprocals of this lane's tokens 4(lane/16)..+3 of the
+  // next page, requested one page ahead (one value held, not one per page buffer), before
+  // the loads of the page after, so waiting for them never waits for those
+  auto load_norms = [&](int pg) -> uint2 {
+    if constexpr (S::NORM)
+      return *reinterpret_cast<const uint2*>(page_ptr(pg) + S::OFF_N + (h * S::P + 4 * (lane >> 4)) * 2);
+    else
+      return make_uint2(0u, 0u);
+  };
+  uint2 nrm_w = load_norms(pg0);
   rope_stage<S>(skc_lds[0], sv_lds[0], cs_lds[0], tid, r0, nvalid(pg0));
   __syncthreads();
 
   auto step = [&](int pg, int buf, RopeRegs<S>& cur, RopeRegs<S>& nxt) {
     rope_consume<S>(skc_lds[buf], sv_lds[buf], reinterpret_cast<const float2*>(cs_lds[buf]),
-                    w_lds[wave], ident_lds, bk, qf, lane, nvalid(pg), a.score_scale, cur, st);
+                    w_lds[wave], ident_lds, bk, qf, lane, nvalid(pg), a.score_scale, cur, nrm_w,
+                    st);
     const bool more = pg + 1 < pg1;
-    if (more) rope_stage<S>(skc_lds[buf ^ 1], sv_lds[buf ^ 1], cs_lds[buf ^ 1], tid, nxt, nvalid(pg + 1));
+    if (more) {
+      rope_stage<S>(skc_lds[buf ^ 1], sv_lds[buf ^ 1], cs_lds[buf ^ 1], tid, nxt, nvalid(pg + 1));
+      if constexpr (S::NORM) nrm_w = load_norms(pg + 1);
+    }
     if (pg + 2 < pg1)
       rope_issue<S>(page_ptr(pg + 2), a.rope_cs, a.rope_rows, (pg + 2) * S::P, h, tid, lane, cur);
     __syncthreads();
@@ -378,20 +390,25 @@ __global__ void __launch_bounds__(RopeCfg<S>::NT, 2) decode_rope_kernel(const Ro
   }
 
   // ---- partial tuple (m, l, acc_S, acc_R) of this chunk and head, the split decode's layout
+  // (the lane geometry derived anew here, so that nothing computed from it is held across
+  // the page loop)
+  int lane_e = (int)threadIdx.x & 63;
+  asm volatile("" : "+v"(lane_e));
+  const int g_e = lane_e >> 4, n_e = lane_e & 15;
   const size_t slot = ((size_t)b * a.q_len + qi) * a.n_split + split;
   float* dst = a.part + (slot * S::H + h) * S::PART_PAD;
-  if (lane == 0) {
+  if (lane_e == 0) {
     dst[0] = st.m_run;
     dst[1] = st.l_run;
   }
-  *reinterpret_cast<float2*>(dst + 2 + 2 * lane) = make_float2(st.accS0, st.accS1);
+  *reinterpret_cast<float2*>(dst + 2 + 2 * lane_e) = make_float2(st.accS0, st.accS1);
 #pragma unroll
   for (int j = 0; j < C::RVL; ++j) {
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = r16_sum(st.accR[j][e]);  // over the 16 token lanes
-    const int c = g + 4 * j;
-    if (n == 0 && c < S::RC) {
+    const int c = g_e + 4 * j;
+    if (n_e == 0 && c < S::RC) {
       float4* d4 = reinterpret_cast<float4*>(dst + 2 + S::DH + 8 * c);
       d4[0] = make_float4(v[0], v[1], v[2], v[3]);
       d4[1] = make_float4(v[4], v[5], v[6], v[7]);
