@@ -102,6 +102,9 @@ def main():
                     help="also time the B=4 x 8192 prefill (append + multi-query attention)")
     ap.add_argument("--rope", type=int, default=1,
                     help="also time the rotary decode (lrkv_decode_rope) on the same workload")
+    ap.add_argument("--next-rows", type=int, default=1,
+                    help="also time the key-norm and grouped decodes, the key-norm step of an "
+                         "append and the page copy of a shared-prefix fork")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration runs)")
     args = ap.parse_args()
@@ -356,6 +359,11 @@ def main():
             f"bound {bound} {terms[bound] * 1e6:.2f} us")
         del rws_t
 
+    if args.next_rows:
+        result["next_rows"] = next_rows_bench(torch, F, dev, timed, per_call_us, use_graph, qd,
+                                              wd, tab, table.shape[1], lens, B, T, H, dh, r,
+                                              num_pages, req_new, pos_new, args.replicas)
+
     if args.prefill:
         result["prefill"] = prefill_bench(torch, F, synth, dev)
     if args.other_decodes:
@@ -369,6 +377,111 @@ def main():
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3  # MI355X fp32 vector
+
+
+def next_rows_bench(torch, F, dev, timed, per_call_us, use_graph, qd, wd, tab, max_pages, lens,
+                    B, T, H, dh, r, num_pages, req_new, pos_new, replicas):
+    """The rows after the hot path, on the B=8 x 4096 shape (pools of seeded random bf16 rows,
+    rotated across calls as in the main loop; the values do not change the work):
+    - decode over a key-norm layout (LRKV notes §8, RMSNorm): the pages carry one reciprocal
+      per (head, slot) more;
+    - the key-norm step of a decode-step append (8 rows);
+    - decode over a grouped layout (LRKV notes §3: 32 heads, r = 32, 2 shared blocks);
+    - the device part of a shared-prefix fork: whole-page copies (lrkv_copy_pages)."""
+    out_rec = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+
+    def rand_pools(nbytes):
+        p0 = torch.randn(nbytes // 2, device=dev, generator=g).to(torch.bfloat16).view(torch.uint8)
+        return [p0] + [p0.clone() for _ in range(replicas - 1)]
+
+    def hbm_line(name, lay, q, BK, BV, n_heads):
+        pb = F.lrkv_page_bytes(lay)
+        pools = rand_pools(num_pages * pb)
+        ws_bytes = F.lrkv_decode_workspace_bytes(lay, B, 1, T, 0)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        o = torch.empty((B, 1, n_heads, dh), dtype=torch.int16, device=dev)
+
+        def call(k):
+            F.lrkv_decode(lay, q, B, 1, BK, BV, pools[k % len(pools)], tab, max_pages, lens, T, 0,
+                          o, ws, ws_bytes)
+
+        for k in range(5):
+            call(k)
+        ms, _ = timed(call, 96, use_graph)
+        calls = per_call_us(call, 96)
+        nbytes = num_pages * pb
+        t_s = ms * 1e-3
+        rec = {"call_us": round(ms * 1e3, 3),
+               "call_us_p10_p50_p90": [round(float(np.percentile(calls, p)), 3) for p in (10, 50, 90)],
+               "roofline": {"bound": "hbm", "achieved": round(nbytes / t_s / 1e9, 1),
+                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(nbytes / t_s / 1e9 / PEAK_HBM_GBS, 4),
+                            "bytes": nbytes, "page_bytes": pb}}
+        log(f"{name}: {ms * 1e3:.2f} us per call, {nbytes / t_s / 1e9:.0f} GB/s "
+            f"({100 * nbytes / t_s / 1e9 / PEAK_HBM_GBS:.1f} %)")
+        del pools, ws
+        return rec
+
+    # control: the plain layout on the same kind of random rows
+    lay_p = F.lrkv_layout(H, dh, r, 16, F.LRKV_BF16)
+    out_rec["plain_decode_random_rows"] = hbm_line("plain decode, random rows", lay_p, qd,
+                                                   wd["B_K"], wd["B_V"], H)
+    # key-norm layout: same heads, rank and queries as the main workload
+    lay_kn = F.lrkv_layout(H, dh, r, 16, F.LRKV_BF16, 1, 1)
+    out_rec["key_norm_decode"] = hbm_line("key-norm decode", lay_kn, qd, wd["B_K"], wd["B_V"], H)
+    out_rec["key_norm_decode"]["workload"] = "c1_bf16_b8_t4096_key_norm"
+
+    # the key-norm step of a decode-step append: 8 rows, every head
+    pool_kn = torch.randn(num_pages * F.lrkv_page_bytes(lay_kn) // 2, device=dev,
+                          generator=g).to(torch.bfloat16).view(torch.uint8)
+
+    def norms(k):
+        F.lrkv_key_norms(lay_kn, wd["B_K"], 1e-6, req_new, pos_new, B, tab, max_pages, pool_kn,
+                         num_pages)
+
+    for k in range(5):
+        norms(k)
+    ms_n, _ = timed(norms, 96, use_graph)
+    out_rec["key_norm_step"] = {"rows": B, "call_us": round(ms_n * 1e3, 3)}
+    log(f"key-norm step of an 8-row append: {ms_n * 1e3:.2f} us")
+    del pool_kn
+
+    # grouped layout: 32 heads, r = 32, two shared blocks
+    Hg, rg = 32, 32
+    lay_g = F.lrkv_layout(Hg, dh, rg, 16, F.LRKV_BF16, 0, 2)
+    qg = torch.randn(B, 1, Hg, dh, device=dev, generator=g).to(torch.bfloat16).view(torch.int16)
+    BKg = (torch.randn(Hg, dh, rg, device=dev, generator=g) / rg ** 0.5).to(torch.bfloat16).view(torch.int16)
+    BVg = (torch.randn(Hg, dh, rg, device=dev, generator=g) / rg ** 0.5).to(torch.bfloat16).view(torch.int16)
+    out_rec["grouped_decode"] = hbm_line("grouped decode (32 heads, r=32, 2 groups)", lay_g, qg,
+                                         BKg, BVg, Hg)
+    out_rec["grouped_decode"]["workload"] = "bf16_b8_t4096_h32_r32_g2"
+
+    # page copies of a shared-prefix fork (copy on write), 256 pages of the main layout
+    lay = F.lrkv_layout(H, dh, r, 16, F.LRKV_BF16)
+    pb = F.lrkv_page_bytes(lay)
+    n_cp = 256
+    cp_pool = torch.empty(2 * n_cp * pb, dtype=torch.uint8, device=dev)
+    src = torch.arange(n_cp, dtype=torch.int32, device=dev)
+    dst = src + n_cp
+
+    def copy(k):
+        F.lrkv_copy_pages(lay, cp_pool, src, dst, n_cp)
+
+    for k in range(5):
+        copy(k)
+    ms_c, _ = timed(copy, 96, use_graph)
+    moved = 2 * n_cp * pb
+    out_rec["prefix_page_copy"] = {
+        "pages": n_cp, "call_us": round(ms_c * 1e3, 3),
+        "roofline": {"bound": "hbm", "achieved": round(moved / (ms_c * 1e-3) / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(moved / (ms_c * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "bytes": moved}}
+    log(f"page copy, {n_cp} pages: {ms_c * 1e3:.2f} us ({moved / (ms_c * 1e-3) / 1e9:.0f} GB/s)")
+    del cp_pool
+    return out_rec
 
 
 def prefill_bench(torch, F, synth, dev):

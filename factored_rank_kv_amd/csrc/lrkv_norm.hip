@@ -6,10 +6,12 @@
 // is computed once per head from the token's stored rows and kept in the page's N section;
 // decode multiplies it onto the summed score.
 //
-// Workgroup = 16 appended rows, 4 wavefronts; wavefront w takes heads w, w+4, ...  For each
-// head the 16 x d_h block of full keys is formed on MFMA (v_mfma_f32_16x16x32_bf16: A = the
-// rows' R_K[h] chunks read from their pages, B = B_K[h]^T, the accumulator starting from the
-// rows' S_K), squared and summed over the features of each row.
+// Workgroup = (16 appended rows, 4 heads), 4 wavefronts, one head each, so that the heads
+// of a decode step's few rows run side by side on H/4 compute units rather than one after
+// another on one.  For its head a wavefront forms the 16 x d_h block of full keys on MFMA
+// (v_mfma_f32_16x16x32_bf16: A = the rows' R_K[h] chunks read from their pages, B =
+// B_K[h]^T, the accumulator starting from the rows' S_K), squares it and sums over the
+// features of each row.
 #include "lrkv_device.h"
 #include "lrkv_launch.h"
 
@@ -28,6 +30,7 @@ struct NormCfg {
   static constexpr int KB = (S::R + 31) / 32;
   static_assert(S::BF && S::NORM && S::P == 16, "bf16 key-norm layouts");
   static_assert(S::DHC * ROWS == NT, "one S_K chunk of one row per thread");
+  static_assert(S::H % 4 == 0, "heads in groups of four");
 };
 
 template <class S>
@@ -69,7 +72,8 @@ __global__ void __launch_bounds__(256, 2) key_norm_kernel(const NormArgs a) {
   const int n = lane & 15, g = lane >> 4;
   const long long my_page = row_page[lane & 15];  // the A operand's row: lane % 16
   const int my_slot = row_slot[lane & 15];
-  for (int h = wave; h < S::H; h += 4) {
+  {
+    const int h = 4 * (int)blockIdx.y + wave;
     f32x4_n acc[C::NTILE];
 #pragma unroll
     for (int nt = 0; nt < C::NTILE; ++nt) {
@@ -118,7 +122,8 @@ __global__ void __launch_bounds__(256, 2) key_norm_kernel(const NormArgs a) {
 template <class S>
 hipError_t launch_key_norms(const NormArgs& a) {
   const int blocks = (a.n_rows + NormCfg<S>::ROWS - 1) / NormCfg<S>::ROWS;
-  hipLaunchKernelGGL((key_norm_kernel<S>), dim3(blocks), dim3(NormCfg<S>::NT), 0, a.stream, a);
+  hipLaunchKernelGGL((key_norm_kernel<S>), dim3(blocks, S::H / 4), dim3(NormCfg<S>::NT), 0,
+                     a.stream, a);
   return hipGetLastError();
 }
 
