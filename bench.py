@@ -396,9 +396,14 @@ def next_rows_bench(torch, F, dev, timed, per_call_us, use_graph, qd, wd, tab, m
         p0 = torch.randn(nbytes // 2, device=dev, generator=g).to(torch.bfloat16).view(torch.uint8)
         return [p0] + [p0.clone() for _ in range(replicas - 1)]
 
-    def hbm_line(name, lay, q, BK, BV, n_heads):
+    def hbm_line(name, lay, q, BK, BV, n_heads, prepare=None, data_bytes=None):
         pb = F.lrkv_page_bytes(lay)
+        data_bytes = pb if data_bytes is None else data_bytes  # read per page (no padding)
         pools = rand_pools(num_pages * pb)
+        if prepare is not None:  # fix up the first copy, then copy it to the others
+            prepare(pools[0])
+            for p_ in pools[1:]:
+                p_.copy_(pools[0])
         ws_bytes = F.lrkv_decode_workspace_bytes(lay, B, 1, T, 0)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         o = torch.empty((B, 1, n_heads, dh), dtype=torch.int16, device=dev)
@@ -411,14 +416,14 @@ def next_rows_bench(torch, F, dev, timed, per_call_us, use_graph, qd, wd, tab, m
             call(k)
         ms, _ = timed(call, 96, use_graph)
         calls = per_call_us(call, 96)
-        nbytes = num_pages * pb
+        nbytes = num_pages * data_bytes
         t_s = ms * 1e-3
         rec = {"call_us": round(ms * 1e3, 3),
                "call_us_p10_p50_p90": [round(float(np.percentile(calls, p)), 3) for p in (10, 50, 90)],
                "roofline": {"bound": "hbm", "achieved": round(nbytes / t_s / 1e9, 1),
                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(nbytes / t_s / 1e9 / PEAK_HBM_GBS, 4),
-                            "bytes": nbytes, "page_bytes": pb}}
+                            "bytes": nbytes, "page_bytes": pb, "page_data_bytes": data_bytes}}
         log(f"{name}: {ms * 1e3:.2f} us per call, {nbytes / t_s / 1e9:.0f} GB/s "
             f"({100 * nbytes / t_s / 1e9 / PEAK_HBM_GBS:.1f} %)")
         del pools, ws
@@ -430,7 +435,16 @@ def next_rows_bench(torch, F, dev, timed, per_call_us, use_graph, qd, wd, tab, m
                                                    wd["B_K"], wd["B_V"], H)
     # key-norm layout: same heads, rank and queries as the main workload
     lay_kn = F.lrkv_layout(H, dh, r, 16, F.LRKV_BF16, 1, 1)
-    out_rec["key_norm_decode"] = hbm_line("key-norm decode", lay_kn, qd, wd["B_K"], wd["B_V"], H)
+    req_all = torch.arange(B, dtype=torch.int32, device=dev).repeat_interleave(T)
+    pos_all = torch.arange(T, dtype=torch.int32, device=dev).repeat(B)
+
+    def real_norms(pool):  # the reciprocals the key-norm step computes for these rows
+        F.lrkv_key_norms(lay_kn, wd["B_K"], 1e-6, req_all, pos_all, B * T, tab, max_pages, pool,
+                         num_pages)
+
+    kn_data = 16 * 2 * (dh + H * r) * 2 + 16 * H * 2  # eq 9 per page + the reciprocals
+    out_rec["key_norm_decode"] = hbm_line("key-norm decode", lay_kn, qd, wd["B_K"], wd["B_V"], H,
+                                          prepare=real_norms, data_bytes=kn_data)
     out_rec["key_norm_decode"]["workload"] = "c1_bf16_b8_t4096_key_norm"
 
     # the key-norm step of a decode-step append: 8 rows, every head

@@ -269,9 +269,10 @@ size_t lrkv_page_bytes(const lrkv_layout* L) {
   if (!layout_valid(L)) return 0;
   const size_t b = L->dtype == LRKV_BF16 ? 2 : 4;
   const size_t norm = L->key_norm ? (size_t)L->page_size * L->num_heads * b : 0;
-  return (size_t)L->page_size * 2 *
-             ((size_t)groups_of(L) * L->head_dim + (size_t)L->num_heads * L->rank) * b +
-         norm;
+  const size_t data = (size_t)L->page_size * 2 *
+                          ((size_t)groups_of(L) * L->head_dim + (size_t)L->num_heads * L->rank) * b +
+                      norm;
+  return L->key_norm ? (data + 1023) / 1024 * 1024 : data;  // key-norm pages: whole KiB
 }
 
 const char* lrkv_status_string(int status) {

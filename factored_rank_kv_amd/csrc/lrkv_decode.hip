@@ -175,6 +175,8 @@ struct SplitCfg {
   static constexpr int RC_L = (S::RC + SPLIT - 1) / SPLIT;      // private chunks per lane
   static constexpr int S_CHUNKS = 2 * S::DHC * S::P;            // 16-byte chunks of S_K + S_V
   static constexpr int SPT = (S_CHUNKS + NT - 1) / NT;          // per thread
+  static constexpr int NCH = S::NORM ? S::H * S::P * S::EB / 16 : 0;  // chunks of an N section
+  static_assert(NCH <= NT, "one N chunk per thread at most");
   // LDS rows of q and p per head; odd strides (in 16-byte units) spread a wavefront's
   // heads over different banks
   static constexpr int Q_STRIDE = S::DHC + 1;
@@ -211,7 +213,7 @@ struct PageRegs {
   uint4 rk[SplitCfg<S>::RC_L];
   uint4 rv[SplitCfg<S>::RC_L];
   uint4 st[SplitCfg<S>::SPT];
-  uint32_t nrm;  // key-norm layouts: the stored reciprocal of the lane's (head, token)
+  uint4 nst;     // key-norm layouts: threads below NCH hold 16 bytes of the page's N section
 };
 
 // Lane geometry inside the workgroup.
@@ -254,11 +256,8 @@ __device__ __forceinline__ void issue_page(const uint8_t* __restrict__ page, con
     const int cg = min(L.half * C::RC_L + c, S::RC - 1);
     r.rv[c] = load_stream(rvp + cg * S::P);
   }
-  if constexpr (S::NORM) {
-    if constexpr (S::BF)
-      r.nrm = *reinterpret_cast<const uint16_t*>(page + S::OFF_N + (L.h * S::P + L.j) * 2);
-    else
-      r.nrm = *reinterpret_cast<const uint32_t*>(page + S::OFF_N + (L.h * S::P + L.j) * 4);
+  if constexpr (S::NORM) {  // staged through LDS with the shared rows (see stage_shared)
+    if (L.tid < C::NCH) r.nst = load_stream(reinterpret_cast<const uint4*>(page + S::OFF_N) + L.tid);
   }
 }
 
@@ -277,9 +276,14 @@ __device__ __forceinline__ int sv_slot(int t, int chunk) {
 // not be).
 template <class S>
 __device__ __forceinline__ void stage_shared(uint4* __restrict__ sk, uint4* __restrict__ sv,
-                                             uint16_t* __restrict__ svt, int tid,
-                                             const PageRegs<S>& r, int nvalid) {
+                                             uint16_t* __restrict__ svt, uint4* __restrict__ nl,
+                                             int tid, const PageRegs<S>& r, int nvalid) {
   using C = SplitCfg<S>;
+  // key-norm layouts: the page's N section (one reciprocal per head and slot) next to the
+  // shared rows, read by every lane after the barrier; held in LDS rather than as one value
+  // per lane in the page registers, so no wait for it can end up waiting on later loads
+  if constexpr (S::NORM)
+    if (tid < C::NCH) nl[tid] = r.nst;
 #pragma unroll
   for (int i = 0; i < C::SPT; ++i) {
     const int c = tid + i * C::NT;
@@ -472,7 +476,8 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
                                              const uint4* __restrict__ p_lds,
                                              uint16_t* __restrict__ wl, float* __restrict__ al,
                                              const Lane<S>& L, int nvalid, float score_scale,
-                                             PageRegs<S>& r, SplitState<S>& st) {
+                                             const uint4* __restrict__ nl, PageRegs<S>& r,
+                                             SplitState<S>& st) {
   using C = SplitCfg<S>;
   const int j = L.j;
   const bool valid = j < nvalid;
@@ -523,7 +528,8 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
   if constexpr (C::SPLIT == 2) full = add_partner(full);
   float scale = score_scale;
   if constexpr (S::NORM)  // the key's stored joint-norm reciprocal multiplies the summed score
-    scale *= S::BF ? bf16_to_f32((uint16_t)r.nrm) : __uint_as_float(r.nrm);
+    scale *= S::BF ? bf16_to_f32(reinterpret_cast<const uint16_t*>(nl)[L.h * S::P + j])
+                   : reinterpret_cast<const float*>(nl)[L.h * S::P + j];
   // masked slots leave by selection, never by multiplying with zero
   const float s = valid ? full * scale : -INFINITY;
 
@@ -639,6 +645,7 @@ decode_split_kernel(const SplitArgs a) {
   __shared__ int ids_lds[kMaxChunkPages];
   __shared__ int pref_lds[BAL ? kBalancedMaxBatch + 1 : 1];
   __shared__ int wsum_lds[BAL ? C::NW : 1];
+  __shared__ uint4 n_lds[2][C::NCH > 0 ? C::NCH : 1];  // key-norm layouts: N sections
 
   // segment: request b, query row qi, pages [pg0, pg_end) of the request, record slot
   int b, qi, pg0, pg_end;
@@ -745,7 +752,7 @@ decode_split_kernel(const SplitArgs a) {
   issue_page<S>(page_ptr(pg0), L, r0);
   if (pg0 + 1 < pg1) issue_page<S>(page_ptr(pg0 + 1), L, r1);
   form_private_queries<S>(bkr, q_lds, pacc, p_lds, tid);
-  stage_shared<S>(sk_lds[0], sv_lds[0], svt_lds[0], tid, r0, nvalid(pg0));
+  stage_shared<S>(sk_lds[0], sv_lds[0], svt_lds[0], n_lds[0], tid, r0, nvalid(pg0));
   __syncthreads();
 
   // this lane's half of its head's query row, and its share of the private query (hi and
@@ -784,11 +791,11 @@ decode_split_kernel(const SplitArgs a) {
                              L.wave, L.lane);
     }
     consume_page<S, PREG>(sk_lds[buf], sv_lds[buf], qreg, preg, p_lds, w_lds[buf], al_lds[buf],
-                          L, nvalid(pg), a.score_scale, cur, st);
+                          L, nvalid(pg), a.score_scale, n_lds[buf], cur, st);
     const bool more = pg + 1 < pg1;
     if (more)
       stage_shared<S>(sk_lds[buf ^ 1], sv_lds[buf ^ 1], svt_lds[C::MFMA_SV ? (k + 1) % 3 : 0],
-                      tid, nxt, nvalid(pg + 1));
+                      n_lds[buf ^ 1], tid, nxt, nvalid(pg + 1));
     if (pg + 2 < pg1) issue_page<S>(page_ptr(pg + 2), L, cur);
     __syncthreads();
     return more;

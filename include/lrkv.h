@@ -33,6 +33,9 @@
  *
  * With key_norm = 1 a fifth section follows R_V (LRKV notes §8, RMSNorm paragraph):
  *   N[h]         at 2*P*d_h + 2*H*P*r + h*P   P elements: 1/n of head h for slots 0..P-1
+ * and the page is padded to a multiple of 1024 bytes (page_bytes = the sections' bytes
+ * rounded up; the padding is never read or written): a page starting off a 1 KiB boundary
+ * reads markedly slower.  Pages of the other layouts are whole KiB already (P = 16).
  *
  * Grouped pages (LRKV notes §3, after the gradient formulas: one shared block per group of
  * heads, groups = G > 1, H a multiple of G): head h belongs to group g = h / (H/G) and uses

@@ -159,15 +159,32 @@ class Layout:
         return 16 // self.elem_bytes
 
 
-def page_elems(L: Layout) -> int:
-    """Elements in one page: P tokens x (2 shared rows of d_h per group + 2H private rows of
-    r), plus P x H key-norm reciprocals when the layout keeps them."""
+# A page of a key-norm layout is padded to a multiple of this many bytes (zero to 1 KiB - 16
+# bytes of padding at its end, never read or written): the pages fix which rows a page
+# holds, not its byte length, and reads of pages that start off a 1 KiB boundary were
+# measured markedly slower on the target device.  Other layouts are multiples already.
+KEY_NORM_PAGE_ALIGN = 1024
+
+
+def page_data_bytes(L: Layout) -> int:
+    """Bytes of the rows of one page: P tokens x (2 shared rows of d_h per group + 2H
+    private rows of r), plus P x H key-norm reciprocals when the layout keeps them."""
     extra = L.page_size * L.num_heads if L.key_norm else 0
-    return L.page_size * 2 * (L.groups * L.head_dim + L.num_heads * L.rank) + extra
+    return (L.page_size * 2 * (L.groups * L.head_dim + L.num_heads * L.rank) + extra) * L.elem_bytes
 
 
 def page_bytes(L: Layout) -> int:
-    return page_elems(L) * L.elem_bytes
+    """Bytes from one page to the next: the rows, and for a key-norm layout the padding up
+    to a multiple of KEY_NORM_PAGE_ALIGN."""
+    raw = page_data_bytes(L)
+    if L.key_norm:
+        raw = -(-raw // KEY_NORM_PAGE_ALIGN) * KEY_NORM_PAGE_ALIGN
+    return raw
+
+
+def page_elems(L: Layout) -> int:
+    """Elements from one page to the next (rows and padding)."""
+    return page_bytes(L) // L.elem_bytes
 
 
 def section_base(L: Layout, section: str, head: int = 0) -> int:

@@ -164,7 +164,8 @@ def test_decode_rope_rejects_bad_arguments_before_launch():
 def test_key_norm_layouts_and_argument_checks():
     C1N = F.lrkv_layout(16, 128, 56, 16, F.LRKV_BF16, 1)
     L = O.Layout(16, 128, 56, 16, O.BF16, key_norm=True)
-    assert F.lrkv_page_bytes(C1N) == O.page_bytes(L) == 65536 + 16 * 16 * 2
+    # the rows and reciprocals (65,536 + 512 bytes), padded to a whole KiB
+    assert F.lrkv_page_bytes(C1N) == O.page_bytes(L) == 66560
     assert F.lrkv_page_bytes(F.lrkv_layout(16, 128, 56, 16, F.LRKV_BF16, 2)) == 0
 
     def st(lay=C1N, **over):

@@ -792,11 +792,18 @@ def test_key_norm_exact_values():
 
 def test_key_norm_page_bytes_add_one_over_two_dh():
     """One stored reciprocal per head and position costs 1/(2 d_h) of the dense K/V cache on
-    top of eq 9's 1/H + r/d_h (LRKV notes §8)."""
+    top of eq 9's 1/H + r/d_h (LRKV notes §8); the page is then padded to a whole KiB, by
+    less than 1 KiB (65,536 + 512 -> 66,560 bytes at H=16, d_h=128, r=56, bf16)."""
     for H, d_h, r, dt in ((16, 128, 56, O.BF16), (32, 128, 32, O.BF16), (4, 16, 4, O.F32)):
         L = O.Layout(H, d_h, r, 16, dt, key_norm=True)
         dense = 16 * 2 * H * d_h * L.elem_bytes
-        assert Fraction(O.page_bytes(L), dense) == O.cache_ratio(H, r, d_h) + Fraction(1, 2 * d_h)
+        assert Fraction(O.page_data_bytes(L), dense) == O.cache_ratio(H, r, d_h) + Fraction(1, 2 * d_h)
+        assert O.page_bytes(L) % 1024 == 0
+        assert 0 <= O.page_bytes(L) - O.page_data_bytes(L) < 1024
+    assert O.page_bytes(O.Layout(16, 128, 56, 16, O.BF16, key_norm=True)) == 66560
+    # layouts without the section are not padded
+    assert O.page_bytes(O.Layout(16, 128, 56, 16, O.BF16)) == O.page_data_bytes(
+        O.Layout(16, 128, 56, 16, O.BF16)) == 65536
 
 
 def _norm_case(seed, H, d_h, r, dtype, lens, eps, permute=True):
