@@ -103,6 +103,11 @@ struct SplitArgs {
   int q_heads;
   int rec_heads;
   int head0;
+  // grouped layouts in one launch: workgroup row blockIdx.y = g takes group g, whose
+  // B_K slice, block of the page and first head lie these many bytes / heads further on
+  long long group_bk_bytes;
+  long long group_page_bytes;
+  int group_heads;
 };
 
 // Balanced split (single query row per request): the batch's N pages, request after request,
@@ -647,6 +652,10 @@ decode_split_kernel(const SplitArgs a) {
   __shared__ int wsum_lds[BAL ? C::NW : 1];
   __shared__ uint4 n_lds[2][C::NCH > 0 ? C::NCH : 1];  // key-norm layouts: N sections
 
+  const int grp = (int)blockIdx.y;  // 0 unless a grouped layout runs in one launch
+  const uint8_t* BKg = static_cast<const uint8_t*>(a.BK) + (size_t)grp * a.group_bk_bytes;
+  const long long page_off = a.page_off + (long long)grp * a.group_page_bytes;
+  const int head0 = a.head0 + grp * a.group_heads;
   // segment: request b, query row qi, pages [pg0, pg_end) of the request, record slot
   int b, qi, pg0, pg_end;
   size_t slot;
@@ -707,7 +716,7 @@ decode_split_kernel(const SplitArgs a) {
   constexpr int QCH = (S::H * S::DHC + C::NT - 1) / C::NT;
   uint4 q_r[QCH];
   const uint4* qsrc = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.q) +
-                                                     (row * a.q_heads + a.head0) * S::DH * S::EB);
+                                                     (row * a.q_heads + head0) * S::DH * S::EB);
 #pragma unroll
   for (int k = 0; k < QCH; ++k) {
     const int i = tid + k * C::NT;
@@ -735,12 +744,12 @@ decode_split_kernel(const SplitArgs a) {
   // workgroup reads all of B_K, 58 MB of L2 traffic at C1 sizes) and ahead of every page
   // load, since loads return in issue order
   BKRows<S> bkr;
-  load_bk_rows<S, !BAL>(a.BK, tid, bkr);
+  load_bk_rows<S, !BAL>(BKg, tid, bkr);
 
   const int pg1 = (tok1 + S::P - 1) / S::P;
   const uint8_t* pool = a.pool;
   auto page_ptr = [&](int pg) {
-    return pool + (size_t)ids_lds[pg - pg0] * (size_t)a.page_stride + (size_t)a.page_off;
+    return pool + (size_t)ids_lds[pg - pg0] * (size_t)a.page_stride + (size_t)page_off;
   };
   auto nvalid = [&](int pg) { return min(S::P, tok1 - pg * S::P); };
 
@@ -811,7 +820,7 @@ decode_split_kernel(const SplitArgs a) {
 
   // ---- partial tuple of this chunk: m, l, acc_S[DH], acc_R[R] per head
   const float l_tot = r16_sum(st.l_run);
-  float* dst = a.part + (slot * a.rec_heads + a.head0 + L.h) * S::PART_PAD;
+  float* dst = a.part + (slot * a.rec_heads + head0 + L.h) * S::PART_PAD;
   if (L.j == 0 && L.half == 0) {
     dst[0] = st.m_run;
     dst[1] = l_tot;
@@ -835,7 +844,7 @@ decode_split_kernel(const SplitArgs a) {
   }
   if constexpr (C::MFMA_SV) {
     // MFMA tile: lane holds heads 16*ht + 4*(lane/16) + e, feature 16*wave + lane%16
-    float* rec = a.part + (slot * a.rec_heads + a.head0) * S::PART_PAD;
+    float* rec = a.part + (slot * a.rec_heads + head0) * S::PART_PAD;
 #pragma unroll
     for (int ht = 0; ht < C::HT; ++ht)
 #pragma unroll
@@ -846,7 +855,7 @@ decode_split_kernel(const SplitArgs a) {
 #pragma unroll
     for (int x = 0; x < C::HPW; ++x) {
       float2* d2 = reinterpret_cast<float2*>(
-          a.part + (slot * a.rec_heads + a.head0 + C::HPW * L.wave + x) * S::PART_PAD + 2 +
+          a.part + (slot * a.rec_heads + head0 + C::HPW * L.wave + x) * S::PART_PAD + 2 +
           2 * L.lane);
       *d2 = make_float2(st.accS[x][0], st.accS[x][1]);
     }
@@ -1065,12 +1074,13 @@ SplitArgs split_args(const DecodeArgs& a) {
 }
 
 template <class S>
-void launch_split(const DecodeArgs& a, const SplitArgs& s) {
+void launch_split(const DecodeArgs& a, const SplitArgs& s, int group_rows = 1) {
   if (a.groups > 0)
-    hipLaunchKernelGGL((decode_split_kernel<S, true>), dim3(a.groups), dim3(SplitCfg<S>::NT), 0,
-                       a.stream, s);
+    hipLaunchKernelGGL((decode_split_kernel<S, true>), dim3(a.groups, group_rows),
+                       dim3(SplitCfg<S>::NT), 0, a.stream, s);
   else
-    hipLaunchKernelGGL((decode_split_kernel<S, false>), dim3((a.batch * a.q_len * a.n_split + 7) / 8 * 8),
+    hipLaunchKernelGGL((decode_split_kernel<S, false>),
+                       dim3((a.batch * a.q_len * a.n_split + 7) / 8 * 8, group_rows),
                        dim3(SplitCfg<S>::NT), 0, a.stream, s);
 }
 
@@ -1092,15 +1102,15 @@ hipError_t launch_decode(const DecodeArgs& a) {
 template <class Sg, class S>
 hipError_t launch_decode_grouped(const DecodeArgs& a, int G) {
   static_assert(Sg::DH == S::DH && Sg::R == S::R && Sg::BF == S::BF && !S::NORM, "group blocks");
-  for (int g = 0; g < G; ++g) {
+  {  // every group in one launch: workgroup row g takes group g
     SplitArgs s = split_args<Sg>(a);
-    s.BK = static_cast<const uint8_t*>(a.B_K) + (size_t)g * Sg::H * Sg::DH * Sg::R * Sg::EB;
     s.page_stride = (long long)G * Sg::PAGE;
-    s.page_off = (long long)g * Sg::PAGE;
     s.q_heads = S::H;
     s.rec_heads = S::H;
-    s.head0 = g * Sg::H;
-    launch_split<Sg>(a, s);
+    s.group_bk_bytes = (long long)Sg::H * Sg::DH * Sg::R * Sg::EB;
+    s.group_page_bytes = Sg::PAGE;
+    s.group_heads = Sg::H;
+    launch_split<Sg>(a, s, G);
   }
   if (a.groups > 0) {
     hipLaunchKernelGGL((merge_expand_kernel<S, true>), dim3(S::H, 1, a.batch), dim3(256), 0,
