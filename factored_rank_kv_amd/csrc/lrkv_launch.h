@@ -90,9 +90,9 @@ constexpr int kBalancedMaxBatch = 1024;
 constexpr int kPrefillMinRows = 64;
 
 // Rotary decode: heads per workgroup (one wavefront each) and the workgroups one wave of the
-// grid holds (two per compute unit: the kernel's registers allow two wavefronts per SIMD).
-constexpr int kRopeHeadsPerWorkgroup = 4;
-constexpr int kRopeWaveWorkgroups = 512;
+// grid holds (one per compute unit: eight wavefronts, two per SIMD, fill its registers).
+constexpr int kRopeHeadsPerWorkgroup = 8;
+constexpr int kRopeWaveWorkgroups = 256;
 
 template <class S>
 hipError_t launch_prefill(const DecodeArgs& a);
