@@ -60,9 +60,10 @@ struct RopeCfg {
   static constexpr int CS_ROW = PAIRS / 2 + 1;
   static constexpr int SV_BUFS = 3;   // S_V of page k is read in step k + 1
   static constexpr int MQ_ROWS = 17;  // 16 rows of a pair-block operand and a zero row
+  static constexpr int FT = S::DH / (16 * HG);  // shared-value feature tiles per wavefront
   static_assert(S::BF && S::P == 16 && S::DH % 16 == 0 && S::H % HG == 0, "bf16 pages of 16");
   static_assert(S_CHUNKS % NT == 0 && CS_CHUNKS % NT == 0, "whole chunks per thread");
-  static_assert(S::DH == 16 * HG, "wavefront w takes shared-value features 16w..16w+15");
+  static_assert(S::DH % (16 * HG) == 0, "wavefront w takes shared-value tiles FT w .. FT w + FT - 1");
   static_assert(HG % 4 == 0 && HG <= 16, "heads fill whole 4-row groups of one MFMA tile");
 };
 
@@ -169,7 +170,8 @@ template <class S>
 struct RopeState {
   float m_run;   // reference max (base-2 units), the same in every lane
   float l_lane;  // exp-sum share of this lane's token (each 16-lane row holds every token)
-  f32x4_r accS;  // shared value: heads 4(lane/16) + e of the group, feature 16 wave + lane%16
+  f32x4_r accS[RopeCfg<S>::FT];  // shared value: heads 4(lane/16) + e of the group, features
+                                 // 16 (FT wave + t) + lane%16
   float accR[RopeCfg<S>::RVL][8];  // chunk lane/16 + 4j of acc_R, token lane%16
 };
 
@@ -259,12 +261,12 @@ __device__ __forceinline__ void rope_scores(const uint4* __restrict__ skc,
   }
 }
 
-// Shared value of one page for all heads of the group, features 16 wave .. +15:
+// Shared value of one page for all heads of the group, feature tiles FT wave .. +FT-1:
 //   acc_S[h][f] = acc_S[h][f] * alpha[h] + sum_t (hi + lo)[h][t] S_V[t][f]
-// as one v_mfma_f32_16x16x32_bf16 (A rows = heads, k = 16 tokens of hi then of lo; B = the
-// page's S_V^T tile twice, read by the 16-lane transposing LDS read: lane L of group g
-// points at token 4g + L/4, features 16 wave + 4(L%4) .. +3, so lane i receives tokens
-// 4g..4g+3 of feature 16 wave + i).
+// as one v_mfma_f32_16x16x32_bf16 per tile (A rows = heads, k = 16 tokens of hi then of lo;
+// B = the page's S_V^T tile twice, read by the 16-lane transposing LDS read: lane L of group
+// g points at token 4g + L/4, features 16 tile + 4(L%4) .. +3, so lane i receives tokens
+// 4g..4g+3 of feature 16 tile + i).
 template <class S>
 __device__ __forceinline__ void rope_shared_value(const uint4* __restrict__ sv,
                                                   const uint4* __restrict__ wa,
@@ -272,17 +274,21 @@ __device__ __forceinline__ void rope_shared_value(const uint4* __restrict__ sv,
                                                   int lane, RopeState<S>& st) {
   using C = RopeCfg<S>;
   const int j = lane & 15, g = lane >> 4;
-  const uint4 av = wa[j * 4 + g];  // head j (zero rows past the group), tokens 4g..4g+3
-  const uint8_t* bp = reinterpret_cast<const uint8_t*>(sv + (2 * wave + ((j & 3) >> 1)) * C::SV_STRIDE +
-                                                       4 * g + (j >> 2)) + 8 * (j & 1);
-  const short4_r b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_r*)(bp));
+  const bf16x8_r av = __builtin_bit_cast(bf16x8_r, wa[j * 4 + g]);  // head j (zero past the group)
   const float4 al = *reinterpret_cast<const float4*>(alpha + 4 * (g & (C::HG / 4 - 1)));
-  st.accS[0] *= al.x;
-  st.accS[1] *= al.y;
-  st.accS[2] *= al.z;
-  st.accS[3] *= al.w;
-  const bf16x8_r bb = __builtin_bit_cast(bf16x8_r, __builtin_shufflevector(b, b, 0, 1, 2, 3, 0, 1, 2, 3));
-  st.accS = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_r, av), bb, st.accS, 0, 0, 0);
+#pragma unroll
+  for (int t = 0; t < C::FT; ++t) {
+    const int ft = C::FT * wave + t;
+    const uint8_t* bp = reinterpret_cast<const uint8_t*>(sv + (2 * ft + ((j & 3) >> 1)) * C::SV_STRIDE +
+                                                         4 * g + (j >> 2)) + 8 * (j & 1);
+    const short4_r b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_r*)(bp));
+    st.accS[t][0] *= al.x;
+    st.accS[t][1] *= al.y;
+    st.accS[t][2] *= al.z;
+    st.accS[t][3] *= al.w;
+    const bf16x8_r bb = __builtin_bit_cast(bf16x8_r, __builtin_shufflevector(b, b, 0, 1, 2, 3, 0, 1, 2, 3));
+    st.accS[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bb, st.accS[t], 0, 0, 0);
+  }
 }
 
 template <class S>
@@ -295,6 +301,7 @@ decode_rope_kernel(const RopeArgs a) {
   __shared__ uint4 wa_lds[2][16 * 4];          // weights as A rows: [head][4 x 16 bytes]
   __shared__ __align__(16) float al_lds[2][C::HG];
   __shared__ uint2 mq_lds[C::HG][2][C::NTILE * C::MQ_ROWS];  // pair-block A operands: bf16, f16
+  __shared__ uint32_t q_lds[C::HG][S::DH / 2];  // each wavefront's query row (bf16 pairs)
   __shared__ int ids_lds[kRopeMaxChunkPages];
 
   // (request, row, chunk, head group) in order, each XCD a contiguous range (blocks go to
@@ -318,6 +325,12 @@ decode_rope_kernel(const RopeArgs a) {
   const int pg1 = (tok1 + S::P - 1) / S::P;
   const int n_pg = pg1 - pg0;
   for (int i = tid; i < n_pg; i += C::NT) ids_lds[i] = a.page_table[(size_t)b * a.max_pages + pg0 + i];
+  {  // this wavefront's query row to LDS before the B_K rows are requested (loads return in order)
+    const size_t row = (size_t)b * a.q_len + qi;
+    const uint32_t* qrow = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.q) +
+                                                             (row * S::H + h) * S::DH * 2);
+    for (int x = lane; x < S::DH / 2; x += 64) q_lds[wave][x] = qrow[x];
+  }
   // zero rows of the weights' A operand (heads past the group), both buffers
   for (int i = tid; i < 2 * (16 - C::HG) * 4; i += C::NT)
     wa_lds[i / ((16 - C::HG) * 4)][C::HG * 4 + i % ((16 - C::HG) * 4)] = make_uint4(0u, 0u, 0u, 0u);
@@ -335,32 +348,8 @@ decode_rope_kernel(const RopeArgs a) {
       bk[kb][nt] = k0 < S::R ? *reinterpret_cast<const uint4*>(bkh + ((size_t)(16 * nt + n) * S::R + k0) * 2)
                              : make_uint4(0u, 0u, 0u, 0u);
     }
-  // the query's pair blocks M_q as the A operand of the (a, b) product, per tile: row i is
-  // a (even i) or b (odd i) of pair p = i/2 (features 2p, 2p+1 of the tile), stored as the
-  // four k = 4(i/4) .. +3 lane i of group i/4 holds; other groups read the zero row 16
-  {
-    const size_t row = (size_t)b * a.q_len + qi;
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(a.q) +
-                                                             (row * S::H + h) * S::DH * 2);
-    for (int x = lane; x < C::NTILE * C::MQ_ROWS; x += 64) {
-      const int nt = x / C::MQ_ROWS, i = x % C::MQ_ROWS;
-      uint16_t vb[4] = {0, 0, 0, 0}, vh[4] = {0, 0, 0, 0};
-      if (i < 16) {
-        const int p = i >> 1, pos = 2 * (p & 1);
-        const uint16_t q0 = qrow[16 * nt + 2 * p], q1 = qrow[16 * nt + 2 * p + 1];
-        const uint16_t e0 = (i & 1) ? q1 : q0;
-        const uint16_t e1 = (i & 1) ? (uint16_t)(q0 ^ 0x8000u) : q1;  // b: -q_2p
-        vb[pos] = e0;
-        vb[pos + 1] = e1;
-        vh[pos] = __builtin_bit_cast(uint16_t, (_Float16)bf16_to_f32(e0));
-        vh[pos + 1] = __builtin_bit_cast(uint16_t, (_Float16)bf16_to_f32(e1));
-      }
-      mq_lds[wave][0][x] = make_uint2(vb[0] | ((uint32_t)vb[1] << 16), vb[2] | ((uint32_t)vb[3] << 16));
-      mq_lds[wave][1][x] = make_uint2(vh[0] | ((uint32_t)vh[1] << 16), vh[2] | ((uint32_t)vh[3] << 16));
-    }
-  }
   const int mq_row = (g == (n >> 2)) ? n : 16;
-  __syncthreads();  // page ids, zero rows in LDS
+  __syncthreads();  // page ids, query rows, zero rows in LDS
 
   auto page_ptr = [&](int pg) { return a.pool + (size_t)ids_lds[pg - pg0] * S::PAGE; };
   auto nvalid = [&](int pg) { return min(S::P, tok1 - pg * S::P); };
@@ -368,7 +357,8 @@ decode_rope_kernel(const RopeArgs a) {
   RopeState<S> st;
   st.m_run = -INFINITY;
   st.l_lane = 0.f;
-  st.accS = f32x4_r{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < C::FT; ++t) st.accS[t] = f32x4_r{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < C::RVL; ++j)
 #pragma unroll
@@ -382,6 +372,29 @@ decode_rope_kernel(const RopeArgs a) {
   issue(pg0, r0);
   issue(pg0 + 1, r1);
   issue(pg0 + 2, r2);
+  // the query's pair blocks M_q as the A operand of the (a, b) product, per tile, built while
+  // the first pages travel: row i is a (even i) or b (odd i) of pair p = i/2 (features 2p,
+  // 2p+1 of the tile), stored as the four k = 4(i/4) .. +3 that lane i of group i/4 holds;
+  // the other groups read the zero row 16
+  {
+    const uint16_t* qh = reinterpret_cast<const uint16_t*>(q_lds[wave]);
+    for (int x = lane; x < C::NTILE * C::MQ_ROWS; x += 64) {
+      const int nt = x / C::MQ_ROWS, i = x % C::MQ_ROWS;
+      uint16_t vb[4] = {0, 0, 0, 0}, vh[4] = {0, 0, 0, 0};
+      if (i < 16) {
+        const int p = i >> 1, pos = 2 * (p & 1);
+        const uint16_t q0 = qh[16 * nt + 2 * p], q1 = qh[16 * nt + 2 * p + 1];
+        const uint16_t e0 = (i & 1) ? q1 : q0;
+        const uint16_t e1 = (i & 1) ? (uint16_t)(q0 ^ 0x8000u) : q1;  // b: -q_2p
+        vb[pos] = e0;
+        vb[pos + 1] = e1;
+        vh[pos] = __builtin_bit_cast(uint16_t, (_Float16)bf16_to_f32(e0));
+        vh[pos + 1] = __builtin_bit_cast(uint16_t, (_Float16)bf16_to_f32(e1));
+      }
+      mq_lds[wave][0][x] = make_uint2(vb[0] | ((uint32_t)vb[1] << 16), vb[2] | ((uint32_t)vb[3] << 16));
+      mq_lds[wave][1][x] = make_uint2(vh[0] | ((uint32_t)vh[1] << 16), vh[2] | ((uint32_t)vh[3] << 16));
+    }
+  }
   rope_stage<S>(skc_lds[0], sv_lds[0], cs_lds[0], tid, r0, nvalid(pg0));
   __syncthreads();
 
@@ -424,9 +437,12 @@ decode_rope_kernel(const RopeArgs a) {
     dst[0] = st.m_run;
     dst[1] = l;
   }
-  if (g_e < C::HG / 4) {  // acc_S rows: heads 4 g_e + e, feature 16 wave + n_e
+  if (g_e < C::HG / 4) {  // acc_S rows: heads 4 g_e + e, features 16 (FT wave + t) + n_e
 #pragma unroll
-    for (int e = 0; e < 4; ++e) rec[(4 * g_e + e) * S::PART_PAD + 2 + 16 * wave + n_e] = st.accS[e];
+    for (int t = 0; t < C::FT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        rec[(4 * g_e + e) * S::PART_PAD + 2 + 16 * (C::FT * wave + t) + n_e] = st.accS[t][e];
   }
 #pragma unroll
   for (int j = 0; j < C::RVL; ++j) {
