@@ -216,9 +216,13 @@ int lrkv_decode(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_le
  *   s_j      = q~ . k_j / sqrt(d_h) = ((q~ D_j^T) . S_K[j] + ((q~ D_j^T) B_K[h]) . R_K[h, j]) / sqrt(d_h)
  *   out[b,i,h] = softmax over the visible j, applied to S_V + R_V[h] B_V[h]^T (values unturned)
  * The cache holds unrotated rows (lrkv_append as usual).  Because D_j depends on the key
- * position, the private query (q~ D_j^T) B_K[h] cannot be formed once (eq 6): this call forms
- * each page's unrotated key block on the matrix cores and dots it with the query turned
- * back by each key's angle, so it does more arithmetic than lrkv_decode.
+ * position, the private query (q~ D_j^T) B_K[h] cannot be formed once (eq 6): this call forms,
+ * per page and head, the private part of the unrotated keys P = R_K[h] B_K[h]^T on the matrix
+ * cores (float32) and then, per feature pair m, a = k_2m q~_2m + k_2m+1 q~_2m+1 and
+ * b = k_2m q~_2m+1 - k_2m+1 q~_2m of the unrotated key k, so that s_j sums c a + s b over the
+ * pairs; it does more arithmetic than lrkv_decode.  The S_K part of a and b is exact; P
+ * enters rounded to f16 (11 significant bits), so the entries of P and of q~ must stay below
+ * 65504 (the largest finite f16) in magnitude, or the scores overflow.
  * D_j turns feature pairs (2m, 2m+1) of a row vector:
  *   (x_2m, x_2m+1) D_j = (x_2m c - x_2m+1 s,  x_2m s + x_2m+1 c),  (c, s) = rope_cs[j][m]
  *   rope_cs    device, float32 [rope_rows][d_h/2][2], (cos, sin) of position j in row j;

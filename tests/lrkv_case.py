@@ -185,13 +185,15 @@ def bases_and_queries(seed, L: O.Layout, B, q_len, q_scale=1.0):
 
 
 def iid_case(seed, H, dh, r, dtype, lens, q_len=1, permute=True, q_scale=1.0, fill=0,
-             key_norm_eps=None):
+             key_norm_eps=None, key_scale=1.0):
     """Cached rows drawn i.i.d. N(0,1), packed by the oracle's bulk placement.  With
     key_norm_eps, the layout keeps the key-norm section, filled by the oracle's key-norm step
-    (its reciprocals of the stored keys)."""
+    (its reciprocals of the stored keys).  key_scale multiplies the cached key rows (S_K and
+    R_K) before they are rounded to the cache type."""
     L = O.Layout(H, dh, r, 16, dtype, key_norm=key_norm_eps is not None)
     n = int(sum(lens))
     SK, SV, RK, RV = synth.factored_rows(seed, n, H, dh, r)
+    SK, RK = SK * key_scale, RK * key_scale
     table, npg = synth.page_assignment(seed + 7, lens, 16, permute)
     pool = O.pack_pool(L, table, lens, as_codes(SK, dtype), as_codes(SV, dtype),
                        as_codes(RK, dtype), as_codes(RV, dtype), npg, fill=fill)

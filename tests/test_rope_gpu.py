@@ -63,6 +63,17 @@ def test_rope_peaked_queries_and_long_table():
     check(case.run_rope(cs), case.reference_rope(cs), "rope peaked")
 
 
+def test_rope_keys_near_half_precision_range():
+    """Private key parts z B_K^T up to 4.7e4, close to the largest finite f16 (65504) in
+    which the call holds them for the pair products (cached key rows x 9e3, which bf16
+    holds; the query x 4.4e-4 so that the scores stay moderate, its smallest entries below
+    the f16 normal range)."""
+    case = iid_case(407, 16, 128, 56, O.BF16, [300, 45], permute=True, q_scale=4.4e-4,
+                    key_scale=9e3, fill=0x7FC0)
+    cs = synth.rope_table(300, 128)
+    check(case.run_rope(cs), case.reference_rope(cs), "rope, private key parts up to 4.7e4")
+
+
 @pytest.mark.slow
 def test_rope_full_b8_t4096_all_outputs():
     """B=8, T=4096, H=16, d_h=128, r=56, rows from the oracle's append of X through
