@@ -134,6 +134,87 @@ append_few_rows_mfma_kernel(AppendArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
+// At most 8 rows, bf16 (the usual decode step): the same product with two k-blocks per
+// MFMA.  Rows 8..15 of the A operand repeat X rows 0..7 at a second k-block and columns
+// 8..15 of the B operand hold the 8 weight columns at that block, so the product's two
+// diagonal 8 x 8 blocks are partial sums over two different k-blocks (the off-diagonal
+// blocks pair different blocks and are dropped): out[r][c] = D[r][c] + D[r+8][c+8].  Every
+// lane of every 16-byte load carries product data, half the load instructions and products
+// of the 16-row kernel.  Loads are unconditional (rows past the last re-read a valid row,
+// whose outputs are dropped; k past d reads a valid chunk and the weights are masked to
+// zero), so that the compiler waits for each operand in turn rather than for all of them.
+// ---------------------------------------------------------------------------------------
+template <class S>
+__global__ void __launch_bounds__(256)
+append_eight_rows_mfma_kernel(AppendArgs a) {
+  static_assert(S::BF, "bf16 cache");
+  // every argument requested at entry, under one wait: first used inside different
+  // branches, they were otherwise fetched in four dependent rounds of scalar loads
+  asm volatile("" ::"s"(a.X), "s"(a.n_rows), "s"(a.d), "s"(a.W_SK), "s"(a.W_SV), "s"(a.U_K),
+               "s"(a.U_V), "s"(a.row_req), "s"(a.row_pos), "s"(a.page_table), "s"(a.max_pages),
+               "s"(a.pool), "s"(a.page_elems), "s"(a.elem_off));
+  constexpr int NB = 8;  // products (pairs of 32-k blocks) per wavefront and pass
+  __shared__ float red[4][2][8][8];
+  const int col0 = blockIdx.x * 8;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int half = li >> 3;                 // which k-block of the pair this lane carries
+  const int nr = min(8, a.n_rows);
+  const size_t rb = (size_t)a.d * 2;  // bytes per X row and per weight row
+
+  // storing thread t < 64: row t/8, column t%8
+  const bool storer = t < 64 && (t >> 3) < nr;
+  const int srow = min(t >> 3, nr - 1);
+  int req = 0, pos = 0, page = 0;
+  if (t < 64) {
+    req = a.row_req[srow];
+    pos = a.row_pos[srow];
+  }
+  const uint8_t* wr = weight_row<S>(a, col0 + (li & 7));
+  const uint8_t* xr = static_cast<const uint8_t*>(a.X) + (size_t)min(li & 7, nr - 1) * rb;
+  const int nkb = (a.d + 31) / 32;
+  f32x4_v acc = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  bool have_page = false;
+  for (int kb0 = wave; kb0 < nkb; kb0 += 8 * NB) {
+    bf16x8_v av[NB], bv[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int k = (kb0 + 4 * (2 * u + half)) * 32 + 8 * lg;  // block kb0 + 4(2u + half)
+      const int kc = min(k, a.d - 8) * 2;
+      const uint4 w = *reinterpret_cast<const uint4*>(wr + kc);
+      const uint32_t m = k < a.d ? ~0u : 0u;  // weights past d: zero
+      bv[u] = __builtin_bit_cast(bf16x8_v, make_uint4(w.x & m, w.y & m, w.z & m, w.w & m));
+      av[u] = *reinterpret_cast<const bf16x8_v*>(xr + kc);
+    }
+    if (!have_page && t < 64) {
+      // after the operand loads: req and pos made opaque here, or the page-table address is
+      // computed before the loop and the row lookups waited for before the first load
+      asm volatile("" : "+v"(req), "+v"(pos)::"memory");
+      page = a.page_table[(size_t)req * a.max_pages + pos / S::P];
+      have_page = true;
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u], acc, 0, 0, 0);
+  }
+  if (!have_page && t < 64) page = a.page_table[(size_t)req * a.max_pages + pos / S::P];
+  // D[i][j] at lane 16*(i/4) + j, element i%4: the diagonal blocks are lanes g < 2, j < 8
+  // (D[r][c]) and g >= 2, j >= 8 (D[r+8][c+8])
+  if ((lg >> 1) == half) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[wave][half][4 * (lg & 1) + e][li & 7] = acc[e];
+  }
+  __syncthreads();
+  if (storer) {
+    const int r = t >> 3, c = t & 7;
+    const float sum = ((red[0][0][r][c] + red[0][1][r][c]) + (red[1][0][r][c] + red[1][1][r][c])) +
+                      ((red[2][0][r][c] + red[2][1][r][c]) + (red[3][0][r][c] + red[3][1][r][c]));
+    store_elem<S>(a.pool, (size_t)page * a.page_elems + a.elem_off + append_dest<S>(col0 + c, pos % S::P),
+                  sum);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Few rows, float32 cache.  Workgroup = 4 product columns x 8 rows, 256 threads = (row,
 // column, k-lane) with 8 k-lanes taking 4 consecutive k at a time (float4 loads of X and of
 // the weight row); the k-lanes add in a fixed order through LDS.
@@ -458,8 +539,11 @@ hipError_t launch_append(const AppendArgs& a_in) {
   constexpr int N = 2 * S::DH + 2 * S::H * S::R;
   if constexpr (S::BF) {
     static_assert(N % 8 == 0, "8-column workgroups");
-    hipLaunchKernelGGL(append_few_rows_mfma_kernel<S>, dim3(N / 8, (a.n_rows + 15) / 16),
-                       dim3(256), 0, a.stream, a);
+    if (a.n_rows <= 8)
+      hipLaunchKernelGGL(append_eight_rows_mfma_kernel<S>, dim3(N / 8), dim3(256), 0, a.stream, a);
+    else
+      hipLaunchKernelGGL(append_few_rows_mfma_kernel<S>, dim3(N / 8, (a.n_rows + 15) / 16),
+                         dim3(256), 0, a.stream, a);
   } else {
     static_assert(N % 4 == 0, "4-column workgroups");
     hipLaunchKernelGGL(append_few_rows_f32_kernel<S>, dim3(N / 4, (a.n_rows + 7) / 8), dim3(256),
