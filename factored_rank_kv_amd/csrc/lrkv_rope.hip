@@ -295,6 +295,10 @@ template <class S>
 __global__ void __launch_bounds__(RopeCfg<S>::NT, RopeCfg<S>::MIN_BLOCKS)
 decode_rope_kernel(const RopeArgs a) {
   using C = RopeCfg<S>;
+  // every argument requested at entry, under one wait
+  asm volatile("" ::"s"(a.q), "s"(a.BK), "s"(a.pool), "s"(a.page_table), "s"(a.seq_lens),
+               "s"(a.rope_cs), "s"(a.part), "s"(a.rope_rows), "s"(a.max_pages), "s"(a.q_len),
+               "s"(a.n_split), "s"(a.chunk), "s"(a.batch), "s"(a.score_scale));
   __shared__ uint4 skc_lds[2][S::DHC * S::P];
   __shared__ uint4 sv_lds[C::SV_BUFS][S::DHC * C::SV_STRIDE];
   __shared__ uint4 cs_lds[2][S::P * C::CS_ROW];
