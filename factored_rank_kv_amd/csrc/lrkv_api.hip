@@ -66,7 +66,8 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // (512 threads at up to 256 VGPRs), so one dispatch wave is 256 groups: the work is spread
 // over that many chunks (measured best for equal lengths: B=8 x 4096 in 128-token chunks,
 // B=4 x 131072 in 2048-token chunks, 84 % of 8 TB/s), at least 4 pages and at most
-// kAutoChunkTokens long.  The host does not see the lengths (they stay on the device), so a
+// kAutoChunkTokens long.  A grouped layout's split runs its G groups side by side, so its
+// wave holds 256 / G chunks per group.  The host does not see the lengths (they stay on the device), so a
 // ragged batch is sized by its longest request; such a batch does better with several
 // waves of shorter chunks (B=32, lengths 512..32768: 768-token chunks, 405-420 µs), which
 // a caller who knows the lengths can ask for.
@@ -76,7 +77,7 @@ int pick_chunk(const lrkv_layout* L, int batch, int q_len, int max_seq_len, int 
   if (chunk_tokens > 0) return chunk_tokens;
   const int P = L->page_size;
   const long long work = (long long)batch * q_len * (long long)max_seq_len;
-  const long long one_wave = 256;
+  const long long one_wave = 256 / groups_of(L);
   long long c = (work + one_wave - 1) / one_wave;
   c = (c + P - 1) / P * P;
   if (c < 4LL * P) c = 4LL * P;
@@ -122,7 +123,7 @@ DecodeSizes decode_sizes(const lrkv_layout* L, int batch, int q_len, int max_seq
     // every range fits the page ids a workgroup holds (kMaxChunkPages - 1 pages and a part)
     const long long pages = (long long)batch * ((max_seq_len + L->page_size - 1) / L->page_size);
     long long g = (pages + (kMaxChunkTokens / L->page_size) - 2) / ((kMaxChunkTokens / L->page_size) - 1);
-    if (g < kBalancedGroups) g = kBalancedGroups;
+    if (g < kBalancedGroups / groups_of(L)) g = kBalancedGroups / groups_of(L);  // one wave
     z.groups = (int)g;
     z.chunk = 0;
     z.n_split = 0;
