@@ -43,8 +43,10 @@ def ternary(g, shape):
 
 
 @pytest.mark.parametrize("shape", [(16, 128, 56), (32, 128, 32)])
-@pytest.mark.parametrize("n_rows", [1, 5, 13])
+@pytest.mark.parametrize("n_rows", [1, 5, 8, 9, 13])
 def test_exact_inputs_bit_exact_with_sentinels(shape, n_rows):
+    """Up to 8 rows go through the two-k-blocks-per-product kernel, 9 to 63 through the
+    16-row one: both bit-exact on inputs whose products and sums are exact in float32."""
     H, dh, r = shape
     L = O.Layout(H, dh, r, 16, O.BF16)
     d = 256
@@ -67,10 +69,11 @@ def test_exact_inputs_bit_exact_with_sentinels(shape, n_rows):
         n_rows * (2 * dh + 2 * H * r)
 
 
-@pytest.mark.parametrize("n_rows,d", [(3, 8), (21, 40), (50, 96)])
+@pytest.mark.parametrize("n_rows,d", [(3, 8), (7, 72), (21, 40), (50, 96)])
 def test_exact_inputs_small_widths(n_rows, d):
     """Few-row appends with d below one 32-wide block per wavefront (d = 8: only the first
-    wavefront has k; d = 40: a partial block) and with several 16-row blocks."""
+    wavefront has k; d = 40, 72: a partial block, 72 through the 8-row kernel, whose second
+    block of each pair lies past d) and with several 16-row blocks."""
     H, dh, r = 16, 128, 56
     L = O.Layout(H, dh, r, 16, O.BF16)
     g = np.random.default_rng(270 + d)
