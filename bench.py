@@ -7,10 +7,12 @@ GPU by lrkv_append from X ~ N(0,1) and N(0, 1/fan_in) weights (synthetic inputs)
 replicated so that consecutive steps read different copies (more bytes than the 256 MB
 Infinity Cache holds, so every step reads HBM).
 
-One step = one decode step of the hot path: lrkv_append of the 8 new tokens' rows (at
-position 4095) into the step's pool copy, then lrkv_decode of one query row per request
-over all 4096 positions.  `value` = algorithmic cache bytes per step (eq 9 of the LRKV
-notes: 2 b (sum of T) (d_h + H r)) / measured step time, in GB/s.
+One step = one decode step of the hot path: lrkv_append_pq (the 8 new tokens' rows
+appended at position 4095 into the step's pool copy, and each query row's private queries
+p = q B_K formed, in one launch), then lrkv_decode_pq of one query row per request over all
+4096 positions.  Its output equals lrkv_append + lrkv_decode bit for bit (checked before the
+timing); that path is timed too and reported beside it.  `value` = algorithmic cache bytes
+per step (eq 9 of the LRKV notes: 2 b (sum of T) (d_h + H r)) / measured step time, in GB/s.
 
 Printed: one JSON line on stdout; progress on stderr.
 """
@@ -41,7 +43,8 @@ def log(msg):
 
 # the sources that decide the decode call's kernels and launches (the traffic record holds
 # for them only)
-DECODE_SOURCES = ("lrkv_api.hip", "lrkv_decode.hip", "lrkv_device.h", "lrkv_launch.h")
+DECODE_SOURCES = ("lrkv_api.hip", "lrkv_decode.hip", "lrkv_device.h", "lrkv_launch.h",
+                  "lrkv_private.h")
 
 
 def source_digest() -> str:
@@ -170,9 +173,37 @@ def main():
         F.lrkv_decode(lay, qd, B, 1, wd["B_K"], wd["B_V"], pools[k % len(pools)], tab,
                       table.shape[1], lens, T, args.chunk, out, ws, ws_bytes)
 
-    def step(k):
+    def step_plain(k):
         append(k)
         decode(k)
+
+    # the private queries p = q B_K formed once per query row, with the append
+    pq_bytes = F.lrkv_private_queries_bytes(lay, B, 1)
+    pbuf = torch.empty(pq_bytes, dtype=torch.uint8, device=dev)
+
+    def append_pq(k):
+        F.lrkv_append_pq(lay, X_new, B, d, wd["W_SK"], wd["W_SV"], wd["U_K"], wd["U_V"], req_new,
+                         pos_new, tab, table.shape[1], pools[k % len(pools)], num_pages, qd, B, 1,
+                         wd["B_K"], pbuf, pq_bytes)
+
+    def decode_pq(k):
+        F.lrkv_decode_pq(lay, qd, pbuf, B, 1, wd["B_V"], pools[k % len(pools)], tab,
+                         table.shape[1], lens, T, args.chunk, out, ws, ws_bytes)
+
+    def step(k):
+        append_pq(k)
+        decode_pq(k)
+
+    # the two paths give the same bits
+    step_plain(0)
+    torch.cuda.synchronize()
+    want = out.clone()
+    out.fill_(-1)
+    step(0)
+    torch.cuda.synchronize()
+    if not torch.equal(out, want):
+        raise RuntimeError("lrkv_append_pq + lrkv_decode_pq differ from lrkv_append + lrkv_decode")
+    del want
 
     stream = torch.cuda.current_stream()
 
@@ -228,11 +259,16 @@ def main():
     torch.cuda.synchronize()
     use_graph = bool(args.graph)
     ms_step, n_steps = timed(step, args.steps, use_graph)
-    ms_decode, _ = timed(decode, args.steps, use_graph)
-    ms_append, _ = timed(append, args.steps, use_graph)
-    log(f"step {ms_step * 1e3:.2f} us (decode {ms_decode * 1e3:.2f} us, append "
+    ms_decode, _ = timed(decode_pq, args.steps, use_graph)
+    ms_append, _ = timed(append_pq, args.steps, use_graph)
+    log(f"step {ms_step * 1e3:.2f} us (lrkv_decode_pq {ms_decode * 1e3:.2f} us, lrkv_append_pq "
         f"{ms_append * 1e3:.2f} us), graph={use_graph}, {n_steps} steps")
-    calls = per_call_us(decode, max(240, args.steps))
+    ms_step_plain, _ = timed(step_plain, args.steps, use_graph)
+    ms_decode_plain, _ = timed(decode, args.steps, use_graph)
+    ms_append_plain, _ = timed(append, args.steps, use_graph)
+    log(f"plain step {ms_step_plain * 1e3:.2f} us (lrkv_decode {ms_decode_plain * 1e3:.2f} us, "
+        f"lrkv_append {ms_append_plain * 1e3:.2f} us)")
+    calls = per_call_us(decode_pq, max(240, args.steps))
     pct = {p: float(np.percentile(calls, p)) for p in (10, 50, 90)}
     log(f"decode call by event pairs over {len(calls)} calls: p10 {pct[10]:.2f} p50 "
         f"{pct[50]:.2f} p90 {pct[90]:.2f} us")
@@ -275,7 +311,8 @@ def main():
     trec = traffic_record()
     roofline = {
         "bound": "hbm",
-        "kernel": "lrkv_decode call (decode_split_kernel + merge_expand_kernel)",
+        "kernel": "lrkv_decode_pq call (decode_split_kernel with the private queries given + "
+                  "merge_expand_kernel)",
         "achieved": round(achieved, 1),
         "peak": PEAK_HBM_GBS,
         "unit": "GB/s",
@@ -309,7 +346,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": work.name, "B": B, "T": T, "H": H, "d_h": dh, "r": r, "d": d,
                    "page_size": work.page_size, "layout": "identity page table",
-                   "step": "lrkv_append of B new rows + lrkv_decode (q_len=1)",
+                   "step": "lrkv_append_pq (B new rows + the private queries, one launch) + "
+                           "lrkv_decode_pq (q_len=1)",
                    "pool_replicas": len(pools), "chunk_tokens": args.chunk,
                    "hip_graph": use_graph},
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
@@ -317,6 +355,12 @@ def main():
         "query_heads_per_s": round(H * B / step_s, 1),
         "decode_only_gbps": round(achieved, 1),
         "append_us": round(ms_append * 1e3, 3),
+        "plain_step": {"step": "lrkv_append + lrkv_decode (private queries formed in every "
+                               "split workgroup)",
+                       "step_us": round(ms_step_plain * 1e3, 3),
+                       "decode_us": round(ms_decode_plain * 1e3, 3),
+                       "append_us": round(ms_append_plain * 1e3, 3),
+                       "GB/s": round(alg_bytes / (ms_step_plain * 1e-3) / 1e9, 1)},
         "roofline": roofline,
         "cpu_baseline": None,
     }

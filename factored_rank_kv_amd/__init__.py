@@ -106,6 +106,15 @@ def _load():
     lib.lrkv_read_probe.restype = ctypes.c_int
     lib.lrkv_status_string.argtypes = [ctypes.c_int]
     lib.lrkv_status_string.restype = ctypes.c_char_p
+    lib.lrkv_private_queries_bytes.argtypes = [LP, I32, I32]
+    lib.lrkv_private_queries_bytes.restype = SZ
+    lib.lrkv_private_queries.argtypes = [LP, P, I32, I32, P, P, SZ, P]
+    lib.lrkv_private_queries.restype = ctypes.c_int
+    lib.lrkv_decode_pq.argtypes = [LP, P, P, I32, I32, P, P, P, I32, P, I32, I32, P, P, SZ, P]
+    lib.lrkv_decode_pq.restype = ctypes.c_int
+    lib.lrkv_append_pq.argtypes = [LP, P, I32, I32, P, P, P, P, P, P, P, I32, P, I64, P, I32, I32,
+                                   P, P, SZ, P]
+    lib.lrkv_append_pq.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -114,7 +123,9 @@ EXPORTS = ("lrkv_page_bytes", "lrkv_append", "lrkv_decode_workspace_bytes", "lrk
            "lrkv_decode_noalloc", "lrkv_decode_rope", "lrkv_decode_rope_workspace_bytes",
            "lrkv_key_norms", "lrkv_pages_init", "lrkv_pages_alloc", "lrkv_pages_retain",
            "lrkv_pages_release", "lrkv_fork_prefix", "lrkv_copy_pages",
-           "lrkv_check_indices", "lrkv_read_probe", "lrkv_status_string")
+           "lrkv_check_indices", "lrkv_read_probe", "lrkv_status_string",
+           "lrkv_private_queries_bytes", "lrkv_private_queries", "lrkv_decode_pq",
+           "lrkv_append_pq")
 
 
 def library():
@@ -289,6 +300,44 @@ def lrkv_decode_rope(layout, q, batch, q_len, B_K, B_V, pool, page_table, max_pa
                                   _stream(stream))
     if check and st != LRKV_OK:
         raise LRKVError(st, "lrkv_decode_rope")
+    return st
+
+
+def lrkv_private_queries_bytes(layout, batch, q_len) -> int:
+    return _load().lrkv_private_queries_bytes(_layout(layout), batch, q_len)
+
+
+def lrkv_private_queries(layout, q, batch, q_len, B_K, p, p_bytes, stream=None,
+                         check=True) -> int:
+    st = _load().lrkv_private_queries(_layout(layout), _ptr(q), batch, q_len, _ptr(B_K), _ptr(p),
+                                      p_bytes, _stream(stream))
+    if check and st != LRKV_OK:
+        raise LRKVError(st, "lrkv_private_queries")
+    return st
+
+
+def lrkv_append_pq(layout, X, n_rows, d, W_SK, W_SV, U_K, U_V, row_req, row_pos, page_table,
+                   max_pages_per_req, pool, num_pages, q, batch, q_len, B_K, p, p_bytes,
+                   stream=None, check=True) -> int:
+    st = _load().lrkv_append_pq(_layout(layout), _ptr(X), n_rows, d, _ptr(W_SK), _ptr(W_SV),
+                                _ptr(U_K), _ptr(U_V), _ptr(row_req), _ptr(row_pos),
+                                _ptr(page_table), max_pages_per_req, _ptr(pool), num_pages,
+                                _ptr(q), batch, q_len, _ptr(B_K), _ptr(p), p_bytes,
+                                _stream(stream))
+    if check and st != LRKV_OK:
+        raise LRKVError(st, "lrkv_append_pq")
+    return st
+
+
+def lrkv_decode_pq(layout, q, p, batch, q_len, B_V, pool, page_table, max_pages_per_req,
+                   seq_lens, max_seq_len, chunk_tokens, out, workspace, workspace_bytes,
+                   stream=None, check=True) -> int:
+    st = _load().lrkv_decode_pq(_layout(layout), _ptr(q), _ptr(p), batch, q_len, _ptr(B_V),
+                                _ptr(pool), _ptr(page_table), max_pages_per_req, _ptr(seq_lens),
+                                max_seq_len, chunk_tokens, _ptr(out), _ptr(workspace),
+                                workspace_bytes, _stream(stream))
+    if check and st != LRKV_OK:
+        raise LRKVError(st, "lrkv_decode_pq")
     return st
 
 

@@ -206,8 +206,10 @@ int decode_check(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_l
 int decode_launch(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_len,
                   const void* B_K, const void* B_V, const void* pool, const int32_t* page_table,
                   int32_t max_pages_per_req, const int32_t* seq_lens, void* out,
-                  void* workspace, const DecodeSizes& z, void* stream) {
+                  void* workspace, const DecodeSizes& z, void* stream,
+                  const void* p_ext = nullptr) {
   DecodeArgs a{};
+  a.p_ext = p_ext;
   a.q = q;
   a.batch = batch;
   a.q_len = q_len;
@@ -262,6 +264,67 @@ int scratch_address(hipStream_t stream, void** ws) {
   return LRKV_OK;
 }
 
+// private queries formed once per query row: plain layouts only (one group, no key-norm
+// section)
+bool pq_variant(Variant v) { return v == V_C0 || v == V_C1 || v == V_C3; }
+
+size_t pq_row_bytes(Variant v) {
+  switch (v) {
+    case V_C0: return private_query_row_bytes<ShapeC0>();
+    case V_C1: return private_query_row_bytes<ShapeC1>();
+    case V_C3: return private_query_row_bytes<ShapeC3>();
+    default: return 0;
+  }
+}
+
+// lrkv_private_queries' argument checks (no launch)
+int private_queries_check(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_len,
+                          const void* B_K, const void* p, size_t p_bytes) {
+  if (!layout_valid(L)) return LRKV_ERR_INVALID_ARG;
+  if (batch <= 0 || q_len <= 0 || batch > 65535 || q_len > 65535) return LRKV_ERR_INVALID_ARG;
+  if (!q || !B_K || !p || !aligned16(q) || !aligned16(B_K) || !aligned16(p))
+    return LRKV_ERR_INVALID_ARG;
+  if (!pq_variant(find_variant(L))) return LRKV_ERR_UNSUPPORTED;
+  if ((long long)batch * q_len > kMaxPrivateQueryRows) return LRKV_ERR_INVALID_ARG;
+  if (p_bytes < (size_t)batch * (size_t)q_len * pq_row_bytes(find_variant(L)))
+    return LRKV_ERR_INVALID_ARG;
+  return LRKV_OK;
+}
+
+// lrkv_append's argument checks; fills *a on success (no launch)
+int append_check(const lrkv_layout* L, const void* X, int32_t n_rows, int32_t d,
+                 const void* W_SK, const void* W_SV, const void* U_K, const void* U_V,
+                 const int32_t* row_req, const int32_t* row_pos, const int32_t* page_table,
+                 int32_t max_pages_per_req, void* pool, int64_t num_pages, void* stream,
+                 AppendArgs* a) {
+  if (!layout_valid(L)) return LRKV_ERR_INVALID_ARG;
+  if (n_rows < 0 || d <= 0 || d % 8 || max_pages_per_req <= 0 || num_pages <= 0)
+    return LRKV_ERR_INVALID_ARG;
+  if (n_rows > 65535 * 8) return LRKV_ERR_INVALID_ARG;
+  if (!X || !W_SK || !W_SV || !U_K || !U_V || !row_req || !row_pos || !page_table || !pool)
+    return LRKV_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(W_SK) || !aligned16(W_SV) || !aligned16(U_K) ||
+      !aligned16(U_V) || !aligned16(row_req) || !aligned16(row_pos) || !aligned16(page_table) ||
+      !aligned16(pool))
+    return LRKV_ERR_INVALID_ARG;
+  if (find_variant(L) == V_NONE) return LRKV_ERR_UNSUPPORTED;
+  *a = AppendArgs{};
+  a->X = X;
+  a->n_rows = n_rows;
+  a->d = d;
+  a->W_SK = W_SK;
+  a->W_SV = W_SV;
+  a->U_K = U_K;
+  a->U_V = U_V;
+  a->row_req = row_req;
+  a->row_pos = row_pos;
+  a->page_table = page_table;
+  a->max_pages = max_pages_per_req;
+  a->pool = pool;
+  a->stream = static_cast<hipStream_t>(stream);
+  return LRKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -311,6 +374,73 @@ int lrkv_decode(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_le
   if (workspace_bytes < z.total) return LRKV_ERR_INVALID_ARG;
   return decode_launch(L, q, batch, q_len, B_K, B_V, pool, page_table, max_pages_per_req,
                        seq_lens, out, workspace, z, stream);
+}
+
+// ---- private queries formed once per query row, and the decode that takes them ----------
+size_t lrkv_private_queries_bytes(const lrkv_layout* L, int32_t batch, int32_t q_len) {
+  if (!layout_valid(L) || batch <= 0 || q_len <= 0) return 0;
+  const Variant v = find_variant(L);
+  if (!pq_variant(v)) return 0;
+  return (size_t)batch * (size_t)q_len * pq_row_bytes(v);
+}
+
+int lrkv_private_queries(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_len,
+                         const void* B_K, void* p, size_t p_bytes, void* stream) {
+  const int st = private_queries_check(L, q, batch, q_len, B_K, p, p_bytes);
+  if (st != LRKV_OK) return st;
+  const int rows = batch * q_len;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (find_variant(L)) {
+    case V_C0: return hip_status(launch_private_queries<ShapeC0>(q, B_K, rows, p, s));
+    case V_C1: return hip_status(launch_private_queries<ShapeC1>(q, B_K, rows, p, s));
+    case V_C3: return hip_status(launch_private_queries<ShapeC3>(q, B_K, rows, p, s));
+    default: return LRKV_ERR_UNSUPPORTED;
+  }
+}
+
+int lrkv_append_pq(const lrkv_layout* L, const void* X, int32_t n_rows, int32_t d,
+                   const void* W_SK, const void* W_SV, const void* U_K, const void* U_V,
+                   const int32_t* row_req, const int32_t* row_pos, const int32_t* page_table,
+                   int32_t max_pages_per_req, void* pool, int64_t num_pages, const void* q,
+                   int32_t batch, int32_t q_len, const void* B_K, void* p, size_t p_bytes,
+                   void* stream) {
+  // every argument of both steps is checked before anything is launched
+  int st = private_queries_check(L, q, batch, q_len, B_K, p, p_bytes);
+  if (st != LRKV_OK) return st;
+  AppendArgs a{};
+  st = append_check(L, X, n_rows, d, W_SK, W_SV, U_K, U_V, row_req, row_pos, page_table,
+                    max_pages_per_req, pool, num_pages, stream, &a);
+  if (st != LRKV_OK) return st;
+  const int rows = batch * q_len;
+  const Variant v = find_variant(L);
+  if (n_rows >= 1 && n_rows <= 8 && L->dtype == LRKV_BF16 && d >= 8) {  // one launch
+    if (v == V_C1) return hip_status(launch_append_pq<ShapeC1>(a, q, B_K, rows, p));
+    if (v == V_C3) return hip_status(launch_append_pq<ShapeC3>(a, q, B_K, rows, p));
+  }
+  st = lrkv_append(L, X, n_rows, d, W_SK, W_SV, U_K, U_V, row_req, row_pos, page_table,
+                   max_pages_per_req, pool, num_pages, stream);
+  if (st != LRKV_OK) return st;
+  return lrkv_private_queries(L, q, batch, q_len, B_K, p, p_bytes, stream);
+}
+
+int lrkv_decode_pq(const lrkv_layout* L, const void* q, const void* p, int32_t batch,
+                   int32_t q_len, const void* B_V, const void* pool, const int32_t* page_table,
+                   int32_t max_pages_per_req, const int32_t* seq_lens, int32_t max_seq_len,
+                   int32_t chunk_tokens, void* out, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  DecodeSizes z{};
+  // p takes the place of B_K in the common checks (non-null, 16-byte aligned)
+  const int st = decode_check(L, q, batch, q_len, p, B_V, pool, page_table, max_pages_per_req,
+                              seq_lens, max_seq_len, chunk_tokens, out, &z);
+  if (st != LRKV_OK) return st;
+  const Variant v = find_variant(L);
+  if (!pq_variant(v)) return LRKV_ERR_UNSUPPORTED;
+  // the multi-query kernel forms its own private queries: such calls go to lrkv_decode
+  if (L->dtype == LRKV_BF16 && q_len >= kPrefillMinRows) return LRKV_ERR_UNSUPPORTED;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return LRKV_ERR_INVALID_ARG;
+  if (workspace_bytes < z.total) return LRKV_ERR_INVALID_ARG;
+  return decode_launch(L, q, batch, q_len, nullptr, B_V, pool, page_table, max_pages_per_req,
+                       seq_lens, out, workspace, z, stream, p);
 }
 
 size_t lrkv_decode_rope_workspace_bytes(const lrkv_layout* L, int32_t batch, int32_t q_len,
@@ -388,35 +518,12 @@ int lrkv_append(const lrkv_layout* L, const void* X, int32_t n_rows, int32_t d,
                 const void* W_SK, const void* W_SV, const void* U_K, const void* U_V,
                 const int32_t* row_req, const int32_t* row_pos, const int32_t* page_table,
                 int32_t max_pages_per_req, void* pool, int64_t num_pages, void* stream) {
-  if (!layout_valid(L)) return LRKV_ERR_INVALID_ARG;
-  if (n_rows < 0 || d <= 0 || d % 8 || max_pages_per_req <= 0 || num_pages <= 0)
-    return LRKV_ERR_INVALID_ARG;
-  if (n_rows > 65535 * 8) return LRKV_ERR_INVALID_ARG;
-  if (!X || !W_SK || !W_SV || !U_K || !U_V || !row_req || !row_pos || !page_table || !pool)
-    return LRKV_ERR_INVALID_ARG;
-  if (!aligned16(X) || !aligned16(W_SK) || !aligned16(W_SV) || !aligned16(U_K) ||
-      !aligned16(U_V) || !aligned16(row_req) || !aligned16(row_pos) || !aligned16(page_table) ||
-      !aligned16(pool))
-    return LRKV_ERR_INVALID_ARG;
-  const Variant v = find_variant(L);
-  if (v == V_NONE) return LRKV_ERR_UNSUPPORTED;
-  if (n_rows == 0) return LRKV_OK;
-
   AppendArgs a{};
-  a.X = X;
-  a.n_rows = n_rows;
-  a.d = d;
-  a.W_SK = W_SK;
-  a.W_SV = W_SV;
-  a.U_K = U_K;
-  a.U_V = U_V;
-  a.row_req = row_req;
-  a.row_pos = row_pos;
-  a.page_table = page_table;
-  a.max_pages = max_pages_per_req;
-  a.pool = pool;
-  a.stream = static_cast<hipStream_t>(stream);
-  switch (v) {
+  const int st = append_check(L, X, n_rows, d, W_SK, W_SV, U_K, U_V, row_req, row_pos,
+                              page_table, max_pages_per_req, pool, num_pages, stream, &a);
+  if (st != LRKV_OK) return st;
+  if (n_rows == 0) return LRKV_OK;
+  switch (find_variant(L)) {
     case V_C0: return hip_status(launch_append<ShapeC0>(a));
     case V_C1: return hip_status(launch_append<ShapeC1>(a));
     case V_C3: return hip_status(launch_append<ShapeC3>(a));

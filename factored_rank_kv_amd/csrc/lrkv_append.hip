@@ -9,6 +9,7 @@
 // atomics), so results are deterministic.
 #include "lrkv_device.h"
 #include "lrkv_launch.h"
+#include "lrkv_private.h"
 
 namespace lrkv {
 
@@ -145,8 +146,7 @@ append_few_rows_mfma_kernel(AppendArgs a) {
 // zero), so that the compiler waits for each operand in turn rather than for all of them.
 // ---------------------------------------------------------------------------------------
 template <class S>
-__global__ void __launch_bounds__(256)
-append_eight_rows_mfma_kernel(AppendArgs a) {
+__device__ __forceinline__ void append_eight_rows(const AppendArgs& a, int blk) {
   static_assert(S::BF, "bf16 cache");
   // every argument requested at entry, under one wait: first used inside different
   // branches, they were otherwise fetched in four dependent rounds of scalar loads
@@ -155,7 +155,7 @@ append_eight_rows_mfma_kernel(AppendArgs a) {
                "s"(a.pool), "s"(a.page_elems), "s"(a.elem_off));
   constexpr int NB = 8;  // products (pairs of 32-k blocks) per wavefront and pass
   __shared__ float red[4][2][8][8];
-  const int col0 = blockIdx.x * 8;
+  const int col0 = blk * 8;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int li = lane & 15, lg = lane >> 4;
@@ -212,6 +212,37 @@ append_eight_rows_mfma_kernel(AppendArgs a) {
     store_elem<S>(a.pool, (size_t)page * a.page_elems + a.elem_off + append_dest<S>(col0 + c, pos % S::P),
                   sum);
   }
+}
+
+template <class S>
+__global__ void __launch_bounds__(256)
+append_eight_rows_mfma_kernel(AppendArgs a) {
+  append_eight_rows<S>(a, (int)blockIdx.x);
+}
+
+// The decode step's two independent products in one launch: the last append_blocks
+// workgroups append the new rows as above, the ones before them form the private queries
+// p = q B_K of the step's query rows (a workgroup per head and block of rows,
+// lrkv_private.h).  The formation goes first: dispatched after the append workgroups, its
+// loads queued behind their weight stream and the launch took 5.6 us against 4.9 (B=8,
+// C1 sizes, the append alone 3.6 us).
+struct PrivArgs {
+  const void* q;
+  const void* BK;
+  int rows;
+  uint4* p;
+};
+
+template <class S>
+__global__ void __launch_bounds__(256)
+append_eight_rows_pq_kernel(AppendArgs a, PrivArgs pa, int append_blocks) {
+  const int pq_blocks = (int)gridDim.x - append_blocks;
+  const int blk = (int)blockIdx.x;
+  if (blk >= pq_blocks) {
+    append_eight_rows<S>(a, blk - pq_blocks);
+    return;
+  }
+  private_query_block<S>(pa.q, pa.BK, pa.rows, pa.p, blk);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -551,6 +582,26 @@ hipError_t launch_append(const AppendArgs& a_in) {
   }
   return hipGetLastError();
 }
+
+template <class S>
+hipError_t launch_append_pq(const AppendArgs& a_in, const void* q, const void* BK, int rows,
+                            void* p) {
+  static_assert(S::BF, "the 8-row append is the bf16 kernel");
+  AppendArgs a = a_in;
+  if (a.page_elems == 0) a.page_elems = S::PAGE / S::EB;
+  constexpr int N = 2 * S::DH + 2 * S::H * S::R;
+  static_assert(N % 8 == 0, "8-column workgroups");
+  if (a.n_rows < 1 || a.n_rows > 8 || rows < 1) return hipErrorInvalidValue;
+  static_assert(PrivBlockCfg<S>::NT == 256, "workgroup size");
+  const int pq_blocks = (int)private_query_workgroups<S>(rows);
+  PrivArgs pa{q, BK, rows, static_cast<uint4*>(p)};
+  hipLaunchKernelGGL(append_eight_rows_pq_kernel<S>, dim3(N / 8 + pq_blocks), dim3(256), 0,
+                     a.stream, a, pa, N / 8);
+  return hipGetLastError();
+}
+
+template hipError_t launch_append_pq<ShapeC1>(const AppendArgs&, const void*, const void*, int, void*);
+template hipError_t launch_append_pq<ShapeC3>(const AppendArgs&, const void*, const void*, int, void*);
 
 template hipError_t launch_append<ShapeC0>(const AppendArgs&);
 template hipError_t launch_append<ShapeC1>(const AppendArgs&);

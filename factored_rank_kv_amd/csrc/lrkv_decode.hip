@@ -19,6 +19,7 @@
 // page slots are removed by integer selects, so NaN bytes there never reach arithmetic.
 #include "lrkv_device.h"
 #include "lrkv_launch.h"
+#include "lrkv_private.h"
 
 namespace lrkv {
 
@@ -108,6 +109,9 @@ struct SplitArgs {
   long long group_bk_bytes;
   long long group_page_bytes;
   int group_heads;
+  // lrkv_decode_pq: each query row's private-query block (H * P_STRIDE 16-byte slots, as
+  // form_private_queries leaves it in LDS), formed beforehand by private_queries_kernel
+  const uint4* p_ext;
 };
 
 // Balanced split (single query row per request): the batch's N pages, request after request,
@@ -172,12 +176,12 @@ __device__ __forceinline__ int group_of_page(int p, int N, int G) {
 
 template <class S>
 struct SplitCfg {
-  static constexpr int HPW = S::H <= 4 ? 4 : (S::H / 8 > 2 ? S::H / 8 : 2);  // heads per wave
-  static constexpr int SPLIT = 4 / HPW;        // lanes per (head, token) pair
+  static constexpr int HPW = PrivCfg<S>::HPW;    // heads per wave
+  static constexpr int SPLIT = PrivCfg<S>::SPLIT;  // lanes per (head, token) pair
   static constexpr int NW = S::H / HPW;
-  static constexpr int NT = NW * 64;
+  static constexpr int NT = PrivCfg<S>::NT;
   static constexpr int DHC_L = S::DHC / SPLIT;                  // S_K chunks per lane
-  static constexpr int RC_L = (S::RC + SPLIT - 1) / SPLIT;      // private chunks per lane
+  static constexpr int RC_L = PrivCfg<S>::RC_L;                 // private chunks per lane
   static constexpr int S_CHUNKS = 2 * S::DHC * S::P;            // 16-byte chunks of S_K + S_V
   static constexpr int SPT = (S_CHUNKS + NT - 1) / NT;          // per thread
   static constexpr int NCH = S::NORM ? S::H * S::P * S::EB / 16 : 0;  // chunks of an N section
@@ -185,15 +189,13 @@ struct SplitCfg {
   // LDS rows of q and p per head; odd strides (in 16-byte units) spread a wavefront's
   // heads over different banks
   static constexpr int Q_STRIDE = S::DHC + 1;
-  static constexpr int P_PER_CHUNK = S::BF ? 2 : 1;  // uint4 per chunk (bf16: hi, lo)
-  // room for SPLIT*RC_L chunks: the slots past RC hold zeros, so a lane whose half runs
-  // past the last private chunk adds nothing for it
-  static constexpr int P_STRIDE = (SPLIT * RC_L * P_PER_CHUNK) | 1;
+  // private-query block of a row (its layout and sums: lrkv_private.h)
+  static constexpr int P_PER_CHUNK = PrivCfg<S>::P_PER_CHUNK;
+  static constexpr int P_STRIDE = PrivCfg<S>::P_STRIDE;
   static constexpr int PREG_N = RC_L * P_PER_CHUNK;  // uint4 of a lane's private query share
-  // private queries: one job per (head, 16-byte chunk of p), d_h split over PQ_GROUPS
-  static constexpr int PQ_JOBS = S::H * S::RC;
-  static constexpr int PQ_GROUPS = NT / PQ_JOBS > 0 ? NT / PQ_JOBS : 1;
-  static constexpr int PQ_DSPAN = S::DH / PQ_GROUPS;
+  static constexpr int PQ_JOBS = PrivCfg<S>::PQ_JOBS;
+  static constexpr int PQ_GROUPS = PrivCfg<S>::PQ_GROUPS;
+  static constexpr int PQ_DSPAN = PrivCfg<S>::PQ_DSPAN;
   // bf16 cache: the shared value sum_j w[h][j] S_V[j] runs on MFMA, wave w owning the
   // 16-feature tile [16w, 16w+16) for every head (HT tiles of 16 heads)
   static constexpr bool MFMA_SV = S::BF;
@@ -202,7 +204,6 @@ struct SplitCfg {
                 "MFMA shared value: 16-head tiles, one 16-feature tile per wave, 16-token pages");
   static_assert(HPW * SPLIT == 4, "64 lanes = HPW heads x SPLIT x 16 tokens");
   static_assert(S::DHC % SPLIT == 0, "shared chunks split evenly");
-  static_assert(S::DH % PQ_GROUPS == 0, "d_h split evenly");
   static_assert(NT <= 1024, "workgroup size");
 };
 
@@ -344,10 +345,6 @@ __device__ __forceinline__ void shared_value_mfma(f32x4* acc, const uint16_t* __
   }
 }
 
-// p = q B_K[h] for every head of the row, float32 sums over d_h in a fixed order, packed
-// into LDS for the private score.  bf16 cache: per 8-feature chunk, 4 words of bfloat16
-// pairs of hi(p) then 4 words of lo(p) = bf16(p - hi(p)), so p.R_K[h,j] = dot2(hi, r) +
-// dot2(lo, r) keeps about 16 significant bits of p.  float32 cache: p as it is.
 // B_K rows of this thread's private-query job: job (head h, 16-byte chunk c of p), rows
 // d in group g's span.  Issued before any page load: vector loads return in issue order,
 // so rows requested after the pages would wait for the pages.
@@ -377,10 +374,9 @@ __device__ __forceinline__ void load_bk_rows(const void* __restrict__ BK, int ti
   asm volatile("" ::: "memory");  // keep them ahead of the page loads that follow
 }
 
-// p = q B_K[h] for every head of the row, float32 sums over d_h in a fixed order, packed
-// into LDS for the private score.  bf16 cache: per 8-feature chunk, 4 words of bfloat16
-// pairs of hi(p) then 4 words of lo(p) = bf16(p - hi(p)), so p.R_K[h,j] = dot2(hi, r) +
-// dot2(lo, r) keeps about 16 significant bits of p.  float32 cache: p as it is.
+// p = q B_K[h] for every head of the row, float32 sums over d_h in a fixed order (the one
+// private_query_block follows), packed into LDS for the private score as
+// store_private_chunk lays it out.
 template <class S>
 __device__ __forceinline__ void form_private_queries(const BKRows<S>& bkr,
                                                      const uint4* __restrict__ q_lds,
@@ -437,22 +433,7 @@ __device__ __forceinline__ void form_private_queries(const BKRows<S>& bkr,
       for (int gg = 0; gg < C::PQ_GROUPS; ++gg) v += pacc[(gg * C::PQ_JOBS + tid) * S::CE + e];
       p[e] = v;
     }
-    uint4* dst = p_lds + h * C::P_STRIDE;
-    if constexpr (S::BF) {
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t h0 = f32_to_bf16_rne(p[2 * e]), h1 = f32_to_bf16_rne(p[2 * e + 1]);
-        hi[e] = h0 | (h1 << 16);
-        lo[e] = f32_to_bf16_rne(p[2 * e] - bf16_to_f32((uint16_t)h0)) |
-                (f32_to_bf16_rne(p[2 * e + 1] - bf16_to_f32((uint16_t)h1)) << 16);
-      }
-      dst[2 * c] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      dst[2 * c + 1] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    } else {
-      dst[c] = make_uint4(__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]),
-                          __float_as_uint(p[3]));
-    }
+    store_private_chunk<S>(p_lds + h * C::P_STRIDE + c * C::P_PER_CHUNK, p);
   }
 }
 
@@ -628,7 +609,7 @@ __device__ __forceinline__ void consume_page(const uint4* __restrict__ sk,
   }
 }
 
-template <class S, bool BAL>
+template <class S, bool BAL, bool EXTP = false>
 __global__ void __launch_bounds__(SplitCfg<S>::NT, 1)
 decode_split_kernel(const SplitArgs a) {
   using C = SplitCfg<S>;
@@ -722,6 +703,18 @@ decode_split_kernel(const SplitArgs a) {
     const int i = tid + k * C::NT;
     if (i < S::H * S::DHC) q_r[k] = qsrc[i];
   }
+  // lrkv_decode_pq: the row's private-query block travels with them, in place of the B_K
+  // rows and the formation below
+  constexpr int PBL = S::H * C::P_STRIDE;  // 16-byte slots of a row's block
+  constexpr int PCH = EXTP ? (PBL + C::NT - 1) / C::NT : 1;
+  uint4 p_r[PCH];
+  if constexpr (EXTP) {
+#pragma unroll
+    for (int k = 0; k < PCH; ++k) {
+      const int i = tid + k * C::NT;
+      if (i < PBL) p_r[k] = a.p_ext[row * PBL + i];
+    }
+  }
   // the request length is read first (a scalar load)
   const int len_b = a.seq_lens[b];
   const int vis = visible_tokens(len_b, a.q_len, qi);
@@ -739,12 +732,19 @@ decode_split_kernel(const SplitArgs a) {
     const int i = tid + k * C::NT;
     if (i < S::H * S::DHC) q_lds[(i / S::DHC) * C::Q_STRIDE + i % S::DHC] = q_r[k];
   }
-  __syncthreads();  // page ids and q in LDS
+  if constexpr (EXTP) {
+#pragma unroll
+    for (int k = 0; k < PCH; ++k) {
+      const int i = tid + k * C::NT;
+      if (i < PBL) p_lds[i] = p_r[k];
+    }
+  }
+  __syncthreads();  // page ids and q (and the private queries, given) in LDS
   // B_K rows go out once the page ids are in (ahead of them they delay the ids: every
   // workgroup reads all of B_K, 58 MB of L2 traffic at C1 sizes) and ahead of every page
   // load, since loads return in issue order
   BKRows<S> bkr;
-  load_bk_rows<S, !BAL>(BKg, tid, bkr);
+  if constexpr (!EXTP) load_bk_rows<S, !BAL>(BKg, tid, bkr);
 
   const int pg1 = (tok1 + S::P - 1) / S::P;
   const uint8_t* pool = a.pool;
@@ -760,7 +760,7 @@ decode_split_kernel(const SplitArgs a) {
   // pages pg0, pg0+1 go in flight while the private queries are formed
   issue_page<S>(page_ptr(pg0), L, r0);
   if (pg0 + 1 < pg1) issue_page<S>(page_ptr(pg0 + 1), L, r1);
-  form_private_queries<S>(bkr, q_lds, pacc, p_lds, tid);
+  if constexpr (!EXTP) form_private_queries<S>(bkr, q_lds, pacc, p_lds, tid);
   stage_shared<S>(sk_lds[0], sv_lds[0], svt_lds[0], n_lds[0], tid, r0, nvalid(pg0));
   __syncthreads();
 
@@ -1047,8 +1047,35 @@ merge_expand_kernel(const float* __restrict__ part, const void* __restrict__ BV,
 }
 
 // ---------------------------------------------------------------------------------------
+// Private queries once per query row (eq 6 of the LRKV notes), for lrkv_decode_pq: one
+// workgroup per (head, block of query rows), private_query_block (the split kernel's own
+// sums, in its order, and its hi + lo packing; B_K[h] read once per workgroup).  A split
+// workgroup that reads the block instead of forming it holds bit for bit the same private
+// queries.
+// ---------------------------------------------------------------------------------------
+template <class S>
+__global__ void __launch_bounds__(256)
+private_queries_kernel(const void* __restrict__ q, const void* __restrict__ BK, int rows,
+                       uint4* __restrict__ p_out) {
+  private_query_block<S>(q, BK, rows, p_out, blockIdx.x);
+}
+
+// ---------------------------------------------------------------------------------------
 // host launcher
 // ---------------------------------------------------------------------------------------
+template <class S>
+size_t private_query_row_bytes() {
+  return (size_t)PrivCfg<S>::ROW_SLOTS * 16;
+}
+
+template <class S>
+hipError_t launch_private_queries(const void* q, const void* BK, int rows, void* p, hipStream_t stream) {
+  static_assert(PrivBlockCfg<S>::NT == 256, "workgroup size");
+  hipLaunchKernelGGL((private_queries_kernel<S>), dim3((unsigned)private_query_workgroups<S>(rows)),
+                     dim3(256), 0, stream, q, BK, rows, static_cast<uint4*>(p));
+  return hipGetLastError();
+}
+
 template <class S>
 SplitArgs split_args(const DecodeArgs& a) {
   SplitArgs s{};
@@ -1073,23 +1100,29 @@ SplitArgs split_args(const DecodeArgs& a) {
   return s;
 }
 
-template <class S>
+template <class S, bool EXTP = false>
 void launch_split(const DecodeArgs& a, const SplitArgs& s, int group_rows = 1) {
   if (a.groups > 0)
-    hipLaunchKernelGGL((decode_split_kernel<S, true>), dim3(a.groups, group_rows),
+    hipLaunchKernelGGL((decode_split_kernel<S, true, EXTP>), dim3(a.groups, group_rows),
                        dim3(SplitCfg<S>::NT), 0, a.stream, s);
   else
-    hipLaunchKernelGGL((decode_split_kernel<S, false>),
+    hipLaunchKernelGGL((decode_split_kernel<S, false, EXTP>),
                        dim3((a.batch * a.q_len * a.n_split + 7) / 8 * 8, group_rows),
                        dim3(SplitCfg<S>::NT), 0, a.stream, s);
 }
 
 template <class S>
 hipError_t launch_decode(const DecodeArgs& a) {
-  if constexpr (S::BF && !S::NORM) {  // key-norm layouts: every row through the split
-    if (a.q_len >= kPrefillMinRows) return launch_prefill<S>(a);
+  if (a.p_ext) {  // lrkv_decode_pq: private queries formed beforehand (split path only)
+    SplitArgs s = split_args<S>(a);
+    s.p_ext = static_cast<const uint4*>(a.p_ext);
+    if constexpr (!S::NORM) launch_split<S, true>(a, s);
+  } else {
+    if constexpr (S::BF && !S::NORM) {  // key-norm layouts: every row through the split
+      if (a.q_len >= kPrefillMinRows) return launch_prefill<S>(a);
+    }
+    launch_split<S>(a, split_args<S>(a));
   }
-  launch_split<S>(a, split_args<S>(a));
   if (a.groups > 0) {  // balanced split, one query row per request
     hipLaunchKernelGGL((merge_expand_kernel<S, true>), dim3(S::H, 1, a.batch), dim3(256), 0,
                        a.stream, a.part_ws, a.B_V, a.seq_lens, 1, 0, 0, a.batch, a.groups,
@@ -1136,6 +1169,12 @@ template hipError_t launch_merge<ShapeC3>(const DecodeArgs&);
 template hipError_t launch_merge<ShapeC1N>(const DecodeArgs&);
 template hipError_t launch_merge<ShapeC3N>(const DecodeArgs&);
 
+template size_t private_query_row_bytes<ShapeC0>();
+template size_t private_query_row_bytes<ShapeC1>();
+template size_t private_query_row_bytes<ShapeC3>();
+template hipError_t launch_private_queries<ShapeC0>(const void*, const void*, int, void*, hipStream_t);
+template hipError_t launch_private_queries<ShapeC1>(const void*, const void*, int, void*, hipStream_t);
+template hipError_t launch_private_queries<ShapeC3>(const void*, const void*, int, void*, hipStream_t);
 template hipError_t launch_decode<ShapeC0>(const DecodeArgs&);
 template hipError_t launch_decode<ShapeC1>(const DecodeArgs&);
 template hipError_t launch_decode<ShapeC3>(const DecodeArgs&);

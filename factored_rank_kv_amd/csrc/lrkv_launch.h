@@ -36,6 +36,9 @@ struct DecodeArgs {
   // or, balanced, [groups + batch][H]
   float* part_ws;
   hipStream_t stream;
+  // lrkv_decode_pq: the rows' private queries as private_queries_kernel writes them (null:
+  // the split workgroups form them from B_K)
+  const void* p_ext;
 };
 
 struct AppendArgs {
@@ -60,6 +63,17 @@ struct AppendArgs {
 
 template <class S>
 hipError_t launch_decode(const DecodeArgs& a);
+
+// Private queries formed once per query row, for lrkv_decode_pq (plain layouts): bytes per
+// row of the block, and the launch over `rows` rows of q.
+template <class S>
+size_t private_query_row_bytes();
+template <class S>
+hipError_t launch_private_queries(const void* q, const void* BK, int rows, void* p, hipStream_t stream);
+// The append of a.n_rows (1..8) bf16 rows and the private queries of `rows` query rows in
+// one launch on a.stream: workgroups of the formation, then the 8-row append's.
+template <class S>
+hipError_t launch_append_pq(const AppendArgs& a, const void* q, const void* BK, int rows, void* p);
 
 // Grouped layout of G blocks of shape Sg (G * Sg::H = S::H heads): the split kernels run
 // per group on its block, one merge of shape S covers every head.
@@ -88,6 +102,10 @@ constexpr int kBalancedMaxBatch = 1024;
 // Query rows per request at or above which a bf16 lrkv_decode call takes the multi-query
 // (prefill) kernel; it needs no workspace.
 constexpr int kPrefillMinRows = 64;
+
+// Most query rows (batch x q_len) of one private-query formation (its grid, H workgroups
+// per block of 9 or more rows, stays well under 2^31 workgroups).
+constexpr long long kMaxPrivateQueryRows = 1LL << 22;
 
 // Rotary decode: heads per workgroup (one wavefront each) and the workgroups one wave of the
 // grid holds (one per compute unit: eight wavefronts, two per SIMD, fill its registers).

@@ -242,6 +242,56 @@ int lrkv_decode_rope(const lrkv_layout* L, const void* q, int32_t batch, int32_t
 size_t lrkv_decode_rope_workspace_bytes(const lrkv_layout* L, int32_t batch, int32_t q_len,
                                         int32_t max_seq_len, int32_t chunk_tokens);
 
+/* The private queries of eq 6 (LRKV notes §3: p_h = q_h B_K[h], one r-vector per query row
+ * and head, shared by every key position) formed once per query row, for lrkv_decode_pq.
+ * lrkv_decode forms them inside each of its split workgroups (each reads all of B_K); a
+ * decode step can instead form them here (or with the step's new rows in one launch,
+ * lrkv_append_pq: p depends on q and B_K only) and hand them to lrkv_decode_pq.
+ *   q          device, [batch][q_len][H][d_h] in L->dtype (the decode call's queries)
+ *   B_K        device, [H][d_h][r] in L->dtype
+ *   p          device, >= lrkv_private_queries_bytes(L, batch, q_len) bytes, 16-byte
+ *              aligned, written by this call.  Its layout is this library's (per row and
+ *              head, float32 sums over d_h rounded to bfloat16 hi + lo pairs per 8-rank
+ *              chunk for a bf16 cache, float32 for a float32 cache, with zero padding): it is
+ *              only read by lrkv_decode_pq with the same layout, batch and q_len.
+ * Plain layouts only (groups <= 1, key_norm = 0): (4, 16, 4) float32, (16, 128, 56) and
+ * (32, 128, 32) bf16; others return LRKV_ERR_UNSUPPORTED.  batch * q_len <= 4194304 rows
+ * (LRKV_ERR_INVALID_ARG beyond).  Same arithmetic, in the same order, as lrkv_decode's own
+ * formation, so lrkv_decode_pq's output equals lrkv_decode's bit for bit. */
+int lrkv_private_queries(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_len,
+                         const void* B_K, void* p, size_t p_bytes, void* stream);
+
+/* Infrastructure of this library: the bytes of lrkv_private_queries' output (0 for an
+ * unsupported layout or invalid sizes). */
+size_t lrkv_private_queries_bytes(const lrkv_layout* L, int32_t batch, int32_t q_len);
+
+/* lrkv_append and lrkv_private_queries in one call: the n_rows new rows of Algorithm 1
+ * (LRKV notes §3) appended to the pool, and the private queries of the batch * q_len query
+ * rows q formed into p, with every argument of both checked before anything is launched
+ * (arguments and their rules as in those two calls).  For 1..8 new rows of a bf16 cache
+ * the two products run as one launch, the formation on compute units the few append
+ * workgroups leave free (the decode step's case); otherwise as the two calls, in order, on
+ * `stream`.  Plain layouts only, as lrkv_private_queries. */
+int lrkv_append_pq(const lrkv_layout* L, const void* X, int32_t n_rows, int32_t d,
+                   const void* W_SK, const void* W_SV, const void* U_K, const void* U_V,
+                   const int32_t* row_req, const int32_t* row_pos, const int32_t* page_table,
+                   int32_t max_pages_per_req, void* pool, int64_t num_pages, const void* q,
+                   int32_t batch, int32_t q_len, const void* B_K, void* p, size_t p_bytes,
+                   void* stream);
+
+/* lrkv_decode with the private queries given (p from lrkv_private_queries for these q,
+ * B_K, batch and q_len) instead of B_K: the same split and merge, the same output bit for
+ * bit, without each split workgroup reading B_K and forming p.  Arguments as lrkv_decode,
+ * with p in place of B_K; workspace >= lrkv_decode_workspace_bytes(L, batch, q_len,
+ * max_seq_len, chunk_tokens).  Plain layouts as lrkv_private_queries; a bf16 call with
+ * q_len >= 64 (which lrkv_decode sends to its multi-query kernel) returns
+ * LRKV_ERR_UNSUPPORTED. */
+int lrkv_decode_pq(const lrkv_layout* L, const void* q, const void* p, int32_t batch,
+                   int32_t q_len, const void* B_V, const void* pool, const int32_t* page_table,
+                   int32_t max_pages_per_req, const int32_t* seq_lens, int32_t max_seq_len,
+                   int32_t chunk_tokens, void* out, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
 /* lrkv_decode without a workspace argument, for callers that cannot allocate device memory
  * for it (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation).  Same arguments, semantics and kernels as lrkv_decode, minus workspace and

@@ -1,6 +1,7 @@
 """HIP graph capture of the library's calls, as a serving loop replays one graph per decode
 step: lrkv_append (decode-step and prompt-sized), lrkv_decode (chunked and balanced split),
-lrkv_decode_noalloc and lrkv_decode_rope, each captured by torch's graph capture on the
+lrkv_decode_noalloc, lrkv_decode_rope and the step lrkv_append_pq + lrkv_decode_pq, each
+captured by torch's graph capture on the
 launch stream and replayed several times, with eager work on the same stream between the
 replays (the output and the workspace poisoned, an unrelated reduction).  Every replay must
 give the eager call's result bit for bit: the kernels are deterministic, and the library
@@ -154,3 +155,61 @@ def test_append_replays(n_rows):
     assert int((want != 0).sum()) > 0
     gr = capture(call)
     replay_and_check(gr, pool, want, lambda i: pool.copy_(pool0), f"lrkv_append, {n_rows} rows")
+
+
+def test_append_pq_decode_pq_step_replays():
+    """The decode step with the private queries formed beside the append: lrkv_append_pq
+    then lrkv_decode_pq, captured as one graph; p, the output and the workspace are poisoned
+    between the replays."""
+    H, dh, r, d = 16, 128, 56, 256
+    lens_before = [120, 7, 64, 31]
+    B = len(lens_before)
+    case = iid_case(506, H, dh, r, O.BF16, [t + 1 for t in lens_before], fill=0x7FC0)
+    dv = case.dev
+    L = case.L
+    lay = layout_c(L)
+    g = np.random.default_rng(507)
+    Xd = to_dev(as_codes(g.standard_normal((B, d)).astype(np.float32), O.BF16))
+    wdev = {k: to_dev(output_major(as_codes((g.standard_normal(s) / np.sqrt(d)).astype(np.float32),
+                                            O.BF16)))
+            for k, s in {"W_SK": (d, dh), "W_SV": (d, dh), "U_K": (d, H, r),
+                         "U_V": (d, H, r)}.items()}
+    reqd = to_dev(np.arange(B, dtype=np.int32))
+    posd = to_dev(np.array(lens_before, np.int32))
+    msl = int(case.lens.max())
+    nb = F.lrkv_decode_workspace_bytes(lay, B, 1, msl, 0)
+    ws = fresh_workspace(nb, 0xFF)
+    pb = F.lrkv_private_queries_bytes(lay, B, 1)
+    p = fresh_workspace(pb, 0xFF)
+    pool = dv["pool"].clone()
+    out = torch.empty(case.q_codes.shape, dtype=dv["q"].dtype, device=DEV)
+
+    def call():
+        F.lrkv_append_pq(lay, Xd, B, d, wdev["W_SK"], wdev["W_SV"], wdev["U_K"], wdev["U_V"], reqd,
+                         posd, dv["table"], case.table.shape[1], pool, case.num_pages, dv["q"], B, 1,
+                         dv["BK"], p, pb)
+        F.lrkv_decode_pq(lay, dv["q"], p, B, 1, dv["BV"], pool, dv["table"], case.table.shape[1],
+                         dv["lens"], msl, 0, out, ws, nb)
+
+    call()
+    torch.cuda.synchronize()
+    want = out.clone()
+    pool_want = pool.clone()
+    # the eager step against lrkv_append + lrkv_decode on a fresh copy of the cache
+    pool2 = dv["pool"].clone()
+    out2 = torch.empty_like(out)
+    F.lrkv_append(lay, Xd, B, d, wdev["W_SK"], wdev["W_SV"], wdev["U_K"], wdev["U_V"], reqd, posd,
+                  dv["table"], case.table.shape[1], pool2, case.num_pages)
+    F.lrkv_decode(lay, dv["q"], B, 1, dv["BK"], dv["BV"], pool2, dv["table"], case.table.shape[1],
+                  dv["lens"], msl, 0, out2, fresh_workspace(nb, 0xFF), nb)
+    torch.cuda.synchronize()
+    assert torch.equal(want, out2) and torch.equal(pool_want, pool2)
+    gr = capture(call)
+
+    def clobber(i):
+        out.fill_(-1)
+        p.fill_(0xFF if i % 2 else 0x00)
+        ws.fill_(0x00 if i % 2 else 0xFF)
+
+    replay_and_check(gr, out, want, clobber, "lrkv_append_pq + lrkv_decode_pq")
+    assert torch.equal(pool, pool_want)

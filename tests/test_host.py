@@ -203,6 +203,67 @@ def test_append_rejects_bad_arguments_before_launch():
     assert append_status(n_rows=0) == F.LRKV_OK  # nothing to do, nothing launched
 
 
+def test_private_query_calls_reject_bad_arguments_before_launch():
+    """lrkv_private_queries / lrkv_append_pq / lrkv_decode_pq: sizes follow the layout;
+    layouts without that split path (key norms, grouped blocks) and bf16 decode calls of 64
+    or more query rows per request (those take the multi-query kernel) are refused."""
+    n1 = F.lrkv_private_queries_bytes(C1, 1, 1)
+    assert n1 > 0 and n1 % 16 == 0
+    assert F.lrkv_private_queries_bytes(C1, 8, 3) == 24 * n1
+    assert F.lrkv_private_queries_bytes(C3, 2, 1) > 0
+    assert F.lrkv_private_queries_bytes(C0, 2, 5) > 0
+    C1N = F.lrkv_layout(16, 128, 56, 16, F.LRKV_BF16, 1)
+    C3G = F.lrkv_layout(32, 128, 32, 16, F.LRKV_BF16, 0, 2)
+    assert F.lrkv_private_queries_bytes(C1N, 1, 1) == 0
+    assert F.lrkv_private_queries_bytes(C3G, 1, 1) == 0
+    assert F.lrkv_private_queries_bytes(C1, 0, 1) == 0
+
+    def pq(lay=C1, **over):
+        args = dict(q=FAKE, batch=2, q_len=1, B_K=FAKE, p=FAKE, p_bytes=1 << 30)
+        args.update(over)
+        return F.lrkv_private_queries(lay, check=False, stream=0, **args)
+
+    bad = F.LRKV_ERR_INVALID_ARG
+    assert pq(q=None) == bad
+    assert pq(p=FAKE + 8) == bad
+    assert pq(batch=0) == bad
+    assert pq(p_bytes=2 * n1 - 16) == bad
+    assert pq(C1N) == F.LRKV_ERR_UNSUPPORTED
+    assert pq(C3G) == F.LRKV_ERR_UNSUPPORTED
+
+    def dec(lay=C1, **over):
+        args = dict(q=FAKE, p=FAKE, batch=2, q_len=1, B_V=FAKE, pool=FAKE, page_table=FAKE,
+                    max_pages_per_req=4, seq_lens=FAKE, max_seq_len=64, chunk_tokens=0,
+                    out=FAKE, workspace=FAKE, workspace_bytes=1 << 30)
+        args.update(over)
+        return F.lrkv_decode_pq(lay, check=False, stream=0, **args)
+
+    assert dec(p=None) == bad
+    assert dec(p=FAKE + 4) == bad
+    assert dec(workspace=FAKE + 16) == bad
+    assert dec(workspace_bytes=16) == bad
+    assert dec(chunk_tokens=24) == bad
+    assert dec(C1N) == F.LRKV_ERR_UNSUPPORTED
+    assert dec(C3G) == F.LRKV_ERR_UNSUPPORTED
+    assert dec(q_len=64, max_seq_len=64) == F.LRKV_ERR_UNSUPPORTED
+
+    def apq(lay=C1, **over):
+        args = dict(X=FAKE, n_rows=8, d=2048, W_SK=FAKE, W_SV=FAKE, U_K=FAKE, U_V=FAKE,
+                    row_req=FAKE, row_pos=FAKE, page_table=FAKE, max_pages_per_req=4, pool=FAKE,
+                    num_pages=8, q=FAKE, batch=8, q_len=1, B_K=FAKE, p=FAKE, p_bytes=8 * n1)
+        args.update(over)
+        return F.lrkv_append_pq(lay, check=False, stream=0, **args)
+
+    # a bad argument of either step stops the call before anything is launched
+    assert apq(X=None) == bad
+    assert apq(d=100) == bad
+    assert apq(q=None) == bad
+    assert apq(p_bytes=8 * n1 - 16) == bad
+    assert apq(batch=0) == bad
+    assert apq(C1N) == F.LRKV_ERR_UNSUPPORTED
+    assert apq(C3G) == F.LRKV_ERR_UNSUPPORTED
+
+
 def check_status(lay=C1, **over):
     args = dict(page_table=FAKE, batch=2, max_pages_per_req=4, seq_lens=FAKE, max_seq_len=64,
                 row_req=FAKE, row_pos=FAKE, n_rows=3, num_pages=8, errors=FAKE)
