@@ -93,18 +93,43 @@ __device__ __forceinline__ void private_query_block(const void* __restrict__ q,
   const int t = (int)threadIdx.x;
   const int h = (int)(blk % S::H);
   const long long row0 = (blk / S::H) * W::ROWS_WG;
-  // B_K[h] (d_h rows of RC chunks, contiguous) and the block's query rows of head h
+  // B_K[h] (d_h rows of RC chunks, contiguous) and the block's query rows of head h: every
+  // load of the thread goes out before its first LDS write (as a loop, each load was
+  // waited for before the next went out)
+  constexpr int BKN = S::DH * S::RC, BKI = (BKN + W::NT - 1) / W::NT;
+  constexpr int QN = W::ROWS_WG * S::DHC, QI = (QN + W::NT - 1) / W::NT;
   const uint4* bkg = reinterpret_cast<const uint4*>(BK) + (size_t)h * S::DH * S::RC;
-  for (int e = t; e < S::DH * S::RC; e += W::NT) {
-    const int d = e / S::RC, c = e - d * S::RC;
-    const int g = d / C::PQ_DSPAN, dd = d - g * C::PQ_DSPAN;
-    bk_lds[(g * (C::PQ_DSPAN + 1) + dd) * S::RC + c] = bkg[e];
+  uint4 bkv[BKI], qvv[QI];
+#pragma unroll
+  for (int k = 0; k < BKI; ++k) {
+    const int e = min(t + k * W::NT, BKN - 1);  // lanes past the end re-read the last chunk
+    bkv[k] = bkg[e];
   }
-  for (int e = t; e < W::ROWS_WG * S::DHC; e += W::NT) {
-    const int rl = e / S::DHC, k = e - rl * S::DHC;
+#pragma unroll
+  for (int k = 0; k < QI; ++k) {
+    const int e = min(t + k * W::NT, QN - 1);
+    const int rl = e / S::DHC, kk = e - rl * S::DHC;
     const long long row = row0 + rl < rows ? row0 + rl : rows - 1;  // past the end: a valid row
-    q_lds[e] = reinterpret_cast<const uint4*>(q)[((size_t)row * S::H + h) * S::DHC + k];
+    qvv[k] = reinterpret_cast<const uint4*>(q)[((size_t)row * S::H + h) * S::DHC + kk];
   }
+  // (an empty statement taking each value keeps the loads from sinking into the
+  // conditional stores below, one round trip each)
+#pragma unroll
+  for (int k = 0; k < BKI; ++k) asm volatile("" ::"v"(bkv[k].x), "v"(bkv[k].y), "v"(bkv[k].z), "v"(bkv[k].w));
+#pragma unroll
+  for (int k = 0; k < QI; ++k) asm volatile("" ::"v"(qvv[k].x), "v"(qvv[k].y), "v"(qvv[k].z), "v"(qvv[k].w));
+#pragma unroll
+  for (int k = 0; k < BKI; ++k) {
+    const int e = t + k * W::NT;
+    if (e < BKN) {
+      const int d = e / S::RC, c = e - d * S::RC;
+      const int g = d / C::PQ_DSPAN, dd = d - g * C::PQ_DSPAN;
+      bk_lds[(g * (C::PQ_DSPAN + 1) + dd) * S::RC + c] = bkv[k];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < QI; ++k)
+    if (t + k * W::NT < QN) q_lds[t + k * W::NT] = qvv[k];
   __syncthreads();
   const int g = t % C::PQ_GROUPS;
   const int c = (t / C::PQ_GROUPS) % S::RC;
@@ -112,17 +137,44 @@ __device__ __forceinline__ void private_query_block(const void* __restrict__ q,
   const uint8_t* qs = reinterpret_cast<const uint8_t*>(q_lds + rl * S::DHC) +
                       (size_t)g * C::PQ_DSPAN * S::EB;
   const uint4* bks = bk_lds + g * (C::PQ_DSPAN + 1) * S::RC + c;
+  // the chain's operands in registers, every LDS read before the first product (left to
+  // the scheduler, each read waited for right before its product)
+  constexpr int QV = (C::PQ_DSPAN * S::EB) % 16 == 0 ? C::PQ_DSPAN * S::EB / 16 : 0;
+  uint4 qv[QV > 0 ? QV : 1];
+  float qsc[QV > 0 ? 1 : C::PQ_DSPAN];
+  if constexpr (QV > 0) {
+#pragma unroll
+    for (int k = 0; k < QV; ++k) qv[k] = reinterpret_cast<const uint4*>(qs)[k];
+  } else {
+#pragma unroll
+    for (int dd = 0; dd < C::PQ_DSPAN; ++dd)
+      qsc[dd] = S::BF ? bf16_to_f32(reinterpret_cast<const uint16_t*>(qs)[dd])
+                      : reinterpret_cast<const float*>(qs)[dd];
+  }
+  uint4 b4[C::PQ_DSPAN];
+#pragma unroll
+  for (int dd = 0; dd < C::PQ_DSPAN; ++dd) b4[dd] = bks[dd * S::RC];
+#pragma unroll
+  for (int dd = 0; dd < C::PQ_DSPAN; ++dd)
+    asm volatile("" ::"v"(b4[dd].x), "v"(b4[dd].y), "v"(b4[dd].z), "v"(b4[dd].w));
   float acc[S::CE];
 #pragma unroll
   for (int e = 0; e < S::CE; ++e) acc[e] = 0.f;
 #pragma unroll
   for (int dd = 0; dd < C::PQ_DSPAN; ++dd) {
     float qd;
-    if constexpr (S::BF)
-      qd = bf16_to_f32(reinterpret_cast<const uint16_t*>(qs)[dd]);
-    else
-      qd = reinterpret_cast<const float*>(qs)[dd];
-    const uint4 b = bks[dd * S::RC];
+    if constexpr (QV > 0) {
+      const uint4 w4 = qv[dd * S::EB / 16];
+      const int wi = (dd * S::EB / 4) % 4;
+      const uint32_t w = wi == 0 ? w4.x : wi == 1 ? w4.y : wi == 2 ? w4.z : w4.w;
+      if constexpr (S::BF)
+        qd = (dd & 1) ? bf16_hi(w) : bf16_lo(w);
+      else
+        qd = __uint_as_float(w);
+    } else {
+      qd = qsc[dd];
+    }
+    const uint4 b = b4[dd];
     if constexpr (S::BF) {
       acc[0] = fmaf(qd, bf16_lo(b.x), acc[0]);
       acc[1] = fmaf(qd, bf16_hi(b.x), acc[1]);
