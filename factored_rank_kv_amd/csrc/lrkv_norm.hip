@@ -41,12 +41,30 @@ __global__ void __launch_bounds__(256, 2) key_norm_kernel(const NormArgs a) {
   __shared__ int row_slot[C::ROWS];
   const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = (int)blockIdx.x * C::ROWS;
+  const int n = lane & 15, g = lane >> 4;
+  const int h = 4 * (int)blockIdx.y + wave;
+  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+  // B_K[h] operands depend on nothing: requested first, beside the rows' destinations.
+  // B: B_K[h][16nt + lane%16][k0 .. k0 + 8), k0 = 32 kb + 8 (lane/16); k0 past r reads a
+  // valid chunk and is zeroed
+  const uint8_t* bkh = static_cast<const uint8_t*>(a.B_K) + (size_t)h * S::DH * S::R * 2;
+  uint4 bvv[C::KB][C::NTILE];
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb) {
+    const int k0 = 32 * kb + 8 * g;
+    const int kc = min(k0, S::R - 8);
+#pragma unroll
+    for (int nt = 0; nt < C::NTILE; ++nt) {
+      const uint4 v = *reinterpret_cast<const uint4*>(bkh + ((size_t)(16 * nt + n) * S::R + kc) * 2);
+      bvv[kb][nt] = k0 < S::R ? v : zero;
+    }
+  }
   if (tid < C::ROWS) {
-    const int n = n0 + tid;
+    const int nr = n0 + tid;
     long long off = -1;
     int slot = 0;
-    if (n < a.n_rows) {
-      const int req = a.row_req[n], pos = a.row_pos[n];
+    if (nr < a.n_rows) {
+      const int req = a.row_req[nr], pos = a.row_pos[nr];
       off = (long long)a.page_table[(size_t)req * a.max_pages + pos / S::P] * S::PAGE;
       slot = pos % S::P;
     }
@@ -55,49 +73,48 @@ __global__ void __launch_bounds__(256, 2) key_norm_kernel(const NormArgs a) {
   }
   __syncthreads();
   const uint8_t* pool = static_cast<const uint8_t*>(a.pool);
-  {  // thread (row i, chunk c): 8 features of the row's S_K, transposed into skt
-    const int i = tid / S::DHC, c = tid % S::DHC;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (row_page[i] >= 0)
-      v = *reinterpret_cast<const uint4*>(pool + row_page[i] + (c * S::P + row_slot[i]) * 16);
+  // the rows' S_K chunks (thread (row i, chunk c)) and this lane's R_K[h] chunks, requested
+  // together (rows past the last read page 0 and are zeroed)
+  const int i_s = tid / S::DHC, c_s = tid % S::DHC;
+  const long long p_s = row_page[i_s];
+  const uint4 sk0 = *reinterpret_cast<const uint4*>(pool + (p_s >= 0 ? p_s : 0) +
+                                                    (c_s * S::P + row_slot[i_s]) * 16);
+  const long long my_page = row_page[lane & 15];  // the A operand's row: lane % 16
+  const int my_slot = row_slot[lane & 15];
+  uint4 av[C::KB];
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb) {
+    const int c = 4 * kb + g;  // A: R_K[h] chunk c of row lane % 16
+    const int cl = min(c, S::RC - 1);
+    const uint4 x = *reinterpret_cast<const uint4*>(pool + (my_page >= 0 ? my_page : 0) + S::OFF_RK +
+                                                    h * S::SEC_R + (cl * S::P + my_slot) * 16);
+    av[kb] = (c < S::RC && my_page >= 0) ? x : zero;
+  }
+  {  // S_K of the rows, transposed into skt
+    const uint4 v = p_s >= 0 ? sk0 : zero;
     const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      skt[(8 * c + 2 * e) * C::ROWS + i] = (uint16_t)(w4[e] & 0xffffu);
-      skt[(8 * c + 2 * e + 1) * C::ROWS + i] = (uint16_t)(w4[e] >> 16);
+      skt[(8 * c_s + 2 * e) * C::ROWS + i_s] = (uint16_t)(w4[e] & 0xffffu);
+      skt[(8 * c_s + 2 * e + 1) * C::ROWS + i_s] = (uint16_t)(w4[e] >> 16);
     }
   }
   __syncthreads();
 
-  const int n = lane & 15, g = lane >> 4;
-  const long long my_page = row_page[lane & 15];  // the A operand's row: lane % 16
-  const int my_slot = row_slot[lane & 15];
   {
-    const int h = 4 * (int)blockIdx.y + wave;
     f32x4_n acc[C::NTILE];
 #pragma unroll
     for (int nt = 0; nt < C::NTILE; ++nt) {
       const uint2 v = *reinterpret_cast<const uint2*>(skt + (16 * nt + n) * C::ROWS + 4 * g);
       acc[nt] = f32x4_n{bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
     }
-    const uint8_t* bkh = static_cast<const uint8_t*>(a.B_K) + (size_t)h * S::DH * S::R * 2;
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-      const int c = 4 * kb + g;  // A: R_K[h] chunk c of row lane % 16
-      uint4 av = make_uint4(0u, 0u, 0u, 0u);
-      if (c < S::RC && my_page >= 0)
-        av = *reinterpret_cast<const uint4*>(pool + my_page + S::OFF_RK + h * S::SEC_R +
-                                             (c * S::P + my_slot) * 16);
-      const int k0 = 32 * kb + 8 * g;  // B: B_K[h][16nt + lane%16][k0 .. k0 + 8)
+    for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-      for (int nt = 0; nt < C::NTILE; ++nt) {
-        const uint4 bv = k0 < S::R ? *reinterpret_cast<const uint4*>(bkh + ((size_t)(16 * nt + n) * S::R + k0) * 2)
-                                   : make_uint4(0u, 0u, 0u, 0u);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_n, av),
-                                                          __builtin_bit_cast(bf16x8_n, bv), acc[nt],
-                                                          0, 0, 0);
-      }
-    }
+      for (int nt = 0; nt < C::NTILE; ++nt)
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_n, av[kb]),
+                                                          __builtin_bit_cast(bf16x8_n, bvv[kb][nt]),
+                                                          acc[nt], 0, 0, 0);
     // lane holds rows 4g..4g+3 of feature 16nt + lane%16: sum of squares over the features
     float ss[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
