@@ -321,24 +321,21 @@ decode_rope_kernel(const RopeArgs a) {
   const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = hg * C::HG + wave;
 
-  const int vis = visible_tokens(a.seq_lens[b], a.q_len, qi);
+  // the chunk's page ids, this wavefront's query row and its head's B_K rows are requested
+  // before the length is known (each valid to read whatever it is), so that one round trip
+  // serves them all; the length decides what is kept.  (As loops, each id and query load was
+  // waited for before the next load went out: four round trips before the first page.)
   const int pg0 = split * (a.chunk / S::P);
-  const int tok0 = pg0 * S::P;
-  const int tok1 = min(vis, min(pg0 + a.chunk / S::P, a.max_pages) * S::P);
-  if (tok0 >= tok1) return;  // uniform: no record for a chunk past the visible tokens
-  const int pg1 = (tok1 + S::P - 1) / S::P;
-  const int n_pg = pg1 - pg0;
-  for (int i = tid; i < n_pg; i += C::NT) ids_lds[i] = a.page_table[(size_t)b * a.max_pages + pg0 + i];
-  {  // this wavefront's query row to LDS before the B_K rows are requested (loads return in order)
-    const size_t row = (size_t)b * a.q_len + qi;
-    const uint32_t* qrow = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.q) +
-                                                             (row * S::H + h) * S::DH * 2);
-    for (int x = lane; x < S::DH / 2; x += 64) q_lds[wave][x] = qrow[x];
-  }
-  // zero rows of the weights' A operand (heads past the group), both buffers
-  for (int i = tid; i < 2 * (16 - C::HG) * 4; i += C::NT)
-    wa_lds[i / ((16 - C::HG) * 4)][C::HG * 4 + i % ((16 - C::HG) * 4)] = make_uint4(0u, 0u, 0u, 0u);
-
+  const int n_ids = min(a.chunk / S::P, a.max_pages - pg0);  // table entries of the chunk
+  constexpr int IDK = (kRopeMaxChunkPages + C::NT - 1) / C::NT;
+  int id_r[IDK];
+  const int32_t* tab = a.page_table + (size_t)b * a.max_pages + pg0;
+#pragma unroll
+  for (int k = 0; k < IDK; ++k) id_r[k] = tab[min(tid + k * C::NT, n_ids - 1)];
+  static_assert(S::DH / 2 == 64, "one query pair per lane");
+  const size_t qrow_i = ((size_t)b * a.q_len + qi) * S::H + h;
+  const uint32_t q_r =
+      reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.q) + qrow_i * S::DH * 2)[lane];
   // this wavefront's head: B_K[h] as the MFMA A operand (lane: feature 16nt + lane%16,
   // rank 32kb + 8(lane/16) .. +8; zero past r)
   const int n = lane & 15, g = lane >> 4;
@@ -349,9 +346,28 @@ decode_rope_kernel(const RopeArgs a) {
 #pragma unroll
     for (int nt = 0; nt < C::NTILE; ++nt) {
       const int k0 = 32 * kb + 8 * g;
-      bk[kb][nt] = k0 < S::R ? *reinterpret_cast<const uint4*>(bkh + ((size_t)(16 * nt + n) * S::R + k0) * 2)
-                             : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 v = *reinterpret_cast<const uint4*>(bkh + ((size_t)(16 * nt + n) * S::R +
+                                                             min(k0, S::R - 8)) * 2);
+      bk[kb][nt] = k0 < S::R ? v : make_uint4(0u, 0u, 0u, 0u);
     }
+#pragma unroll
+  for (int k = 0; k < IDK; ++k) asm volatile("" ::"v"(id_r[k]));
+  asm volatile("" ::"v"(q_r));
+
+  const int vis = visible_tokens(a.seq_lens[b], a.q_len, qi);
+  const int tok0 = pg0 * S::P;
+  const int tok1 = min(vis, min(pg0 + a.chunk / S::P, a.max_pages) * S::P);
+  if (tok0 >= tok1) return;  // uniform: no record for a chunk past the visible tokens
+  const int pg1 = (tok1 + S::P - 1) / S::P;
+  const int n_pg = pg1 - pg0;
+#pragma unroll
+  for (int k = 0; k < IDK; ++k)
+    if (tid + k * C::NT < n_pg) ids_lds[tid + k * C::NT] = id_r[k];
+  q_lds[wave][lane] = q_r;
+  // zero rows of the weights' A operand (heads past the group), both buffers
+  for (int i = tid; i < 2 * (16 - C::HG) * 4; i += C::NT)
+    wa_lds[i / ((16 - C::HG) * 4)][C::HG * 4 + i % ((16 - C::HG) * 4)] = make_uint4(0u, 0u, 0u, 0u);
+
   const int mq_row = (g == (n >> 2)) ? n : 16;
   __syncthreads();  // page ids, query rows, zero rows in LDS
 
