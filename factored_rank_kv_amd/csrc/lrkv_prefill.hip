@@ -142,15 +142,31 @@ struct PrefillArgs {
 };
 
 // Stage a [rows x R] bf16 matrix (B_K[h] or B_V[h]) as rows of RP columns (zeros past R).
+// Every load of the thread goes out before its first LDS write (as a plain loop, each load
+// was waited for before the next went out).
 template <class S>
 __device__ __forceinline__ void stage_basis(uint8_t* lds, const void* src, int h, int t) {
   using C = PrefillCfg<S>;
+  constexpr int N = S::DH * (C::RP / 8), K = (N + C::NT - 1) / C::NT;
   const uint4* g = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(src) +
                                                   (size_t)h * S::DH * S::R * 2);
-  for (int i = t; i < S::DH * (C::RP / 8); i += C::NT) {
+  uint4 v[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int i = min(t + k * C::NT, N - 1);
     const int row = i / (C::RP / 8), c = i % (C::RP / 8);
-    const uint4 v = c < S::RC ? g[row * S::RC + c] : make_uint4(0u, 0u, 0u, 0u);
-    *reinterpret_cast<uint4*>(lds + row * C::R_STRIDE + 16 * c) = v;
+    const uint4 x = g[row * S::RC + min(c, S::RC - 1)];
+    v[k] = c < S::RC ? x : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) asm volatile("" ::"v"(v[k].x), "v"(v[k].y), "v"(v[k].z), "v"(v[k].w));
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int i = t + k * C::NT;
+    if (i < N) {
+      const int row = i / (C::RP / 8), c = i % (C::RP / 8);
+      *reinterpret_cast<uint4*>(lds + row * C::R_STRIDE + 16 * c) = v[k];
+    }
   }
 }
 
