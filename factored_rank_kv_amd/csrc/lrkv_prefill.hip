@@ -76,10 +76,6 @@ __device__ __forceinline__ float xor_max(float x) {
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __builtin_fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ __forceinline__ float xor_sum(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
-}
 
 }  // namespace
 
@@ -255,13 +251,17 @@ prefill_kernel(const PrefillArgs a) {
       pkl[w][kp] = cat8(ptl[w][2 * kp], ptl[w][2 * kp + 1]);
     }
 
-  // zero pad columns of the R_K / R_V rows (never overwritten by staging)
+  // pad columns of the R_K / R_V rows (never overwritten by staging): zeros, except that
+  // R_V column r holds 1.0 for every token, so that row r of O_R^T accumulates the row's
+  // exp-sum on the matrix cores, from the very bf16 weights the value products use (B_V's
+  // column r is zero, so the expansion drops it)
+  static_assert(S::R < C::RP && S::R % 8 == 0, "a pad column for the exp-sum");
   for (int i = t; i < 2 * C::BT * (C::RP / 8 - S::RC); i += C::NT) {
     const int which = i / (C::BT * (C::RP / 8 - S::RC));
     const int rem = i % (C::BT * (C::RP / 8 - S::RC));
     const int tok = rem / (C::RP / 8 - S::RC), c = S::RC + rem % (C::RP / 8 - S::RC);
     *reinterpret_cast<uint4*>(lds + (which ? C::RV_OFF : C::RK_OFF) + tok * C::R_STRIDE + 16 * c) =
-        make_uint4(0u, 0u, 0u, 0u);
+        make_uint4(which && c == S::RC ? 0x3F80u : 0u, 0u, 0u, 0u);
   }
 
   f32x4_p os[RW][C::FB], orr[RW][C::RB];
@@ -272,16 +272,12 @@ prefill_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < C::RB; ++i) orr[w][i] = f32x4_p{0.f, 0.f, 0.f, 0.f};
   }
-  // m_run: running max of the row (scaled, base-2 units); l_part: this lane's 4-token share
-  // of its exp-sum.  The max starts at a finite floor far below any score, so exp2 of a
-  // masked score (-inf) minus it is exactly 0 with no select, and the first visible score
-  // always moves it.
-  float m_run[RW], l_part[RW];
+  // m_run: running max of the row (scaled, base-2 units; the exp-sum is row r of O_R^T).
+  // The max starts at a finite floor far below any score, so exp2 of a masked score (-inf)
+  // minus it is exactly 0 with no select, and the first visible score always moves it.
+  float m_run[RW];
 #pragma unroll
-  for (int w = 0; w < RW; ++w) {
-    m_run[w] = -1e30f;
-    l_part[w] = 0.f;
-  }
+  for (int w = 0; w < RW; ++w) m_run[w] = -1e30f;
 
   const int32_t* tab = a.page_table + (size_t)b * a.max_pages;
   auto fill_ids = [&](int kt0) {  // page ids of key tiles kt0 .. kt0 + TPB - 1 (0 past the table)
@@ -439,7 +435,6 @@ prefill_kernel(const PrefillArgs a) {
         asm volatile("" ::: "memory");
         const float m_new = bump ? mt : m_run[w];
         const float alpha = exp2_fast(m_run[w] - m_new);  // 1 if not bumped, 0 on the first
-        l_part[w] *= alpha;
 #pragma unroll
         for (int i = 0; i < C::FB; ++i) os[w][i] *= alpha;
 #pragma unroll
@@ -456,10 +451,6 @@ prefill_kernel(const PrefillArgs a) {
         }
         const uint4 pw = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                     pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
-        // the exp-sum takes the same bf16-rounded weights the value products use, so the
-        // normalisation divides by exactly the weights that were summed
-        l_part[w] += ((bf16_lo(pw.x) + bf16_hi(pw.x)) + (bf16_lo(pw.y) + bf16_hi(pw.y))) +
-                     ((bf16_lo(pw.z) + bf16_hi(pw.z)) + (bf16_lo(pw.w) + bf16_hi(pw.w)));
         pp[w][tp] = __builtin_bit_cast(bf16x8_p, pw);
       }
     }
@@ -501,7 +492,9 @@ prefill_kernel(const PrefillArgs a) {
     short4_p orh[C::RB], orl[C::RB];
 #pragma unroll
     for (int rb = 0; rb < C::RB; ++rb) split4(orr[w][rb], orh[rb], orl[rb]);
-    const float l_row = xor_sum(l_part[w]);
+    // the exp-sum of row li: O_R^T[r][li], at lane 16 ((r % 16) / 4) + li, element r % 4 of
+    // block r / 16
+    const float l_row = __shfl(orr[w][S::R / 16][S::R % 4], 16 * ((S::R % 16) / 4) + li, 64);
     const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
     const size_t orow = (((size_t)b * a.q_len + row[w]) * S::H + h) * S::DH;
 #pragma unroll
