@@ -440,7 +440,7 @@ def next_rows_bench(torch, F, dev, timed, per_call_us, use_graph, qd, wd, tab, m
         p0 = torch.randn(nbytes // 2, device=dev, generator=g).to(torch.bfloat16).view(torch.uint8)
         return [p0] + [p0.clone() for _ in range(replicas - 1)]
 
-    def hbm_line(name, lay, q, BK, BV, n_heads, prepare=None, data_bytes=None):
+    def hbm_line(name, lay, q, BK, BV, n_heads, prepare=None, data_bytes=None, pq=False):
         pb = F.lrkv_page_bytes(lay)
         data_bytes = pb if data_bytes is None else data_bytes  # read per page (no padding)
         pools = rand_pools(num_pages * pb)
@@ -451,10 +451,18 @@ def next_rows_bench(torch, F, dev, timed, per_call_us, use_graph, qd, wd, tab, m
         ws_bytes = F.lrkv_decode_workspace_bytes(lay, B, 1, T, 0)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         o = torch.empty((B, 1, n_heads, dh), dtype=torch.int16, device=dev)
+        if pq:  # the private queries formed once per query row beforehand (lrkv_decode_pq)
+            pqb = F.lrkv_private_queries_bytes(lay, B, 1)
+            pbuf = torch.empty(pqb, dtype=torch.uint8, device=dev)
+            F.lrkv_private_queries(lay, q, B, 1, BK, pbuf, pqb)
 
         def call(k):
-            F.lrkv_decode(lay, q, B, 1, BK, BV, pools[k % len(pools)], tab, max_pages, lens, T, 0,
-                          o, ws, ws_bytes)
+            if pq:
+                F.lrkv_decode_pq(lay, q, pbuf, B, 1, BV, pools[k % len(pools)], tab, max_pages,
+                                 lens, T, 0, o, ws, ws_bytes)
+            else:
+                F.lrkv_decode(lay, q, B, 1, BK, BV, pools[k % len(pools)], tab, max_pages, lens,
+                              T, 0, o, ws, ws_bytes)
 
         for k in range(5):
             call(k)
@@ -490,6 +498,10 @@ def next_rows_bench(torch, F, dev, timed, per_call_us, use_graph, qd, wd, tab, m
     out_rec["key_norm_decode"] = hbm_line("key-norm decode", lay_kn, qd, wd["B_K"], wd["B_V"], H,
                                           prepare=real_norms, data_bytes=kn_data)
     out_rec["key_norm_decode"]["workload"] = "c1_bf16_b8_t4096_key_norm"
+    out_rec["key_norm_decode_pq"] = hbm_line("key-norm decode, private queries given", lay_kn, qd,
+                                             wd["B_K"], wd["B_V"], H, prepare=real_norms,
+                                             data_bytes=kn_data, pq=True)
+    out_rec["key_norm_decode_pq"]["workload"] = "c1_bf16_b8_t4096_key_norm"
 
     # the key-norm step of a decode-step append: 8 rows, every head
     pool_kn = torch.randn(num_pages * F.lrkv_page_bytes(lay_kn) // 2, device=dev,

@@ -264,15 +264,17 @@ int scratch_address(hipStream_t stream, void** ws) {
   return LRKV_OK;
 }
 
-// private queries formed once per query row: plain layouts only (one group, no key-norm
-// section)
-bool pq_variant(Variant v) { return v == V_C0 || v == V_C1 || v == V_C3; }
+// private queries formed once per query row: one-group layouts (with or without the
+// key-norm section, which p does not involve: a key-norm layout's block is its plain twin's)
+bool pq_variant(Variant v) {
+  return v == V_C0 || v == V_C1 || v == V_C3 || v == V_C1N || v == V_C3N;
+}
 
 size_t pq_row_bytes(Variant v) {
   switch (v) {
     case V_C0: return private_query_row_bytes<ShapeC0>();
-    case V_C1: return private_query_row_bytes<ShapeC1>();
-    case V_C3: return private_query_row_bytes<ShapeC3>();
+    case V_C1: case V_C1N: return private_query_row_bytes<ShapeC1>();
+    case V_C3: case V_C3N: return private_query_row_bytes<ShapeC3>();
     default: return 0;
   }
 }
@@ -394,6 +396,8 @@ int lrkv_private_queries(const lrkv_layout* L, const void* q, int32_t batch, int
     case V_C0: return hip_status(launch_private_queries<ShapeC0>(q, B_K, rows, p, s));
     case V_C1: return hip_status(launch_private_queries<ShapeC1>(q, B_K, rows, p, s));
     case V_C3: return hip_status(launch_private_queries<ShapeC3>(q, B_K, rows, p, s));
+    case V_C1N: return hip_status(launch_private_queries<ShapeC1>(q, B_K, rows, p, s));
+    case V_C3N: return hip_status(launch_private_queries<ShapeC3>(q, B_K, rows, p, s));
     default: return LRKV_ERR_UNSUPPORTED;
   }
 }
@@ -416,6 +420,8 @@ int lrkv_append_pq(const lrkv_layout* L, const void* X, int32_t n_rows, int32_t 
   if (n_rows >= 1 && n_rows <= 8 && L->dtype == LRKV_BF16 && d >= 8) {  // one launch
     if (v == V_C1) return hip_status(launch_append_pq<ShapeC1>(a, q, B_K, rows, p));
     if (v == V_C3) return hip_status(launch_append_pq<ShapeC3>(a, q, B_K, rows, p));
+    if (v == V_C1N) return hip_status(launch_append_pq<ShapeC1N>(a, q, B_K, rows, p));
+    if (v == V_C3N) return hip_status(launch_append_pq<ShapeC3N>(a, q, B_K, rows, p));
   }
   st = lrkv_append(L, X, n_rows, d, W_SK, W_SV, U_K, U_V, row_req, row_pos, page_table,
                    max_pages_per_req, pool, num_pages, stream);
@@ -436,7 +442,9 @@ int lrkv_decode_pq(const lrkv_layout* L, const void* q, const void* p, int32_t b
   const Variant v = find_variant(L);
   if (!pq_variant(v)) return LRKV_ERR_UNSUPPORTED;
   // the multi-query kernel forms its own private queries: such calls go to lrkv_decode
-  if (L->dtype == LRKV_BF16 && q_len >= kPrefillMinRows) return LRKV_ERR_UNSUPPORTED;
+  // (a key-norm layout takes every query row through the split kernel, either way)
+  if (L->dtype == LRKV_BF16 && !L->key_norm && q_len >= kPrefillMinRows)
+    return LRKV_ERR_UNSUPPORTED;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return LRKV_ERR_INVALID_ARG;
   if (workspace_bytes < z.total) return LRKV_ERR_INVALID_ARG;
   return decode_launch(L, q, batch, q_len, nullptr, B_V, pool, page_table, max_pages_per_req,

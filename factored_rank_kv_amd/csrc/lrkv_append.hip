@@ -610,6 +610,8 @@ hipError_t launch_append_pq(const AppendArgs& a_in, const void* q, const void* B
 
 template hipError_t launch_append_pq<ShapeC1>(const AppendArgs&, const void*, const void*, int, void*);
 template hipError_t launch_append_pq<ShapeC3>(const AppendArgs&, const void*, const void*, int, void*);
+template hipError_t launch_append_pq<ShapeC1N>(const AppendArgs&, const void*, const void*, int, void*);
+template hipError_t launch_append_pq<ShapeC3N>(const AppendArgs&, const void*, const void*, int, void*);
 
 template hipError_t launch_append<ShapeC0>(const AppendArgs&);
 template hipError_t launch_append<ShapeC1>(const AppendArgs&);

@@ -1116,7 +1116,7 @@ hipError_t launch_decode(const DecodeArgs& a) {
   if (a.p_ext) {  // lrkv_decode_pq: private queries formed beforehand (split path only)
     SplitArgs s = split_args<S>(a);
     s.p_ext = static_cast<const uint4*>(a.p_ext);
-    if constexpr (!S::NORM) launch_split<S, true>(a, s);
+    launch_split<S, true>(a, s);
   } else {
     if constexpr (S::BF && !S::NORM) {  // key-norm layouts: every row through the split
       if (a.q_len >= kPrefillMinRows) return launch_prefill<S>(a);

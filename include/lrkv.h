@@ -254,8 +254,8 @@ size_t lrkv_decode_rope_workspace_bytes(const lrkv_layout* L, int32_t batch, int
  *              head, float32 sums over d_h rounded to bfloat16 hi + lo pairs per 8-rank
  *              chunk for a bf16 cache, float32 for a float32 cache, with zero padding): it is
  *              only read by lrkv_decode_pq with the same layout, batch and q_len.
- * Plain layouts only (groups <= 1, key_norm = 0): (4, 16, 4) float32, (16, 128, 56) and
- * (32, 128, 32) bf16; others return LRKV_ERR_UNSUPPORTED.  batch * q_len <= 4194304 rows
+ * One-group layouts (groups <= 1, with or without key norms): (4, 16, 4) float32,
+ * (16, 128, 56) and (32, 128, 32) bf16; grouped layouts return LRKV_ERR_UNSUPPORTED.  batch * q_len <= 4194304 rows
  * (LRKV_ERR_INVALID_ARG beyond).  Same arithmetic, in the same order, as lrkv_decode's own
  * formation, so lrkv_decode_pq's output equals lrkv_decode's bit for bit. */
 int lrkv_private_queries(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_len,
@@ -271,7 +271,8 @@ size_t lrkv_private_queries_bytes(const lrkv_layout* L, int32_t batch, int32_t q
  * (arguments and their rules as in those two calls).  For 1..8 new rows of a bf16 cache
  * the two products run as one launch, the formation on compute units the few append
  * workgroups leave free (the decode step's case); otherwise as the two calls, in order, on
- * `stream`.  Plain layouts only, as lrkv_private_queries. */
+ * `stream`.  Layouts as lrkv_private_queries (a key-norm layout's norms are then written by
+ * lrkv_key_norms, as after lrkv_append). */
 int lrkv_append_pq(const lrkv_layout* L, const void* X, int32_t n_rows, int32_t d,
                    const void* W_SK, const void* W_SV, const void* U_K, const void* U_V,
                    const int32_t* row_req, const int32_t* row_pos, const int32_t* page_table,
@@ -283,8 +284,8 @@ int lrkv_append_pq(const lrkv_layout* L, const void* X, int32_t n_rows, int32_t 
  * B_K, batch and q_len) instead of B_K: the same split and merge, the same output bit for
  * bit, without each split workgroup reading B_K and forming p.  Arguments as lrkv_decode,
  * with p in place of B_K; workspace >= lrkv_decode_workspace_bytes(L, batch, q_len,
- * max_seq_len, chunk_tokens).  Plain layouts as lrkv_private_queries; a bf16 call with
- * q_len >= 64 (which lrkv_decode sends to its multi-query kernel) returns
+ * max_seq_len, chunk_tokens).  Layouts as lrkv_private_queries; a bf16 call without key
+ * norms and with q_len >= 64 (which lrkv_decode sends to its multi-query kernel) returns
  * LRKV_ERR_UNSUPPORTED. */
 int lrkv_decode_pq(const lrkv_layout* L, const void* q, const void* p, int32_t batch,
                    int32_t q_len, const void* B_V, const void* pool, const int32_t* page_table,

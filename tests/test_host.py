@@ -204,9 +204,10 @@ def test_append_rejects_bad_arguments_before_launch():
 
 
 def test_private_query_calls_reject_bad_arguments_before_launch():
-    """lrkv_private_queries / lrkv_append_pq / lrkv_decode_pq: sizes follow the layout;
-    layouts without that split path (key norms, grouped blocks) and bf16 decode calls of 64
-    or more query rows per request (those take the multi-query kernel) are refused."""
+    """lrkv_private_queries / lrkv_append_pq / lrkv_decode_pq: sizes follow the layout (a
+    key-norm layout's are its plain twin's); grouped layouts and bf16 decode calls of 64 or
+    more query rows per request without key norms (those take the multi-query kernel) are
+    refused."""
     n1 = F.lrkv_private_queries_bytes(C1, 1, 1)
     assert n1 > 0 and n1 % 16 == 0
     assert F.lrkv_private_queries_bytes(C1, 8, 3) == 24 * n1
@@ -214,7 +215,7 @@ def test_private_query_calls_reject_bad_arguments_before_launch():
     assert F.lrkv_private_queries_bytes(C0, 2, 5) > 0
     C1N = F.lrkv_layout(16, 128, 56, 16, F.LRKV_BF16, 1)
     C3G = F.lrkv_layout(32, 128, 32, 16, F.LRKV_BF16, 0, 2)
-    assert F.lrkv_private_queries_bytes(C1N, 1, 1) == 0
+    assert F.lrkv_private_queries_bytes(C1N, 1, 1) == n1
     assert F.lrkv_private_queries_bytes(C3G, 1, 1) == 0
     assert F.lrkv_private_queries_bytes(C1, 0, 1) == 0
 
@@ -228,7 +229,6 @@ def test_private_query_calls_reject_bad_arguments_before_launch():
     assert pq(p=FAKE + 8) == bad
     assert pq(batch=0) == bad
     assert pq(p_bytes=2 * n1 - 16) == bad
-    assert pq(C1N) == F.LRKV_ERR_UNSUPPORTED
     assert pq(C3G) == F.LRKV_ERR_UNSUPPORTED
 
     def dec(lay=C1, **over):
@@ -243,9 +243,9 @@ def test_private_query_calls_reject_bad_arguments_before_launch():
     assert dec(workspace=FAKE + 16) == bad
     assert dec(workspace_bytes=16) == bad
     assert dec(chunk_tokens=24) == bad
-    assert dec(C1N) == F.LRKV_ERR_UNSUPPORTED
     assert dec(C3G) == F.LRKV_ERR_UNSUPPORTED
     assert dec(q_len=64, max_seq_len=64) == F.LRKV_ERR_UNSUPPORTED
+    assert dec(C1N, q_len=64, max_seq_len=64, workspace_bytes=1) == bad  # accepted up to the size check
 
     def apq(lay=C1, **over):
         args = dict(X=FAKE, n_rows=8, d=2048, W_SK=FAKE, W_SV=FAKE, U_K=FAKE, U_V=FAKE,
@@ -260,7 +260,6 @@ def test_private_query_calls_reject_bad_arguments_before_launch():
     assert apq(q=None) == bad
     assert apq(p_bytes=8 * n1 - 16) == bad
     assert apq(batch=0) == bad
-    assert apq(C1N) == F.LRKV_ERR_UNSUPPORTED
     assert apq(C3G) == F.LRKV_ERR_UNSUPPORTED
 
 

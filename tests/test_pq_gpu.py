@@ -48,6 +48,12 @@ CASES = {
                                       lens=[48, 1, 130] * 8), (0,)),
     "C0 float32, three query rows": (dict(H=4, dh=16, r=4, dtype=O.F32, lens=[40, 7, 0],
                                           q_len=3), (0, 16)),
+    "C1 key norm": (dict(H=16, dh=128, r=56, dtype=O.BF16, lens=[300, 17, 1, 0],
+                         key_norm_eps=1e-6), (0, 64)),
+    "C1 key norm, balanced": (dict(H=16, dh=128, r=56, dtype=O.BF16, lens=[70, 5] * 9,
+                                   key_norm_eps=1e-6), (0,)),
+    "C3 key norm, 70 query rows": (dict(H=32, dh=128, r=32, dtype=O.BF16, lens=[150, 90],
+                                        q_len=70, key_norm_eps=1e-6), (0,)),
 }
 
 
@@ -142,14 +148,17 @@ def append_inputs(seed, L, n_rows, d, lens):
     (32, 128, 32, O.BF16, 8, 1),   # one launch
     (16, 128, 56, O.BF16, 13, 1),  # more than 8 rows: the two calls in turn
     (4, 16, 4, O.F32, 6, 3),       # float32: the two calls in turn
+    (16, 128, 56, -1, 8, 1),       # key-norm pages (dtype -1: bf16 with the N section)
 ])
 def test_append_pq_matches_the_two_calls(H, dh, r, dtype, n_rows, q_len):
     """lrkv_append_pq leaves the pool lrkv_append leaves, byte for byte, and the private
     queries lrkv_private_queries forms, bit for bit."""
-    L = O.Layout(H, dh, r, 16, dtype)
+    key_norm = dtype == -1
+    dtype = O.BF16 if key_norm else dtype
+    L = O.Layout(H, dh, r, 16, dtype, key_norm=key_norm)
     lay = layout_c(L)
     d = 256
-    seed = 960 + n_rows + H
+    seed = 960 + n_rows + H + key_norm
     lens = [70, 33, 150]
     Xd, wdev, table, npg, reqd, posd = append_inputs(seed, L, n_rows, d, lens)
     tabd = to_dev(np.ascontiguousarray(table, np.int32))
