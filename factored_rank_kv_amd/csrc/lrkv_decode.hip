@@ -727,19 +727,24 @@ decode_split_kernel(const SplitArgs a) {
     const int i = tid + k * C::NT;
     if (i < nid) ids_lds[i] = id_r[k];
   }
+  // q (and the private queries, given) go to LDS: before the barrier where the private
+  // queries are formed here, after the first pages are requested where they are given
+  auto store_q_p = [&]() {
 #pragma unroll
-  for (int k = 0; k < QCH; ++k) {
-    const int i = tid + k * C::NT;
-    if (i < S::H * S::DHC) q_lds[(i / S::DHC) * C::Q_STRIDE + i % S::DHC] = q_r[k];
-  }
-  if constexpr (EXTP) {
-#pragma unroll
-    for (int k = 0; k < PCH; ++k) {
+    for (int k = 0; k < QCH; ++k) {
       const int i = tid + k * C::NT;
-      if (i < PBL) p_lds[i] = p_r[k];
+      if (i < S::H * S::DHC) q_lds[(i / S::DHC) * C::Q_STRIDE + i % S::DHC] = q_r[k];
     }
-  }
-  __syncthreads();  // page ids and q (and the private queries, given) in LDS
+    if constexpr (EXTP) {
+#pragma unroll
+      for (int k = 0; k < PCH; ++k) {
+        const int i = tid + k * C::NT;
+        if (i < PBL) p_lds[i] = p_r[k];
+      }
+    }
+  };
+  if constexpr (!EXTP) store_q_p();
+  __syncthreads();  // page ids (and q where the private queries are formed here) in LDS
   // B_K rows go out once the page ids are in (ahead of them they delay the ids: every
   // workgroup reads all of B_K, 58 MB of L2 traffic at C1 sizes) and ahead of every page
   // load, since loads return in issue order
@@ -760,6 +765,7 @@ decode_split_kernel(const SplitArgs a) {
   // pages pg0, pg0+1 go in flight while the private queries are formed
   issue_page<S>(page_ptr(pg0), L, r0);
   if (pg0 + 1 < pg1) issue_page<S>(page_ptr(pg0 + 1), L, r1);
+  if constexpr (EXTP) store_q_p();  // the barrier after the first page's staging covers them
   if constexpr (!EXTP) form_private_queries<S>(bkr, q_lds, pacc, p_lds, tid);
   stage_shared<S>(sk_lds[0], sv_lds[0], svt_lds[0], n_lds[0], tid, r0, nvalid(pg0));
   __syncthreads();
