@@ -527,6 +527,9 @@ def next_rows_bench(torch, F, dev, timed, per_call_us, use_graph, qd, wd, tab, m
     out_rec["grouped_decode"] = hbm_line("grouped decode (32 heads, r=32, 2 groups)", lay_g, qg,
                                          BKg, BVg, Hg)
     out_rec["grouped_decode"]["workload"] = "bf16_b8_t4096_h32_r32_g2"
+    out_rec["grouped_decode_pq"] = hbm_line("grouped decode, private queries given", lay_g, qg,
+                                            BKg, BVg, Hg, pq=True)
+    out_rec["grouped_decode_pq"]["workload"] = "bf16_b8_t4096_h32_r32_g2"
 
     # page copies of a shared-prefix fork (copy on write), 256 pages of the main layout
     lay = F.lrkv_layout(H, dh, r, 16, F.LRKV_BF16)

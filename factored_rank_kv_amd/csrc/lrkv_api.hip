@@ -264,10 +264,11 @@ int scratch_address(hipStream_t stream, void** ws) {
   return LRKV_OK;
 }
 
-// private queries formed once per query row: one-group layouts (with or without the
-// key-norm section, which p does not involve: a key-norm layout's block is its plain twin's)
+// private queries formed once per query row: every compiled layout (the key-norm section
+// does not enter p, so a key-norm layout's block is its plain twin's; a grouped layout's row
+// holds one block per group)
 bool pq_variant(Variant v) {
-  return v == V_C0 || v == V_C1 || v == V_C3 || v == V_C1N || v == V_C3N;
+  return v == V_C0 || v == V_C1 || v == V_C3 || v == V_C1N || v == V_C3N || v == V_C3G2;
 }
 
 size_t pq_row_bytes(Variant v) {
@@ -275,6 +276,7 @@ size_t pq_row_bytes(Variant v) {
     case V_C0: return private_query_row_bytes<ShapeC0>();
     case V_C1: case V_C1N: return private_query_row_bytes<ShapeC1>();
     case V_C3: case V_C3N: return private_query_row_bytes<ShapeC3>();
+    case V_C3G2: return 2 * private_query_row_bytes<ShapeC3G>();  // each group's block
     default: return 0;
   }
 }
@@ -398,6 +400,7 @@ int lrkv_private_queries(const lrkv_layout* L, const void* q, int32_t batch, int
     case V_C3: return hip_status(launch_private_queries<ShapeC3>(q, B_K, rows, p, s));
     case V_C1N: return hip_status(launch_private_queries<ShapeC1>(q, B_K, rows, p, s));
     case V_C3N: return hip_status(launch_private_queries<ShapeC3>(q, B_K, rows, p, s));
+    case V_C3G2: return hip_status(launch_private_queries<ShapeC3G>(q, B_K, rows, p, s, 2));
     default: return LRKV_ERR_UNSUPPORTED;
   }
 }
@@ -442,8 +445,8 @@ int lrkv_decode_pq(const lrkv_layout* L, const void* q, const void* p, int32_t b
   const Variant v = find_variant(L);
   if (!pq_variant(v)) return LRKV_ERR_UNSUPPORTED;
   // the multi-query kernel forms its own private queries: such calls go to lrkv_decode
-  // (a key-norm layout takes every query row through the split kernel, either way)
-  if (L->dtype == LRKV_BF16 && !L->key_norm && q_len >= kPrefillMinRows)
+  // (key-norm and grouped layouts take every query row through the split kernel, either way)
+  if (L->dtype == LRKV_BF16 && !L->key_norm && groups_of(L) == 1 && q_len >= kPrefillMinRows)
     return LRKV_ERR_UNSUPPORTED;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return LRKV_ERR_INVALID_ARG;
   if (workspace_bytes < z.total) return LRKV_ERR_INVALID_ARG;

@@ -112,6 +112,7 @@ struct SplitArgs {
   // lrkv_decode_pq: each query row's private-query block (H * P_STRIDE 16-byte slots, as
   // form_private_queries leaves it in LDS), formed beforehand by private_queries_kernel
   const uint4* p_ext;
+  int p_row_slots;  // uint4 from one row's private-query blocks to the next
 };
 
 // Balanced split (single query row per request): the batch's N pages, request after request,
@@ -712,7 +713,7 @@ decode_split_kernel(const SplitArgs a) {
 #pragma unroll
     for (int k = 0; k < PCH; ++k) {
       const int i = tid + k * C::NT;
-      if (i < PBL) p_r[k] = a.p_ext[row * PBL + i];
+      if (i < PBL) p_r[k] = a.p_ext[row * a.p_row_slots + (size_t)grp * PBL + i];
     }
   }
   // the request length is read first (a scalar load)
@@ -1063,7 +1064,10 @@ template <class S>
 __global__ void __launch_bounds__(256)
 private_queries_kernel(const void* __restrict__ q, const void* __restrict__ BK, int rows,
                        uint4* __restrict__ p_out) {
-  private_query_block<S>(q, BK, rows, p_out, blockIdx.x);
+  // workgroup row blockIdx.y = g: group g of a grouped layout (gridDim.y groups)
+  const int g = (int)blockIdx.y, G = (int)gridDim.y;
+  private_query_block<S>(q, BK, rows, p_out + (size_t)g * PrivCfg<S>::ROW_SLOTS, blockIdx.x,
+                         G * S::H, g * S::H, G * PrivCfg<S>::ROW_SLOTS);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1075,9 +1079,10 @@ size_t private_query_row_bytes() {
 }
 
 template <class S>
-hipError_t launch_private_queries(const void* q, const void* BK, int rows, void* p, hipStream_t stream) {
+hipError_t launch_private_queries(const void* q, const void* BK, int rows, void* p, hipStream_t stream,
+                                  int groups) {
   static_assert(PrivBlockCfg<S>::NT == 256, "workgroup size");
-  hipLaunchKernelGGL((private_queries_kernel<S>), dim3((unsigned)private_query_workgroups<S>(rows)),
+  hipLaunchKernelGGL((private_queries_kernel<S>), dim3((unsigned)private_query_workgroups<S>(rows), groups),
                      dim3(256), 0, stream, q, BK, rows, static_cast<uint4*>(p));
   return hipGetLastError();
 }
@@ -1122,6 +1127,7 @@ hipError_t launch_decode(const DecodeArgs& a) {
   if (a.p_ext) {  // lrkv_decode_pq: private queries formed beforehand (split path only)
     SplitArgs s = split_args<S>(a);
     s.p_ext = static_cast<const uint4*>(a.p_ext);
+    s.p_row_slots = PrivCfg<S>::ROW_SLOTS;
     launch_split<S, true>(a, s);
   } else {
     if constexpr (S::BF && !S::NORM) {  // key-norm layouts: every row through the split
@@ -1149,7 +1155,13 @@ hipError_t launch_decode_grouped(const DecodeArgs& a, int G) {
     s.group_bk_bytes = (long long)Sg::H * Sg::DH * Sg::R * Sg::EB;
     s.group_page_bytes = Sg::PAGE;
     s.group_heads = Sg::H;
-    launch_split<Sg>(a, s, G);
+    if (a.p_ext) {  // lrkv_decode_pq: group g's private-query blocks follow group g - 1's
+      s.p_ext = static_cast<const uint4*>(a.p_ext);
+      s.p_row_slots = G * PrivCfg<Sg>::ROW_SLOTS;
+      launch_split<Sg, true>(a, s, G);
+    } else {
+      launch_split<Sg>(a, s, G);
+    }
   }
   if (a.groups > 0) {
     hipLaunchKernelGGL((merge_expand_kernel<S, true>), dim3(S::H, 1, a.batch), dim3(256), 0,
@@ -1178,9 +1190,11 @@ template hipError_t launch_merge<ShapeC3N>(const DecodeArgs&);
 template size_t private_query_row_bytes<ShapeC0>();
 template size_t private_query_row_bytes<ShapeC1>();
 template size_t private_query_row_bytes<ShapeC3>();
-template hipError_t launch_private_queries<ShapeC0>(const void*, const void*, int, void*, hipStream_t);
-template hipError_t launch_private_queries<ShapeC1>(const void*, const void*, int, void*, hipStream_t);
-template hipError_t launch_private_queries<ShapeC3>(const void*, const void*, int, void*, hipStream_t);
+template hipError_t launch_private_queries<ShapeC0>(const void*, const void*, int, void*, hipStream_t, int);
+template hipError_t launch_private_queries<ShapeC1>(const void*, const void*, int, void*, hipStream_t, int);
+template hipError_t launch_private_queries<ShapeC3>(const void*, const void*, int, void*, hipStream_t, int);
+template hipError_t launch_private_queries<ShapeC3G>(const void*, const void*, int, void*, hipStream_t, int);
+template size_t private_query_row_bytes<ShapeC3G>();
 template hipError_t launch_decode<ShapeC0>(const DecodeArgs&);
 template hipError_t launch_decode<ShapeC1>(const DecodeArgs&);
 template hipError_t launch_decode<ShapeC3>(const DecodeArgs&);

@@ -69,7 +69,8 @@ hipError_t launch_decode(const DecodeArgs& a);
 template <class S>
 size_t private_query_row_bytes();
 template <class S>
-hipError_t launch_private_queries(const void* q, const void* BK, int rows, void* p, hipStream_t stream);
+hipError_t launch_private_queries(const void* q, const void* BK, int rows, void* p, hipStream_t stream,
+                                  int groups = 1);
 // The append of a.n_rows (1..8) bf16 rows and the private queries of `rows` query rows in
 // one launch on a.stream: workgroups of the formation, then the 8-row append's.
 template <class S>

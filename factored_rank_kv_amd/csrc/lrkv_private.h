@@ -60,8 +60,11 @@ __device__ __forceinline__ void store_private_chunk(uint4* __restrict__ dst, con
 // and the spans are added in order g = 0, 1, ... to a zero start: the same float32
 // arithmetic, in the same order, as the split decode's own formation, so either gives the
 // same bits.  The PQ_GROUPS threads of a job sit in one wavefront (PQ_GROUPS divides 64).
-// q: [rows][H][d_h]; BK: [H][d_h][r]; p_out: rows blocks of ROW_SLOTS uint4, every slot
-// written (the pad slots zero).  Every thread of the workgroup must make the call.
+// q: [rows][q_heads][d_h], heads head0 .. head0 + H - 1 taken; BK: [..][d_h][r] from head
+// head0; p_out: a row's block of ROW_SLOTS uint4 every row_slots, every slot written (the
+// pad slots zero).  (A grouped layout forms group g's blocks with head0 = g H and
+// row_slots = G ROW_SLOTS, p_out advanced by g ROW_SLOTS.)  Every thread of the workgroup
+// must make the call.
 template <class S>
 struct PrivBlockCfg {
   using C = PrivCfg<S>;
@@ -83,7 +86,9 @@ __host__ __device__ constexpr long long private_query_workgroups(long long rows)
 template <class S>
 __device__ __forceinline__ void private_query_block(const void* __restrict__ q,
                                                     const void* __restrict__ BK, int rows,
-                                                    uint4* __restrict__ p_out, long long blk) {
+                                                    uint4* __restrict__ p_out, long long blk,
+                                                    int q_heads = S::H, int head0 = 0,
+                                                    int row_slots = PrivCfg<S>::ROW_SLOTS) {
   using C = PrivCfg<S>;
   using W = PrivBlockCfg<S>;
   static_assert(64 % C::PQ_GROUPS == 0 && C::PQ_GROUPS >= 2, "a job's spans in one wavefront");
@@ -98,7 +103,7 @@ __device__ __forceinline__ void private_query_block(const void* __restrict__ q,
   // waited for before the next went out)
   constexpr int BKN = S::DH * S::RC, BKI = (BKN + W::NT - 1) / W::NT;
   constexpr int QN = W::ROWS_WG * S::DHC, QI = (QN + W::NT - 1) / W::NT;
-  const uint4* bkg = reinterpret_cast<const uint4*>(BK) + (size_t)h * S::DH * S::RC;
+  const uint4* bkg = reinterpret_cast<const uint4*>(BK) + (size_t)(head0 + h) * S::DH * S::RC;
   uint4 bkv[BKI], qvv[QI];
 #pragma unroll
   for (int k = 0; k < BKI; ++k) {
@@ -110,7 +115,7 @@ __device__ __forceinline__ void private_query_block(const void* __restrict__ q,
     const int e = min(t + k * W::NT, QN - 1);
     const int rl = e / S::DHC, kk = e - rl * S::DHC;
     const long long row = row0 + rl < rows ? row0 + rl : rows - 1;  // past the end: a valid row
-    qvv[k] = reinterpret_cast<const uint4*>(q)[((size_t)row * S::H + h) * S::DHC + kk];
+    qvv[k] = reinterpret_cast<const uint4*>(q)[((size_t)row * q_heads + head0 + h) * S::DHC + kk];
   }
   // (an empty statement taking each value keeps the loads from sinking into the
   // conditional stores below, one round trip each)
@@ -204,7 +209,7 @@ __device__ __forceinline__ void private_query_block(const void* __restrict__ q,
   }
   const long long row = row0 + t / W::JOB_THREADS;
   if (t >= W::ROWS_WG * W::JOB_THREADS || row >= rows) return;
-  uint4* dst = p_out + (size_t)row * C::ROW_SLOTS + (size_t)h * C::P_STRIDE;
+  uint4* dst = p_out + (size_t)row * row_slots + (size_t)h * C::P_STRIDE;
   if (g == 0) store_private_chunk<S>(dst + c * C::P_PER_CHUNK, p);
   if (c == 0 && g >= 1 && g <= C::PAD)
     dst[S::RC * C::P_PER_CHUNK + g - 1] = make_uint4(0u, 0u, 0u, 0u);

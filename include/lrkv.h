@@ -254,8 +254,9 @@ size_t lrkv_decode_rope_workspace_bytes(const lrkv_layout* L, int32_t batch, int
  *              head, float32 sums over d_h rounded to bfloat16 hi + lo pairs per 8-rank
  *              chunk for a bf16 cache, float32 for a float32 cache, with zero padding): it is
  *              only read by lrkv_decode_pq with the same layout, batch and q_len.
- * One-group layouts (groups <= 1, with or without key norms): (4, 16, 4) float32,
- * (16, 128, 56) and (32, 128, 32) bf16; grouped layouts return LRKV_ERR_UNSUPPORTED.  batch * q_len <= 4194304 rows
+ * Every compiled layout: (4, 16, 4) float32; (16, 128, 56) and (32, 128, 32) bf16, with or
+ * without key norms (which p does not involve); (32, 128, 32) bf16 in 2 groups (a row then
+ * holds one block per group of 16 heads).  batch * q_len <= 4194304 rows
  * (LRKV_ERR_INVALID_ARG beyond).  Same arithmetic, in the same order, as lrkv_decode's own
  * formation, so lrkv_decode_pq's output equals lrkv_decode's bit for bit. */
 int lrkv_private_queries(const lrkv_layout* L, const void* q, int32_t batch, int32_t q_len,
@@ -284,9 +285,9 @@ int lrkv_append_pq(const lrkv_layout* L, const void* X, int32_t n_rows, int32_t 
  * B_K, batch and q_len) instead of B_K: the same split and merge, the same output bit for
  * bit, without each split workgroup reading B_K and forming p.  Arguments as lrkv_decode,
  * with p in place of B_K; workspace >= lrkv_decode_workspace_bytes(L, batch, q_len,
- * max_seq_len, chunk_tokens).  Layouts as lrkv_private_queries; a bf16 call without key
- * norms and with q_len >= 64 (which lrkv_decode sends to its multi-query kernel) returns
- * LRKV_ERR_UNSUPPORTED. */
+ * max_seq_len, chunk_tokens).  Layouts as lrkv_private_queries; a call of q_len >= 64 over
+ * a one-group bf16 layout without key norms (which lrkv_decode sends to its multi-query
+ * kernel) returns LRKV_ERR_UNSUPPORTED. */
 int lrkv_decode_pq(const lrkv_layout* L, const void* q, const void* p, int32_t batch,
                    int32_t q_len, const void* B_V, const void* pool, const int32_t* page_table,
                    int32_t max_pages_per_req, const int32_t* seq_lens, int32_t max_seq_len,

@@ -205,9 +205,9 @@ def test_append_rejects_bad_arguments_before_launch():
 
 def test_private_query_calls_reject_bad_arguments_before_launch():
     """lrkv_private_queries / lrkv_append_pq / lrkv_decode_pq: sizes follow the layout (a
-    key-norm layout's are its plain twin's); grouped layouts and bf16 decode calls of 64 or
-    more query rows per request without key norms (those take the multi-query kernel) are
-    refused."""
+    key-norm layout's are its plain twin's, a grouped layout's one block per group); decode
+    calls of 64 or more query rows per request over a one-group bf16 layout without key norms
+    (those take the multi-query kernel) are refused."""
     n1 = F.lrkv_private_queries_bytes(C1, 1, 1)
     assert n1 > 0 and n1 % 16 == 0
     assert F.lrkv_private_queries_bytes(C1, 8, 3) == 24 * n1
@@ -216,7 +216,8 @@ def test_private_query_calls_reject_bad_arguments_before_launch():
     C1N = F.lrkv_layout(16, 128, 56, 16, F.LRKV_BF16, 1)
     C3G = F.lrkv_layout(32, 128, 32, 16, F.LRKV_BF16, 0, 2)
     assert F.lrkv_private_queries_bytes(C1N, 1, 1) == n1
-    assert F.lrkv_private_queries_bytes(C3G, 1, 1) == 0
+    n3 = F.lrkv_private_queries_bytes(C3, 1, 1)
+    assert F.lrkv_private_queries_bytes(C3G, 1, 1) == n3  # 2 blocks of 16 heads
     assert F.lrkv_private_queries_bytes(C1, 0, 1) == 0
 
     def pq(lay=C1, **over):
@@ -229,7 +230,7 @@ def test_private_query_calls_reject_bad_arguments_before_launch():
     assert pq(p=FAKE + 8) == bad
     assert pq(batch=0) == bad
     assert pq(p_bytes=2 * n1 - 16) == bad
-    assert pq(C3G) == F.LRKV_ERR_UNSUPPORTED
+    assert pq(C3G, p_bytes=2 * n3 - 16) == bad
 
     def dec(lay=C1, **over):
         args = dict(q=FAKE, p=FAKE, batch=2, q_len=1, B_V=FAKE, pool=FAKE, page_table=FAKE,
@@ -243,7 +244,7 @@ def test_private_query_calls_reject_bad_arguments_before_launch():
     assert dec(workspace=FAKE + 16) == bad
     assert dec(workspace_bytes=16) == bad
     assert dec(chunk_tokens=24) == bad
-    assert dec(C3G) == F.LRKV_ERR_UNSUPPORTED
+    assert dec(C3G, q_len=64, max_seq_len=64, workspace_bytes=1) == bad  # accepted up to the size check
     assert dec(q_len=64, max_seq_len=64) == F.LRKV_ERR_UNSUPPORTED
     assert dec(C1N, q_len=64, max_seq_len=64, workspace_bytes=1) == bad  # accepted up to the size check
 
@@ -260,7 +261,7 @@ def test_private_query_calls_reject_bad_arguments_before_launch():
     assert apq(q=None) == bad
     assert apq(p_bytes=8 * n1 - 16) == bad
     assert apq(batch=0) == bad
-    assert apq(C3G) == F.LRKV_ERR_UNSUPPORTED
+    assert apq(C3G, p_bytes=8 * n3 - 16) == bad
 
 
 def check_status(lay=C1, **over):

@@ -20,6 +20,11 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
+def grouped_case(seed, lens, q_len=1):
+    from test_grouped_gpu import grouped_case as make
+    return make(seed, lens, q_len=q_len)
+
+
 def run_pq(case, chunk_tokens=0, p_fill=0xFF):
     d = case.dev
     lay = layout_c(case.L)
@@ -75,6 +80,22 @@ def test_decode_pq_matches_decode(name):
         err = max_rel_err(g64[live], ref[live])
         log(f"{name}, chunk {chunk}: bit-identical to lrkv_decode, max rel err {err:.3e}")
         assert err <= tolerance(case.L.dtype)
+
+
+@pytest.mark.parametrize("lens,q_len,chunks", [
+    ([1, 17, 100, 16, 33, 250, 0], 1, (0, 64)),        # chunked
+    ([48] * 10 + [300, 0, 5, 17, 1000, 64], 1, (0,)),  # balanced
+    ([150, 70], 70, (0,)),                             # 70 query rows through the split
+])
+def test_decode_pq_grouped(lens, q_len, chunks):
+    """Grouped layout (32 heads, r=32, 2 blocks of 16): p formed per group, the output equal
+    to lrkv_decode's bit for bit."""
+    case = grouped_case(990 + len(lens), lens, q_len)
+    for chunk in chunks:
+        want = case.run(chunk_tokens=chunk)
+        got = run_pq(case, chunk)
+        assert torch.equal(got, want), f"grouped, chunk {chunk}: differs from lrkv_decode"
+    log(f"grouped decode_pq ({len(lens)} requests, q_len {q_len}): bit-identical to lrkv_decode")
 
 
 def test_private_queries_written_whole():
