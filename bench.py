@@ -662,13 +662,20 @@ def other_decodes(torch, F, synth, dev):
         msl = max(lens)
         alg = 2 * 2 * sum(lens) * (dh + H * r)
         o = torch.empty(B, 1, H, dh, dtype=torch.int16, device=dev)
-        for ch in chunks:
+        pqb = F.lrkv_private_queries_bytes(lay, B, 1)
+        pbuf = torch.empty(pqb, dtype=torch.uint8, device=dev)
+        F.lrkv_private_queries(lay, q, B, 1, BK.view(torch.int16), pbuf, pqb)
+        for ch, pq in [(c, False) for c in chunks] + [(0, True)]:
             n = F.lrkv_decode_workspace_bytes(lay, B, 1, msl, ch)
             ws = torch.empty(n, dtype=torch.uint8, device=dev)
 
             def call():
-                F.lrkv_decode(lay, q, B, 1, BK.view(torch.int16), BV.view(torch.int16), pool, tab,
-                              table.shape[1], lt, msl, ch, o, ws, n)
+                if pq:  # the private queries formed once beforehand (lrkv_decode_pq)
+                    F.lrkv_decode_pq(lay, q, pbuf, B, 1, BV.view(torch.int16), pool, tab,
+                                     table.shape[1], lt, msl, ch, o, ws, n)
+                else:
+                    F.lrkv_decode(lay, q, B, 1, BK.view(torch.int16), BV.view(torch.int16), pool,
+                                  tab, table.shape[1], lt, msl, ch, o, ws, n)
 
             for _ in range(3):
                 call()
@@ -681,10 +688,13 @@ def other_decodes(torch, F, synth, dev):
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) / 20 * 1e3
             gbs = alg / us / 1e3
-            key = work.name + ("" if ch == 0 else f"_chunk{ch}")
+            key = work.name + ("" if ch == 0 else f"_chunk{ch}") + ("_pq" if pq else "")
             out[key] = {"call_us": round(us, 2), "algorithmic_bytes": alg,
                         "achieved_gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
                         "chunk_tokens": ch}
+            if pq:
+                out[key]["private_queries"] = "formed once beforehand by lrkv_private_queries " \
+                    "(in a decode step, beside the append), outside the timed calls"
             log(f"{key}: {us:.1f} us per call, {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f} %)")
         del pool
         torch.cuda.empty_cache()
