@@ -187,7 +187,7 @@ def main():
                          wd["B_K"], pbuf, pq_bytes)
 
     def decode_pq(k):
-        F.lrkv_decode_pq(lay, qd, pbuf, B, 1, wd["B_V"], pools[k % len(pools)], tab,
+        F.lrkv_decode_pq(lay, qd, pbuf, pq_bytes, B, 1, wd["B_V"], pools[k % len(pools)], tab,
                          table.shape[1], lens, T, args.chunk, out, ws, ws_bytes)
 
     def step(k):
@@ -458,7 +458,7 @@ def next_rows_bench(torch, F, dev, timed, per_call_us, use_graph, qd, wd, tab, m
 
         def call(k):
             if pq:
-                F.lrkv_decode_pq(lay, q, pbuf, B, 1, BV, pools[k % len(pools)], tab, max_pages,
+                F.lrkv_decode_pq(lay, q, pbuf, pqb, B, 1, BV, pools[k % len(pools)], tab, max_pages,
                                  lens, T, 0, o, ws, ws_bytes)
             else:
                 F.lrkv_decode(lay, q, B, 1, BK, BV, pools[k % len(pools)], tab, max_pages, lens,
@@ -671,7 +671,7 @@ def other_decodes(torch, F, synth, dev):
 
             def call():
                 if pq:  # the private queries formed once beforehand (lrkv_decode_pq)
-                    F.lrkv_decode_pq(lay, q, pbuf, B, 1, BV.view(torch.int16), pool, tab,
+                    F.lrkv_decode_pq(lay, q, pbuf, pqb, B, 1, BV.view(torch.int16), pool, tab,
                                      table.shape[1], lt, msl, ch, o, ws, n)
                 else:
                     F.lrkv_decode(lay, q, B, 1, BK.view(torch.int16), BV.view(torch.int16), pool,

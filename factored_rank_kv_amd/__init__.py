@@ -110,7 +110,7 @@ def _load():
     lib.lrkv_private_queries_bytes.restype = SZ
     lib.lrkv_private_queries.argtypes = [LP, P, I32, I32, P, P, SZ, P]
     lib.lrkv_private_queries.restype = ctypes.c_int
-    lib.lrkv_decode_pq.argtypes = [LP, P, P, I32, I32, P, P, P, I32, P, I32, I32, P, P, SZ, P]
+    lib.lrkv_decode_pq.argtypes = [LP, P, P, SZ, I32, I32, P, P, P, I32, P, I32, I32, P, P, SZ, P]
     lib.lrkv_decode_pq.restype = ctypes.c_int
     lib.lrkv_append_pq.argtypes = [LP, P, I32, I32, P, P, P, P, P, P, P, I32, P, I64, P, I32, I32,
                                    P, P, SZ, P]
@@ -329,10 +329,11 @@ def lrkv_append_pq(layout, X, n_rows, d, W_SK, W_SV, U_K, U_V, row_req, row_pos,
     return st
 
 
-def lrkv_decode_pq(layout, q, p, batch, q_len, B_V, pool, page_table, max_pages_per_req,
-                   seq_lens, max_seq_len, chunk_tokens, out, workspace, workspace_bytes,
-                   stream=None, check=True) -> int:
-    st = _load().lrkv_decode_pq(_layout(layout), _ptr(q), _ptr(p), batch, q_len, _ptr(B_V),
+def lrkv_decode_pq(layout, q, p, p_bytes, batch, q_len, B_V, pool, page_table,
+                   max_pages_per_req, seq_lens, max_seq_len, chunk_tokens, out, workspace,
+                   workspace_bytes, stream=None, check=True) -> int:
+    st = _load().lrkv_decode_pq(_layout(layout), _ptr(q), _ptr(p), p_bytes, batch, q_len,
+                                _ptr(B_V),
                                 _ptr(pool), _ptr(page_table), max_pages_per_req, _ptr(seq_lens),
                                 max_seq_len, chunk_tokens, _ptr(out), _ptr(workspace),
                                 workspace_bytes, _stream(stream))

@@ -432,8 +432,8 @@ int lrkv_append_pq(const lrkv_layout* L, const void* X, int32_t n_rows, int32_t 
   return lrkv_private_queries(L, q, batch, q_len, B_K, p, p_bytes, stream);
 }
 
-int lrkv_decode_pq(const lrkv_layout* L, const void* q, const void* p, int32_t batch,
-                   int32_t q_len, const void* B_V, const void* pool, const int32_t* page_table,
+int lrkv_decode_pq(const lrkv_layout* L, const void* q, const void* p, size_t p_bytes,
+                   int32_t batch, int32_t q_len, const void* B_V, const void* pool, const int32_t* page_table,
                    int32_t max_pages_per_req, const int32_t* seq_lens, int32_t max_seq_len,
                    int32_t chunk_tokens, void* out, void* workspace, size_t workspace_bytes,
                    void* stream) {
@@ -444,6 +444,8 @@ int lrkv_decode_pq(const lrkv_layout* L, const void* q, const void* p, int32_t b
   if (st != LRKV_OK) return st;
   const Variant v = find_variant(L);
   if (!pq_variant(v)) return LRKV_ERR_UNSUPPORTED;
+  if ((long long)batch * q_len > kMaxPrivateQueryRows) return LRKV_ERR_INVALID_ARG;
+  if (p_bytes < (size_t)batch * (size_t)q_len * pq_row_bytes(v)) return LRKV_ERR_INVALID_ARG;
   // the multi-query kernel forms its own private queries: such calls go to lrkv_decode
   // (key-norm and grouped layouts take every query row through the split kernel, either way)
   if (L->dtype == LRKV_BF16 && !L->key_norm && groups_of(L) == 1 && q_len >= kPrefillMinRows)

@@ -284,12 +284,14 @@ int lrkv_append_pq(const lrkv_layout* L, const void* X, int32_t n_rows, int32_t 
 /* lrkv_decode with the private queries given (p from lrkv_private_queries for these q,
  * B_K, batch and q_len) instead of B_K: the same split and merge, the same output bit for
  * bit, without each split workgroup reading B_K and forming p.  Arguments as lrkv_decode,
- * with p in place of B_K; workspace >= lrkv_decode_workspace_bytes(L, batch, q_len,
- * max_seq_len, chunk_tokens).  Layouts as lrkv_private_queries; a call of q_len >= 64 over
+ * with p and its size p_bytes in place of B_K: p_bytes <
+ * lrkv_private_queries_bytes(L, batch, q_len), like a workspace smaller than
+ * lrkv_decode_workspace_bytes(L, batch, q_len, max_seq_len, chunk_tokens), returns
+ * LRKV_ERR_INVALID_ARG before anything is launched.  Layouts as lrkv_private_queries; a call of q_len >= 64 over
  * a one-group bf16 layout without key norms (which lrkv_decode sends to its multi-query
  * kernel) returns LRKV_ERR_UNSUPPORTED. */
-int lrkv_decode_pq(const lrkv_layout* L, const void* q, const void* p, int32_t batch,
-                   int32_t q_len, const void* B_V, const void* pool, const int32_t* page_table,
+int lrkv_decode_pq(const lrkv_layout* L, const void* q, const void* p, size_t p_bytes,
+                   int32_t batch, int32_t q_len, const void* B_V, const void* pool, const int32_t* page_table,
                    int32_t max_pages_per_req, const int32_t* seq_lens, int32_t max_seq_len,
                    int32_t chunk_tokens, void* out, void* workspace, size_t workspace_bytes,
                    void* stream);

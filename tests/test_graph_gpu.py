@@ -188,7 +188,7 @@ def test_append_pq_decode_pq_step_replays():
         F.lrkv_append_pq(lay, Xd, B, d, wdev["W_SK"], wdev["W_SV"], wdev["U_K"], wdev["U_V"], reqd,
                          posd, dv["table"], case.table.shape[1], pool, case.num_pages, dv["q"], B, 1,
                          dv["BK"], p, pb)
-        F.lrkv_decode_pq(lay, dv["q"], p, B, 1, dv["BV"], pool, dv["table"], case.table.shape[1],
+        F.lrkv_decode_pq(lay, dv["q"], p, pb, B, 1, dv["BV"], pool, dv["table"], case.table.shape[1],
                          dv["lens"], msl, 0, out, ws, nb)
 
     call()

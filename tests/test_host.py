@@ -233,9 +233,9 @@ def test_private_query_calls_reject_bad_arguments_before_launch():
     assert pq(C3G, p_bytes=2 * n3 - 16) == bad
 
     def dec(lay=C1, **over):
-        args = dict(q=FAKE, p=FAKE, batch=2, q_len=1, B_V=FAKE, pool=FAKE, page_table=FAKE,
-                    max_pages_per_req=4, seq_lens=FAKE, max_seq_len=64, chunk_tokens=0,
-                    out=FAKE, workspace=FAKE, workspace_bytes=1 << 30)
+        args = dict(q=FAKE, p=FAKE, p_bytes=1 << 30, batch=2, q_len=1, B_V=FAKE, pool=FAKE,
+                    page_table=FAKE, max_pages_per_req=4, seq_lens=FAKE, max_seq_len=64,
+                    chunk_tokens=0, out=FAKE, workspace=FAKE, workspace_bytes=1 << 30)
         args.update(over)
         return F.lrkv_decode_pq(lay, check=False, stream=0, **args)
 
@@ -243,6 +243,8 @@ def test_private_query_calls_reject_bad_arguments_before_launch():
     assert dec(p=FAKE + 4) == bad
     assert dec(workspace=FAKE + 16) == bad
     assert dec(workspace_bytes=16) == bad
+    assert dec(p_bytes=2 * n1 - 16) == bad  # smaller than lrkv_private_queries_bytes
+    assert dec(C3G, p_bytes=2 * n3 - 16) == bad
     assert dec(chunk_tokens=24) == bad
     assert dec(C3G, q_len=64, max_seq_len=64, workspace_bytes=1) == bad  # accepted up to the size check
     assert dec(q_len=64, max_seq_len=64) == F.LRKV_ERR_UNSUPPORTED

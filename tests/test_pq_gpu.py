@@ -36,7 +36,7 @@ def run_pq(case, chunk_tokens=0, p_fill=0xFF):
     nb = F.lrkv_decode_workspace_bytes(lay, case.B, case.q_len, msl, chunk_tokens)
     ws = fresh_workspace(nb, 0xFF)
     out = torch.empty(case.q_codes.shape, dtype=d["q"].dtype, device=DEV)
-    F.lrkv_decode_pq(lay, d["q"], p, case.B, case.q_len, d["BV"], d["pool"], d["table"],
+    F.lrkv_decode_pq(lay, d["q"], p, pb, case.B, case.q_len, d["BV"], d["pool"], d["table"],
                      case.table.shape[1], d["lens"], msl, chunk_tokens, out, ws, nb)
     torch.cuda.synchronize()
     return out
@@ -136,7 +136,7 @@ def test_decode_pq_reuses_private_queries():
             ws = fresh_workspace(nb, 0xFF)
             out = torch.empty(case.q_codes.shape, dtype=d["q"].dtype, device=DEV)
             if use_p:
-                F.lrkv_decode_pq(lay, d["q"], p, case.B, 1, d["BV"], d["pool"], d["table"],
+                F.lrkv_decode_pq(lay, d["q"], p, pb, case.B, 1, d["BV"], d["pool"], d["table"],
                                  case.table.shape[1], lens_dev, msl, 0, out, ws, nb)
             else:
                 F.lrkv_decode(lay, d["q"], case.B, 1, d["BK"], d["BV"], d["pool"], d["table"],
@@ -241,7 +241,7 @@ def test_append_pq_step_then_decode_pq():
         if fused:
             p = fresh_workspace(pb, 0xFF)
             F.lrkv_append_pq(lay, *args, dv["q"], B, 1, dv["BK"], p, pb)
-            F.lrkv_decode_pq(lay, dv["q"], p, B, 1, dv["BV"], pool, dv["table"],
+            F.lrkv_decode_pq(lay, dv["q"], p, pb, B, 1, dv["BV"], pool, dv["table"],
                              case.table.shape[1], dv["lens"], msl, 0, out, ws, nb)
         else:
             F.lrkv_append(lay, *args)
