@@ -294,18 +294,20 @@ append_few_rows_f32_kernel(AppendArgs a) {
 
 // ---------------------------------------------------------------------------------------
 // Many rows (prefill, cache build), bf16: the product on MFMA.  Workgroup = 256 rows x 256
-// product columns, 512 threads = 2 x 4 wavefronts of 128 x 64, K in steps of 32 through a
-// ring of three LDS stages that direct global->LDS loads fill two steps ahead of the
-// products (no register staging); v_mfma_f32_16x16x32_bf16 with float32 accumulation.  A
+// product columns, 512 threads = 2 x 4 wavefronts of 128 x 64, K in stages of 64 through
+// two LDS buffers that direct global->LDS loads fill one stage ahead of the products (no
+// register staging); v_mfma_f32_16x16x32_bf16 with float32 accumulation.  A
 // 256 x 256 tile reads (256 + 256) x d operands for 256^2 outputs, a third less L2 -> LDS
 // traffic per product than 256 x 128.  The 256 columns may span weight matrices (W_SK and
 // W_SV, U_K and U_V): each 16-column group of the staging loads is one matrix's rows, with a
 // base of its own.  X tiles ([row][k]) and weight tiles ([column][k], the weights being
 // output-major) are stored alike, and each lane reads the 8 consecutive k of one row (A
 // operand) or of one column (B operand) as one 16-byte LDS read; a wavefront's A and B
-// reads serve 8 x 4 products.  The operand reads run one step ahead in registers: halfway
-// through a step's products the next stage is waited for (one barrier per step) and its
-// operands are read while the second half of the products runs.  The result is rounded to
+// reads serve 8 x 4 products.  The operand reads run 32 k ahead in registers: a stage's
+// second 32 k are read during its first 32 k's products, then the next stage is waited for
+// (one barrier per 64 k, half as many as with stages of 32: 245.5 -> 228.7 us for 32768
+// rows, the plain hipBLASLt product 228.7 us in the same process) and its first operands
+// are read during the second 32 k's products.  The result is rounded to
 // bf16 into LDS, 128 rows at a time, then written to the pages as 16-byte chunks (16
 // consecutive rows of one page fill 256 contiguous bytes of a section).  Blocks are
 // numbered so that the column tiles of one row block run on one XCD (blocks go to the 8
@@ -313,20 +315,19 @@ append_few_rows_f32_kernel(AppendArgs a) {
 // ---------------------------------------------------------------------------------------
 template <class S>
 struct GemmCfg {
-  static constexpr int BM = 256, BN = 256, BK = 32, NT = 512;
+  static constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
   static constexpr int NWN = 4;                  // wavefronts across the columns
   static constexpr int WM = BM / 2, WN = BN / NWN;  // rows and columns per wavefront
   static constexpr int IT = WM / 16, JT = WN / 16;  // 16 x 16 product tiles per wavefront
-  // bytes per X row / weight column in LDS: the 64 bytes of k, the four 16-byte chunks of
-  // row r at positions c ^ ((r ^ r >> 1) & 3).  Measured with the LDS bank-conflict counter
-  // on this part: both the operand reads (16 consecutive rows, one chunk per 16 lanes) and
-  // the staging writes (4 rows x 4 chunks per 16 lanes) run without conflicts, where rows
-  // padded to 96 bytes left the writes at twice the cycles.
+  // bytes per X row / weight column in LDS: the 128 bytes of a stage's k, the eight 16-byte
+  // chunks of row r at positions c ^ (r & 7), so that the 16 rows an operand read touches
+  // (one chunk each) spread over all chunk positions, 8 rows apart; the staging writes are
+  // whole 1 KiB blocks.
   static constexpr int XS = BK * 2;
   static constexpr int X_BYTES = BM * XS;
   static constexpr int W_BYTES = BN * XS;
   static constexpr int STAGE = X_BYTES + W_BYTES;
-  static constexpr int NSTAGE = 3;
+  static constexpr int NSTAGE = 2;
   static constexpr int OUT_ROWS = 128;           // result rows staged in LDS at a time
   static constexpr int OS = BN * 2 + 16;         // bytes per output row in LDS (padded)
   static constexpr int N = 2 * S::DH + 2 * S::H * S::R;  // product columns
@@ -334,9 +335,9 @@ struct GemmCfg {
   static_assert(S::BF && N % BN == 0, "256-column tiles");
   static_assert(S::DH % 16 == 0 && (S::H * S::R) % 16 == 0,
                 "16-column staging groups never straddle two weight matrices");
-  // staging: 1 KiB (16 rows of 64 bytes) per wavefront load; 2 of X and 2 of weights
+  // staging: 1 KiB (8 rows of 128 bytes) per wavefront load; 4 of X and 4 of weights
   // per wavefront and stage
-  static_assert(BK == 32 && NT == 512 && X_BYTES == 2 * 8 * 1024 && W_BYTES == 2 * 8 * 1024,
+  static_assert(BK == 64 && NT == 512 && X_BYTES == 4 * 8 * 1024 && W_BYTES == 4 * 8 * 1024,
                 "staging geometry");
   static constexpr int SMEM = NSTAGE * STAGE;    // the output tile reuses the stage buffers
   static_assert(OUT_ROWS * OS <= SMEM && BM % OUT_ROWS == 0 && OUT_ROWS == WM, "output staging");
@@ -344,31 +345,39 @@ struct GemmCfg {
 
 // One GEMM stage of direct global->LDS loads (global_load_lds_dwordx4, 16 bytes per lane:
 // lane i of the wavefront writes LDS bytes [m0 + 16 i, m0 + 16 i + 16), M0 wave-uniform):
-// two 1 KiB loads of X rows (global xb + xoff[m]) to x_lds and x_lds + 8 KiB, then two of
-// weight rows (global wb0 + woff, wb1 + woff: two 16-column groups, each of one weight
-// matrix) to w_lds and w_lds + 8 KiB.  The global bases are wave-uniform (scalar
-// registers), the per-lane parts 32-bit offsets; M0 is set, stepped by 8 KiB, and restored
-// at the end.  Written as inline assembly, so the compiler's wait counters do not see
-// these loads (it would otherwise wait for all of them before any LDS read); the caller
-// waits with s_waitcnt vmcnt and a barrier before reading the bytes.
+// four 1 KiB loads of X rows (global xb + xoff[2 m + h]) to x_lds + 16 KiB m + 1 KiB h,
+// then four of weight rows (global wb0 + woff[h], wb1 + woff[h]: two 16-column groups, each
+// of one weight matrix) to w_lds + 1 KiB h and w_lds + 16 KiB + 1 KiB h.  The global bases
+// are wave-uniform (scalar registers), the per-lane parts 32-bit offsets; M0 is set,
+// stepped, and restored at the end.  Written as inline assembly, so the compiler's wait
+// counters do not see these loads (it would otherwise wait for all of them before any LDS
+// read); the caller waits with s_waitcnt vmcnt and a barrier before reading the bytes.
 __device__ __forceinline__ void lds_dma_stage(const void* xb, const void* wb0, const void* wb1,
-                                              const uint32_t (&xoff)[2], uint32_t woff,
+                                              const uint32_t (&xoff)[4], const uint32_t (&woff)[2],
                                               uint32_t x_lds, uint32_t w_lds) {
   uint32_t keep;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %4\n\t"
-      "global_load_lds_dwordx4 %1, %6\n\t"
-      "s_add_u32 m0, m0, 0x2000\n\t"
-      "global_load_lds_dwordx4 %2, %6\n\t"
       "s_mov_b32 m0, %5\n\t"
+      "global_load_lds_dwordx4 %1, %7\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %2, %7\n\t"
+      "s_add_u32 m0, m0, 0x3c00\n\t"
       "global_load_lds_dwordx4 %3, %7\n\t"
-      "s_add_u32 m0, m0, 0x2000\n\t"
-      "global_load_lds_dwordx4 %3, %8\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %4, %7\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "global_load_lds_dwordx4 %8, %9\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %10, %9\n\t"
+      "s_add_u32 m0, m0, 0x3c00\n\t"
+      "global_load_lds_dwordx4 %8, %11\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "global_load_lds_dwordx4 %10, %11\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(keep)
-      : "v"(xoff[0]), "v"(xoff[1]), "v"(woff), "s"(x_lds), "s"(w_lds), "s"(xb), "s"(wb0),
-        "s"(wb1)
+      : "v"(xoff[0]), "v"(xoff[1]), "v"(xoff[2]), "v"(xoff[3]), "s"(x_lds), "s"(w_lds), "s"(xb),
+        "v"(woff[0]), "s"(wb0), "v"(woff[1]), "s"(wb1)
       : "memory", "scc");
 }
 
@@ -397,29 +406,33 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
   const int li = lane & 15, lg = lane >> 4;
 
   // global -> LDS staging by direct loads (global_load_lds_dwordx4): one wavefront
-  // instruction fills 1 KiB = 16 rows x 64 bytes; lane i writes bytes [16 i, 16 i + 16) of
-  // it, i.e. row i/4, chunk position i%4, so it loads k-chunk (i%4) ^ f(i/4) of that row.
-  // Wavefront w stages X rows and weight columns 16 (w + 8 m) + i/4, m = 0, 1.
+  // instruction fills 1 KiB = 8 rows x 128 bytes; lane i writes bytes [16 i, 16 i + 16) of
+  // it, i.e. row i/8, chunk position i%8, so it loads k-chunk (i%8) ^ (i/8) of that row.
+  // Wavefront w stages X rows and weight columns 16 (w + 8 m) + 8 h + i/8, m, h = 0, 1.
   const uint8_t* X = static_cast<const uint8_t*>(a.X);
   const size_t xrow = (size_t)a.d * 2;  // bytes per X row and per weight row
-  const int rr = lane >> 2;
-  const int kc = (lane & 3) ^ ((rr ^ (rr >> 1)) & 3);
+  const int r8 = lane >> 3;          // row within a 1 KiB block of 8 rows of 128 bytes
+  const int kc = (lane & 7) ^ r8;     // position lane & 7 of the row holds k-chunk kc
   // per-lane 32-bit offsets from the X and weight bases (loop invariant); rows past the
   // end read row n-1
-  uint32_t xoff[2];
+  uint32_t xoff[4], woff[2];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int r = min(row0 + 16 * (wave + 8 * m) + rr, a.n_rows - 1);
-    xoff[m] = (uint32_t)((size_t)r * xrow + 16 * kc);
-  }
-  const uint32_t woff = (uint32_t)((size_t)rr * xrow + 16 * kc);
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = min(row0 + 16 * (wave + 8 * m) + 8 * h + r8, a.n_rows - 1);
+      xoff[2 * m + h] = (uint32_t)((size_t)r * xrow + 16 * kc);
+    }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) woff[h] = (uint32_t)((size_t)(8 * h + r8) * xrow + 16 * kc);
   const uint8_t* W0 = weight_row<S>(a, col0 + 16 * wave);
   const uint8_t* W1 = weight_row<S>(a, col0 + 16 * (wave + 8));
-  const int lsw = 16 * (lg ^ ((li ^ (li >> 1)) & 3));  // operand reads: rows 16 x + li
+  const int lsw0 = 16 * (lg ^ (li & 7));  // operand reads of rows 16 x + li, k-chunks 0..3
+  const int lsw1 = lsw0 ^ 64;              // k-chunks 4..7
   typedef __attribute__((address_space(3))) uint8_t* lds_p;
   const uint32_t smem_base = (uint32_t)(size_t)(lds_p)smem;
   auto issue = [&](int ks, int buf) {
-    const uint32_t st = smem_base + buf * G::STAGE + 1024 * wave;
+    const uint32_t st = smem_base + buf * G::STAGE + 2048 * wave;
     const size_t ko = (size_t)ks * G::BK * 2;
     lds_dma_stage(X + ko, W0 + ko, W1 + ko, xoff, woff, st, st + G::X_BYTES);
   };
@@ -444,7 +457,7 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
     row_page[i] = page;
     row_slot[i] = slot;
   }
-  if (nk > 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  if (nk > 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   // operand fragments of one stage: B (JT columns blocks) and A (IT row blocks)
@@ -452,8 +465,9 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
     bf16x8_v b[G::JT];
     bf16x8_v a[G::IT];
   };
-  auto load_frag = [&](int buf, Frag& f) {
+  auto load_frag = [&](int buf, int sub, Frag& f) {
     const uint8_t* st = smem + buf * G::STAGE;
+    const int lsw = sub ? lsw1 : lsw0;
 #pragma unroll
     for (int j = 0; j < G::JT; ++j)
       f.b[j] = *reinterpret_cast<const bf16x8_v*>(st + G::X_BYTES +
@@ -462,52 +476,40 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
     for (int i = 0; i < G::IT; ++i)
       f.a[i] = *reinterpret_cast<const bf16x8_v*>(st + (G::WM * wm + 16 * i + li) * G::XS + lsw);
   };
-  // step ks: stage ks's fragments are in fc; the first half of the products runs, then the
-  // stage ks + 1 bytes are waited for (own loads, then the barrier for every wavefront's),
-  // and its fragments are read into fn during the second half.  The barrier also orders
-  // every wavefront's reads of stage ks - 1 (done before this step) before the loads of
-  // step ks + 1 refill that stage.
-  auto step = [&](int ks, int buf, Frag& fc, Frag& fn) {
-    const int nb = buf == 0 ? 2 : buf - 1;  // (ks + 2) % 3
-    if (ks + 2 < nk) issue(ks + 2, nb);
+  // step ks (stage ks in buffer ks & 1, its first 32 k in fc): the first 32 k's products
+  // with the reads of the second 32 k (same stage, no barrier) between them; then the next
+  // stage's bytes are waited for (own loads, then every wavefront's through the barrier,
+  // which also orders every wavefront's reads of this stage before the refill issued right
+  // after it); then the second 32 k's products with the next stage's first reads between
+  // them (the last step re-reads its own stage, unused)
+  auto products = [&](const Frag& f) {
 #pragma unroll
-    for (int i = 0; i < G::IT / 2; ++i)
-#pragma unroll
-      for (int j = 0; j < G::JT; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fc.a[i], fc.b[j], acc[i][j], 0, 0, 0);
-    // every read of fc done here on both paths, so the products below wait on nothing the
-    // next stage's reads add (s_waitcnt lgkmcnt(0), other counters left alone)
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    if (ks + 2 < nk) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    // the next stage's operand reads (the last step re-reads its own stage, unused), two
-    // at a time between the second half's products: issued as one burst after the barrier,
-    // every wavefront's reads queued on the LDS together (240.6 -> 232.9 us for 32768 rows)
-    load_frag(ks + 1 < nk ? (buf == 2 ? 0 : buf + 1) : buf, fn);
-#pragma unroll
-    for (int i = G::IT / 2; i < G::IT; ++i)
+    for (int i = 0; i < G::IT; ++i)
 #pragma unroll
       for (int j = 0; j < G::JT; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fc.a[i], fc.b[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
     for (int k = 0; k < (G::IT + G::JT) / 2 - 1; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, G::IT / 2 * G::JT - ((G::IT + G::JT) / 2 - 1), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, G::IT * G::JT - ((G::IT + G::JT) / 2 - 1), 0);
   };
   Frag f0, f1;
-  load_frag(0, f0);
-  int buf = 0;
-  for (int ks = 0; ks < nk; ks += 2) {
-    step(ks, buf, f0, f1);
-    buf = buf == 2 ? 0 : buf + 1;
-    if (ks + 1 < nk) {
-      step(ks + 1, buf, f1, f0);
-      buf = buf == 2 ? 0 : buf + 1;
-    }
+  load_frag(0, 0, f0);
+  for (int ks = 0; ks < nk; ++ks) {
+    const int buf = ks & 1;
+    __builtin_amdgcn_sched_barrier(0);
+    load_frag(buf, 1, f1);
+    products(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    if (ks + 1 < nk) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (ks + 2 < nk) issue(ks + 2, buf);
+    load_frag(ks + 1 < nk ? buf ^ 1 : buf, 0, f0);
+    products(f1);
   }
 
   // result tile -> bf16 [row][column] in LDS, one wavefront row (128 rows) at a time

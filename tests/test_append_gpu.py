@@ -94,12 +94,13 @@ def test_exact_inputs_small_widths(n_rows, d):
 
 @pytest.mark.parametrize("shape", [(16, 128, 56), (32, 128, 32)])
 @pytest.mark.parametrize("n_rows,d", [(64, 256), (300, 256), (300, 264), (470, 256), (96, 32),
-                                      (200, 64), (257, 96)])
+                                      (200, 64), (130, 128), (257, 192), (257, 96)])
 def test_exact_inputs_bit_exact_many_rows(shape, n_rows, d):
-    """Prefill-sized appends (the MFMA product; d = 264 is not a multiple of its 32-wide K
-    step and takes the row kernel; d = 32, 64, 96 give one, two and three K steps, shorter
-    than the product's three-stage ring): exact arithmetic, bit-exact pool with sentinels,
-    a ragged last block of rows, permuted pages and scattered positions."""
+    """Prefill-sized appends (the MFMA product; d = 32, 96 and 264 are not multiples of its
+    64-wide K stage and take the row kernel; d = 64, 128, 192 give one, two and three K
+    stages, i.e. the last stage with no next one, one refill, two): exact arithmetic,
+    bit-exact pool with sentinels, a ragged last block of rows, permuted pages and scattered
+    positions."""
     H, dh, r = shape
     L = O.Layout(H, dh, r, 16, O.BF16)
     g = np.random.default_rng(250 + n_rows + d)
@@ -121,9 +122,10 @@ def test_exact_inputs_bit_exact_many_rows(shape, n_rows, d):
 
 
 def test_round_to_nearest_even_ties_many_rows():
-    """The tie rows of the test below, 48 of each, through the MFMA product (d = 288)."""
+    """The tie rows of the test below, 48 of each, through the MFMA product (d = 320, five
+    K stages)."""
     L = O.Layout(16, 128, 56, 16, O.BF16)
-    d, n = 288, 96
+    d, n = 320, 96
     X = np.zeros((n, d), np.float32)
     X[0::2, :257] = 1
     X[1::2, :259] = 1
