@@ -482,19 +482,21 @@ append_gemm_kernel(AppendArgs a, int row_tiles) {
   // which also orders every wavefront's reads of this stage before the refill issued right
   // after it); then the second 32 k's products with the next stage's first reads between
   // them (the last step re-reads its own stage, unused)
+  // the 32 products of 32 k, with the 12 operand reads issued just before them placed one
+  // between consecutive products (two at a time measured 227.9 against 224.7 us)
   auto products = [&](const Frag& f) {
 #pragma unroll
     for (int i = 0; i < G::IT; ++i)
 #pragma unroll
       for (int j = 0; j < G::JT; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
-    for (int k = 0; k < (G::IT + G::JT) / 2 - 1; ++k) {
+    for (int k = 0; k < G::IT + G::JT - 1; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, G::IT * G::JT - ((G::IT + G::JT) / 2 - 1), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, G::IT * G::JT - (G::IT + G::JT - 1), 0);
   };
   Frag f0, f1;
   load_frag(0, 0, f0);
